@@ -1,0 +1,328 @@
+"""Seeded synthetic inputs for one decode step of shared-prefix attention.
+
+This module only draws random numbers and lays them out in memory: the
+logical (unpaged) key/value arrays that the fp64 oracle reads, and the
+shuffled paged pool plus block table that the GPU path reads.  It contains
+none of the attention arithmetic.  It is the only code that the oracle side
+and the GPU side share.
+
+Workload shapes follow the pages' own setups:
+  * "Hydragen: High-Throughput LLM Inference with Shared Prefixes" --
+    CodeLlama-13b end-to-end sweep of the shared prefix from 1K to 16K tokens
+    at a large batch (section "Estimating Throughput Improvements" and the
+    evaluation it summarises), and the two-level few-shot/problem/solution
+    tree (section "Hierarchical Sharing").
+  * "Read Once, Answer Many: Parallel Prompting for Shared-Context LLM
+    Inference" -- one long document read by many question streams with
+    CodeLlama-7B (its evaluation setup).
+  * "Shared Prefix KV Caching, in depth" -- the Llama-3-8B-shaped cache
+    (8 KV heads, head dim 128) and its paged block layout (section "The
+    arithmetic of a decode step").
+
+The datasets those pages measure on are not used: every tensor here is drawn
+from N(0, 1) with a seeded torch CPU generator, at the pages' shapes.
+"""
+from __future__ import annotations
+
+import dataclasses
+import hashlib
+import math
+from typing import List, Optional, Sequence, Tuple
+
+import numpy as np
+import torch
+
+BLOCK_SIZE = 16          # tokens per paged KV block
+SPARE_FRACTION = 0.125   # extra never-referenced pool blocks (NaN-filled traps)
+TAIL_K = 0.0             # key value stored in slots past a sequence's end
+TAIL_V = 8192.0          # value stored there (exact in fp32, fp16 and bf16): a read of a tail slot shows up as a large error
+
+_TORCH_DTYPES = {"f32": torch.float32, "f16": torch.float16, "bf16": torch.bfloat16}
+_ESIZE = {"f32": 4, "f16": 2, "bf16": 2}
+
+
+@dataclasses.dataclass(frozen=True)
+class Config:
+    """Shape of one decode step.
+
+    ``levels`` is a tuple of tree levels; each level is a tuple of prefix nodes
+    ``(len, seq_begin, seq_end)``: sequences ``[seq_begin, seq_end)`` attend
+    that node's ``len`` keys.  Suffix lengths are drawn uniformly from the
+    inclusive integer range ``[suffix_lo, suffix_hi]``.
+    """
+    name: str
+    B: int
+    Hq: int
+    Hkv: int
+    d: int
+    dtype: str
+    levels: Tuple[Tuple[Tuple[int, int, int], ...], ...]
+    suffix_lo: int
+    suffix_hi: int
+    paged: bool = True
+    description: str = ""
+
+    @property
+    def G(self) -> int:
+        return self.Hq // self.Hkv
+
+    @property
+    def max_blocks(self) -> int:
+        return max(1, -(-self.suffix_hi // BLOCK_SIZE))
+
+    @property
+    def esize(self) -> int:
+        return _ESIZE[self.dtype]
+
+    @property
+    def torch_dtype(self) -> torch.dtype:
+        return _TORCH_DTYPES[self.dtype]
+
+
+def tiny_f32() -> Config:
+    return Config("tiny_f32", B=4, Hq=1, Hkv=1, d=64, dtype="f32",
+                  levels=(((512, 0, 4),),), suffix_lo=1, suffix_hi=64, paged=False,
+                  description="tiny fp32 cascade, prefix 512, suffix U[1,64], contiguous suffix")
+
+
+def llama3_8b_gqa() -> Config:
+    return Config("llama3_8b_gqa", B=64, Hq=32, Hkv=8, d=128, dtype="bf16",
+                  levels=(((4096, 0, 64),),), suffix_lo=1, suffix_hi=256,
+                  description="Llama-3-8B-shaped layer, GQA 32/8, prefix 4096, B=64, suffix U[1,256]")
+
+
+def codellama13b_mha(prefix: int = 16384) -> Config:
+    return Config(f"codellama13b_mha_p{prefix}", B=256, Hq=40, Hkv=40, d=128, dtype="f16",
+                  levels=(((prefix, 0, 256),),), suffix_lo=1, suffix_hi=128,
+                  description=f"CodeLlama-13B-shaped layer, MHA 40, fp16, prefix {prefix}, "
+                              f"B=256, suffix U[1,128]")
+
+
+CODELLAMA13B_SWEEP = (1024, 2048, 4096, 8192, 16384)
+
+
+def docqa_codellama7b() -> Config:
+    return Config("docqa_codellama7b", B=256, Hq=32, Hkv=32, d=128, dtype="bf16",
+                  levels=(((16384, 0, 256),),), suffix_lo=64, suffix_hi=512,
+                  description="shared 16384-token document, 256 question streams, "
+                              "CodeLlama-7B-shaped MHA 32, suffix U[64,512]")
+
+
+def two_level_gqa() -> Config:
+    groups = tuple((1024, 32 * g, 32 * g + 32) for g in range(8))
+    return Config("two_level_gqa", B=256, Hq=32, Hkv=8, d=128, dtype="bf16",
+                  levels=(((2048, 0, 256),), groups), suffix_lo=1, suffix_hi=128,
+                  description="two-level tree: global prefix 2048, 8 groups x sub-prefix 1024, "
+                              "32 sequences per group, GQA 32/8, suffix U[1,128]")
+
+
+def all_configs() -> List[Config]:
+    """The five workload shapes, with the CodeLlama-13B sweep at its largest prefix."""
+    return [tiny_f32(), llama3_8b_gqa(), codellama13b_mha(16384), docqa_codellama7b(),
+            two_level_gqa()]
+
+
+def custom(name: str, B: int, Hq: int, Hkv: int, d: int, dtype: str, levels, suffix_lo: int,
+           suffix_hi: int, paged: bool = True) -> Config:
+    """A reduced shape for tests (same structure, smaller sizes)."""
+    lv = tuple(tuple(tuple(int(x) for x in node) for node in level) for level in levels)
+    return Config(name, B, Hq, Hkv, d, dtype, lv, suffix_lo, suffix_hi, paged)
+
+
+@dataclasses.dataclass
+class Node:
+    k: torch.Tensor        # [len][Hkv][d]
+    v: torch.Tensor        # [len][Hkv][d]
+    seq_begin: int
+    seq_end: int
+
+    @property
+    def length(self) -> int:
+        return int(self.k.shape[0])
+
+
+@dataclasses.dataclass
+class Step:
+    """All inputs of one decode step, on the CPU.
+
+    Logical suffix: token ``t`` of sequence ``b`` is row ``suf_offsets[b] + t``
+    of ``suf_k`` / ``suf_v`` (the oracle reads these).  Paged suffix: the same
+    bytes sit at ``k_pool[block_table[b][t // 16]][t % 16]`` (the GPU reads
+    these).  Unreferenced pool blocks are NaN; slots past a sequence's end in
+    its last block hold key 0 and value 8192.
+    """
+    cfg: Config
+    seed: int
+    scale: float
+    q: torch.Tensor
+    levels: List[List[Node]]
+    seq_lens: torch.Tensor
+    suf_offsets: torch.Tensor
+    suf_k: torch.Tensor
+    suf_v: torch.Tensor
+    k_pool: torch.Tensor
+    v_pool: torch.Tensor
+    block_table: torch.Tensor
+
+    @property
+    def num_blocks(self) -> int:
+        return int(self.k_pool.shape[0])
+
+    def suffix(self, b: int) -> Tuple[torch.Tensor, torch.Tensor]:
+        lo, hi = int(self.suf_offsets[b]), int(self.suf_offsets[b + 1])
+        return self.suf_k[lo:hi], self.suf_v[lo:hi]
+
+    def nodes_of(self, b: int) -> List[Node]:
+        """Prefix nodes sequence ``b`` attends, root level first."""
+        out = []
+        for level in self.levels:
+            for n in level:
+                if n.seq_begin <= b < n.seq_end:
+                    out.append(n)
+        return out
+
+    def digest(self) -> str:
+        """Hash of every generated byte (detects generator drift)."""
+        h = hashlib.sha256()
+        for t in [self.q, self.seq_lens, self.suf_k, self.suf_v, self.k_pool, self.v_pool,
+                  self.block_table]:
+            h.update(t.contiguous().view(torch.uint8).numpy().tobytes())
+        for level in self.levels:
+            for n in level:
+                h.update(n.k.contiguous().view(torch.uint8).numpy().tobytes())
+                h.update(n.v.contiguous().view(torch.uint8).numpy().tobytes())
+        return h.hexdigest()
+
+
+def scale_for(d: int) -> float:
+    """The float32 value of 1/sqrt(d), as the kernels receive it."""
+    return float(np.float32(1.0 / math.sqrt(d)))
+
+
+def _randn(g: torch.Generator, shape, dtype: torch.dtype, mult: float = 1.0) -> torch.Tensor:
+    x = torch.randn(*shape, generator=g, dtype=torch.float32)
+    if mult != 1.0:
+        x.mul_(mult)
+    return x.to(dtype)  # round to nearest even
+
+
+def _validate_config(cfg: Config) -> None:
+    if cfg.Hq % cfg.Hkv:
+        raise ValueError("Hq must be a multiple of Hkv")
+    for level in cfg.levels:
+        prev_end = 0
+        for (ln, b0, b1) in level:
+            if not (0 <= b0 < b1 <= cfg.B) or b0 < prev_end or ln < 0:
+                raise ValueError(f"bad prefix node {(ln, b0, b1)} in {cfg.name}")
+            prev_end = b1
+    if not (0 <= cfg.suffix_lo <= cfg.suffix_hi):
+        raise ValueError("bad suffix range")
+
+
+def generate(cfg: Config, seed: int = 0, q_mult: float = 1.0,
+             seq_lens: Optional[Sequence[int]] = None) -> Step:
+    """Draw one decode step's inputs.
+
+    Draw order (all from one ``torch.Generator`` seeded with ``seed``): suffix
+    lengths, Q, each prefix node's K then V (root level first), the logical
+    suffix K then V, then a permutation of the pool blocks.  ``q_mult``
+    scales Q before rounding (a "peaky" variant with a wider score range).
+    ``seq_lens`` overrides the drawn suffix lengths (the draw still happens,
+    so the rest of the stream is unchanged).
+    """
+    _validate_config(cfg)
+    g = torch.Generator().manual_seed(int(seed))
+    dt = cfg.torch_dtype
+    drawn = torch.randint(cfg.suffix_lo, cfg.suffix_hi + 1, (cfg.B,), generator=g,
+                          dtype=torch.int64)
+    if seq_lens is not None:
+        lst = [int(x) for x in seq_lens]
+        if len(lst) != cfg.B or any(x < 0 or x > cfg.max_blocks * BLOCK_SIZE for x in lst):
+            raise ValueError("seq_lens override out of range")
+        drawn = torch.as_tensor(lst, dtype=torch.int64)
+    lens = drawn
+    q = _randn(g, (cfg.B, cfg.Hq, cfg.d), dt, q_mult)
+    levels: List[List[Node]] = []
+    for level in cfg.levels:
+        nodes = []
+        for (ln, b0, b1) in level:
+            k = _randn(g, (ln, cfg.Hkv, cfg.d), dt)
+            v = _randn(g, (ln, cfg.Hkv, cfg.d), dt)
+            nodes.append(Node(k, v, b0, b1))
+        levels.append(nodes)
+    total = int(lens.sum())
+    offsets = torch.zeros(cfg.B + 1, dtype=torch.int64)
+    offsets[1:] = torch.cumsum(lens, 0)
+    suf_k = _randn(g, (total, cfg.Hkv, cfg.d), dt)
+    suf_v = _randn(g, (total, cfg.Hkv, cfg.d), dt)
+
+    nblk = (lens + BLOCK_SIZE - 1) // BLOCK_SIZE
+    used = int(nblk.sum())
+    mb = cfg.max_blocks
+    if cfg.paged:
+        spare = max(1, int(math.ceil(used * SPARE_FRACTION)))
+        num_blocks = used + spare
+        perm = torch.randperm(num_blocks, generator=g).to(torch.int64)
+        table = torch.empty(cfg.B, mb, dtype=torch.int64)
+        pad_block = perm[used] if used < num_blocks else perm[0]
+        table.fill_(int(pad_block))
+        starts = torch.zeros(cfg.B + 1, dtype=torch.int64)
+        starts[1:] = torch.cumsum(nblk, 0)
+        for b in range(cfg.B):
+            n = int(nblk[b])
+            table[b, :n] = perm[int(starts[b]):int(starts[b]) + n]
+    else:
+        # identity table: sequence b owns blocks [b*mb, (b+1)*mb), one contiguous
+        # [mb*16][Hkv][d] suffix region per sequence; unused blocks are the traps.
+        num_blocks = cfg.B * mb + 1
+        torch.randperm(num_blocks, generator=g)  # keep the draw stream uniform
+        table = torch.arange(cfg.B * mb, dtype=torch.int64).view(cfg.B, mb)
+    k_pool = torch.full((num_blocks, BLOCK_SIZE, cfg.Hkv, cfg.d), float("nan"), dtype=dt)
+    v_pool = torch.full((num_blocks, BLOCK_SIZE, cfg.Hkv, cfg.d), float("nan"), dtype=dt)
+    if total:
+        seq_of_tok = torch.repeat_interleave(torch.arange(cfg.B), lens)
+        pos = torch.arange(total) - offsets[seq_of_tok]
+        dest = table[seq_of_tok, pos // BLOCK_SIZE] * BLOCK_SIZE + pos % BLOCK_SIZE
+        k_pool.view(-1, cfg.Hkv, cfg.d)[dest] = suf_k
+        v_pool.view(-1, cfg.Hkv, cfg.d)[dest] = suf_v
+    # finite sentinels in the tail slots of each sequence's last block
+    for b in range(cfg.B):
+        s = int(lens[b])
+        if s % BLOCK_SIZE:
+            blk = int(table[b, s // BLOCK_SIZE])
+            k_pool[blk, s % BLOCK_SIZE:] = TAIL_K
+            v_pool[blk, s % BLOCK_SIZE:] = TAIL_V
+    return Step(cfg=cfg, seed=int(seed), scale=scale_for(cfg.d), q=q, levels=levels,
+                seq_lens=lens.to(torch.int32), suf_offsets=offsets, suf_k=suf_k, suf_v=suf_v,
+                k_pool=k_pool, v_pool=v_pool, block_table=table.to(torch.int32))
+
+
+# ----------------------------------------------------------------------------------------
+# Byte and FLOP accounting (what one step must move / compute; no attention arithmetic)
+# ----------------------------------------------------------------------------------------
+
+def kv_bytes_per_token(Hkv: int, d: int, esize: int, layers: int = 1) -> int:
+    """K and V bytes of one token: 2 (K and V) x layers x Hkv x d x element size."""
+    return 2 * layers * Hkv * d * esize
+
+
+def algorithmic_bytes(cfg: Config, seq_lens: Sequence[int]) -> dict:
+    """Bytes one step must move: every prefix node's KV once, each sequence's suffix KV,
+    Q in, and fp32 O and LSE out.  Partials and metadata are excluded."""
+    tok = kv_bytes_per_token(cfg.Hkv, cfg.d, cfg.esize)
+    prefix = sum(ln for level in cfg.levels for (ln, _, _) in level) * tok
+    suffix = int(sum(int(s) for s in seq_lens)) * tok
+    q = cfg.B * cfg.Hq * cfg.d * cfg.esize
+    out = cfg.B * cfg.Hq * cfg.d * 4 + cfg.B * cfg.Hq * 4
+    return {"prefix": prefix, "suffix": suffix, "q": q, "out": out,
+            "total": prefix + suffix + q + out}
+
+
+def prefix_flops(cfg: Config) -> int:
+    """Dense-product FLOPs of the prefix pass: 2 products (QK^T and PV) x 2 FLOP per MAC x
+    rows x keys x d, with rows = sequences of the node x query heads."""
+    total = 0
+    for level in cfg.levels:
+        for (ln, b0, b1) in level:
+            total += 4 * (b1 - b0) * cfg.Hq * ln * cfg.d
+    return total
