@@ -1,0 +1,299 @@
+#!/usr/bin/env python3
+"""Benchmark of one shared-prefix decode step on one MI355X.
+
+Workload (default): a CodeLlama-13B-shaped attention layer -- 40 query heads =
+40 KV heads, head dim 128, fp16 -- with B=256 sequences sharing a 16384-token
+prefix and each owning a paged suffix of U[1,128] tokens (block size 16,
+shuffled block tables).  Inputs are synthetic N(0,1), drawn from a seeded
+generator and resident in HBM before timing starts.
+
+A "step" is one hp_cascade_step: the prefix pass, the suffix pass and the
+merge, for every (sequence, query head) row.  Prints ONE JSON line with
+steps/s (the metric), query-tokens/s, effective HBM GB/s of the whole step
+against 8 TB/s, the roofline of the dominant kernel (timed with HIP events on
+the stream it runs on), the prefix pass's MFMA fraction, a prefix-length sweep
+(1K..16K), and the fp64 CPU oracle timed on a bounded sample of the same rows.
+"""
+from __future__ import annotations
+
+import argparse
+import ctypes
+import hashlib
+import json
+import math
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+if ROOT not in sys.path:
+    sys.path.insert(0, ROOT)
+
+HBM_PEAK_GBPS = 8000.0          # MI355X HBM3E
+MFMA_F16_PEAK_TFLOPS = 2500.0   # dense fp16/bf16 matrix peak
+MFMA_F32_PEAK_TFLOPS = 157.3
+METRIC = "decode attention steps/s + effective HBM GB/s (% roofline) at B=256, 16K prefix"
+KERNEL_SOURCES = ["prefix_kernel.hip", "suffix_kernel.hip", "merge_kernel.hip", "api.cpp",
+                  "common.hpp"]
+
+
+class HipEvents:
+    """hipEvent_t handles through the HIP runtime (timing of the library's own launches)."""
+
+    def __init__(self):
+        self.rt = ctypes.CDLL("libamdhip64.so")
+        self.rt.hipEventCreate.argtypes = [ctypes.POINTER(ctypes.c_void_p)]
+        self.rt.hipEventElapsedTime.argtypes = [ctypes.POINTER(ctypes.c_float), ctypes.c_void_p,
+                                                ctypes.c_void_p]
+        self.rt.hipEventSynchronize.argtypes = [ctypes.c_void_p]
+        self.rt.hipEventDestroy.argtypes = [ctypes.c_void_p]
+        self.made = []
+
+    def create(self, n):
+        out = []
+        for _ in range(n):
+            h = ctypes.c_void_p()
+            if self.rt.hipEventCreate(ctypes.byref(h)) != 0:
+                raise RuntimeError("hipEventCreate failed")
+            out.append(h.value)
+        self.made += out
+        return out
+
+    def ms(self, a, b) -> float:
+        self.rt.hipEventSynchronize(b)
+        t = ctypes.c_float()
+        if self.rt.hipEventElapsedTime(ctypes.byref(t), a, b) != 0:
+            raise RuntimeError("hipEventElapsedTime failed")
+        return float(t.value)
+
+    def close(self):
+        for h in self.made:
+            self.rt.hipEventDestroy(h)
+        self.made = []
+
+
+def kernel_hash() -> str:
+    h = hashlib.sha256()
+    for f in KERNEL_SOURCES:
+        with open(os.path.join(ROOT, "decode_attention_shared_amd", "csrc", f), "rb") as fh:
+            h.update(fh.read())
+    return h.hexdigest()[:16]
+
+
+def workload(name: str):
+    import workloads
+    if name.startswith("codellama13b_mha_p"):
+        return workloads.codellama13b_mha(int(name.rsplit("p", 1)[1]))
+    for c in workloads.all_configs():
+        if c.name == name:
+            return c
+    raise SystemExit(f"unknown workload {name}")
+
+
+def prepare(cfg, seed: int):
+    import torch
+    import workloads
+    import decode_attention_shared_amd as hp
+    step = workloads.generate(cfg, seed=seed)
+    dev = "cuda:0"
+    levels = [[(n.k.to(dev), n.v.to(dev), n.seq_begin, n.seq_end) for n in lvl]
+              for lvl in step.levels]
+    call = hp.CascadeCall(step.q.to(dev), levels, step.k_pool.to(dev), step.v_pool.to(dev),
+                          step.block_table.to(dev), step.seq_lens.to(dev), step.scale)
+    torch.cuda.synchronize()
+    return step, call
+
+
+def time_steps(call, ev: HipEvents, steps: int, warmup: int):
+    """Returns wall seconds for `steps` back-to-back steps and per-pass event times (ms)."""
+    import torch
+    for _ in range(warmup):
+        call()
+    evs = [ev.create(4) for _ in range(steps)]
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for k in range(steps):
+        call.timed(evs[k])
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    passes = {"prefix": [], "suffix": [], "merge": [], "step": []}
+    for e in evs:
+        passes["prefix"].append(ev.ms(e[0], e[1]))
+        passes["suffix"].append(ev.ms(e[1], e[2]))
+        passes["merge"].append(ev.ms(e[2], e[3]))
+        passes["step"].append(ev.ms(e[0], e[3]))
+    ev.close()
+    return wall, passes
+
+
+def time_cold(call, ev: HipEvents, steps: int) -> float:
+    """Median step time (ms) with 1 GiB written between steps (more than 2x the 256 MB
+    Infinity Cache), so no step starts with its inputs cached."""
+    import torch
+    flush = torch.empty(1 << 28, dtype=torch.float32, device="cuda:0")
+    times = []
+    for _ in range(steps):
+        flush.fill_(1.0)
+        e = ev.create(4)
+        call.timed(e)
+        times.append(ev.ms(e[0], e[3]))
+    ev.close()
+    del flush
+    times.sort()
+    return times[len(times) // 2]
+
+
+def mean(xs):
+    return sum(xs) / max(1, len(xs))
+
+
+def cpu_baseline(step, target_s: float):
+    """The fp64 oracle, as it stands, on a bounded sample of the same rows."""
+    import numpy as np
+    import oracle
+    cfg = step.cfg
+    total = cfg.B * cfg.Hq
+    threads = len(os.sched_getaffinity(0))
+    if os.environ.get("OMP_NUM_THREADS", "").isdigit():
+        threads = min(threads, int(os.environ["OMP_NUM_THREADS"]))
+    rng = np.random.default_rng(0)
+    probe = np.sort(rng.choice(total, size=min(total, max(threads, 32)), replace=False))
+    t0 = time.perf_counter()
+    oracle.step_attention(step, "all", rows=probe, nthreads=threads)
+    per_row = (time.perf_counter() - t0) / len(probe)
+    n = int(min(total, max(len(probe), target_s / max(per_row, 1e-9))))
+    rows = np.sort(rng.choice(total, size=n, replace=False))
+    t0 = time.perf_counter()
+    oracle.step_attention(step, "all", rows=rows, nthreads=threads)
+    el = time.perf_counter() - t0
+    steps_per_s = (n / total) / el
+    return {"value": steps_per_s, "unit": "steps/s", "cores": threads, "kind": "oracle",
+            "sample": f"{n} of {total} (sequence, query head) rows of the same step, seed 0, "
+                      f"{el:.1f} s of fp64 work; steps/s scaled by rows"}
+
+
+def load_traffic(name: str, khash: str):
+    path = os.path.join(ROOT, "profiles", "traffic.json")
+    if not os.path.exists(path):
+        return None
+    with open(path) as f:
+        data = json.load(f)
+    ent = data.get(name)
+    if not ent or ent.get("kernel_hash") != khash:
+        return None
+    return ent
+
+
+def main():
+    ap = argparse.ArgumentParser(description=__doc__.split("\n\n")[0])
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=200)
+    ap.add_argument("--warmup", type=int, default=20)
+    ap.add_argument("--workload", default="codellama13b_mha_p16384")
+    ap.add_argument("--seed", type=int, default=0)
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--cpu-seconds", type=float, default=15.0)
+    ap.add_argument("--no-sweep", action="store_true")
+    ap.add_argument("--sweep-steps", type=int, default=50)
+    ap.add_argument("--profile-only", action="store_true",
+                    help="only run warmup + timed steps (for rocprofv3); no sweep or CPU leg")
+    args = ap.parse_args()
+
+    world = int(os.environ.get("WORLD_SIZE", "1"))
+    if args.gpus != 1 or world != 1:
+        print("bench.py measures one GPU only: this build has no multi-GPU path (it would "
+              "shard by KV head with no exchange; see the design notes). Run with --gpus 1.",
+              file=sys.stderr)
+        sys.exit(2)
+
+    import torch
+    import workloads
+    if not torch.cuda.is_available():
+        raise SystemExit("bench.py needs a GPU")
+
+    cfg = workload(args.workload)
+    print(f"[bench] generating {cfg.name} seed {args.seed}", file=sys.stderr, flush=True)
+    step, call = prepare(cfg, args.seed)
+    ev = HipEvents()
+    print(f"[bench] timing {args.steps} steps after {args.warmup} warmup", file=sys.stderr,
+          flush=True)
+    wall, passes = time_steps(call, ev, args.steps, args.warmup)
+    lens = step.seq_lens.tolist()
+    ab = workloads.algorithmic_bytes(cfg, lens)
+    flops = workloads.prefix_flops(cfg)
+    step_ms = mean(passes["step"])
+    ms_per_step = wall / args.steps * 1e3
+    steps_per_s = args.steps / wall
+    pass_bytes = {"prefix": ab["prefix"] + ab["q"], "suffix": ab["suffix"] + ab["q"],
+                  "merge": ab["out"]}
+    pass_ms = {k: mean(passes[k]) for k in ("prefix", "suffix", "merge")}
+    dom = max(pass_ms, key=pass_ms.get)
+    achieved = pass_bytes[dom] / (pass_ms[dom] * 1e-3) / 1e9
+    khash = kernel_hash()
+    traffic = load_traffic(f"{cfg.name}:{dom}", khash)
+    mfma_peak = MFMA_F32_PEAK_TFLOPS if cfg.dtype == "f32" else MFMA_F16_PEAK_TFLOPS
+    prefix_tflops = flops / (pass_ms["prefix"] * 1e-3) / 1e12
+    eff = ab["total"] / (step_ms * 1e-3) / 1e9
+    result = {
+        "metric": METRIC,
+        "value": round(steps_per_s, 2),
+        "unit": "steps/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms_per_step, 4),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "f16" if cfg.dtype == "f16" else cfg.dtype,
+        "data": "synthetic N(0,1), seeded; inputs resident in HBM",
+        "config": {"workload": cfg.name, "B": cfg.B, "Hq": cfg.Hq, "Hkv": cfg.Hkv, "d": cfg.d,
+                   "prefix_tokens": [n[0] for lvl in cfg.levels for n in lvl],
+                   "suffix": f"U[{cfg.suffix_lo},{cfg.suffix_hi}] paged, block 16",
+                   "seed": args.seed, "parallelism": "single GPU"},
+        "query_tokens_per_s": round(steps_per_s * cfg.B, 1),
+        "step_ms_events": round(step_ms, 4),
+        "effective_gbps": round(eff, 1),
+        "hbm_roofline_frac": round(eff / HBM_PEAK_GBPS, 4),
+        "algorithmic_bytes": ab,
+        "pass_ms": {k: round(v, 4) for k, v in pass_ms.items()},
+        "prefix_mfma_frac": round(prefix_tflops / mfma_peak, 4),
+        "prefix_tflops": round(prefix_tflops, 1),
+        "roofline": {"kernel": dom, "bound": "hbm", "achieved": round(achieved, 1),
+                     "peak": HBM_PEAK_GBPS, "unit": "GB/s",
+                     "frac": round(achieved / HBM_PEAK_GBPS, 4),
+                     "traffic": (traffic or {}).get("bytes_per_launch"),
+                     "algorithmic_bytes_per_launch": pass_bytes[dom],
+                     "kernel_hash": khash},
+    }
+    if not args.profile_only:
+        print("[bench] cold (cache-flushed) steps", file=sys.stderr, flush=True)
+        result["cold_step_ms_median"] = round(time_cold(call, ev, 20), 4)
+    del call
+    torch.cuda.empty_cache()
+    if not args.profile_only and not args.no_sweep and cfg.name.startswith("codellama13b"):
+        sweep = []
+        for P in workloads.CODELLAMA13B_SWEEP:
+            c = workloads.codellama13b_mha(P)
+            print(f"[bench] sweep prefix {P}", file=sys.stderr, flush=True)
+            st, cl = prepare(c, args.seed)
+            w, ps = time_steps(cl, ev, args.sweep_steps, 5)
+            sm = mean(ps["step"])
+            b = workloads.algorithmic_bytes(c, st.seq_lens.tolist())["total"]
+            sweep.append({"prefix": P, "steps_per_s": round(args.sweep_steps / w, 1),
+                          "step_ms_events": round(sm, 4),
+                          "effective_gbps": round(b / (sm * 1e-3) / 1e9, 1),
+                          "hbm_roofline_frac": round(b / (sm * 1e-3) / 1e9 / HBM_PEAK_GBPS, 4),
+                          "pass_ms": {k: round(mean(ps[k]), 4) for k in ("prefix", "suffix",
+                                                                         "merge")}})
+            del cl, st
+            torch.cuda.empty_cache()
+        result["prefix_sweep"] = sweep
+    if not args.profile_only and not args.no_cpu_baseline:
+        print("[bench] CPU oracle baseline", file=sys.stderr, flush=True)
+        result["cpu_baseline"] = cpu_baseline(step, args.cpu_seconds)
+    print(json.dumps(result), flush=True)
+
+
+if __name__ == "__main__":
+    main()

@@ -1,0 +1,560 @@
+// Host side of the C ABI declared in hp_attn.h: argument and tree
+// validation, work partitioning, workspace layout and kernel launches.
+// No allocation, no synchronisation, no host-to-device copies: everything a
+// kernel needs goes in its by-value arguments, so every entry point can be
+// captured into a HIP graph.
+#include <hip/hip_runtime.h>
+
+#include <algorithm>
+#include <cmath>
+#include <cstdint>
+#include <cstring>
+
+#include "common.hpp"
+#include "hp_attn.h"
+
+namespace hp {
+hipError_t launch_prefix(const PrefixArgs &a, int dtype, int d, int nw, int wgs, hipStream_t s);
+hipError_t launch_suffix(const SuffixArgs &a, int dtype, int d, int G, hipStream_t s);
+hipError_t launch_merge(const MergeArgs &a, int d, hipStream_t s);
+}  // namespace hp
+
+namespace {
+
+using namespace hp;
+
+thread_local int32_t g_last_hip_error = 0;
+
+constexpr int kTileKeys = 64;           // keys per prefix tile (matches the kernels)
+constexpr int kTargetWgs = 512;         // prefix workgroups aimed for per launch (2 per CU)
+constexpr int kMinTilesPerSplit = 4;    // keep >= 256 keys per split: partial traffic stays small
+constexpr int kSuffixSplitBlocks = 8;   // 128 suffix tokens per suffix work item
+constexpr size_t kWsAlign = 256;
+
+inline size_t round_up(size_t x, size_t a) { return (x + a - 1) / a * a; }
+inline int64_t cdiv(int64_t a, int64_t b) { return (a + b - 1) / b; }
+inline bool aligned16(const void *p) { return ((uintptr_t)p & 15u) == 0; }
+inline int esize(int dtype) { return dtype == HP_F32 ? 4 : 2; }
+
+hp_status fail_hip(hipError_t e) {
+    g_last_hip_error = (int32_t)e;
+    return HP_ERR_HIP;
+}
+
+hp_status check_query(const hp_query *q) {
+    if (!q) return HP_ERR_NULL;
+    if (q->B < 0 || q->Hq <= 0 || q->Hkv <= 0 || q->Hq % q->Hkv != 0) return HP_ERR_INVALID_ARG;
+    if (q->dtype < HP_F32 || q->dtype > HP_BF16) return HP_ERR_INVALID_ARG;
+    if (!std::isfinite(q->scale)) return HP_ERR_INVALID_ARG;
+    if (q->d != 64 && q->d != 128) return HP_ERR_UNSUPPORTED;
+    const int G = q->Hq / q->Hkv;
+    if (G > 8 || (G & (G - 1)) != 0) return HP_ERR_UNSUPPORTED;
+    if (q->B > 0 && !q->q) return HP_ERR_NULL;
+    if (q->B > 0 && !aligned16(q->q)) return HP_ERR_INVALID_ARG;
+    return HP_OK;
+}
+
+hp_status check_node(const hp_query *q, const hp_prefix_node *n) {
+    if (!n) return HP_ERR_NULL;
+    if (n->len < 0) return HP_ERR_INVALID_ARG;
+    if (n->seq_begin < 0 || n->seq_begin >= n->seq_end || n->seq_end > q->B)
+        return HP_ERR_INVALID_ARG;
+    if (n->len == 0) return HP_OK;
+    if (!n->k || !n->v) return HP_ERR_NULL;
+    if (!aligned16(n->k) || !aligned16(n->v)) return HP_ERR_INVALID_ARG;
+    const int64_t vec = 16 / esize(q->dtype);  // elements per 16 bytes
+    if (n->stride_tok <= 0 || n->stride_head <= 0 || n->stride_tok % vec || n->stride_head % vec)
+        return HP_ERR_INVALID_ARG;
+    if (q->Hkv > 1 && n->stride_head < q->d) return HP_ERR_INVALID_ARG;  // heads would overlap
+    return HP_OK;
+}
+
+hp_status check_tree(const hp_query *q, const hp_prefix_tree *t, int *total_nodes) {
+    *total_nodes = 0;
+    if (!t) return HP_OK;
+    if (t->num_levels < 0 || t->num_levels > HP_MAX_LEVELS) return HP_ERR_UNSUPPORTED;
+    int total = 0;
+    for (int l = 0; l < t->num_levels; ++l) {
+        if (t->nodes_per_level[l] < 0) return HP_ERR_INVALID_ARG;
+        total += t->nodes_per_level[l];
+        if (total > HP_MAX_NODES) return HP_ERR_UNSUPPORTED;
+    }
+    if (total > 0 && !t->nodes) return HP_ERR_NULL;
+    int idx = 0;
+    for (int l = 0; l < t->num_levels; ++l) {
+        int prev_end = 0;
+        for (int i = 0; i < t->nodes_per_level[l]; ++i, ++idx) {
+            const hp_prefix_node *n = &t->nodes[idx];
+            hp_status st = check_node(q, n);
+            if (st != HP_OK) return st;
+            if (n->seq_begin < prev_end) return HP_ERR_INVALID_ARG;  // unsorted or overlapping
+            prev_end = n->seq_end;
+        }
+    }
+    *total_nodes = total;
+    return HP_OK;
+}
+
+hp_status check_kv(const hp_query *q, const hp_paged_kv *kv) {
+    if (!kv) return HP_ERR_NULL;
+    if (kv->block_size != HP_BLOCK_SIZE) return HP_ERR_UNSUPPORTED;
+    if (kv->max_blocks < 1 || kv->num_blocks < 1) return HP_ERR_INVALID_ARG;
+    if ((int64_t)kv->max_blocks * HP_BLOCK_SIZE > INT32_MAX) return HP_ERR_INVALID_ARG;
+    if (!kv->k_pool || !kv->v_pool || !kv->block_table || !kv->seq_lens) return HP_ERR_NULL;
+    if (!aligned16(kv->k_pool) || !aligned16(kv->v_pool)) return HP_ERR_INVALID_ARG;
+    if (((uintptr_t)kv->block_table & 3u) || ((uintptr_t)kv->seq_lens & 3u))
+        return HP_ERR_INVALID_ARG;
+    return HP_OK;
+}
+
+hp_status check_out(const float *o, const float *lse) {
+    if (!o) return HP_ERR_NULL;
+    if (!aligned16(o) || ((uintptr_t)lse & 3u)) return HP_ERR_INVALID_ARG;
+    return HP_OK;
+}
+
+// ---------------------------------------------------------------------------
+// Work partitioning
+// ---------------------------------------------------------------------------
+
+int choose_nw(int64_t M) { return M <= 32 ? 1 : M <= 64 ? 2 : M <= 128 ? 4 : 8; }
+
+struct NodePlan {
+    int nsplit = 1, tiles_per_split = 0, rowblocks = 1, units_padded = 0, wgs = 0;
+    int64_t rows = 0;  // (seq_end - seq_begin) * Hq output rows
+};
+
+// Plans every node of one launch (a tree level) together: the split count
+// spreads the launch over about kTargetWgs workgroups.
+struct LevelPlan {
+    int nw = 1;
+    int first = 0, count = 0;
+    NodePlan nodes[HP_MAX_NODES];
+};
+
+void plan_level(const hp_query &q, const hp_prefix_node *nodes, int count, LevelPlan &lp) {
+    const int G = q.Hq / q.Hkv;
+    int64_t maxM = 1;
+    for (int i = 0; i < count; ++i)
+        maxM = std::max<int64_t>(maxM, (int64_t)(nodes[i].seq_end - nodes[i].seq_begin) * G);
+    lp.nw = choose_nw(maxM);
+    const int64_t rows_per_wg = 32 * lp.nw;
+    int64_t base = 0;
+    for (int i = 0; i < count; ++i) {
+        const int64_t M = (int64_t)(nodes[i].seq_end - nodes[i].seq_begin) * G;
+        lp.nodes[i].rowblocks = (int)cdiv(M, rows_per_wg);
+        base += (int64_t)q.Hkv * lp.nodes[i].rowblocks;
+    }
+    const int64_t want = std::max<int64_t>(1, cdiv(kTargetWgs, std::max<int64_t>(1, base)));
+    for (int i = 0; i < count; ++i) {
+        NodePlan &np = lp.nodes[i];
+        const int64_t tiles = cdiv(nodes[i].len, kTileKeys);
+        int64_t ns = std::min<int64_t>(want, std::max<int64_t>(1, tiles / kMinTilesPerSplit));
+        ns = std::max<int64_t>(1, ns);
+        np.tiles_per_split = tiles ? (int)cdiv(tiles, ns) : 0;
+        np.nsplit = tiles ? (int)cdiv(tiles, np.tiles_per_split) : 1;
+        const int64_t units = (int64_t)q.Hkv * np.nsplit;
+        np.units_padded = (int)(np.rowblocks > 1 ? round_up(units, 8) : units);
+        np.wgs = np.units_padded * np.rowblocks;
+        np.rows = (int64_t)(nodes[i].seq_end - nodes[i].seq_begin) * q.Hq;
+    }
+    lp.count = count;
+}
+
+size_t node_ws_bytes(const NodePlan &np, int d) {
+    return round_up((size_t)np.nsplit * np.rows * d * sizeof(float), kWsAlign) +
+           round_up((size_t)np.nsplit * np.rows * sizeof(float), kWsAlign);
+}
+
+struct SuffixPlan {
+    int bps = kSuffixSplitBlocks, nsplit = 1;
+};
+
+SuffixPlan plan_suffix(const hp_paged_kv &kv) {
+    SuffixPlan sp;
+    sp.nsplit = (int)cdiv(kv.max_blocks, sp.bps);
+    return sp;
+}
+
+size_t suffix_ws_bytes(const hp_query &q, const SuffixPlan &sp) {
+    const size_t rows = (size_t)q.B * q.Hq;
+    return round_up((size_t)sp.nsplit * rows * q.d * sizeof(float), kWsAlign) +
+           round_up((size_t)sp.nsplit * rows * sizeof(float), kWsAlign);
+}
+
+PrefixArgs base_prefix_args(const hp_query &q) {
+    PrefixArgs a;
+    std::memset(&a, 0, sizeof a);
+    a.q = q.q;
+    a.B = q.B;
+    a.Hq = q.Hq;
+    a.Hkv = q.Hkv;
+    a.G = q.Hq / q.Hkv;
+    a.scale_log2 = (float)((double)q.scale * 1.4426950408889634);
+    return a;
+}
+
+PrefixNodeArg node_arg(const hp_prefix_node &n, const NodePlan &np, int wg_begin, RowDest dest) {
+    PrefixNodeArg na;
+    std::memset(&na, 0, sizeof na);
+    na.k = n.k;
+    na.v = n.v;
+    na.stride_tok = n.stride_tok;
+    na.stride_head = n.stride_head;
+    na.len = n.len;
+    na.seq_begin = n.seq_begin;
+    na.seq_end = n.seq_end;
+    na.nsplit = np.nsplit;
+    na.tiles_per_split = np.tiles_per_split;
+    na.rowblocks = np.rowblocks;
+    na.units_padded = np.units_padded;
+    na.wg_begin = wg_begin;
+    na.dest = dest;
+    return na;
+}
+
+// Launch the prefix pass for nodes [0, count) of one level, at most
+// kMaxLaunchNodes per launch.  dests[i] is where node i's results go.
+hp_status run_level(const hp_query &q, const hp_prefix_node *nodes, const LevelPlan &lp,
+                    const RowDest *dests, hipStream_t s) {
+    for (int c0 = 0; c0 < lp.count; c0 += kMaxLaunchNodes) {
+        PrefixArgs a = base_prefix_args(q);
+        int wg = 0;
+        const int c1 = std::min(lp.count, c0 + kMaxLaunchNodes);
+        for (int i = c0; i < c1; ++i) {
+            a.nodes[a.num_nodes++] = node_arg(nodes[i], lp.nodes[i], wg, dests[i]);
+            wg += lp.nodes[i].wgs;
+        }
+        if (wg == 0) continue;
+        hipError_t e = launch_prefix(a, q.dtype, q.d, lp.nw, wg, s);
+        if (e != hipSuccess) return fail_hip(e);
+    }
+    return HP_OK;
+}
+
+SuffixArgs suffix_args(const hp_query &q, const hp_paged_kv &kv, const SuffixPlan &sp,
+                       RowDest dest) {
+    SuffixArgs a;
+    std::memset(&a, 0, sizeof a);
+    a.q = q.q;
+    a.k_pool = kv.k_pool;
+    a.v_pool = kv.v_pool;
+    a.table = kv.block_table;
+    a.lens = kv.seq_lens;
+    a.B = q.B;
+    a.Hq = q.Hq;
+    a.Hkv = q.Hkv;
+    a.max_blocks = kv.max_blocks;
+    a.num_blocks = kv.num_blocks;
+    a.blocks_per_split = sp.bps;
+    a.nsplit = sp.nsplit;
+    a.scale_log2 = (float)((double)q.scale * 1.4426950408889634);
+    a.dest = dest;
+    return a;
+}
+
+// Plan of a whole cascade step (shared by the size query and the run).
+struct CascadePlan {
+    int total_nodes = 0;
+    int num_levels = 0;
+    LevelPlan levels[HP_MAX_LEVELS];
+    bool has_suffix = false;
+    SuffixPlan sp;
+    size_t node_off[HP_MAX_NODES];
+    size_t suffix_off = 0;
+    size_t bytes = 0;
+};
+
+hp_status plan_cascade(const hp_query *q, const hp_prefix_tree *tree, const hp_paged_kv *kv,
+                       CascadePlan &cp) {
+    hp_status st = check_query(q);
+    if (st != HP_OK) return st;
+    st = check_tree(q, tree, &cp.total_nodes);
+    if (st != HP_OK) return st;
+    if (kv) {
+        st = check_kv(q, kv);
+        if (st != HP_OK) return st;
+    }
+    size_t off = 0;
+    int idx = 0;
+    cp.num_levels = tree ? tree->num_levels : 0;
+    for (int l = 0; l < cp.num_levels; ++l) {
+        LevelPlan &lp = cp.levels[l];
+        lp.first = idx;
+        plan_level(*q, tree->nodes + idx, tree->nodes_per_level[l], lp);
+        for (int i = 0; i < lp.count; ++i) {
+            cp.node_off[idx + i] = off;
+            off += node_ws_bytes(lp.nodes[i], q->d);
+        }
+        idx += lp.count;
+    }
+    cp.has_suffix = kv != nullptr;
+    if (kv) {
+        cp.sp = plan_suffix(*kv);
+        cp.suffix_off = off;
+        off += suffix_ws_bytes(*q, cp.sp);
+    }
+    cp.bytes = off;
+    return HP_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+const char *hp_status_string(hp_status s) {
+    switch (s) {
+    case HP_OK: return "ok";
+    case HP_ERR_NULL: return "a required pointer is NULL";
+    case HP_ERR_INVALID_ARG: return "invalid argument (size, range, stride or alignment)";
+    case HP_ERR_UNSUPPORTED: return "unsupported (outside the implemented domain)";
+    case HP_ERR_WORKSPACE: return "workspace missing or too small";
+    case HP_ERR_HIP: return "HIP launch failed";
+    default: return "unknown status";
+    }
+}
+
+int32_t hp_last_hip_error(void) { return g_last_hip_error; }
+
+const char *hp_version(void) { return "hp_attn 0.1 gfx950"; }
+
+// ------------------------------- prefix -----------------------------------
+
+hp_status hp_prefix_attn_workspace_size(const hp_query *q, const hp_prefix_node *node,
+                                        size_t *bytes) {
+    if (!bytes) return HP_ERR_NULL;
+    hp_status st = check_query(q);
+    if (st != HP_OK) return st;
+    st = check_node(q, node);
+    if (st != HP_OK) return st;
+    LevelPlan lp;
+    plan_level(*q, node, 1, lp);
+    *bytes = lp.nodes[0].nsplit > 1 ? node_ws_bytes(lp.nodes[0], q->d) : 0;
+    return HP_OK;
+}
+
+hp_status hp_prefix_attn(const hp_query *q, const hp_prefix_node *node, float *o, float *lse,
+                         void *ws, size_t ws_bytes, void *stream) {
+    hp_status st = check_query(q);
+    if (st != HP_OK) return st;
+    st = check_node(q, node);
+    if (st != HP_OK) return st;
+    st = check_out(o, lse);
+    if (st != HP_OK) return st;
+    LevelPlan lp;
+    plan_level(*q, node, 1, lp);
+    const NodePlan &np = lp.nodes[0];
+    hipStream_t s = (hipStream_t)stream;
+    if (np.nsplit == 1) {
+        const RowDest dest{o, lse, 0, 0, 0};
+        return run_level(*q, node, lp, &dest, s);
+    }
+    const size_t need = node_ws_bytes(np, q->d);
+    if (!ws || ws_bytes < need || !aligned16(ws)) return HP_ERR_WORKSPACE;
+    float *wo = (float *)ws;
+    float *wl = (float *)((char *)ws + round_up((size_t)np.nsplit * np.rows * q->d * 4, kWsAlign));
+    const RowDest dest{wo, wl, np.rows * q->d, np.rows, node->seq_begin};
+    st = run_level(*q, node, lp, &dest, s);
+    if (st != HP_OK) return st;
+    MergeArgs m;
+    std::memset(&m, 0, sizeof m);
+    m.src[0] = MergeSrc{wo, wl, np.rows * q->d, np.rows, np.nsplit, 0, node->seq_begin,
+                        node->seq_end};
+    m.nsrc = 1;
+    m.Hq = q->Hq;
+    m.row_b0 = node->seq_begin;
+    m.row_b1 = node->seq_end;
+    m.o = o;
+    m.lse = lse;
+    hipError_t e = launch_merge(m, q->d, s);
+    return e == hipSuccess ? HP_OK : fail_hip(e);
+}
+
+// ------------------------------- suffix -----------------------------------
+
+hp_status hp_suffix_decode_workspace_size(const hp_query *q, const hp_paged_kv *kv,
+                                          size_t *bytes) {
+    if (!bytes) return HP_ERR_NULL;
+    hp_status st = check_query(q);
+    if (st != HP_OK) return st;
+    st = check_kv(q, kv);
+    if (st != HP_OK) return st;
+    const SuffixPlan sp = plan_suffix(*kv);
+    *bytes = sp.nsplit > 1 ? suffix_ws_bytes(*q, sp) : 0;
+    return HP_OK;
+}
+
+hp_status hp_suffix_decode(const hp_query *q, const hp_paged_kv *kv, float *o, float *lse,
+                           void *ws, size_t ws_bytes, void *stream) {
+    hp_status st = check_query(q);
+    if (st != HP_OK) return st;
+    st = check_kv(q, kv);
+    if (st != HP_OK) return st;
+    st = check_out(o, lse);
+    if (st != HP_OK) return st;
+    if (q->B == 0) return HP_OK;
+    const SuffixPlan sp = plan_suffix(*kv);
+    hipStream_t s = (hipStream_t)stream;
+    if (sp.nsplit == 1) {
+        const SuffixArgs a = suffix_args(*q, *kv, sp, RowDest{o, lse, 0, 0, 0});
+        hipError_t e = launch_suffix(a, q->dtype, q->d, q->Hq / q->Hkv, s);
+        return e == hipSuccess ? HP_OK : fail_hip(e);
+    }
+    const size_t need = suffix_ws_bytes(*q, sp);
+    if (!ws || ws_bytes < need || !aligned16(ws)) return HP_ERR_WORKSPACE;
+    const int64_t rows = (int64_t)q->B * q->Hq;
+    float *wo = (float *)ws;
+    float *wl = (float *)((char *)ws + round_up((size_t)sp.nsplit * rows * q->d * 4, kWsAlign));
+    const SuffixArgs a = suffix_args(*q, *kv, sp, RowDest{wo, wl, rows * q->d, rows, 0});
+    hipError_t e = launch_suffix(a, q->dtype, q->d, q->Hq / q->Hkv, s);
+    if (e != hipSuccess) return fail_hip(e);
+    MergeArgs m;
+    std::memset(&m, 0, sizeof m);
+    m.src[0] = MergeSrc{wo, wl, rows * q->d, rows, sp.nsplit, sp.bps, 0, q->B};
+    m.nsrc = 1;
+    m.lens = kv->seq_lens;
+    m.max_len = kv->max_blocks * HP_BLOCK_SIZE;
+    m.Hq = q->Hq;
+    m.row_b0 = 0;
+    m.row_b1 = q->B;
+    m.o = o;
+    m.lse = lse;
+    e = launch_merge(m, q->d, s);
+    return e == hipSuccess ? HP_OK : fail_hip(e);
+}
+
+// -------------------------------- merge -----------------------------------
+
+hp_status hp_lse_merge(int32_t n, const float *const *o_in, const float *const *lse_in, float *o,
+                       float *lse, int64_t rows, int32_t d, void *stream) {
+    if (!o_in || !lse_in || !o) return HP_ERR_NULL;
+    if (n < 1 || n > HP_MAX_MERGE || rows < 0) return HP_ERR_INVALID_ARG;
+    if (d != 64 && d != 128) return HP_ERR_UNSUPPORTED;
+    if (!aligned16(o) || ((uintptr_t)lse & 3u)) return HP_ERR_INVALID_ARG;
+    const uintptr_t olo = (uintptr_t)o, ohi = olo + (uintptr_t)rows * d * sizeof(float);
+    const uintptr_t llo = (uintptr_t)lse, lhi = llo + (uintptr_t)rows * sizeof(float);
+    for (int i = 0; i < n; ++i) {
+        if (!o_in[i] || !lse_in[i]) return HP_ERR_NULL;
+        if (!aligned16(o_in[i]) || ((uintptr_t)lse_in[i] & 3u)) return HP_ERR_INVALID_ARG;
+        const uintptr_t a0 = (uintptr_t)o_in[i], a1 = a0 + (uintptr_t)rows * d * sizeof(float);
+        const uintptr_t b0 = (uintptr_t)lse_in[i], b1 = b0 + (uintptr_t)rows * sizeof(float);
+        auto overlap = [](uintptr_t x0, uintptr_t x1, uintptr_t y0, uintptr_t y1) {
+            return x0 < y1 && y0 < x1;
+        };
+        if (rows > 0 && (overlap(olo, ohi, a0, a1) || overlap(olo, ohi, b0, b1) ||
+                         (lse && (overlap(llo, lhi, a0, a1) || overlap(llo, lhi, b0, b1)))))
+            return HP_ERR_INVALID_ARG;
+    }
+    if (rows == 0) return HP_OK;
+    MergeArgs m;
+    std::memset(&m, 0, sizeof m);
+    for (int i = 0; i < n; ++i) m.src[i] = MergeSrc{o_in[i], lse_in[i], 0, 0, 1, 0, 0, rows};
+    m.nsrc = n;
+    m.Hq = 1;
+    m.row_b0 = 0;
+    m.row_b1 = rows;
+    m.o = o;
+    m.lse = lse;
+    hipError_t e = launch_merge(m, d, (hipStream_t)stream);
+    return e == hipSuccess ? HP_OK : fail_hip(e);
+}
+
+// ------------------------------- cascade ----------------------------------
+
+hp_status hp_cascade_workspace_size(const hp_query *q, const hp_prefix_tree *tree,
+                                    const hp_paged_kv *kv, size_t *bytes) {
+    if (!bytes) return HP_ERR_NULL;
+    CascadePlan cp;
+    hp_status st = plan_cascade(q, tree, kv, cp);
+    if (st != HP_OK) return st;
+    *bytes = cp.bytes;
+    return HP_OK;
+}
+
+}  // extern "C"
+
+namespace {
+
+hp_status record(void *const *events, int i, hipStream_t s) {
+    if (!events || !events[i]) return HP_OK;
+    hipError_t e = hipEventRecord((hipEvent_t)events[i], s);
+    return e == hipSuccess ? HP_OK : fail_hip(e);
+}
+
+hp_status cascade_impl(const hp_query *q, const hp_prefix_tree *tree, const hp_paged_kv *kv,
+                       float *o, float *lse, void *ws, size_t ws_bytes, void *stream,
+                       void *const *events) {
+    CascadePlan cp;
+    hp_status st = plan_cascade(q, tree, kv, cp);
+    if (st != HP_OK) return st;
+    st = check_out(o, lse);
+    if (st != HP_OK) return st;
+    if (q->B == 0) return HP_OK;
+    if (cp.bytes > 0 && (!ws || ws_bytes < cp.bytes || !aligned16(ws))) return HP_ERR_WORKSPACE;
+    hipStream_t s = (hipStream_t)stream;
+    char *base = (char *)ws;
+    if ((st = record(events, 0, s)) != HP_OK) return st;
+
+    MergeArgs m;
+    std::memset(&m, 0, sizeof m);
+    // Prefix pass, level by level (root first).
+    for (int l = 0; l < cp.num_levels; ++l) {
+        const LevelPlan &lp = cp.levels[l];
+        RowDest dests[HP_MAX_NODES];
+        for (int i = 0; i < lp.count; ++i) {
+            const NodePlan &np = lp.nodes[i];
+            const hp_prefix_node &nd = tree->nodes[lp.first + i];
+            float *wo = (float *)(base + cp.node_off[lp.first + i]);
+            float *wl = (float *)((char *)wo +
+                                  round_up((size_t)np.nsplit * np.rows * q->d * 4, kWsAlign));
+            dests[i] = RowDest{wo, wl, np.rows * q->d, np.rows, nd.seq_begin};
+            m.src[m.nsrc++] = MergeSrc{wo, wl, np.rows * q->d, np.rows, np.nsplit, 0,
+                                       nd.seq_begin, nd.seq_end};
+        }
+        st = run_level(*q, tree->nodes + lp.first, lp, dests, s);
+        if (st != HP_OK) return st;
+    }
+    if ((st = record(events, 1, s)) != HP_OK) return st;
+    // Suffix pass.
+    if (cp.has_suffix) {
+        const int64_t rows = (int64_t)q->B * q->Hq;
+        float *wo = (float *)(base + cp.suffix_off);
+        float *wl = (float *)((char *)wo +
+                              round_up((size_t)cp.sp.nsplit * rows * q->d * 4, kWsAlign));
+        const SuffixArgs a = suffix_args(*q, *kv, cp.sp, RowDest{wo, wl, rows * q->d, rows, 0});
+        hipError_t e = launch_suffix(a, q->dtype, q->d, q->Hq / q->Hkv, s);
+        if (e != hipSuccess) return fail_hip(e);
+        m.src[m.nsrc++] = MergeSrc{wo, wl, rows * q->d, rows, cp.sp.nsplit, cp.sp.bps, 0, q->B};
+        m.lens = kv->seq_lens;
+        m.max_len = kv->max_blocks * HP_BLOCK_SIZE;
+    }
+    if ((st = record(events, 2, s)) != HP_OK) return st;
+    // One n-way merge of every level's splits and the suffix splits.
+    m.Hq = q->Hq;
+    m.row_b0 = 0;
+    m.row_b1 = q->B;
+    m.o = o;
+    m.lse = lse;
+    hipError_t e = launch_merge(m, q->d, s);
+    if (e != hipSuccess) return fail_hip(e);
+    return record(events, 3, s);
+}
+
+}  // namespace
+
+extern "C" {
+
+hp_status hp_cascade_step(const hp_query *q, const hp_prefix_tree *tree, const hp_paged_kv *kv,
+                          float *o, float *lse, void *ws, size_t ws_bytes, void *stream) {
+    return cascade_impl(q, tree, kv, o, lse, ws, ws_bytes, stream, nullptr);
+}
+
+hp_status hp_cascade_step_timed(const hp_query *q, const hp_prefix_tree *tree,
+                                const hp_paged_kv *kv, float *o, float *lse, void *ws,
+                                size_t ws_bytes, void *stream, void *const *events,
+                                int32_t n_events) {
+    if (n_events != 0 && n_events != 4) return HP_ERR_INVALID_ARG;
+    return cascade_impl(q, tree, kv, o, lse, ws, ws_bytes, stream, n_events ? events : nullptr);
+}
+
+}  // extern "C"

@@ -1,0 +1,161 @@
+// Device helpers and launch-argument structs shared by the gfx950 kernels and
+// the host entry points.  Internal to the library (not part of the C ABI).
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+#include "hp_attn.h"
+
+namespace hp {
+
+typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef _Float16 f16x8 __attribute__((ext_vector_type(8)));
+typedef float f32x16 __attribute__((ext_vector_type(16)));
+typedef float f32x4 __attribute__((ext_vector_type(4)));
+typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
+
+constexpr float kLog2e = 1.4426950408889634f;
+constexpr float kLn2 = 0.6931471805599453f;
+constexpr int kWave = 64;
+constexpr int kBlock = HP_BLOCK_SIZE;
+
+// ---------------------------------------------------------------------------
+// Launch arguments.  Everything a kernel needs travels by value, so a launch
+// reads no host memory and needs no host-to-device copy (graph-capture safe).
+// ---------------------------------------------------------------------------
+
+// Destination of a pass's per-row results: normalised O and natural-log LSE.
+// Row (b, h) of split s lands at o + s*o_split + ((b - row_base)*Hq + h)*d.
+struct RowDest {
+    float *o;
+    float *lse;          // may be null only for direct writes with lse == NULL
+    int64_t o_split;     // elements between splits
+    int64_t lse_split;
+    int32_t row_base;
+};
+
+constexpr int kMaxLaunchNodes = 16;
+
+struct PrefixNodeArg {
+    const void *k;
+    const void *v;
+    int64_t stride_tok;
+    int64_t stride_head;
+    int32_t len;
+    int32_t seq_begin;
+    int32_t seq_end;
+    int32_t nsplit;           // key-range splits
+    int32_t tiles_per_split;  // 64-key tiles per split
+    int32_t rowblocks;        // row blocks per (KV head, split)
+    int32_t units_padded;     // (KV head, split) units, rounded up to a multiple of 8 when rowblocks > 1
+    int32_t wg_begin;         // first workgroup of this node in the launch
+    RowDest dest;
+};
+
+struct PrefixArgs {
+    const void *q;
+    int32_t B, Hq, Hkv, G;
+    float scale_log2;         // scale * log2(e): scores go straight to the exp2 domain
+    int32_t num_nodes;
+    PrefixNodeArg nodes[kMaxLaunchNodes];
+};
+
+struct SuffixArgs {
+    const void *q;
+    const void *k_pool;
+    const void *v_pool;
+    const int32_t *table;
+    const int32_t *lens;
+    int32_t B, Hq, Hkv;
+    int32_t max_blocks, num_blocks;
+    int32_t blocks_per_split, nsplit;
+    float scale_log2;
+    RowDest dest;
+};
+
+constexpr int kMaxMergeSrc = HP_MAX_NODES + 1;
+
+// One source of partials for the merge.  Row (b, h) reads split s at
+// o + s*o_split + ((b - b0)*Hq + h)*d when b in [b0, b1).  When
+// split_blocks > 0 the source is a suffix pass: only the first
+// ceil(ceil(len_b / 16) / split_blocks) splits hold keys.
+struct MergeSrc {
+    const float *o;
+    const float *lse;
+    int64_t o_split;
+    int64_t lse_split;
+    int32_t nsplit;
+    int32_t split_blocks;
+    int64_t b0, b1;
+};
+
+struct MergeArgs {
+    MergeSrc src[kMaxMergeSrc];
+    int32_t nsrc;
+    const int32_t *lens;      // suffix lengths (for suffix sources), may be null otherwise
+    int32_t max_len;          // capacity check for lens
+    int32_t Hq;
+    int64_t row_b0, row_b1;   // sequences whose rows are written
+    float *o;                 // [B][Hq][d], indexed by absolute b
+    float *lse;               // may be null
+};
+
+// ---------------------------------------------------------------------------
+// Device helpers
+// ---------------------------------------------------------------------------
+
+__device__ __forceinline__ float bf16_bits_to_float(uint32_t bits16) {
+    return __uint_as_float(bits16 << 16);
+}
+
+__device__ __forceinline__ float f16_bits_to_float(uint32_t bits16) {
+    _Float16 h = __builtin_bit_cast(_Float16, (uint16_t)bits16);
+    return (float)h;
+}
+
+template <bool kBf16>
+__device__ __forceinline__ float half_bits_to_float(uint32_t bits16) {
+    if constexpr (kBf16) return bf16_bits_to_float(bits16);
+    else return f16_bits_to_float(bits16);
+}
+
+// Round fp32 to the 16-bit type (nearest even), returned as raw bits.
+template <bool kBf16>
+__device__ __forceinline__ uint32_t float_to_half_bits(float x) {
+    if constexpr (kBf16) {
+        __bf16 b = (__bf16)x;
+        return __builtin_bit_cast(uint16_t, b);
+    } else {
+        _Float16 h = (_Float16)x;
+        return __builtin_bit_cast(uint16_t, h);
+    }
+}
+
+__device__ __forceinline__ float fast_exp2(float x) { return __builtin_amdgcn_exp2f(x); }
+__device__ __forceinline__ float fast_log2(float x) { return __builtin_amdgcn_logf(x); }
+
+template <int kWidth>
+__device__ __forceinline__ float xor_sum(float x) {
+#pragma unroll
+    for (int off = 1; off < kWidth; off <<= 1) x += __shfl_xor(x, off, kWave);
+    return x;
+}
+
+// Max over lanes that differ only in the bits [from, 64): lanes l, l^from, l^2from, ...
+template <int kFrom>
+__device__ __forceinline__ float xor_max_from(float x) {
+#pragma unroll
+    for (int off = kFrom; off < kWave; off <<= 1) x = fmaxf(x, __shfl_xor(x, off, kWave));
+    return x;
+}
+
+template <int kFrom>
+__device__ __forceinline__ float xor_sum_from(float x) {
+#pragma unroll
+    for (int off = kFrom; off < kWave; off <<= 1) x += __shfl_xor(x, off, kWave);
+    return x;
+}
+
+}  // namespace hp

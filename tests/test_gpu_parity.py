@@ -1,0 +1,364 @@
+"""GPU parity: every pass of the HIP path against the fp64 oracle, through the C ABI.
+
+Tolerances (written in gpu_util.TOL): fp32 inputs max-abs 1e-5; bf16/fp16 inputs
+max-abs 1e-2, mean-abs 1e-3, LSE max-abs 1e-3.  Block-table indexing is checked
+bit-exactly with needles (one key scores 0, every other key scores about -1450,
+so softmax puts weight exactly 1 on it and O must equal that key's value row).
+"""
+import numpy as np
+import pytest
+import torch
+
+import decode_attention_shared_amd as hp
+import oracle
+import workloads
+from gpu_util import DEV, cascade, compare, dev_step, sample_rows, say
+
+pytestmark = pytest.mark.gpu
+
+
+@pytest.fixture(scope="module", autouse=True)
+def _gpu():
+    if not torch.cuda.is_available():
+        pytest.fail("GPU tests need an MI355X (no GPU visible)")
+    hp.lib()
+
+
+def _one_level(name, dtype, d, B, Hq, Hkv, P, b0, b1, lo=1, hi=1, paged=True):
+    return workloads.custom(name, B=B, Hq=Hq, Hkv=Hkv, d=d, dtype=dtype,
+                            levels=(((P, b0, b1),),), suffix_lo=lo, suffix_hi=hi, paged=paged)
+
+
+# ------------------------------------------------------------------ prefix pass
+
+PREFIX_CASES = [
+    # dtype, d, B, Hq, Hkv, P, seq_begin, seq_end
+    ("bf16", 128, 75, 8, 2, 1000, 0, 75),     # 300 rows per KV head: 2 row blocks, key splits
+    ("f16", 128, 5, 8, 2, 65, 1, 4),          # 12 rows, a sub-range of sequences, ragged tile
+    ("bf16", 64, 12, 4, 1, 2500, 0, 12),      # d=64, 48 rows, many splits
+    ("f16", 64, 30, 8, 8, 1, 0, 30),          # a single key
+    ("bf16", 128, 32, 4, 4, 64, 0, 32),       # exactly one tile of keys
+    ("f16", 128, 100, 1, 1, 3000, 0, 100),    # 100 rows, one head
+    ("bf16", 128, 130, 8, 1, 700, 0, 130),    # MQA-like group of 8: 1040 rows, 5 row blocks
+    ("f32", 64, 4, 1, 1, 512, 0, 4),          # the tiny fp32 shape
+    ("f32", 128, 9, 4, 2, 777, 0, 9),         # fp32, d=128, GQA
+    ("f32", 64, 70, 2, 1, 300, 5, 70),        # fp32, 130 rows
+]
+
+
+@pytest.mark.parametrize("case", PREFIX_CASES, ids=lambda c: "-".join(map(str, c)))
+def test_prefix_pass(case):
+    dtype, d, B, Hq, Hkv, P, b0, b1 = case
+    say(f"prefix {case}")
+    step = workloads.generate(_one_level("pfx", dtype, d, B, Hq, Hkv, P, b0, b1), seed=1)
+    node = step.levels[0][0]
+    q = step.q.to(DEV)
+    out = torch.full((B, Hq, d), 7.0, device=DEV)
+    lse = torch.full((B, Hq), 7.0, device=DEV)
+    hp.prefix_attn(q, node.k.to(DEV), node.v.to(DEV), b0, b1, step.scale, out=out, lse=lse)
+    torch.cuda.synchronize()
+    rows = np.arange(b0 * Hq, b1 * Hq)
+    ref_o, ref_l = oracle.step_attention(step, "prefix", rows=rows)
+    compare(out, lse, ref_o, ref_l, dtype, "prefix", rows=rows)
+    outside = torch.ones(B, dtype=torch.bool)
+    outside[b0:b1] = False
+    assert torch.all(out.cpu()[outside] == 7.0) and torch.all(lse.cpu()[outside] == 7.0), \
+        "rows outside the node were written"
+
+
+def test_prefix_empty_node():
+    step = workloads.generate(_one_level("e", "bf16", 128, 4, 4, 2, 0, 0, 4), seed=0)
+    q = step.q.to(DEV)
+    k = torch.zeros(0, 2, 128, dtype=torch.bfloat16, device=DEV)
+    out, lse = hp.prefix_attn(q, k, k, 0, 4, step.scale)
+    torch.cuda.synchronize()
+    assert torch.all(out == 0) and torch.all(lse == -float("inf"))
+
+
+# ------------------------------------------------------------------ suffix pass
+
+SUFFIX_CASES = [
+    # dtype, d, B, Hq, Hkv, lo, hi
+    ("bf16", 128, 40, 32, 8, 1, 300),    # group 4, suffixes split over 3 work items
+    ("f16", 128, 20, 40, 40, 1, 128),    # MHA
+    ("bf16", 64, 16, 16, 2, 0, 40),      # group 8, d=64, empty suffixes included
+    ("f32", 64, 4, 1, 1, 1, 64),         # tiny fp32
+    ("f32", 128, 6, 4, 2, 1, 200),       # fp32 group 2 with splits
+    ("f16", 64, 33, 2, 1, 16, 17),       # block boundaries
+    ("bf16", 128, 8, 8, 4, 300, 512),    # long suffixes, 4 splits
+]
+
+
+@pytest.mark.parametrize("case", SUFFIX_CASES, ids=lambda c: "-".join(map(str, c)))
+@pytest.mark.parametrize("paged", [True, False])
+def test_suffix_pass(case, paged):
+    dtype, d, B, Hq, Hkv, lo, hi = case
+    say(f"suffix {case} paged={paged}")
+    step = workloads.generate(_one_level("suf", dtype, d, B, Hq, Hkv, 0, 0, B, lo, hi, paged),
+                              seed=2)
+    ds = dev_step(step)
+    out, lse = hp.suffix_decode(ds["q"], ds["k_pool"], ds["v_pool"], ds["block_table"],
+                                ds["seq_lens"], step.scale)
+    torch.cuda.synchronize()
+    ref_o, ref_l = oracle.step_attention(step, "suffix")
+    compare(out, lse, ref_o, ref_l, dtype, "suffix")
+
+
+def test_suffix_lengths_at_block_edges():
+    lens = [0, 1, 15, 16, 17, 31, 32, 33, 127, 128, 129, 255, 256, 300]
+    cfg = _one_level("edges", "bf16", 128, len(lens), 8, 2, 0, 0, len(lens), 0, 300)
+    step = workloads.generate(cfg, seed=3, seq_lens=lens)
+    ds = dev_step(step)
+    out, lse = hp.suffix_decode(ds["q"], ds["k_pool"], ds["v_pool"], ds["block_table"],
+                                ds["seq_lens"], step.scale)
+    torch.cuda.synchronize()
+    ref_o, ref_l = oracle.step_attention(step, "suffix")
+    compare(out, lse, ref_o, ref_l, "bf16", "suffix edges")
+    assert torch.all(out[0] == 0) and torch.all(lse[0] == -float("inf"))
+
+
+@pytest.mark.parametrize("dtype", ["f32", "f16", "bf16"])
+def test_single_suffix_token_returns_value_exactly(dtype):
+    cfg = _one_level("one", dtype, 128, 10, 8, 2, 0, 0, 10, 1, 1)
+    step = workloads.generate(cfg, seed=4)
+    ds = dev_step(step)
+    out, lse = hp.suffix_decode(ds["q"], ds["k_pool"], ds["v_pool"], ds["block_table"],
+                                ds["seq_lens"], step.scale)
+    torch.cuda.synchronize()
+    G = 4
+    want = step.suf_v.float().repeat_interleave(G, dim=1)  # [B][Hq][d]: token 0 of each sequence
+    assert torch.equal(out.cpu(), want), "one key: O must equal its value row exactly"
+
+
+# ------------------------------------------------------------------ merge
+
+@pytest.mark.parametrize("n", [1, 2, 3, 16])
+@pytest.mark.parametrize("d", [64, 128])
+def test_lse_merge(n, d):
+    g = torch.Generator().manual_seed(n * 100 + d)
+    rows = 1000
+    os_ = [torch.randn(rows, d, generator=g) for _ in range(n)]
+    ls_ = [torch.randn(rows, generator=g) * 5 for _ in range(n)]
+    for i in range(n):                       # some empty partials, and some all-empty rows
+        ls_[i][i::7] = -float("inf")
+        os_[i][i::7] = 0.0
+    for i in range(n):
+        ls_[i][::97] = -float("inf")
+        os_[i][::97] = 0.0
+    out, lse = hp.lse_merge([o.to(DEV) for o in os_], [l.to(DEV) for l in ls_])
+    torch.cuda.synchronize()
+    ref_o, ref_l = oracle.merge([o.numpy() for o in os_], [l.numpy() for l in ls_])
+    go, gl = out.double().cpu().numpy(), lse.double().cpu().numpy()
+    fin = np.isfinite(ref_l)
+    assert np.array_equal(np.isfinite(gl), fin)
+    assert np.all(go[~fin] == 0)
+    # fp32 arithmetic on fp32 partials: the fp32 tolerance of this path (1e-5)
+    assert np.abs(go - ref_o).max() <= 1e-5 * max(1.0, np.abs(ref_o).max())
+    assert np.abs(gl[fin] - ref_l[fin]).max() <= 1e-5 * max(1.0, np.abs(ref_l[fin]).max())
+    if n == 1:
+        assert np.array_equal(go[fin], os_[0].double().numpy()[fin]), "one part passes through"
+
+
+# ------------------------------------------------------------------ whole step, reduced sizes
+
+REDUCED = [
+    workloads.tiny_f32(),
+    workloads.custom("llama3_8b_gqa_small", B=16, Hq=32, Hkv=8, d=128, dtype="bf16",
+                     levels=(((1000, 0, 16),),), suffix_lo=1, suffix_hi=256),
+    workloads.custom("codellama13b_small", B=24, Hq=40, Hkv=40, d=128, dtype="f16",
+                     levels=(((1500, 0, 24),),), suffix_lo=1, suffix_hi=128),
+    workloads.custom("docqa_small", B=12, Hq=32, Hkv=32, d=128, dtype="bf16",
+                     levels=(((2000, 0, 12),),), suffix_lo=64, suffix_hi=512),
+    workloads.custom("two_level_small", B=24, Hq=32, Hkv=8, d=128, dtype="bf16",
+                     levels=(((700, 0, 24),), ((300, 0, 8), (300, 8, 16), (300, 16, 24))),
+                     suffix_lo=1, suffix_hi=128),
+    workloads.custom("forest_gaps", B=20, Hq=8, Hkv=8, d=64, dtype="f16",
+                     levels=(((129, 2, 20),), ((64, 2, 5), (17, 9, 14)), ((5, 10, 12),)),
+                     suffix_lo=0, suffix_hi=70),
+]
+
+
+@pytest.mark.parametrize("cfg", REDUCED, ids=lambda c: c.name)
+@pytest.mark.parametrize("seed", [0, 1])
+def test_cascade_reduced(cfg, seed):
+    say(f"cascade {cfg.name} seed {seed}")
+    step = workloads.generate(cfg, seed=seed)
+    ds = dev_step(step)
+    out, lse = cascade(ds, step.scale)
+    torch.cuda.synchronize()
+    ref_o, ref_l = oracle.step_attention(step, "all")
+    compare(out, lse, ref_o, ref_l, cfg.dtype, cfg.name)
+
+
+def test_cascade_peaky_scores():
+    """Q scaled by 8: a wide score range exercises large online-softmax rescales."""
+    cfg = REDUCED[1]
+    step = workloads.generate(cfg, seed=5, q_mult=8.0)
+    ds = dev_step(step)
+    out, lse = cascade(ds, step.scale)
+    torch.cuda.synchronize()
+    ref_o, ref_l = oracle.step_attention(step, "all")
+    compare(out, lse, ref_o, ref_l, cfg.dtype, "peaky")
+
+
+def test_cascade_prefix_only_and_suffix_only():
+    cfg = REDUCED[4]
+    step = workloads.generate(cfg, seed=6)
+    ds = dev_step(step)
+    out, lse = cascade(ds, step.scale, paged=False)
+    torch.cuda.synchronize()
+    ref_o, ref_l = oracle.step_attention(step, "prefix")
+    compare(out, lse, ref_o, ref_l, cfg.dtype, "tree only")
+    out, lse = cascade(ds, step.scale, levels=[])
+    torch.cuda.synchronize()
+    ref_o, ref_l = oracle.step_attention(step, "suffix")
+    compare(out, lse, ref_o, ref_l, cfg.dtype, "suffix only")
+
+
+def test_cascade_deterministic():
+    cfg = REDUCED[3]
+    step = workloads.generate(cfg, seed=7)
+    ds = dev_step(step)
+    call = hp.CascadeCall(ds["q"], ds["levels"], ds["k_pool"], ds["v_pool"], ds["block_table"],
+                          ds["seq_lens"], step.scale)
+    o1, l1 = [t.clone() for t in call()]
+    o2, l2 = [t.clone() for t in call()]
+    torch.cuda.synchronize()
+    assert torch.equal(o1, o2) and torch.equal(l1, l2)
+
+
+def test_bad_metadata_gives_nan_rows_only():
+    cfg = REDUCED[1]
+    step = workloads.generate(cfg, seed=8)
+    ds = dev_step(step)
+    ds["block_table"][3, 0] = step.num_blocks          # block id out of range
+    ds["block_table"][5, 0] = -1
+    ds["seq_lens"][9] = cfg.max_blocks * 16 + 1        # longer than the table
+    out, lse = cascade(ds, step.scale)
+    torch.cuda.synchronize()
+    bad = [3, 5, 9]
+    assert torch.isnan(out[bad]).all() and torch.isnan(lse[bad]).all()
+    good = [b for b in range(cfg.B) if b not in bad]
+    rows = np.array([b * cfg.Hq + h for b in good for h in range(cfg.Hq)])
+    ref_o, ref_l = oracle.step_attention(step, "all", rows=rows)
+    compare(out, lse, ref_o, ref_l, cfg.dtype, "good rows", rows=rows)
+
+
+# ------------------------------------------------------------------ needles: bit-exact indexing
+
+NEG = -16384.0   # exact in bf16 and fp16; scale * NEG ~ -1448 underflows exp to exactly 0
+
+
+def _needle_q(step):
+    """q[b][h] = e_c with c = (b*G + h%G) % d: every (KV head, dim) pair has its rows."""
+    cfg = step.cfg
+    q = torch.zeros_like(step.q)
+    for b in range(cfg.B):
+        for h in range(cfg.Hq):
+            q[b, h, (b * cfg.G + h % cfg.G) % cfg.d] = 1.0
+    return q
+
+
+def test_needles_suffix_every_position():
+    cfg = workloads.custom("needle_suf", B=24, Hq=8, Hkv=4, d=128, dtype="bf16",
+                           levels=(((200, 0, 24),),), suffix_lo=1, suffix_hi=100)
+    step = workloads.generate(cfg, seed=9)
+    ds = dev_step(step)
+    ds["q"].zero_()
+    ds["q"][:, :, 0] = 1.0
+    pk = ds["k_pool"]
+    for lvl in ds["levels"]:
+        for (k, v, _, _) in lvl:
+            k[:, :, 0] = NEG
+    valid = torch.zeros(pk.shape[:3], dtype=torch.bool)   # (block, slot, head) holding a token
+    lens = step.seq_lens.tolist()
+    tbl = step.block_table
+    for b in range(cfg.B):
+        for t in range(lens[b]):
+            valid[int(tbl[b, t // 16]), t % 16, :] = True
+    pk[..., 0][valid.to(DEV)] = NEG
+    call = hp.CascadeCall(ds["q"], ds["levels"], pk, ds["v_pool"], ds["block_table"],
+                          ds["seq_lens"], step.scale)
+    suf_v = step.suf_v.float()
+    offs = step.suf_offsets.tolist()
+    G = cfg.G
+    for r in range(max(lens)):
+        blks, slots, heads, want_rows = [], [], [], []
+        for b in range(cfg.B):
+            for g in range(cfg.Hkv):
+                t = (r + g) % lens[b]
+                blks.append(int(tbl[b, t // 16]))
+                slots.append(t % 16)
+                heads.append(g)
+                want_rows.append(suf_v[offs[b] + t, g])
+        idx = (torch.tensor(blks, device=DEV), torch.tensor(slots, device=DEV),
+               torch.tensor(heads, device=DEV))
+        pk[idx + (0,)] = 0.0
+        out, lse = call()
+        got = out.cpu()
+        want = torch.stack(want_rows).view(cfg.B, cfg.Hkv, 1, cfg.d).expand(
+            cfg.B, cfg.Hkv, G, cfg.d).reshape(cfg.B, cfg.Hq, cfg.d)
+        assert torch.equal(got, want), f"needle run {r}: wrong key picked"
+        assert torch.all(lse.cpu() == 0.0), f"needle run {r}: LSE must be exactly 0"
+        pk[idx + (0,)] = NEG
+    say(f"  suffix needles: {max(lens)} runs, every logical position of every sequence")
+
+
+@pytest.mark.parametrize("level", [0, 1])
+def test_needles_prefix_nodes(level):
+    cfg = workloads.custom("needle_pfx", B=64, Hq=8, Hkv=2, d=128, dtype="f16",
+                           levels=(((1000, 0, 64),), ((300, 0, 32), (260, 32, 64))),
+                           suffix_lo=1, suffix_hi=40)
+    step = workloads.generate(cfg, seed=10)
+    ds = dev_step(step)
+    q = _needle_q(step)
+    ds["q"].copy_(q.to(DEV))
+    for lvl in ds["levels"]:
+        for (k, v, _, _) in lvl:
+            k.fill_(NEG)
+    ds["k_pool"].fill_(NEG)
+    call = hp.CascadeCall(ds["q"], ds["levels"], ds["k_pool"], ds["v_pool"], ds["block_table"],
+                          ds["seq_lens"], step.scale)
+    d, G = cfg.d, cfg.G
+    nodes = ds["levels"][level]
+    cpu_nodes = step.levels[level]
+    P = max(n[0].shape[0] for n in nodes)
+    runs = -(-P // d)
+    for r in range(runs):
+        want = torch.empty(cfg.B, cfg.Hq, d)
+        for (k, v, b0, b1), cn in zip(nodes, cpu_nodes):
+            L = k.shape[0]
+            for g in range(cfg.Hkv):
+                for c in range(d):
+                    k[(r * d + c + 7 * g) % L, g, c] = 0.0
+            for b in range(b0, b1):
+                for h in range(cfg.Hq):
+                    g, c = h // G, (b * G + h % G) % d
+                    want[b, h] = cn.v[(r * d + c + 7 * g) % L, g].float()
+        out, lse = call()
+        assert torch.equal(out.cpu(), want), f"prefix needle run {r} (level {level}) wrong key"
+        assert torch.all(lse.cpu() == 0.0)
+        for (k, v, b0, b1) in nodes:
+            k.fill_(NEG)
+    say(f"  prefix needles level {level}: {runs} runs cover every key of every node")
+
+
+# ------------------------------------------------------------------ full sizes, sampled rows
+
+FULL = [workloads.tiny_f32(), workloads.llama3_8b_gqa(), workloads.codellama13b_mha(1024),
+        workloads.codellama13b_mha(16384), workloads.docqa_codellama7b(),
+        workloads.two_level_gqa()]
+
+
+@pytest.mark.parametrize("cfg", FULL, ids=lambda c: c.name)
+def test_cascade_full_size_sampled(cfg):
+    say(f"full {cfg.name}: generating")
+    step = workloads.generate(cfg, seed=0)
+    ds = dev_step(step)
+    say(f"full {cfg.name}: running")
+    out, lse = cascade(ds, step.scale)
+    torch.cuda.synchronize()
+    rows = sample_rows(cfg.B, cfg.Hq, 48)
+    ref_o, ref_l = oracle.step_attention(step, "all", rows=rows)
+    compare(out, lse, ref_o, ref_l, cfg.dtype, cfg.name, rows=rows)
+    assert torch.isfinite(out).all() and torch.isfinite(lse).all()
