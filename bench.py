@@ -197,6 +197,9 @@ def main():
     ap.add_argument("--sweep-steps", type=int, default=50)
     ap.add_argument("--profile-only", action="store_true",
                     help="only run warmup + timed steps (for rocprofv3); no sweep or CPU leg")
+    ap.add_argument("--copy-probe", type=int, default=0, metavar="MIB",
+                    help="instead of the step, run --steps device-to-device copies of MIB MiB "
+                         "(a plain copy of known size, to calibrate HBM byte counters)")
     args = ap.parse_args()
 
     world = int(os.environ.get("WORLD_SIZE", "1"))
@@ -210,6 +213,20 @@ def main():
     import workloads
     if not torch.cuda.is_available():
         raise SystemExit("bench.py needs a GPU")
+
+    if args.copy_probe:
+        n = args.copy_probe << 20
+        src = torch.ones(n // 4, dtype=torch.float32, device="cuda:0")
+        dst = torch.empty_like(src)
+        torch.cuda.synchronize()
+        t0 = time.perf_counter()
+        for _ in range(args.steps):
+            dst.copy_(src)
+        torch.cuda.synchronize()
+        el = time.perf_counter() - t0
+        print(json.dumps({"copy_probe_bytes": n, "copies": args.steps,
+                          "gbps_read_plus_write": round(2 * n * args.steps / el / 1e9, 1)}))
+        return
 
     cfg = workload(args.workload)
     print(f"[bench] generating {cfg.name} seed {args.seed}", file=sys.stderr, flush=True)

@@ -15,7 +15,7 @@
 
 namespace hp {
 hipError_t launch_prefix(const PrefixArgs &a, int dtype, int d, int nw, int wgs, hipStream_t s);
-hipError_t launch_suffix(const SuffixArgs &a, int dtype, int d, int G, hipStream_t s);
+hipError_t launch_suffix(const SuffixArgs &a, int dtype, int d, int G, int nws, hipStream_t s);
 hipError_t launch_merge(const MergeArgs &a, int d, hipStream_t s);
 }  // namespace hp
 
@@ -26,9 +26,12 @@ using namespace hp;
 thread_local int32_t g_last_hip_error = 0;
 
 constexpr int kTileKeys = 64;           // keys per prefix tile (matches the kernels)
-constexpr int kTargetWgs = 512;         // prefix workgroups aimed for per launch (2 per CU)
-constexpr int kMinTilesPerSplit = 4;    // keep >= 256 keys per split: partial traffic stays small
-constexpr int kSuffixSplitBlocks = 8;   // 128 suffix tokens per suffix work item
+constexpr int kCUs = 256;               // MI355X compute units
+constexpr int kWavesPerCU = 8;          // two waves per SIMD at the prefix kernels' register use
+// Cost of one byte of split partials (written once, read once by the merge),
+// in units of one tile of prefix work per resident workgroup (~1 us at
+// ~5 TB/s effective): used to trade scheduling rounds against partial traffic.
+constexpr double kPartialByteCost = 2e-7;
 constexpr size_t kWsAlign = 256;
 
 inline size_t round_up(size_t x, size_t a) { return (x + a - 1) / a * a; }
@@ -124,39 +127,62 @@ struct NodePlan {
     int64_t rows = 0;  // (seq_end - seq_begin) * Hq output rows
 };
 
-// Plans every node of one launch (a tree level) together: the split count
-// spreads the launch over about kTargetWgs workgroups.
+// Plan of every node of one launch (a tree level).
 struct LevelPlan {
     int nw = 1;
     int first = 0, count = 0;
     NodePlan nodes[HP_MAX_NODES];
 };
 
+// Splits of the key range: every node of a level gets splits of (about) the
+// same number of tiles T, chosen to minimise
+//     rounds(T) * T + kPartialByteCost * partial_bytes(T)
+// where rounds(T) is how many times the launch fills the GPU's workgroup slots
+// (a partly filled last round costs a full round) and partial_bytes(T) the
+// split results written and read back by the merge.
 void plan_level(const hp_query &q, const hp_prefix_node *nodes, int count, LevelPlan &lp) {
     const int G = q.Hq / q.Hkv;
-    int64_t maxM = 1;
-    for (int i = 0; i < count; ++i)
+    int64_t maxM = 1, max_tiles = 0;
+    for (int i = 0; i < count; ++i) {
         maxM = std::max<int64_t>(maxM, (int64_t)(nodes[i].seq_end - nodes[i].seq_begin) * G);
+        max_tiles = std::max<int64_t>(max_tiles, cdiv(nodes[i].len, kTileKeys));
+    }
     lp.nw = choose_nw(maxM);
     const int64_t rows_per_wg = 32 * lp.nw;
-    int64_t base = 0;
+    const int64_t slots = (int64_t)kCUs * kWavesPerCU / lp.nw;
     for (int i = 0; i < count; ++i) {
         const int64_t M = (int64_t)(nodes[i].seq_end - nodes[i].seq_begin) * G;
         lp.nodes[i].rowblocks = (int)cdiv(M, rows_per_wg);
-        base += (int64_t)q.Hkv * lp.nodes[i].rowblocks;
+        lp.nodes[i].rows = (int64_t)(nodes[i].seq_end - nodes[i].seq_begin) * q.Hq;
     }
-    const int64_t want = std::max<int64_t>(1, cdiv(kTargetWgs, std::max<int64_t>(1, base)));
+    int64_t best_T = std::max<int64_t>(1, max_tiles);
+    double best_cost = 1e300;
+    for (int64_t T = 1; T <= std::max<int64_t>(1, max_tiles); ++T) {
+        int64_t wgs = 0;
+        double pbytes = 0;
+        for (int i = 0; i < count; ++i) {
+            const int64_t tiles = cdiv(nodes[i].len, kTileKeys);
+            const int64_t ns = tiles ? cdiv(tiles, T) : 1;
+            const int64_t units = (int64_t)q.Hkv * ns;
+            const int64_t rb = lp.nodes[i].rowblocks;
+            wgs += (rb > 1 ? (int64_t)round_up(units, 8) : units) * rb;
+            pbytes += (double)ns * lp.nodes[i].rows * (q.d + 1) * 4.0 * 2.0;
+        }
+        const double cost = (double)cdiv(wgs, slots) * T + kPartialByteCost * pbytes;
+        if (cost < best_cost) {
+            best_cost = cost;
+            best_T = T;
+        }
+    }
     for (int i = 0; i < count; ++i) {
         NodePlan &np = lp.nodes[i];
         const int64_t tiles = cdiv(nodes[i].len, kTileKeys);
-        int64_t ns = std::min<int64_t>(want, std::max<int64_t>(1, tiles / kMinTilesPerSplit));
-        ns = std::max<int64_t>(1, ns);
+        const int64_t ns = tiles ? cdiv(tiles, best_T) : 1;
         np.tiles_per_split = tiles ? (int)cdiv(tiles, ns) : 0;
         np.nsplit = tiles ? (int)cdiv(tiles, np.tiles_per_split) : 1;
         const int64_t units = (int64_t)q.Hkv * np.nsplit;
         np.units_padded = (int)(np.rowblocks > 1 ? round_up(units, 8) : units);
         np.wgs = np.units_padded * np.rowblocks;
-        np.rows = (int64_t)(nodes[i].seq_end - nodes[i].seq_begin) * q.Hq;
     }
     lp.count = count;
 }
@@ -166,20 +192,10 @@ size_t node_ws_bytes(const NodePlan &np, int d) {
            round_up((size_t)np.nsplit * np.rows * sizeof(float), kWsAlign);
 }
 
-struct SuffixPlan {
-    int bps = kSuffixSplitBlocks, nsplit = 1;
-};
-
-SuffixPlan plan_suffix(const hp_paged_kv &kv) {
-    SuffixPlan sp;
-    sp.nsplit = (int)cdiv(kv.max_blocks, sp.bps);
-    return sp;
-}
-
-size_t suffix_ws_bytes(const hp_query &q, const SuffixPlan &sp) {
-    const size_t rows = (size_t)q.B * q.Hq;
-    return round_up((size_t)sp.nsplit * rows * q.d * sizeof(float), kWsAlign) +
-           round_up((size_t)sp.nsplit * rows * sizeof(float), kWsAlign);
+// Waves per (sequence, KV head) workgroup of the suffix pass: enough that each
+// wave walks only a few blocks of the longest suffix.
+int suffix_waves(const hp_paged_kv &kv) {
+    return kv.max_blocks <= 2 ? 1 : kv.max_blocks <= 4 ? 2 : 4;
 }
 
 PrefixArgs base_prefix_args(const hp_query &q) {
@@ -232,8 +248,7 @@ hp_status run_level(const hp_query &q, const hp_prefix_node *nodes, const LevelP
     return HP_OK;
 }
 
-SuffixArgs suffix_args(const hp_query &q, const hp_paged_kv &kv, const SuffixPlan &sp,
-                       RowDest dest) {
+SuffixArgs suffix_args(const hp_query &q, const hp_paged_kv &kv, RowDest dest) {
     SuffixArgs a;
     std::memset(&a, 0, sizeof a);
     a.q = q.q;
@@ -246,8 +261,7 @@ SuffixArgs suffix_args(const hp_query &q, const hp_paged_kv &kv, const SuffixPla
     a.Hkv = q.Hkv;
     a.max_blocks = kv.max_blocks;
     a.num_blocks = kv.num_blocks;
-    a.blocks_per_split = sp.bps;
-    a.nsplit = sp.nsplit;
+    a.has_suffix = 1;
     a.scale_log2 = (float)((double)q.scale * 1.4426950408889634);
     a.dest = dest;
     return a;
@@ -259,9 +273,7 @@ struct CascadePlan {
     int num_levels = 0;
     LevelPlan levels[HP_MAX_LEVELS];
     bool has_suffix = false;
-    SuffixPlan sp;
     size_t node_off[HP_MAX_NODES];
-    size_t suffix_off = 0;
     size_t bytes = 0;
 };
 
@@ -289,11 +301,6 @@ hp_status plan_cascade(const hp_query *q, const hp_prefix_tree *tree, const hp_p
         idx += lp.count;
     }
     cp.has_suffix = kv != nullptr;
-    if (kv) {
-        cp.sp = plan_suffix(*kv);
-        cp.suffix_off = off;
-        off += suffix_ws_bytes(*q, cp.sp);
-    }
     cp.bytes = off;
     return HP_OK;
 }
@@ -379,13 +386,14 @@ hp_status hp_suffix_decode_workspace_size(const hp_query *q, const hp_paged_kv *
     if (st != HP_OK) return st;
     st = check_kv(q, kv);
     if (st != HP_OK) return st;
-    const SuffixPlan sp = plan_suffix(*kv);
-    *bytes = sp.nsplit > 1 ? suffix_ws_bytes(*q, sp) : 0;
+    *bytes = 0;  // the waves of one (sequence, KV head) combine in LDS
     return HP_OK;
 }
 
 hp_status hp_suffix_decode(const hp_query *q, const hp_paged_kv *kv, float *o, float *lse,
                            void *ws, size_t ws_bytes, void *stream) {
+    (void)ws;
+    (void)ws_bytes;
     hp_status st = check_query(q);
     if (st != HP_OK) return st;
     st = check_kv(q, kv);
@@ -393,33 +401,9 @@ hp_status hp_suffix_decode(const hp_query *q, const hp_paged_kv *kv, float *o, f
     st = check_out(o, lse);
     if (st != HP_OK) return st;
     if (q->B == 0) return HP_OK;
-    const SuffixPlan sp = plan_suffix(*kv);
-    hipStream_t s = (hipStream_t)stream;
-    if (sp.nsplit == 1) {
-        const SuffixArgs a = suffix_args(*q, *kv, sp, RowDest{o, lse, 0, 0, 0});
-        hipError_t e = launch_suffix(a, q->dtype, q->d, q->Hq / q->Hkv, s);
-        return e == hipSuccess ? HP_OK : fail_hip(e);
-    }
-    const size_t need = suffix_ws_bytes(*q, sp);
-    if (!ws || ws_bytes < need || !aligned16(ws)) return HP_ERR_WORKSPACE;
-    const int64_t rows = (int64_t)q->B * q->Hq;
-    float *wo = (float *)ws;
-    float *wl = (float *)((char *)ws + round_up((size_t)sp.nsplit * rows * q->d * 4, kWsAlign));
-    const SuffixArgs a = suffix_args(*q, *kv, sp, RowDest{wo, wl, rows * q->d, rows, 0});
-    hipError_t e = launch_suffix(a, q->dtype, q->d, q->Hq / q->Hkv, s);
-    if (e != hipSuccess) return fail_hip(e);
-    MergeArgs m;
-    std::memset(&m, 0, sizeof m);
-    m.src[0] = MergeSrc{wo, wl, rows * q->d, rows, sp.nsplit, sp.bps, 0, q->B};
-    m.nsrc = 1;
-    m.lens = kv->seq_lens;
-    m.max_len = kv->max_blocks * HP_BLOCK_SIZE;
-    m.Hq = q->Hq;
-    m.row_b0 = 0;
-    m.row_b1 = q->B;
-    m.o = o;
-    m.lse = lse;
-    e = launch_merge(m, q->d, s);
+    const SuffixArgs a = suffix_args(*q, *kv, RowDest{o, lse, 0, 0, 0});
+    hipError_t e = launch_suffix(a, q->dtype, q->d, q->Hq / q->Hkv, suffix_waves(*kv),
+                                 (hipStream_t)stream);
     return e == hipSuccess ? HP_OK : fail_hip(e);
 }
 
@@ -515,28 +499,25 @@ hp_status cascade_impl(const hp_query *q, const hp_prefix_tree *tree, const hp_p
         if (st != HP_OK) return st;
     }
     if ((st = record(events, 1, s)) != HP_OK) return st;
-    // Suffix pass.
     if (cp.has_suffix) {
-        const int64_t rows = (int64_t)q->B * q->Hq;
-        float *wo = (float *)(base + cp.suffix_off);
-        float *wl = (float *)((char *)wo +
-                              round_up((size_t)cp.sp.nsplit * rows * q->d * 4, kWsAlign));
-        const SuffixArgs a = suffix_args(*q, *kv, cp.sp, RowDest{wo, wl, rows * q->d, rows, 0});
-        hipError_t e = launch_suffix(a, q->dtype, q->d, q->Hq / q->Hkv, s);
+        // Suffix pass with the merge of every level's partials fused in.
+        SuffixArgs a = suffix_args(*q, *kv, RowDest{o, lse, 0, 0, 0});
+        a.nsrc = m.nsrc;
+        for (int i = 0; i < m.nsrc; ++i) a.src[i] = m.src[i];
+        hipError_t e = launch_suffix(a, q->dtype, q->d, q->Hq / q->Hkv, suffix_waves(*kv), s);
         if (e != hipSuccess) return fail_hip(e);
-        m.src[m.nsrc++] = MergeSrc{wo, wl, rows * q->d, rows, cp.sp.nsplit, cp.sp.bps, 0, q->B};
-        m.lens = kv->seq_lens;
-        m.max_len = kv->max_blocks * HP_BLOCK_SIZE;
+        if ((st = record(events, 2, s)) != HP_OK) return st;
+    } else {
+        // Prefix only: one n-way merge of every level's splits.
+        if ((st = record(events, 2, s)) != HP_OK) return st;
+        m.Hq = q->Hq;
+        m.row_b0 = 0;
+        m.row_b1 = q->B;
+        m.o = o;
+        m.lse = lse;
+        hipError_t e = launch_merge(m, q->d, s);
+        if (e != hipSuccess) return fail_hip(e);
     }
-    if ((st = record(events, 2, s)) != HP_OK) return st;
-    // One n-way merge of every level's splits and the suffix splits.
-    m.Hq = q->Hq;
-    m.row_b0 = 0;
-    m.row_b1 = q->B;
-    m.o = o;
-    m.lse = lse;
-    hipError_t e = launch_merge(m, q->d, s);
-    if (e != hipSuccess) return fail_hip(e);
     return record(events, 3, s);
 }
 

@@ -37,6 +37,9 @@ struct RowDest {
 };
 
 constexpr int kMaxLaunchNodes = 16;
+// Rows per workgroup of the wide prefix kernel (4 waves x 64 rows); a launch
+// asks for it with nw = kWideRows / 32.
+constexpr int kWideRows = 256;
 
 struct PrefixNodeArg {
     const void *k;
@@ -62,19 +65,6 @@ struct PrefixArgs {
     PrefixNodeArg nodes[kMaxLaunchNodes];
 };
 
-struct SuffixArgs {
-    const void *q;
-    const void *k_pool;
-    const void *v_pool;
-    const int32_t *table;
-    const int32_t *lens;
-    int32_t B, Hq, Hkv;
-    int32_t max_blocks, num_blocks;
-    int32_t blocks_per_split, nsplit;
-    float scale_log2;
-    RowDest dest;
-};
-
 constexpr int kMaxMergeSrc = HP_MAX_NODES + 1;
 
 // One source of partials for the merge.  Row (b, h) reads split s at
@@ -89,6 +79,23 @@ struct MergeSrc {
     int32_t nsplit;
     int32_t split_blocks;
     int64_t b0, b1;
+};
+
+// Suffix pass with the final merge fused in: every row (b, h) merges its
+// suffix attention with the partials of the sources covering sequence b.
+struct SuffixArgs {
+    const void *q;
+    const void *k_pool;
+    const void *v_pool;
+    const int32_t *table;
+    const int32_t *lens;
+    int32_t B, Hq, Hkv;
+    int32_t max_blocks, num_blocks;
+    int32_t has_suffix;       // 0: no paged suffix (only the sources are merged)
+    float scale_log2;
+    RowDest dest;             // final O and LSE (o_split, lse_split unused)
+    int32_t nsrc;
+    MergeSrc src[kMaxMergeSrc];
 };
 
 struct MergeArgs {

@@ -50,7 +50,7 @@ __global__ __launch_bounds__(256) void merge_kernel(MergeArgs a) {
         const MergeSrc &s = a.src[si];
         const int n = src_count(s, b, a, bad);
         const int64_t ri = (b - s.b0) * a.Hq + h;
-#pragma unroll 1
+#pragma unroll 4
         for (int i = 0; i < n; ++i) {
             const float L = s.lse[(int64_t)i * s.lse_split + ri];
             bad |= (L != L);
@@ -65,7 +65,7 @@ __global__ __launch_bounds__(256) void merge_kernel(MergeArgs a) {
             const MergeSrc &s = a.src[si];
             const int n = src_count(s, b, a, bad);
             const int64_t ri = (b - s.b0) * a.Hq + h;
-#pragma unroll 1
+#pragma unroll 4
             for (int i = 0; i < n; ++i) {
                 const float L = s.lse[(int64_t)i * s.lse_split + ri];
                 const float w = fast_exp2((L - mx) * kLog2e);

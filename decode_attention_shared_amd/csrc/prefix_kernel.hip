@@ -19,8 +19,9 @@
 // Layout on the matrix cores.  A wave owns 32 query rows.  It computes
 // S^T = K Q^T (keys x queries) so that each lane ends up holding the scores
 // of one query (lane % 32) for 16 keys per 32-key block; those probabilities
-// feed O^T = V^T P^T directly as the B operand, with V staged transposed in
-// LDS as the A operand.  Scores stay in fp32 and go to the exp2 domain by
+// feed O^T = V^T P^T directly as the B operand.  V is staged row-major in
+// LDS like K; its transpose for the A operand comes from gfx950's
+// transposing LDS read (ds_read_b64_tr_b16).  Scores stay in fp32 and go to the exp2 domain by
 // folding log2(e) into the scale; P is rounded to the input type for the
 // second product, as the matrix cores require.
 #include "common.hpp"
@@ -37,6 +38,15 @@ __device__ __forceinline__ f32x16 mfma32x32x16(u32x4 a, u32x4 b, f32x16 c) {
     else
         return __builtin_amdgcn_mfma_f32_32x32x16_f16(__builtin_bit_cast(f16x8, a),
                                                       __builtin_bit_cast(f16x8, b), c, 0, 0, 0);
+}
+
+// gfx950 transposing LDS read of 4 x 16-bit: within each 16-lane group, lane i
+// receives element i%4 of the 8-byte chunks read by lanes 4j + i/4, j = 0..3.
+typedef short s16x4 __attribute__((ext_vector_type(4)));
+__device__ __forceinline__ u32x2 lds_read_tr16(const uint16_t *p) {
+    const s16x4 r = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+        (__attribute__((address_space(3))) s16x4 *)(p));
+    return __builtin_bit_cast(u32x2, r);
 }
 
 // Which node, (KV head, split) unit and row block this workgroup owns.
@@ -124,15 +134,126 @@ __device__ __forceinline__ void write_row(const RowDest &dest, int split, int64_
 // ---------------------------------------------------------------------------
 // 16-bit inputs: v_mfma_f32_32x32x16_{bf16,f16}
 // ---------------------------------------------------------------------------
+
+// Lazy rescaling threshold (log2 units).  The running max only moves when a
+// row's tile max exceeds it by more than this; until then probabilities may
+// reach 2^8, which the fp32 accumulators and the 16-bit P operand hold with
+// their usual relative precision, and the per-tile rescale of the O
+// accumulators is skipped.  The result is the same softmax: O / l and
+// m + log2 l do not depend on which shift m was used.
+constexpr float kLazy = 8.f;
+
+typedef float f32x2 __attribute__((ext_vector_type(2)));
+typedef _Float16 f16x2 __attribute__((ext_vector_type(2)));
+typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
+
+// Two fp32 probabilities rounded (nearest even) to the 16-bit type, packed
+// (one v_cvt_pk_{f16,bf16}_f32).
+template <bool kBf16>
+__device__ __forceinline__ uint32_t pack_p(float a, float b) {
+    const f32x2 v = {a, b};
+    if constexpr (kBf16) return __builtin_bit_cast(uint32_t, __builtin_convertvector(v, bf16x2));
+    else return __builtin_bit_cast(uint32_t, __builtin_convertvector(v, f16x2));
+}
+
+// sum + (the two packed 16-bit values), accumulated in fp32 (v_dot2c with ones).
+template <bool kBf16>
+__device__ __forceinline__ float add_packed(uint32_t pk, float sum) {
+    if constexpr (kBf16) {
+        const bf16x2 ones = {(__bf16)1.0f, (__bf16)1.0f};
+        return __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2, pk), ones, sum, false);
+    } else {
+        const f16x2 ones = {(_Float16)1.0f, (_Float16)1.0f};
+        return __builtin_amdgcn_fdot2(__builtin_bit_cast(f16x2, pk), ones, sum, false);
+    }
+}
+
+// Online softmax for one 64-key tile of raw scores q.k (masked keys are
+// -inf), in two halves.  softmax_max: the tile's row max (both half-waves hold
+// keys of the same query) and, when it exceeds the running max by more than
+// kLazy, the new max and the factor alpha by which the running state must be
+// rescaled (the return value, wave-uniform).  softmax_exp: the probabilities
+// 2^(s*c - m) with c = scale * log2(e), packed into 16 pairs of the 16-bit
+// type (the B operand of the value product), and the row sum of exactly those
+// rounded values, so numerator and denominator use the same weights.
+template <bool kBf16>
+__device__ __forceinline__ bool softmax_max(const f32x16 &s0, const f32x16 &s1, float c,
+                                            float &m_run, float &l_run, float &alpha) {
+    float mt = fmaxf(s0[0], s1[0]);
+#pragma unroll
+    for (int i = 1; i < 16; ++i) mt = fmaxf(mt, fmaxf(s0[i], s1[i]));
+    mt = fmaxf(mt, __shfl_xor(mt, 32, kWave));
+    const float mts = mt * c;  // c > 0: the max commutes with the scaling
+    const bool rescale = __any(mts > m_run + kLazy);
+    alpha = 1.f;
+    if (rescale) {
+        const float m_new = fmaxf(m_run, mts);
+        alpha = fast_exp2(m_run - m_new);  // 0 on the first tile (m_run = -inf)
+        l_run *= alpha;
+        m_run = m_new;
+    }
+    return rescale;
+}
+
+template <bool kBf16>
+__device__ __forceinline__ void softmax_exp(const f32x16 &s0, const f32x16 &s1, float c,
+                                            float m_run, float &l_run, uint32_t (&pk)[16]) {
+    const float neg_m = -m_run;
+    float sum = 0.f;
+#pragma unroll
+    for (int i = 0; i < 8; ++i) {
+        pk[i] = pack_p<kBf16>(fast_exp2(fmaf(s0[2 * i], c, neg_m)),
+                              fast_exp2(fmaf(s0[2 * i + 1], c, neg_m)));
+        sum = add_packed<kBf16>(pk[i], sum);
+    }
+#pragma unroll
+    for (int i = 0; i < 8; ++i) {
+        pk[8 + i] = pack_p<kBf16>(fast_exp2(fmaf(s1[2 * i], c, neg_m)),
+                                  fast_exp2(fmaf(s1[2 * i + 1], c, neg_m)));
+        sum = add_packed<kBf16>(pk[8 + i], sum);
+    }
+    l_run += sum;
+}
+
+// s_waitcnt with only vmcnt = n (expcnt and lgkmcnt left unconstrained).
+template <int n>
+__device__ __forceinline__ void wait_vmcnt() {
+    static_assert(n >= 0 && n < 64, "vmcnt range");
+    __builtin_amdgcn_s_waitcnt((n & 15) | (7 << 4) | (15 << 8) | ((n >> 4) << 14));
+}
+
+// 16 bytes from global memory straight into LDS (gfx950 global_load_lds_dwordx4):
+// lane i writes lds_base + 16*i.
+__device__ __forceinline__ void dma16(const void *g, void *lds_base) {
+    __builtin_amdgcn_global_load_lds((const __attribute__((address_space(1))) void *)g,
+                                     (__attribute__((address_space(3))) void *)lds_base, 16, 0,
+                                     0);
+}
+
 template <bool kBf16, int D, int NW>
 __global__ __launch_bounds__(64 * NW) void prefix_mfma16_kernel(PrefixArgs args) {
-    constexpr int kThreads = 64 * NW;
-    constexpr int kKStride = D + 8;      // halves per K row in LDS (16-byte pad)
-    constexpr int kVStride = kTile + 4;  // halves per transposed V row (8-byte pad)
     constexpr int kDSteps = D / 16;
     constexpr int kDBlocks = D / 32;
-    __shared__ __attribute__((aligned(16))) uint16_t ks[kTile * kKStride];
-    __shared__ __attribute__((aligned(16))) uint16_t vt[D * kVStride];
+    constexpr int kRowChunks = D / 8;                     // 16-byte chunks per K/V row
+    constexpr int kRowsPerDma = kWave / kRowChunks;       // rows one wave-wide DMA fills
+    constexpr int kDmas = kTile / kRowsPerDma / NW;       // DMAs per tensor per wave per tile
+    static_assert(kDmas >= 1 && kTile % (kRowsPerDma * NW) == 0, "tile split");
+    constexpr int kPerTile = 2 * kDmas;                   // K and V DMAs per wave per tile
+    // K/V tiles stream through a ring of LDS stages, filled by DMA (no
+    // registers involved), several tiles ahead of the math: each CU needs
+    // tens of KB in flight to cover HBM latency.  Iteration i computes
+    // S(i+1) = K(i+1) Q^T on the matrix cores interleaved with the softmax of
+    // tile i on the vector ALUs, then O += V(i) P(i), and issues tile
+    // i + kStages - 1 into the stage tile i-1 used.
+    constexpr int kStages = NW >= 4 ? 4 : 3;
+    constexpr int kAhead = kStages - 3;  // tiles issued beyond i+1 when waiting for i+1
+    static_assert(kPerTile * (kStages - 2) < 64, "vmcnt range");
+    constexpr int kTileElems = kTile * D;
+    // Rows are unpadded; 16-byte chunk c of row r sits at position c ^ swz(r).
+    // K: 16 consecutive rows hit 16 different chunk positions (the 32 lanes of
+    // an operand read take 32 different rows).  V: the four rows one 16-lane
+    // group of the transposing read touches land 2 chunks apart.
+    __shared__ __attribute__((aligned(1024))) uint16_t lds[kStages][2][kTileElems];
 
     const WgTask task = decode_wg(args);
     if (!task.valid) return;
@@ -140,23 +261,24 @@ __global__ __launch_bounds__(64 * NW) void prefix_mfma16_kernel(PrefixArgs args)
     const int G = args.G;
     const int M = (nd.seq_end - nd.seq_begin) * G;
     const int ntiles = (nd.len + kTile - 1) / kTile;
-    const int tile_begin = task.split * nd.tiles_per_split;
-    const int tile_end = min(tile_begin + nd.tiles_per_split, ntiles);
+    const int tb = task.split * nd.tiles_per_split;  // first tile of this split
+    const int te = min(tb + nd.tiles_per_split, ntiles);
 
-    const int wave = threadIdx.x / kWave;
-    const int lane = threadIdx.x % kWave;
+    const int tid = threadIdx.x;
+    const int wave = tid / kWave;
+    const int lane = tid % kWave;
     const int n = lane & 31;   // query column of this lane
     const int hi = lane >> 5;  // which half of the k-slice this lane supplies
     const int row = task.rb * 32 * NW + wave * 32 + n;
     const bool row_ok = row < M;
     const int b = nd.seq_begin + (row_ok ? row / G : 0);
     const int h = task.g * G + (row_ok ? row % G : 0);
+    const float c = args.scale_log2;
 
     // Q as the B operand of S^T = K Q^T: lane holds 8 consecutive dims per k-step.
     u32x4 qf[kDSteps];
     {
-        const uint16_t *qp =
-            (const uint16_t *)args.q + ((int64_t)b * args.Hq + h) * D + hi * 8;
+        const uint16_t *qp = (const uint16_t *)args.q + ((int64_t)b * args.Hq + h) * D + hi * 8;
 #pragma unroll
         for (int kk = 0; kk < kDSteps; ++kk)
             qf[kk] = row_ok ? *(const u32x4 *)(qp + kk * 16) : u32x4{0, 0, 0, 0};
@@ -170,82 +292,389 @@ __global__ __launch_bounds__(64 * NW) void prefix_mfma16_kernel(PrefixArgs args)
     const uint16_t *kbase = (const uint16_t *)nd.k + (int64_t)task.g * nd.stride_head;
     const uint16_t *vbase = (const uint16_t *)nd.v + (int64_t)task.g * nd.stride_head;
 
-#pragma unroll 1
-    for (int tile = tile_begin; tile < tile_end; ++tile) {
+    // DMA j of this wave fills rows rj .. rj + kRowsPerDma of a tile; lane
+    // `lane` lands at row rj + lane / kRowChunks, position lane % kRowChunks,
+    // so it fetches the logical chunk that belongs there.
+    int dma_row[kDmas], dma_ck[kDmas], dma_cv[kDmas];
+#pragma unroll
+    for (int j = 0; j < kDmas; ++j) {
+        const int r = (wave * kDmas + j) * kRowsPerDma + lane / kRowChunks;
+        const int pos = lane % kRowChunks;
+        dma_row[j] = r;
+        dma_ck[j] = (pos ^ (r % kRowChunks)) * 8;
+        dma_cv[j] = (pos ^ (2 * (r % (kRowChunks / 2)))) * 8;
+    }
+    auto issue = [&](int tile) {
+        const int st = (tile - tb) % kStages;
         const int key0 = tile * kTile;
-        __syncthreads();  // the previous tile's LDS reads are done
-        // Stage K (row-major) and V (transposed) for 64 keys.  Keys past the
-        // node's end are zero-filled, never read.
-        static_assert((kTile * D / 8) % kThreads == 0, "tile chunks must divide evenly");
+        const bool full = key0 + kTile <= nd.len;
 #pragma unroll
-        for (int it = 0; it < kTile * D / 8 / kThreads; ++it) {
-            const int c = threadIdx.x + it * kThreads;
-            const int key = c / (D / 8);
-            const int dc = c % (D / 8);
-            const int t = key0 + key;
-            u32x4 kv = {0, 0, 0, 0}, vv = {0, 0, 0, 0};
-            if (t < nd.len) {
-                const int64_t off = (int64_t)t * nd.stride_tok + dc * 8;
-                kv = *(const u32x4 *)(kbase + off);
-                vv = *(const u32x4 *)(vbase + off);
-            }
-            *(u32x4 *)&ks[key * kKStride + dc * 8] = kv;
-#pragma unroll
-            for (int j = 0; j < 4; ++j) {
-                vt[(dc * 8 + 2 * j) * kVStride + key] = (uint16_t)(vv[j] & 0xffffu);
-                vt[(dc * 8 + 2 * j + 1) * kVStride + key] = (uint16_t)(vv[j] >> 16);
-            }
+        for (int j = 0; j < kDmas; ++j) {
+            // keys past the node's end re-read its last key (finite data whose
+            // scores are masked to -inf)
+            const int t = full ? key0 + dma_row[j] : min(key0 + dma_row[j], nd.len - 1);
+            const int64_t off = (int64_t)t * nd.stride_tok;
+            uint16_t *dst = &lds[st][0][(wave * kDmas + j) * kRowsPerDma * D];
+            dma16(kbase + off + dma_ck[j], dst);
+            dma16(vbase + off + dma_cv[j], dst + kTileElems);
         }
-        __syncthreads();
+    };
 
-        // S^T for keys [0,32) and [32,64) of the tile.
-        f32x16 s0 = f32x16{}, s1 = f32x16{};
+    // Operand reads.  K: rows n and 32+n (same swizzle), logical chunk 2kk+hi.
+    const int k_swz = n % kRowChunks;
+    auto qk = [&](int st, f32x16 &s0, f32x16 &s1) {
+        const uint16_t *kb = &lds[st][0][n * D];
+        s0 = f32x16{};
+        s1 = f32x16{};
 #pragma unroll
         for (int kk = 0; kk < kDSteps; ++kk) {
-            const u32x4 a0 = *(const u32x4 *)&ks[n * kKStride + kk * 16 + hi * 8];
-            const u32x4 a1 = *(const u32x4 *)&ks[(32 + n) * kKStride + kk * 16 + hi * 8];
+            const int col = ((2 * kk + hi) ^ k_swz) * 8;
+            const u32x4 a0 = *(const u32x4 *)&kb[col];
+            const u32x4 a1 = *(const u32x4 *)&kb[32 * D + col];
             s0 = mfma32x32x16<kBf16>(a0, qf[kk], s0);
             s1 = mfma32x32x16<kBf16>(a1, qf[kk], s1);
         }
-        // Accumulator i of a 32x32 block holds key 8*(i/4) + 4*hi + i%4.
-        float x[32];
-        const int valid = nd.len - key0;
+    };
+    // V^T operand: 16-lane group gi covers 16 consecutive d rows; within it
+    // lane 4j + q reads 4 dims of key j, and the transposing read hands lane i
+    // the value of each of the 4 keys at dim (group base + i).  Keys 16u + 4hi
+    // + li/4 (and + 8) share the swizzle 2*(key % (kRowChunks/2)).
+    const int gi = lane >> 4, li = lane & 15;
+    const int v_key = 4 * hi + (li >> 2);
+    const int v_swz = 2 * (v_key % (kRowChunks / 2));
+    int v_col[kDBlocks];
 #pragma unroll
-        for (int i = 0; i < 16; ++i) {
-            const int kr = 8 * (i / 4) + 4 * hi + (i % 4);
-            x[i] = kr < valid ? s0[i] * args.scale_log2 : -INFINITY;
-            x[16 + i] = 32 + kr < valid ? s1[i] * args.scale_log2 : -INFINITY;
-        }
-        const float alpha = softmax_tile(x, m_run, l_run);
-#pragma unroll
-        for (int db = 0; db < kDBlocks; ++db) oacc[db] *= alpha;
-
-        // O^T += V^T P^T in four 16-key steps.  Step u takes accumulators
-        // 8*(u%2) .. +8 of block u/2, i.e. keys 16u + 8*(j/4) + 4*hi + j%4 for
-        // j = 0..7; the A operand reads V^T at the same keys.
+    for (int db = 0; db < kDBlocks; ++db)
+        v_col[db] = v_key * D + ((4 * db + 2 * (gi & 1) + ((li & 3) >> 1)) ^ v_swz) * 8 +
+                    (li & 1) * 4;
+    auto pv = [&](const uint32_t (&pk)[16], int st) {
+        const uint16_t *vb = &lds[st][1][0];
 #pragma unroll
         for (int u = 0; u < 4; ++u) {
-            u32x4 bop;
-#pragma unroll
-            for (int w = 0; w < 4; ++w) {
-                const float p0 = x[(u / 2) * 16 + (u % 2) * 8 + 2 * w];
-                const float p1 = x[(u / 2) * 16 + (u % 2) * 8 + 2 * w + 1];
-                bop[w] = float_to_half_bits<kBf16>(p0) | (float_to_half_bits<kBf16>(p1) << 16);
-            }
+            const u32x4 bop = {pk[4 * u], pk[4 * u + 1], pk[4 * u + 2], pk[4 * u + 3]};
 #pragma unroll
             for (int db = 0; db < kDBlocks; ++db) {
-                const uint16_t *vr = &vt[(db * 32 + n) * kVStride + u * 16 + 4 * hi];
-                const u32x2 lo = *(const u32x2 *)vr;
-                const u32x2 up = *(const u32x2 *)(vr + 8);
+                const uint16_t *vr = vb + 16 * u * D + v_col[db];
+                const u32x2 lo = lds_read_tr16(vr);           // keys 16u + 4hi + 0..3
+                const u32x2 up = lds_read_tr16(vr + 8 * D);   // keys 16u + 8 + 4hi + 0..3
                 const u32x4 aop = {lo.x, lo.y, up.x, up.y};
                 oacc[db] = mfma32x32x16<kBf16>(aop, bop, oacc[db]);
             }
         }
+    };
+    // One tile: softmax of `tile` (scores sc) interleaved with S(tile+1) -> sn,
+    // then the value product.  On a split's last tile the next-S product reads
+    // a stale (in-bounds) stage and is discarded.
+    auto step = [&](int tile, f32x16 &sc0, f32x16 &sc1, f32x16 &sn0, f32x16 &sn1) {
+        // wait for this wave's DMAs of tile+1, then for everyone's
+        if constexpr (kAhead > 0) {
+            if (tile + 2 < te) wait_vmcnt<kAhead * kPerTile>();
+            else wait_vmcnt<0>();
+        } else {
+            wait_vmcnt<0>();
+        }
+        __builtin_amdgcn_s_barrier();
+        if (tile + kStages - 1 < te) issue(tile + kStages - 1);
+
+        // Accumulator i of a 32x32 block holds key 8*(i/4) + 4*hi + i%4.
+        const int valid = nd.len - tile * kTile;
+        if (valid < kTile) {  // only the node's last tile can be partial
+#pragma unroll
+            for (int i = 0; i < 16; ++i) {
+                const int kr = 8 * (i / 4) + 4 * hi + (i % 4);
+                if (kr >= valid) sc0[i] = -INFINITY;
+                if (32 + kr >= valid) sc1[i] = -INFINITY;
+            }
+        }
+        float alpha;
+        if (softmax_max<kBf16>(sc0, sc1, c, m_run, l_run, alpha)) {
+#pragma unroll
+            for (int db = 0; db < kDBlocks; ++db) oacc[db] *= alpha;
+        }
+        qk((tile + 1 - tb) % kStages, sn0, sn1);
+        uint32_t pk[16];
+        softmax_exp<kBf16>(sc0, sc1, c, m_run, l_run, pk);
+        pv(pk, (tile - tb) % kStages);
+#pragma unroll
+        for (int k = 0; k < 2 * kDSteps + 4 * kDBlocks; ++k) {
+            __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);  // one MFMA
+            __builtin_amdgcn_sched_group_barrier(0x002, 4, 0);  // four VALU
+        }
+    };
+
+    if (tb < te) {
+        // Prologue: tiles tb .. tb + kStages - 2 in flight, wait for tb, S(tb).
+#pragma unroll
+        for (int k = 0; k < kStages - 1; ++k)
+            if (tb + k < te) issue(tb + k);
+        const int younger = min(kStages - 2, te - tb - 1);
+        if constexpr (kStages >= 4) {
+            if (younger >= 2) wait_vmcnt<2 * kPerTile>();
+            else if (younger == 1) wait_vmcnt<kPerTile>();
+            else wait_vmcnt<0>();
+        } else {
+            if (younger >= 1) wait_vmcnt<kPerTile>();
+            else wait_vmcnt<0>();
+        }
+        __builtin_amdgcn_s_barrier();
+        f32x16 sa0, sa1, sb0, sb1;
+        qk(0, sa0, sa1);
+        int tile = tb;
+#pragma unroll 1
+        for (; tile + 1 < te; tile += 2) {  // two tiles per trip: the S sets alternate
+            step(tile, sa0, sa1, sb0, sb1);
+            step(tile + 1, sb0, sb1, sa0, sa1);
+        }
+        if (tile < te) step(tile, sa0, sa1, sb0, sb1);
     }
 
     if (row_ok) {
         const int64_t ri = ((int64_t)(b - nd.dest.row_base)) * args.Hq + h;
         write_row<D>(nd.dest, task.split, ri, oacc, hi, m_run, l_run);
+    }
+}
+
+// ---------------------------------------------------------------------------
+// Wide variant for many rows per KV head: 4 waves x 64 query rows.  Each wave
+// owns two 32-row blocks, so every K or V operand it reads from LDS feeds two
+// MFMAs: half the LDS traffic per FLOP of the 32-row layout, which at full
+// matrix-core rate would need about all of the LDS bandwidth.  One wave per
+// SIMD with the whole register file (O accumulators in AGPRs).  Latency is
+// hidden inside the wave by a one-tile skew: iteration i runs the
+// exponentials of tile i on the vector ALUs while the matrix cores do the
+// value product of tile i-1, then computes the scores of tile i+1.
+//
+// Online softmax with the skew: the row max can rise when tile i+1's scores
+// are seen, before tile i's value product (taken with the old max) has been
+// added to O.  The denominator is rescaled at once; the O rescale is deferred
+// until that product is in, so every term of O and l is taken relative to
+// the same max when they meet.
+// ---------------------------------------------------------------------------
+template <bool kBf16, int D>
+__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1)))
+void prefix_mfma16_wide_kernel(PrefixArgs args) {
+    constexpr int NW = 4;
+    constexpr int kDSteps = D / 16;
+    constexpr int kDBlocks = D / 32;
+    constexpr int kRowChunks = D / 8;
+    constexpr int kRowsPerDma = kWave / kRowChunks;
+    constexpr int kDmas = kTile / kRowsPerDma / NW;
+    static_assert(kDmas >= 1 && kTile % (kRowsPerDma * NW) == 0, "tile split");
+    // Stages hold V(i-1) (value product), K(i+1) (next scores) and the tile in
+    // flight; iteration i refills the stage tile i-2 used with tile i+2.
+    constexpr int kStages = 4;
+    constexpr int kTileElems = kTile * D;
+    __shared__ __attribute__((aligned(1024))) uint16_t lds[kStages][2][kTileElems];
+
+    const WgTask task = decode_wg(args);
+    if (!task.valid) return;
+    const PrefixNodeArg &nd = args.nodes[task.node];
+    const int G = args.G;
+    const int M = (nd.seq_end - nd.seq_begin) * G;
+    const int ntiles = (nd.len + kTile - 1) / kTile;
+    const int tb = task.split * nd.tiles_per_split;
+    const int te = min(tb + nd.tiles_per_split, ntiles);
+
+    const int tid = threadIdx.x;
+    const int wave = tid / kWave;
+    const int lane = tid % kWave;
+    const int n = lane & 31;
+    const int hi = lane >> 5;
+    const float c = args.scale_log2;
+    int rowi[2], bi[2], hq[2];
+    bool rok[2];
+#pragma unroll
+    for (int r = 0; r < 2; ++r) {
+        rowi[r] = task.rb * kWideRows + wave * 64 + r * 32 + n;
+        rok[r] = rowi[r] < M;
+        bi[r] = nd.seq_begin + (rok[r] ? rowi[r] / G : 0);
+        hq[r] = task.g * G + (rok[r] ? rowi[r] % G : 0);
+    }
+    u32x4 qf[2][kDSteps];
+#pragma unroll
+    for (int r = 0; r < 2; ++r) {
+        const uint16_t *qp =
+            (const uint16_t *)args.q + ((int64_t)bi[r] * args.Hq + hq[r]) * D + hi * 8;
+#pragma unroll
+        for (int kk = 0; kk < kDSteps; ++kk)
+            qf[r][kk] = rok[r] ? *(const u32x4 *)(qp + kk * 16) : u32x4{0, 0, 0, 0};
+    }
+    f32x16 oacc[2][kDBlocks];
+#pragma unroll
+    for (int r = 0; r < 2; ++r)
+#pragma unroll
+        for (int db = 0; db < kDBlocks; ++db) oacc[r][db] = f32x16{};
+    float m_run[2] = {-INFINITY, -INFINITY}, l_run[2] = {0.f, 0.f};
+    float o_scale[2] = {1.f, 1.f};  // deferred O rescale (see above)
+
+    const uint16_t *kbase = (const uint16_t *)nd.k + (int64_t)task.g * nd.stride_head;
+    const uint16_t *vbase = (const uint16_t *)nd.v + (int64_t)task.g * nd.stride_head;
+    // Per-lane element offsets of this wave's DMAs within a tile (32-bit: the
+    // host picks this kernel only when 64 * stride_tok + d fits).
+    int dma_row[kDmas];
+    uint32_t koff[kDmas], voff[kDmas];
+#pragma unroll
+    for (int j = 0; j < kDmas; ++j) {
+        const int r = (wave * kDmas + j) * kRowsPerDma + lane / kRowChunks;
+        const int pos = lane % kRowChunks;
+        dma_row[j] = r;
+        koff[j] = (uint32_t)(r * nd.stride_tok) + (pos ^ (r % kRowChunks)) * 8;
+        voff[j] = (uint32_t)(r * nd.stride_tok) + (pos ^ (2 * (r % (kRowChunks / 2)))) * 8;
+    }
+    auto issue = [&](int tile) {
+        const int st = (tile - tb) % kStages;
+        const int key0 = tile * kTile;
+        const int64_t tile_off = (int64_t)key0 * nd.stride_tok;
+        const uint16_t *kt = kbase + tile_off;
+        const uint16_t *vt = vbase + tile_off;
+        const bool full = key0 + kTile <= nd.len;
+#pragma unroll
+        for (int j = 0; j < kDmas; ++j) {
+            uint16_t *dst = &lds[st][0][(wave * kDmas + j) * kRowsPerDma * D];
+            uint32_t ko = koff[j], vo = voff[j];
+            if (!full && key0 + dma_row[j] >= nd.len) {
+                // keys past the node's end re-read its last key (masked to -inf)
+                const uint32_t back =
+                    (uint32_t)((key0 + dma_row[j] - (nd.len - 1)) * nd.stride_tok);
+                ko -= back;
+                vo -= back;
+            }
+            dma16(kt + ko, dst);
+            dma16(vt + vo, dst + kTileElems);
+        }
+    };
+    const int k_swz = n % kRowChunks;
+    f32x16 sc[2][2];  // scores of the current tile, both row blocks, both key halves
+    auto qk = [&](int st) {
+        const uint16_t *kb = &lds[st][0][n * D];
+#pragma unroll
+        for (int r = 0; r < 2; ++r) sc[r][0] = sc[r][1] = f32x16{};
+#pragma unroll
+        for (int kk = 0; kk < kDSteps; ++kk) {
+            const int col = ((2 * kk + hi) ^ k_swz) * 8;
+            const u32x4 a0 = *(const u32x4 *)&kb[col];
+            const u32x4 a1 = *(const u32x4 *)&kb[32 * D + col];
+            sc[0][0] = mfma32x32x16<kBf16>(a0, qf[0][kk], sc[0][0]);
+            sc[1][0] = mfma32x32x16<kBf16>(a0, qf[1][kk], sc[1][0]);
+            sc[0][1] = mfma32x32x16<kBf16>(a1, qf[0][kk], sc[0][1]);
+            sc[1][1] = mfma32x32x16<kBf16>(a1, qf[1][kk], sc[1][1]);
+        }
+    };
+    // Mask a partial tile, then the new running max (l rescaled now, O later).
+    auto max_step = [&](int tile) {
+        const int valid = nd.len - tile * kTile;
+        if (valid < kTile) {
+#pragma unroll
+            for (int i = 0; i < 16; ++i) {
+                const int kr = 8 * (i / 4) + 4 * hi + (i % 4);
+#pragma unroll
+                for (int r = 0; r < 2; ++r) {
+                    if (kr >= valid) sc[r][0][i] = -INFINITY;
+                    if (32 + kr >= valid) sc[r][1][i] = -INFINITY;
+                }
+            }
+        }
+#pragma unroll
+        for (int r = 0; r < 2; ++r) {
+            float alpha;
+            if (softmax_max<kBf16>(sc[r][0], sc[r][1], c, m_run[r], l_run[r], alpha))
+                o_scale[r] *= alpha;
+        }
+    };
+    const int gi = lane >> 4, li = lane & 15;
+    const int v_key = 4 * hi + (li >> 2);
+    const int v_swz = 2 * (v_key % (kRowChunks / 2));
+    int v_col[kDBlocks];
+#pragma unroll
+    for (int db = 0; db < kDBlocks; ++db)
+        v_col[db] = v_key * D + ((4 * db + 2 * (gi & 1) + ((li & 3) >> 1)) ^ v_swz) * 8 +
+                    (li & 1) * 4;
+    // O += V P for both row blocks; each V operand read feeds two MFMAs.
+    auto pv = [&](const uint32_t (&pk)[2][16], int st) {
+        const uint16_t *vb = &lds[st][1][0];
+#pragma unroll
+        for (int u = 0; u < 4; ++u) {
+            const u32x4 b0 = {pk[0][4 * u], pk[0][4 * u + 1], pk[0][4 * u + 2], pk[0][4 * u + 3]};
+            const u32x4 b1 = {pk[1][4 * u], pk[1][4 * u + 1], pk[1][4 * u + 2], pk[1][4 * u + 3]};
+#pragma unroll
+            for (int db = 0; db < kDBlocks; ++db) {
+                const uint16_t *vr = vb + 16 * u * D + v_col[db];
+                const u32x2 lo = lds_read_tr16(vr);
+                const u32x2 up = lds_read_tr16(vr + 8 * D);
+                const u32x4 aop = {lo.x, lo.y, up.x, up.y};
+                oacc[0][db] = mfma32x32x16<kBf16>(aop, b0, oacc[0][db]);
+                oacc[1][db] = mfma32x32x16<kBf16>(aop, b1, oacc[1][db]);
+            }
+        }
+    };
+    auto apply_scale = [&]() {
+#pragma unroll
+        for (int r = 0; r < 2; ++r) {
+            if (__any(o_scale[r] != 1.f)) {
+#pragma unroll
+                for (int db = 0; db < kDBlocks; ++db) oacc[r][db] *= o_scale[r];
+                o_scale[r] = 1.f;
+            }
+        }
+    };
+    // Iteration for tile i: refill, exp(i) || PV(i-1), deferred O rescale,
+    // wait for tile i+1, S(i+1) and its max.
+    auto step = [&](int tile, uint32_t (&pk)[2][16], const uint32_t (&pk_prev)[2][16]) {
+        if (tile + 2 < te) issue(tile + 2);
+        softmax_exp<kBf16>(sc[0][0], sc[0][1], c, m_run[0], l_run[0], pk[0]);
+        softmax_exp<kBf16>(sc[1][0], sc[1][1], c, m_run[1], l_run[1], pk[1]);
+        if (tile > tb) {
+            pv(pk_prev, (tile - 1 - tb) % kStages);
+#pragma unroll
+            for (int k = 0; k < 8 * kDBlocks; ++k) {
+                __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);  // one MFMA
+                __builtin_amdgcn_sched_group_barrier(0x002, 4, 0);  // four VALU
+                __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);  // one LDS read
+            }
+        }
+        apply_scale();
+        if (tile + 1 < te) {
+            // tile+1 was issued one iteration ago: this wave's part, then everyone's
+            if (tile + 2 < te) wait_vmcnt<2 * kDmas>();
+            else wait_vmcnt<0>();
+            __builtin_amdgcn_s_barrier();
+            qk((tile + 1 - tb) % kStages);
+            max_step(tile + 1);
+        }
+        // every wave is done with the stage of tile-1 before tile+3 refills it
+        __builtin_amdgcn_s_barrier();
+    };
+
+    if (tb < te) {
+        issue(tb);
+        if (tb + 1 < te) issue(tb + 1);
+        if (tb + 1 < te) wait_vmcnt<2 * kDmas>();
+        else wait_vmcnt<0>();
+        __builtin_amdgcn_s_barrier();
+        qk(0);
+        max_step(tb);
+        uint32_t pa[2][16], pb[2][16];
+        int tile = tb;
+#pragma unroll 1
+        for (; tile + 1 < te; tile += 2) {  // two tiles per trip: the P sets alternate
+            step(tile, pa, pb);
+            step(tile + 1, pb, pa);
+        }
+        if (tile < te) {
+            step(tile, pa, pb);
+            pv(pa, (tile - tb) % kStages);
+        } else {
+            pv(pb, (tile - 1 - tb) % kStages);
+        }
+        apply_scale();
+    }
+
+#pragma unroll
+    for (int r = 0; r < 2; ++r) {
+        if (rok[r]) {
+            const int64_t ri = ((int64_t)(bi[r] - nd.dest.row_base)) * args.Hq + hq[r];
+            write_row<D>(nd.dest, task.split, ri, oacc[r], hi, m_run[r], l_run[r]);
+        }
     }
 }
 
@@ -357,6 +786,9 @@ __global__ __launch_bounds__(64 * NW) void prefix_mfma32_kernel(PrefixArgs args)
     }
 }
 
+// The 64-row-per-wave kernel is off until it has been validated on hardware.
+constexpr bool kWideEnabled = false;
+
 template <int NW>
 static hipError_t launch_nw(const PrefixArgs &a, int dtype, int d, int wgs, hipStream_t s) {
     const dim3 grid(wgs), block(64 * NW);
@@ -374,6 +806,17 @@ static hipError_t launch_nw(const PrefixArgs &a, int dtype, int d, int wgs, hipS
 }
 
 hipError_t launch_prefix(const PrefixArgs &a, int dtype, int d, int nw, int wgs, hipStream_t s) {
+    if (kWideEnabled && nw == kWideRows / 32 && dtype != HP_F32) {  // 4 waves x 64 rows
+        const dim3 grid(wgs), block(256);
+        if (dtype == HP_BF16) {
+            if (d == 128) prefix_mfma16_wide_kernel<true, 128><<<grid, block, 0, s>>>(a);
+            else prefix_mfma16_wide_kernel<true, 64><<<grid, block, 0, s>>>(a);
+        } else {
+            if (d == 128) prefix_mfma16_wide_kernel<false, 128><<<grid, block, 0, s>>>(a);
+            else prefix_mfma16_wide_kernel<false, 64><<<grid, block, 0, s>>>(a);
+        }
+        return hipGetLastError();
+    }
     switch (nw) {
     case 1: return launch_nw<1>(a, dtype, d, wgs, s);
     case 2: return launch_nw<2>(a, dtype, d, wgs, s);

@@ -1,4 +1,5 @@
-// Suffix pass: per-sequence paged decode attention.
+// Suffix pass: per-sequence paged decode attention, with the final merge of
+// the prefix passes' partials fused into its epilogue.
 //
 // Each sequence's private keys cannot be shared with any other query, so this
 // pass is a plain single-query attention per (sequence, KV head), streaming
@@ -6,18 +7,21 @@
 // High-Throughput LLM Inference with Shared Prefixes", section "Inter-Sequence
 // Batched Prefix Attention", on suffix attention; "ChunkAttention: Efficient
 // Self-Attention with Prefix-Aware KV Cache and Two-Phase Partition", section
-// "The Sequence-First Phase Kernel in Detail", for the per-sequence walk over
-// private chunks with an online-softmax reduce).  Its arithmetic intensity is
-// G FLOP per byte at most, so it is bound by HBM: the vector ALUs do the dot
-// products and the matrix cores are not used.
+// "The Sequence-First Phase Kernel in Detail": per sequence, reduce the saved
+// partials of the shared chunks, then walk the private chunks).  Its
+// arithmetic intensity is at most G FLOP per byte, so it is bound by HBM: the
+// vector ALUs do the dot products and the matrix cores are not used.
 //
-// One wave owns one (sequence, KV head, block range) work item and the G
-// query heads of that KV head.  A token's d values are spread over d*size/16
-// lanes (16 bytes per lane, one coalesced row per lane group), so a wave
-// covers 64*16/(d*size) tokens per load; the partial dot products are summed
-// across the lane group, and the online-softmax state is kept per query head.
-// A long suffix is split into fixed ranges of blocks across waves; each range
-// writes its own normalised (O, LSE) partial for the merge.
+// One workgroup owns one (sequence, KV head) and the G query heads of that KV
+// head.  Its waves take the sequence's blocks in turn (wave w: blocks w,
+// w+W, ...), each keeping the next block's loads in flight while it computes
+// the current one.  A token's d values are spread over 16-byte lane slices (16
+// lanes per token for 16-bit d = 128), so one load instruction covers several
+// whole rows; partial dot products are summed inside each 16-lane row with
+// DPP.  The waves' online-softmax states meet in LDS, and one pass merges them
+// with every prefix partial of the row's tree levels, in the exp2 domain:
+// O = sum_i w_i O_i / sum_i w_i, w_i = 2^(L_i - max L) (the Hydragen page's
+// "Attention Decomposition Across Subsequences", Eq. 5, over all parts).
 #include "common.hpp"
 
 namespace hp {
@@ -44,24 +48,43 @@ struct Elem<HP_BF16> {
     }
 };
 
-template <int kDt, int D, int G>
-__global__ __launch_bounds__(256) void suffix_kernel(SuffixArgs a) {
+template <int kCtrl>
+__device__ __forceinline__ float dpp(float x) {
+    return __int_as_float(__builtin_amdgcn_mov_dpp(__float_as_int(x), kCtrl, 0xf, 0xf, true));
+}
+
+// Sum over aligned groups of kWidth consecutive lanes; every lane of a group
+// ends with the group's sum.  Within a 16-lane row: quad swaps, then the
+// half-row mirror (lane i <-> 7-i) and the row mirror (i <-> 15-i), each of
+// which pairs every lane with one from the other half of its group.
+template <int kWidth>
+__device__ __forceinline__ float group_sum(float x) {
+    if constexpr (kWidth >= 2) x += dpp<0xb1>(x);   // quad_perm [1,0,3,2]
+    if constexpr (kWidth >= 4) x += dpp<0x4e>(x);   // quad_perm [2,3,0,1]
+    if constexpr (kWidth >= 8) x += dpp<0x141>(x);  // row_half_mirror
+    if constexpr (kWidth >= 16) x += dpp<0x140>(x); // row_mirror
+    if constexpr (kWidth >= 32) x += __shfl_xor(x, 16, kWave);
+    return x;
+}
+
+template <int kDt, int D, int G, int NWS>
+__global__ __launch_bounds__(64 * NWS) void suffix_kernel(SuffixArgs a) {
     using E = Elem<kDt>;
     constexpr int kEpl = 16 / E::kSize;  // elements per lane per token
     constexpr int kLpt = D / kEpl;       // lanes per token
     constexpr int kTpp = kWave / kLpt;   // tokens per wave-wide load
     constexpr int kPasses = kBlock / kTpp;
+    constexpr int kThreads = 64 * NWS;
     static_assert(kLpt <= kWave && kPasses >= 1, "layout");
+    __shared__ float sm_acc[NWS][G][D];
+    __shared__ float sm_m[NWS][G], sm_l[NWS][G];
+    __shared__ int sm_bad[NWS];
 
-    const int wave = threadIdx.x / kWave;
-    const int lane = threadIdx.x % kWave;
-    const int64_t item = (int64_t)blockIdx.x * 4 + wave;
-    const int64_t total = (int64_t)a.B * a.Hkv * a.nsplit;
-    if (item >= total) return;
-    const int split = (int)(item % a.nsplit);
-    const int64_t bg = item / a.nsplit;
-    const int g = (int)(bg % a.Hkv);
-    const int b = (int)(bg / a.Hkv);
+    const int tid = threadIdx.x;
+    const int wave = tid / kWave;
+    const int lane = tid % kWave;
+    const int g = (int)(blockIdx.x % a.Hkv);
+    const int b = (int)(blockIdx.x / a.Hkv);
     const int tg = lane / kLpt;  // token slot within a load
     const int li = lane % kLpt;  // lane within the token's group
     const int d0 = li * kEpl;
@@ -76,11 +99,13 @@ __global__ __launch_bounds__(256) void suffix_kernel(SuffixArgs a) {
         for (int e = 0; e < kEpl; ++e) qf[j][e] = E::get(w, e);
     }
 
-    const int len = a.lens[b];
-    bool bad = len < 0 || len > a.max_blocks * kBlock;
+    int len = 0;
+    bool bad = false;
+    if (a.has_suffix) {
+        len = a.lens[b];
+        bad = len < 0 || len > a.max_blocks * kBlock;
+    }
     const int nblk = bad ? 0 : (len + kBlock - 1) / kBlock;
-    const int blk0 = split * a.blocks_per_split;
-    const int blk1 = min(blk0 + a.blocks_per_split, nblk);
 
     float m[G], l[G], acc[G][kEpl];
 #pragma unroll
@@ -94,38 +119,42 @@ __global__ __launch_bounds__(256) void suffix_kernel(SuffixArgs a) {
     const int64_t tok_stride = (int64_t)a.Hkv * D * E::kSize;  // bytes between tokens of a block
     const char *kp = (const char *)a.k_pool;
     const char *vp = (const char *)a.v_pool;
+    const int *trow = a.table + (int64_t)b * a.max_blocks;
 
-#pragma unroll 1
-    for (int blk = blk0; blk < blk1; ++blk) {
-        const int id = a.table[(int64_t)b * a.max_blocks + blk];
-        if (id < 0 || id >= a.num_blocks) {  // never dereferenced; the row becomes NaN
-            bad = true;
-            continue;
-        }
-        const int64_t base = ((int64_t)id * kBlock * a.Hkv + g) * D * E::kSize + d0 * E::kSize;
-        u32x4 kr[kPasses], vr[kPasses];
-        bool ok[kPasses];
+    // Issue the loads of one block (keys past the sequence's end and blocks
+    // with an out-of-range id are never read).
+    auto fetch = [&](int blk, u32x4 (&kr)[kPasses], u32x4 (&vr)[kPasses], int &valid) {
+        const int id = trow[blk];
+        const bool id_ok = id >= 0 && id < a.num_blocks;
+        bad |= !id_ok;
+        valid = id_ok ? min(kBlock, len - blk * kBlock) : 0;
+        const int64_t base = ((int64_t)(id_ok ? id : 0) * kBlock * a.Hkv + g) * D * E::kSize +
+                             d0 * E::kSize;
 #pragma unroll
         for (int p = 0; p < kPasses; ++p) {
             const int t = p * kTpp + tg;
-            ok[p] = blk * kBlock + t < len;
+            const bool ok = t < valid;
             const int64_t off = base + t * tok_stride;
-            kr[p] = ok[p] ? *(const u32x4 *)(kp + off) : u32x4{0, 0, 0, 0};
-            vr[p] = ok[p] ? *(const u32x4 *)(vp + off) : u32x4{0, 0, 0, 0};
+            kr[p] = ok ? *(const u32x4 *)(kp + off) : u32x4{0, 0, 0, 0};
+            vr[p] = ok ? *(const u32x4 *)(vp + off) : u32x4{0, 0, 0, 0};
         }
+    };
+    // Online-softmax update with one block (exp2 domain, scale folded in).
+    auto process = [&](const u32x4 (&kr)[kPasses], const u32x4 (&vr)[kPasses], int valid) {
         float x[kPasses][G];
 #pragma unroll
         for (int p = 0; p < kPasses; ++p) {
             float kf[kEpl];
 #pragma unroll
             for (int e = 0; e < kEpl; ++e) kf[e] = E::get(kr[p], e);
+            const bool ok = p * kTpp + tg < valid;
 #pragma unroll
             for (int j = 0; j < G; ++j) {
                 float dot = 0.f;
 #pragma unroll
                 for (int e = 0; e < kEpl; ++e) dot = fmaf(qf[j][e], kf[e], dot);
-                dot = xor_sum<kLpt>(dot);
-                x[p][j] = ok[p] ? dot * a.scale_log2 : -INFINITY;
+                dot = group_sum<kLpt>(dot);
+                x[p][j] = ok ? dot * a.scale_log2 : -INFINITY;
             }
         }
 #pragma unroll
@@ -148,60 +177,150 @@ __global__ __launch_bounds__(256) void suffix_kernel(SuffixArgs a) {
                 for (int e = 0; e < kEpl; ++e) acc[j][e] = fmaf(pw, E::get(vr[p], e), acc[j][e]);
             }
         }
+    };
+
+    // Blocks wave, wave + NWS, ...: two register sets, the next block's loads
+    // are in flight while the current block is computed.
+    {
+        u32x4 k0[kPasses], v0[kPasses], k1[kPasses], v1[kPasses];
+        int n0 = 0, n1 = 0;
+        int blk = wave;
+        if (blk < nblk) fetch(blk, k0, v0, n0);
+#pragma unroll 1
+        for (; blk < nblk; blk += 2 * NWS) {
+            const int b1 = blk + NWS, b2 = blk + 2 * NWS;
+            if (b1 < nblk) fetch(b1, k1, v1, n1);
+            if (n0 > 0) process(k0, v0, n0);
+            if (b2 < nblk) fetch(b2, k0, v0, n0);
+            if (b1 < nblk && n1 > 0) process(k1, v1, n1);
+        }
     }
 
-    // Sum the token groups' partial denominators and value sums.
-    float *obase = a.dest.o + (int64_t)split * a.dest.o_split;
+    // This wave's state: sum the token groups, publish to LDS.
 #pragma unroll
     for (int j = 0; j < G; ++j) {
         const float lt = xor_sum_from<kLpt>(l[j]);
-        float out[kEpl];
 #pragma unroll
-        for (int e = 0; e < kEpl; ++e) out[e] = xor_sum_from<kLpt>(acc[j][e]);
-        const bool empty = !(lt > 0.f);
-        const float inv = empty ? 0.f : 1.f / lt;
-        float lse = empty ? -INFINITY : (m[j] + fast_log2(lt)) * kLn2;
-        if (bad) lse = NAN;
-        if (tg == 0) {
-            const int64_t ri = ((int64_t)(b - a.dest.row_base)) * a.Hq + g * G + j;
-            float *op = obase + ri * D + d0;
-#pragma unroll
-            for (int e = 0; e < kEpl; e += 4) {
-                f32x4 v;
-                v.x = bad ? NAN : out[e + 0] * inv;
-                v.y = bad ? NAN : out[e + 1] * inv;
-                v.z = bad ? NAN : out[e + 2] * inv;
-                v.w = bad ? NAN : out[e + 3] * inv;
-                *(f32x4 *)(op + e) = v;
-            }
-            if (li == 0 && a.dest.lse != nullptr)
-                a.dest.lse[(int64_t)split * a.dest.lse_split + ri] = lse;
+        for (int e = 0; e < kEpl; ++e) {
+            const float s = xor_sum_from<kLpt>(acc[j][e]);
+            if (tg == 0) sm_acc[wave][j][d0 + e] = s;
         }
+        if (lane == 0) {
+            sm_m[wave][j] = m[j];
+            sm_l[wave][j] = lt;
+        }
+    }
+    if (lane == 0) sm_bad[wave] = bad ? 1 : 0;
+    __syncthreads();
+
+    // Final merge: this row's suffix (the waves' states) and every prefix
+    // partial of the tree levels covering sequence b.
+    bool any_bad = false;
+#pragma unroll
+    for (int w = 0; w < NWS; ++w) any_bad |= sm_bad[w] != 0;
+#pragma unroll 1
+    for (int t = tid; t < G * (D / 4); t += kThreads) {
+        const int j = t / (D / 4);
+        const int c4 = (t % (D / 4)) * 4;
+        const int h = g * G + j;
+        // suffix part, unnormalised: (sum_w 2^(m_w - Ms) acc_w, sum_w 2^(m_w - Ms) l_w)
+        float ms = -INFINITY;
+#pragma unroll
+        for (int w = 0; w < NWS; ++w) ms = fmaxf(ms, sm_m[w][j]);
+        f32x4 so = {0.f, 0.f, 0.f, 0.f};
+        float sl = 0.f;
+        if (ms > -INFINITY) {
+#pragma unroll
+            for (int w = 0; w < NWS; ++w) {
+                const float f = fast_exp2(sm_m[w][j] - ms);
+                sl += f * sm_l[w][j];
+                so += f * *(const f32x4 *)&sm_acc[w][j][c4];
+            }
+        }
+        // prefix parts: normalised O_i with natural-log LSE_i
+        float mx = sl > 0.f ? ms : -INFINITY;
+        bool nan_seen = false;
+#pragma unroll 1
+        for (int si = 0; si < a.nsrc; ++si) {
+            const MergeSrc &s = a.src[si];
+            if (b < s.b0 || b >= s.b1) continue;
+            const int64_t ri = (b - s.b0) * a.Hq + h;
+#pragma unroll 4
+            for (int i = 0; i < s.nsplit; ++i) {
+                const float L = s.lse[(int64_t)i * s.lse_split + ri] * kLog2e;
+                nan_seen |= (L != L);
+                mx = fmaxf(mx, L);
+            }
+        }
+        f32x4 out;
+        float lse;
+        if (any_bad || nan_seen) {
+            out = f32x4{NAN, NAN, NAN, NAN};
+            lse = NAN;
+        } else if (!(mx > -INFINITY)) {
+            out = f32x4{0.f, 0.f, 0.f, 0.f};
+            lse = -INFINITY;
+        } else {
+            float den = 0.f;
+            f32x4 num = {0.f, 0.f, 0.f, 0.f};
+            if (sl > 0.f) {
+                const float f = fast_exp2(ms - mx);
+                den = sl * f;
+                num = so * f;
+            }
+#pragma unroll 1
+            for (int si = 0; si < a.nsrc; ++si) {
+                const MergeSrc &s = a.src[si];
+                if (b < s.b0 || b >= s.b1) continue;
+                const int64_t ri = (b - s.b0) * a.Hq + h;
+#pragma unroll 4
+                for (int i = 0; i < s.nsplit; ++i) {
+                    const float w =
+                        fast_exp2(s.lse[(int64_t)i * s.lse_split + ri] * kLog2e - mx);
+                    num += w * *(const f32x4 *)(s.o + (int64_t)i * s.o_split + ri * D + c4);
+                    den += w;
+                }
+            }
+            out = num * (1.f / den);
+            lse = (mx + fast_log2(den)) * kLn2;
+        }
+        const int64_t orow = ((int64_t)b - a.dest.row_base) * a.Hq + h;
+        *(f32x4 *)(a.dest.o + orow * D + c4) = out;
+        if (c4 == 0 && a.dest.lse != nullptr) a.dest.lse[orow] = lse;
     }
 }
 
-template <int kDt, int D>
+template <int kDt, int D, int NWS>
 static void launch_g(const SuffixArgs &a, int G, dim3 grid, hipStream_t s) {
+    constexpr int T = 64 * NWS;
     switch (G) {
-    case 1: suffix_kernel<kDt, D, 1><<<grid, 256, 0, s>>>(a); break;
-    case 2: suffix_kernel<kDt, D, 2><<<grid, 256, 0, s>>>(a); break;
-    case 4: suffix_kernel<kDt, D, 4><<<grid, 256, 0, s>>>(a); break;
-    default: suffix_kernel<kDt, D, 8><<<grid, 256, 0, s>>>(a); break;
+    case 1: suffix_kernel<kDt, D, 1, NWS><<<grid, T, 0, s>>>(a); break;
+    case 2: suffix_kernel<kDt, D, 2, NWS><<<grid, T, 0, s>>>(a); break;
+    case 4: suffix_kernel<kDt, D, 4, NWS><<<grid, T, 0, s>>>(a); break;
+    default: suffix_kernel<kDt, D, 8, NWS><<<grid, T, 0, s>>>(a); break;
     }
+}
+
+template <int kDt, int NWS>
+static void launch_d(const SuffixArgs &a, int d, int G, dim3 grid, hipStream_t s) {
+    if (d == 128) launch_g<kDt, 128, NWS>(a, G, grid, s);
+    else launch_g<kDt, 64, NWS>(a, G, grid, s);
 }
 
 template <int kDt>
-static void launch_dt(const SuffixArgs &a, int d, int G, dim3 grid, hipStream_t s) {
-    if (d == 128) launch_g<kDt, 128>(a, G, grid, s);
-    else launch_g<kDt, 64>(a, G, grid, s);
+static void launch_dt(const SuffixArgs &a, int d, int G, int nws, dim3 grid, hipStream_t s) {
+    switch (nws) {
+    case 1: launch_d<kDt, 1>(a, d, G, grid, s); break;
+    case 2: launch_d<kDt, 2>(a, d, G, grid, s); break;
+    default: launch_d<kDt, 4>(a, d, G, grid, s); break;
+    }
 }
 
-hipError_t launch_suffix(const SuffixArgs &a, int dtype, int d, int G, hipStream_t s) {
-    const int64_t items = (int64_t)a.B * a.Hkv * a.nsplit;
-    const dim3 grid((unsigned)((items + 3) / 4));
-    if (dtype == HP_BF16) launch_dt<HP_BF16>(a, d, G, grid, s);
-    else if (dtype == HP_F16) launch_dt<HP_F16>(a, d, G, grid, s);
-    else launch_dt<HP_F32>(a, d, G, grid, s);
+hipError_t launch_suffix(const SuffixArgs &a, int dtype, int d, int G, int nws, hipStream_t s) {
+    const dim3 grid((unsigned)((int64_t)a.B * a.Hkv));
+    if (dtype == HP_BF16) launch_dt<HP_BF16>(a, d, G, nws, grid, s);
+    else if (dtype == HP_F16) launch_dt<HP_F16>(a, d, G, nws, grid, s);
+    else launch_dt<HP_F32>(a, d, G, nws, grid, s);
     return hipGetLastError();
 }
 
