@@ -127,13 +127,16 @@ def time_steps(call, ev: HipEvents, steps: int, warmup: int):
 
 
 def time_cold(call, ev: HipEvents, steps: int) -> float:
-    """Median step time (ms) with 1 GiB written between steps (more than 2x the 256 MB
-    Infinity Cache), so no step starts with its inputs cached."""
+    """Median step time (ms) with 1 GiB read between steps (more than 2x the 256 MB
+    Infinity Cache), so no step starts with its inputs cached.  The flush reads rather
+    than writes: a written flush leaves the caches full of dirty lines whose write-back
+    then competes with the step's own reads, which measures the flush, not the step."""
     import torch
-    flush = torch.empty(1 << 28, dtype=torch.float32, device="cuda:0")
+    flush = torch.ones(1 << 28, dtype=torch.float32, device="cuda:0")
+    sink = torch.zeros((), dtype=torch.float32, device="cuda:0")
     times = []
     for _ in range(steps):
-        flush.fill_(1.0)
+        sink += flush.sum()
         e = ev.create(4)
         call.timed(e)
         times.append(ev.ms(e[0], e[3]))
@@ -157,7 +160,7 @@ def cpu_baseline(step, target_s: float):
     if os.environ.get("OMP_NUM_THREADS", "").isdigit():
         threads = min(threads, int(os.environ["OMP_NUM_THREADS"]))
     rng = np.random.default_rng(0)
-    probe = np.sort(rng.choice(total, size=min(total, max(threads, 32)), replace=False))
+    probe = np.sort(rng.choice(total, size=min(total, max(4 * threads, 64)), replace=False))
     t0 = time.perf_counter()
     oracle.step_attention(step, "all", rows=probe, nthreads=threads)
     per_row = (time.perf_counter() - t0) / len(probe)

@@ -179,10 +179,13 @@ __device__ __forceinline__ float add_packed(uint32_t pk, float sum) {
 template <bool kBf16>
 __device__ __forceinline__ bool softmax_max(const f32x16 &s0, const f32x16 &s1, float c,
                                             float &m_run, float &l_run, float &alpha) {
-    float mt = fmaxf(s0[0], s1[0]);
+    // maximum (not fmaxf): no NaN canonicalisation of every input, and
+    // v_maximum3 takes two new scores per instruction.
+    float mt = __builtin_elementwise_maximum(s0[0], s1[0]);
 #pragma unroll
-    for (int i = 1; i < 16; ++i) mt = fmaxf(mt, fmaxf(s0[i], s1[i]));
-    mt = fmaxf(mt, __shfl_xor(mt, 32, kWave));
+    for (int i = 1; i < 16; ++i)
+        mt = __builtin_elementwise_maximum(mt, __builtin_elementwise_maximum(s0[i], s1[i]));
+    mt = fmaxf(mt, __shfl_xor(mt, 32, kWave));  // the other half-wave: the other keys of this query
     const float mts = mt * c;  // c > 0: the max commutes with the scaling
     const bool rescale = __any(mts > m_run + kLazy);
     alpha = 1.f;
@@ -215,6 +218,15 @@ __device__ __forceinline__ void softmax_exp(const f32x16 &s0, const f32x16 &s1, 
     l_run += sum;
 }
 
+// Position of a V row's 16-byte chunks in LDS: chunk c of row r sits at
+// c ^ v_swizzle(r).  The transposing read of one half-wave touches 4 rows x
+// 4 consecutive chunks; spreading rows 4 chunks apart within each 256-byte
+// bank line puts those 256 bytes on distinct banks.
+template <int D>
+__device__ __forceinline__ int v_swizzle(int r) {
+    return 4 * ((r / (128 / D)) % (D / 32));
+}
+
 // s_waitcnt with only vmcnt = n (expcnt and lgkmcnt left unconstrained).
 template <int n>
 __device__ __forceinline__ void wait_vmcnt() {
@@ -223,11 +235,33 @@ __device__ __forceinline__ void wait_vmcnt() {
 }
 
 // 16 bytes from global memory straight into LDS (gfx950 global_load_lds_dwordx4):
-// lane i writes lds_base + 16*i.
+// lane i writes lds_base + 16*i; lds_base is wave-uniform (M0).  Issued as
+// inline assembly so that the compiler does not track it: it cannot prove
+// that the transposing LDS reads of other stages do not alias the transfer,
+// and would otherwise wait for every transfer in flight before each of them.
+// Completion is this code's business: wait_vmcnt before block_sync.
 __device__ __forceinline__ void dma16(const void *g, void *lds_base) {
-    __builtin_amdgcn_global_load_lds((const __attribute__((address_space(1))) void *)g,
-                                     (__attribute__((address_space(3))) void *)lds_base, 16, 0,
-                                     0);
+    const uint32_t l = __builtin_amdgcn_readfirstlane(
+        (uint32_t)(uintptr_t)(__attribute__((address_space(3))) void *)lds_base);
+    uint32_t saved;  // M0 is reserved by the compiler: restore it
+    asm volatile(
+        "s_mov_b32 %0, m0\n\ts_mov_b32 m0, %2\n\tglobal_load_lds_dwordx4 %1, off\n\t"
+        "s_mov_b32 m0, %0"
+        : "=&s"(saved)
+        : "v"(g), "s"(l)
+        : "memory");
+}
+
+// Workgroup barrier that the compiler may not move memory accesses across
+// (LDS is written by DMA outside its view), taken after this wave's own LDS
+// reads have returned.
+__device__ __forceinline__ void block_sync() {
+    __builtin_amdgcn_s_waitcnt(0xC07F);  // lgkmcnt(0)
+    __builtin_amdgcn_sched_barrier(0);
+    asm volatile("" ::: "memory");
+    __builtin_amdgcn_s_barrier();
+    asm volatile("" ::: "memory");
+    __builtin_amdgcn_sched_barrier(0);
 }
 
 template <bool kBf16, int D, int NW>
@@ -283,6 +317,9 @@ __global__ __launch_bounds__(64 * NW) void prefix_mfma16_kernel(PrefixArgs args)
         for (int kk = 0; kk < kDSteps; ++kk)
             qf[kk] = row_ok ? *(const u32x4 *)(qp + kk * 16) : u32x4{0, 0, 0, 0};
     }
+    // Q must be in registers before the first transfer: the compiler does not
+    // count the transfers, and would otherwise wait for all of them to retire.
+    wait_vmcnt<0>();
 
     f32x16 oacc[kDBlocks];
 #pragma unroll
@@ -373,7 +410,7 @@ __global__ __launch_bounds__(64 * NW) void prefix_mfma16_kernel(PrefixArgs args)
         } else {
             wait_vmcnt<0>();
         }
-        __builtin_amdgcn_s_barrier();
+        block_sync();
         if (tile + kStages - 1 < te) issue(tile + kStages - 1);
 
         // Accumulator i of a 32x32 block holds key 8*(i/4) + 4*hi + i%4.
@@ -416,7 +453,7 @@ __global__ __launch_bounds__(64 * NW) void prefix_mfma16_kernel(PrefixArgs args)
             if (younger >= 1) wait_vmcnt<kPerTile>();
             else wait_vmcnt<0>();
         }
-        __builtin_amdgcn_s_barrier();
+        block_sync();
         f32x16 sa0, sa1, sb0, sb1;
         qk(0, sa0, sa1);
         int tile = tb;
@@ -439,16 +476,16 @@ __global__ __launch_bounds__(64 * NW) void prefix_mfma16_kernel(PrefixArgs args)
 // owns two 32-row blocks, so every K or V operand it reads from LDS feeds two
 // MFMAs: half the LDS traffic per FLOP of the 32-row layout, which at full
 // matrix-core rate would need about all of the LDS bandwidth.  One wave per
-// SIMD with the whole register file (O accumulators in AGPRs).  Latency is
-// hidden inside the wave by a one-tile skew: iteration i runs the
-// exponentials of tile i on the vector ALUs while the matrix cores do the
-// value product of tile i-1, then computes the scores of tile i+1.
+// SIMD with the whole register file (O accumulators in AGPRs).
 //
-// Online softmax with the skew: the row max can rise when tile i+1's scores
-// are seen, before tile i's value product (taken with the old max) has been
-// added to O.  The denominator is rescaled at once; the O rescale is deferred
-// until that product is in, so every term of O and l is taken relative to
-// the same max when they meet.
+// Keys are handled in 32-key halves of the 64-key DMA tiles, which keeps the
+// live scores and probabilities small.  Iteration j overlaps, inside the
+// wave, the score product of half j+1 on the matrix cores with the
+// exponentials of half j on the vector ALUs, then the value product of half
+// j with the row max of half j+1.  That max can rise before half j's value
+// product is in O: the denominator is rescaled at once, the O rescale is
+// applied after the product, so every term of O and l is relative to the same
+// max when they meet.
 // ---------------------------------------------------------------------------
 template <bool kBf16, int D>
 __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1)))
@@ -460,8 +497,7 @@ void prefix_mfma16_wide_kernel(PrefixArgs args) {
     constexpr int kRowsPerDma = kWave / kRowChunks;
     constexpr int kDmas = kTile / kRowsPerDma / NW;
     static_assert(kDmas >= 1 && kTile % (kRowsPerDma * NW) == 0, "tile split");
-    // Stages hold V(i-1) (value product), K(i+1) (next scores) and the tile in
-    // flight; iteration i refills the stage tile i-2 used with tile i+2.
+    // A ring of 4 tiles: the one being consumed, and up to three in flight.
     constexpr int kStages = 4;
     constexpr int kTileElems = kTile * D;
     __shared__ __attribute__((aligned(1024))) uint16_t lds[kStages][2][kTileElems];
@@ -499,6 +535,7 @@ void prefix_mfma16_wide_kernel(PrefixArgs args) {
         for (int kk = 0; kk < kDSteps; ++kk)
             qf[r][kk] = rok[r] ? *(const u32x4 *)(qp + kk * 16) : u32x4{0, 0, 0, 0};
     }
+    wait_vmcnt<0>();  // as in the 32-row kernel
     f32x16 oacc[2][kDBlocks];
 #pragma unroll
     for (int r = 0; r < 2; ++r)
@@ -510,7 +547,7 @@ void prefix_mfma16_wide_kernel(PrefixArgs args) {
     const uint16_t *kbase = (const uint16_t *)nd.k + (int64_t)task.g * nd.stride_head;
     const uint16_t *vbase = (const uint16_t *)nd.v + (int64_t)task.g * nd.stride_head;
     // Per-lane element offsets of this wave's DMAs within a tile (32-bit: the
-    // host picks this kernel only when 64 * stride_tok + d fits).
+    // launch picks this kernel only when kTile * stride_tok + d fits in int32).
     int dma_row[kDmas];
     uint32_t koff[kDmas], voff[kDmas];
 #pragma unroll
@@ -543,42 +580,66 @@ void prefix_mfma16_wide_kernel(PrefixArgs args) {
             dma16(vt + vo, dst + kTileElems);
         }
     };
+    // Stage and half of key half j (keys 32j .. 32j+31 of the node).
+    auto stage_of = [&](int j) { return (j / 2 - tb) % kStages; };
+
+    // S^T of one half for both row blocks: each K operand read feeds two MFMAs.
     const int k_swz = n % kRowChunks;
-    f32x16 sc[2][2];  // scores of the current tile, both row blocks, both key halves
-    auto qk = [&](int st) {
-        const uint16_t *kb = &lds[st][0][n * D];
-#pragma unroll
-        for (int r = 0; r < 2; ++r) sc[r][0] = sc[r][1] = f32x16{};
+    auto qk = [&](int j, f32x16 (&s)[2]) {
+        const uint16_t *kb = &lds[stage_of(j)][0][(32 * (j & 1) + n) * D];
+        s[0] = f32x16{};
+        s[1] = f32x16{};
 #pragma unroll
         for (int kk = 0; kk < kDSteps; ++kk) {
             const int col = ((2 * kk + hi) ^ k_swz) * 8;
-            const u32x4 a0 = *(const u32x4 *)&kb[col];
-            const u32x4 a1 = *(const u32x4 *)&kb[32 * D + col];
-            sc[0][0] = mfma32x32x16<kBf16>(a0, qf[0][kk], sc[0][0]);
-            sc[1][0] = mfma32x32x16<kBf16>(a0, qf[1][kk], sc[1][0]);
-            sc[0][1] = mfma32x32x16<kBf16>(a1, qf[0][kk], sc[0][1]);
-            sc[1][1] = mfma32x32x16<kBf16>(a1, qf[1][kk], sc[1][1]);
+            const u32x4 a = *(const u32x4 *)&kb[col];
+            s[0] = mfma32x32x16<kBf16>(a, qf[0][kk], s[0]);
+            s[1] = mfma32x32x16<kBf16>(a, qf[1][kk], s[1]);
         }
     };
-    // Mask a partial tile, then the new running max (l rescaled now, O later).
-    auto max_step = [&](int tile) {
-        const int valid = nd.len - tile * kTile;
-        if (valid < kTile) {
+    // Mask keys past the node's end, then the lazy running-max update: l is
+    // rescaled now, O through o_scale after the pending value product.
+    auto max_step = [&](int j, f32x16 (&s)[2]) {
+        const int valid = nd.len - j * 32;
+        if (valid < 32) {
 #pragma unroll
             for (int i = 0; i < 16; ++i) {
                 const int kr = 8 * (i / 4) + 4 * hi + (i % 4);
-#pragma unroll
-                for (int r = 0; r < 2; ++r) {
-                    if (kr >= valid) sc[r][0][i] = -INFINITY;
-                    if (32 + kr >= valid) sc[r][1][i] = -INFINITY;
+                if (kr >= valid) {
+                    s[0][i] = -INFINITY;
+                    s[1][i] = -INFINITY;
                 }
             }
         }
 #pragma unroll
         for (int r = 0; r < 2; ++r) {
-            float alpha;
-            if (softmax_max<kBf16>(sc[r][0], sc[r][1], c, m_run[r], l_run[r], alpha))
+            float mt = s[r][0];
+#pragma unroll
+            for (int i = 1; i < 16; ++i) mt = fmaxf(mt, s[r][i]);
+            mt = fmaxf(mt, __shfl_xor(mt, 32, kWave)) * c;  // c > 0
+            if (__any(mt > m_run[r] + kLazy)) {
+                const float m_new = fmaxf(m_run[r], mt);
+                const float alpha = fast_exp2(m_run[r] - m_new);  // 0 the first time
+                l_run[r] *= alpha;
                 o_scale[r] *= alpha;
+                m_run[r] = m_new;
+            }
+        }
+    };
+    // Probabilities 2^(s*c - m) rounded to the 16-bit type, and the row sums
+    // of exactly those rounded values.
+    auto exp_step = [&](const f32x16 (&s)[2], uint32_t (&pk)[2][8]) {
+#pragma unroll
+        for (int r = 0; r < 2; ++r) {
+            const float neg_m = -m_run[r];
+            float sum = 0.f;
+#pragma unroll
+            for (int i = 0; i < 8; ++i) {
+                pk[r][i] = pack_p<kBf16>(fast_exp2(fmaf(s[r][2 * i], c, neg_m)),
+                                         fast_exp2(fmaf(s[r][2 * i + 1], c, neg_m)));
+                sum = add_packed<kBf16>(pk[r][i], sum);
+            }
+            l_run[r] += sum;
         }
     };
     const int gi = lane >> 4, li = lane & 15;
@@ -589,11 +650,11 @@ void prefix_mfma16_wide_kernel(PrefixArgs args) {
     for (int db = 0; db < kDBlocks; ++db)
         v_col[db] = v_key * D + ((4 * db + 2 * (gi & 1) + ((li & 3) >> 1)) ^ v_swz) * 8 +
                     (li & 1) * 4;
-    // O += V P for both row blocks; each V operand read feeds two MFMAs.
-    auto pv = [&](const uint32_t (&pk)[2][16], int st) {
-        const uint16_t *vb = &lds[st][1][0];
+    // O += V P for one half and both row blocks; each V operand feeds two MFMAs.
+    auto pv = [&](int j, const uint32_t (&pk)[2][8]) {
+        const uint16_t *vb = &lds[stage_of(j)][1][32 * (j & 1) * D];
 #pragma unroll
-        for (int u = 0; u < 4; ++u) {
+        for (int u = 0; u < 2; ++u) {
             const u32x4 b0 = {pk[0][4 * u], pk[0][4 * u + 1], pk[0][4 * u + 2], pk[0][4 * u + 3]};
             const u32x4 b1 = {pk[1][4 * u], pk[1][4 * u + 1], pk[1][4 * u + 2], pk[1][4 * u + 3]};
 #pragma unroll
@@ -617,56 +678,52 @@ void prefix_mfma16_wide_kernel(PrefixArgs args) {
             }
         }
     };
-    // Iteration for tile i: refill, exp(i) || PV(i-1), deferred O rescale,
-    // wait for tile i+1, S(i+1) and its max.
-    auto step = [&](int tile, uint32_t (&pk)[2][16], const uint32_t (&pk_prev)[2][16]) {
-        if (tile + 2 < te) issue(tile + 2);
-        softmax_exp<kBf16>(sc[0][0], sc[0][1], c, m_run[0], l_run[0], pk[0]);
-        softmax_exp<kBf16>(sc[1][0], sc[1][1], c, m_run[1], l_run[1], pk[1]);
-        if (tile > tb) {
-            pv(pk_prev, (tile - 1 - tb) % kStages);
-#pragma unroll
-            for (int k = 0; k < 8 * kDBlocks; ++k) {
-                __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);  // one MFMA
-                __builtin_amdgcn_sched_group_barrier(0x002, 4, 0);  // four VALU
-                __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);  // one LDS read
-            }
-        }
-        apply_scale();
-        if (tile + 1 < te) {
-            // tile+1 was issued one iteration ago: this wave's part, then everyone's
-            if (tile + 2 < te) wait_vmcnt<2 * kDmas>();
+    const int jb = 2 * tb, je = 2 * te;  // key halves of this split
+    // Iteration for half j (scores in sc): when half j+1 starts a tile, wait
+    // for it (this wave's DMAs, then everyone's) and refill the ring; then
+    // S(j+1) || exp(j), and O += V P(j) || max(j+1).
+    auto step = [&](int j, f32x16 (&sc)[2], f32x16 (&sn)[2]) {
+        const bool has_next = j + 1 < je;
+        if (has_next && (j & 1)) {
+            const int t1 = (j + 1) / 2;
+            if (t1 + 1 < te) wait_vmcnt<2 * kDmas>();
             else wait_vmcnt<0>();
-            __builtin_amdgcn_s_barrier();
-            qk((tile + 1 - tb) % kStages);
-            max_step(tile + 1);
+            block_sync();
+            // every wave is past the value product of tile t1-2, whose stage
+            // tile t1+2 takes
+            if (t1 + 2 < te) issue(t1 + 2);
         }
-        // every wave is done with the stage of tile-1 before tile+3 refills it
-        __builtin_amdgcn_s_barrier();
+        if (has_next) qk(j + 1, sn);
+        uint32_t pk[2][8];
+        exp_step(sc, pk);
+#pragma unroll
+        for (int k = 0; k < 2 * kDSteps; ++k) {
+            __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);  // one MFMA
+            __builtin_amdgcn_sched_group_barrier(0x002, 5, 0);  // five VALU
+        }
+        pv(j, pk);
+        if (has_next) max_step(j + 1, sn);
+        apply_scale();
     };
 
     if (tb < te) {
-        issue(tb);
-        if (tb + 1 < te) issue(tb + 1);
-        if (tb + 1 < te) wait_vmcnt<2 * kDmas>();
+#pragma unroll
+        for (int k = 0; k < 3; ++k)
+            if (tb + k < te) issue(tb + k);
+        const int younger = min(2, te - tb - 1);
+        if (younger == 2) wait_vmcnt<4 * kDmas>();
+        else if (younger == 1) wait_vmcnt<2 * kDmas>();
         else wait_vmcnt<0>();
-        __builtin_amdgcn_s_barrier();
-        qk(0);
-        max_step(tb);
-        uint32_t pa[2][16], pb[2][16];
-        int tile = tb;
+        block_sync();
+        f32x16 sa[2], sb[2];
+        qk(jb, sa);
+        max_step(jb, sa);
+        o_scale[0] = o_scale[1] = 1.f;  // O is still zero: nothing to rescale
 #pragma unroll 1
-        for (; tile + 1 < te; tile += 2) {  // two tiles per trip: the P sets alternate
-            step(tile, pa, pb);
-            step(tile + 1, pb, pa);
+        for (int j = jb; j < je; j += 2) {  // two halves per trip: the score sets alternate
+            step(j, sa, sb);
+            step(j + 1, sb, sa);
         }
-        if (tile < te) {
-            step(tile, pa, pb);
-            pv(pa, (tile - tb) % kStages);
-        } else {
-            pv(pb, (tile - 1 - tb) % kStages);
-        }
-        apply_scale();
     }
 
 #pragma unroll
@@ -675,6 +732,200 @@ void prefix_mfma16_wide_kernel(PrefixArgs args) {
             const int64_t ri = ((int64_t)(bi[r] - nd.dest.row_base)) * args.Hq + hq[r];
             write_row<D>(nd.dest, task.split, ri, oacc[r], hi, m_run[r], l_run[r]);
         }
+    }
+}
+
+// ---------------------------------------------------------------------------
+// Ping-pong variant for 256 rows per workgroup: 8 waves of 32 rows.  Waves w
+// and w+4 of a workgroup share a SIMD, so waves 0-3 and 4-7 form two groups
+// with one wave on every SIMD.  The groups run half a tile apart: while one
+// wave of a SIMD issues its matrix products (scores of tile u and the value
+// product of tile u-1) the other runs the softmax of its latest tile on the
+// vector ALUs, and the two swap roles at every workgroup barrier.  The matrix
+// cores and the vector ALUs of each SIMD are thus busy at the same time,
+// which a lockstep schedule of both waves cannot achieve.
+// ---------------------------------------------------------------------------
+
+template <bool kBf16, int D>
+__global__ __launch_bounds__(512) void prefix_mfma16_pp_kernel(PrefixArgs args) {
+    constexpr int NW = 8;
+    constexpr int kDSteps = D / 16;
+    constexpr int kDBlocks = D / 32;
+    constexpr int kRowChunks = D / 8;
+    constexpr int kRowsPerDma = kWave / kRowChunks;
+    constexpr int kDmas = kTile / kRowsPerDma / NW;
+    static_assert(kDmas >= 1 && kTile % (kRowsPerDma * NW) == 0, "tile split");
+    constexpr int kPerTile = 2 * kDmas;
+    // Tile u+2 is issued once both groups are past the value product of
+    // tile u-2, whose stage it takes: four stages, two tiles in flight.
+    constexpr int kStages = 4;
+    constexpr int kTileElems = kTile * D;
+    __shared__ __attribute__((aligned(1024))) uint16_t lds[kStages][2][kTileElems];
+
+    const WgTask task = decode_wg(args);
+    if (!task.valid) return;
+    const PrefixNodeArg &nd = args.nodes[task.node];
+    const int G = args.G;
+    const int M = (nd.seq_end - nd.seq_begin) * G;
+    const int ntiles = (nd.len + kTile - 1) / kTile;
+    const int tb = task.split * nd.tiles_per_split;
+    const int te = min(tb + nd.tiles_per_split, ntiles);
+
+    const int tid = threadIdx.x;
+    const int wave = tid / kWave;
+    const int lane = tid % kWave;
+    const int grp = wave >> 2;
+    const int n = lane & 31;
+    const int hi = lane >> 5;
+    const int row = task.rb * 32 * NW + wave * 32 + n;
+    const bool row_ok = row < M;
+    const int b = nd.seq_begin + (row_ok ? row / G : 0);
+    const int h = task.g * G + (row_ok ? row % G : 0);
+    const float c = args.scale_log2;
+
+    u32x4 qf[kDSteps];
+    {
+        const uint16_t *qp = (const uint16_t *)args.q + ((int64_t)b * args.Hq + h) * D + hi * 8;
+#pragma unroll
+        for (int kk = 0; kk < kDSteps; ++kk)
+            qf[kk] = row_ok ? *(const u32x4 *)(qp + kk * 16) : u32x4{0, 0, 0, 0};
+    }
+    // Q must be in registers before the first transfer: the compiler does not
+    // count the transfers, and would otherwise wait for all of them to retire.
+    wait_vmcnt<0>();
+    f32x16 oacc[kDBlocks];
+#pragma unroll
+    for (int db = 0; db < kDBlocks; ++db) oacc[db] = f32x16{};
+    float m_run = -INFINITY, l_run = 0.f;
+
+    const uint16_t *kbase = (const uint16_t *)nd.k + (int64_t)task.g * nd.stride_head;
+    const uint16_t *vbase = (const uint16_t *)nd.v + (int64_t)task.g * nd.stride_head;
+    int dma_row[kDmas], dma_ck[kDmas], dma_cv[kDmas];
+#pragma unroll
+    for (int j = 0; j < kDmas; ++j) {
+        const int r = (wave * kDmas + j) * kRowsPerDma + lane / kRowChunks;
+        const int pos = lane % kRowChunks;
+        dma_row[j] = r;
+        dma_ck[j] = (pos ^ (r % kRowChunks)) * 8;
+        dma_cv[j] = (pos ^ v_swizzle<D>(r)) * 8;
+    }
+    auto issue = [&](int tile) {
+        const int st = (tile - tb) % kStages;
+        const int key0 = tile * kTile;
+        const bool full = key0 + kTile <= nd.len;
+#pragma unroll
+        for (int j = 0; j < kDmas; ++j) {
+            const int t = full ? key0 + dma_row[j] : min(key0 + dma_row[j], nd.len - 1);
+            const int64_t off = (int64_t)t * nd.stride_tok;
+            uint16_t *dst = &lds[st][0][(wave * kDmas + j) * kRowsPerDma * D];
+            dma16(kbase + off + dma_ck[j], dst);
+            dma16(vbase + off + dma_cv[j], dst + kTileElems);
+        }
+    };
+    const int k_swz = n % kRowChunks;
+    f32x16 s0, s1;  // scores of the latest tile (keys 0-31, 32-63)
+    // All K operands of the tile are read before the first product, so the
+    // matrix core is not left waiting on one LDS round trip per k-step.
+    auto qk = [&](int st) {
+        const uint16_t *kb = &lds[st][0][n * D];
+        u32x4 ka[kDSteps][2];
+#pragma unroll
+        for (int kk = 0; kk < kDSteps; ++kk) {
+            const int col = ((2 * kk + hi) ^ k_swz) * 8;
+            ka[kk][0] = *(const u32x4 *)&kb[col];
+            ka[kk][1] = *(const u32x4 *)&kb[32 * D + col];
+        }
+        s0 = f32x16{};
+        s1 = f32x16{};
+#pragma unroll
+        for (int kk = 0; kk < kDSteps; ++kk) {
+            s0 = mfma32x32x16<kBf16>(ka[kk][0], qf[kk], s0);
+            s1 = mfma32x32x16<kBf16>(ka[kk][1], qf[kk], s1);
+        }
+        __builtin_amdgcn_sched_group_barrier(0x100, 2 * kDSteps, 0);  // the LDS reads
+        __builtin_amdgcn_sched_group_barrier(0x008, 2 * kDSteps, 0);  // then the products
+    };
+    const int gi = lane >> 4, li = lane & 15;
+    const int v_key = 4 * hi + (li >> 2);
+    const int v_swz = v_swizzle<D>(v_key);
+    int v_col[kDBlocks];
+#pragma unroll
+    for (int db = 0; db < kDBlocks; ++db)
+        v_col[db] = v_key * D + ((4 * db + 2 * (gi & 1) + ((li & 3) >> 1)) ^ v_swz) * 8 +
+                    (li & 1) * 4;
+    uint32_t pk[16];  // probabilities of the latest softmaxed tile
+    // V operands stream two key-steps ahead of the products that use them.
+    auto pv = [&](int st) {
+        const uint16_t *vb = &lds[st][1][0];
+#pragma unroll
+        for (int u = 0; u < 4; ++u) {
+            const u32x4 bop = {pk[4 * u], pk[4 * u + 1], pk[4 * u + 2], pk[4 * u + 3]};
+#pragma unroll
+            for (int db = 0; db < kDBlocks; ++db) {
+                const uint16_t *vr = vb + 16 * u * D + v_col[db];
+                const u32x2 lo = lds_read_tr16(vr);
+                const u32x2 up = lds_read_tr16(vr + 8 * D);
+                const u32x4 aop = {lo.x, lo.y, up.x, up.y};
+                oacc[db] = mfma32x32x16<kBf16>(aop, bop, oacc[db]);
+            }
+        }
+        __builtin_amdgcn_sched_group_barrier(0x100, 4 * kDBlocks, 0);  // reads of steps 0, 1
+        __builtin_amdgcn_sched_group_barrier(0x008, kDBlocks, 0);      // products of step 0
+        __builtin_amdgcn_sched_group_barrier(0x100, 2 * kDBlocks, 0);  // reads of step 2
+        __builtin_amdgcn_sched_group_barrier(0x008, kDBlocks, 0);      // products of step 1
+        __builtin_amdgcn_sched_group_barrier(0x100, 2 * kDBlocks, 0);  // reads of step 3
+        __builtin_amdgcn_sched_group_barrier(0x008, 2 * kDBlocks, 0);  // products of steps 2, 3
+    };
+    const int T = te - tb;
+    // Matrix phase of step u: S(u) and O += V(u-1) P(u-1).
+    auto mphase = [&](int u) {
+        if (u < T) qk(u % kStages);
+        if (u >= 1) pv((u - 1) % kStages);
+    };
+    // Vector phase: online softmax of tile u (scores in s0/s1) into pk.  O
+    // already holds every earlier tile, so a rescale applies to all of it.
+    auto vphase = [&](int u) {
+        const int valid = nd.len - (tb + u) * kTile;
+        if (valid < kTile) {  // only the node's last tile can be partial
+#pragma unroll
+            for (int i = 0; i < 16; ++i) {
+                const int kr = 8 * (i / 4) + 4 * hi + (i % 4);
+                if (kr >= valid) s0[i] = -INFINITY;
+                if (32 + kr >= valid) s1[i] = -INFINITY;
+            }
+        }
+        float alpha;
+        if (softmax_max<kBf16>(s0, s1, c, m_run, l_run, alpha)) {
+#pragma unroll
+            for (int db = 0; db < kDBlocks; ++db) oacc[db] *= alpha;
+        }
+        softmax_exp<kBf16>(s0, s1, c, m_run, l_run, pk);
+    };
+
+    if (T > 0) {
+        issue(tb);
+        if (T > 1) issue(tb + 1);
+#pragma unroll 1
+        for (int u = 0; u <= T; ++u) {
+            // this wave's part of tile u has landed (tile u+1 may be in flight)
+            if (u + 1 < T) wait_vmcnt<kPerTile>();
+            else wait_vmcnt<0>();
+            block_sync();
+            if (u + 2 < T) issue(tb + u + 2);
+            if (grp == 0) mphase(u);
+            else if (u >= 1) vphase(u - 1);
+            block_sync();
+            if (grp == 0) {
+                if (u < T) vphase(u);
+            } else {
+                mphase(u);
+            }
+        }
+    }
+
+    if (row_ok) {
+        const int64_t ri = ((int64_t)(b - nd.dest.row_base)) * args.Hq + h;
+        write_row<D>(nd.dest, task.split, ri, oacc, hi, m_run, l_run);
     }
 }
 
@@ -786,8 +1037,8 @@ __global__ __launch_bounds__(64 * NW) void prefix_mfma32_kernel(PrefixArgs args)
     }
 }
 
-// The 64-row-per-wave kernel is off until it has been validated on hardware.
-constexpr bool kWideEnabled = false;
+constexpr bool kPingPongEnabled = true;
+constexpr bool kWideEnabled = false;  // slower than the 32-row kernel on gfx950 so far
 
 template <int NW>
 static hipError_t launch_nw(const PrefixArgs &a, int dtype, int d, int wgs, hipStream_t s) {
@@ -806,7 +1057,22 @@ static hipError_t launch_nw(const PrefixArgs &a, int dtype, int d, int wgs, hipS
 }
 
 hipError_t launch_prefix(const PrefixArgs &a, int dtype, int d, int nw, int wgs, hipStream_t s) {
-    if (kWideEnabled && nw == kWideRows / 32 && dtype != HP_F32) {  // 4 waves x 64 rows
+    // The wide kernel keeps per-lane DMA offsets within a tile in 32 bits.
+    bool wide = kWideEnabled && nw == kWideRows / 32 && dtype != HP_F32;
+    for (int i = 0; wide && i < a.num_nodes; ++i)
+        wide = (int64_t)kTile * a.nodes[i].stride_tok + d <= (int64_t)INT32_MAX;
+    if (kPingPongEnabled && nw == 8 && dtype != HP_F32) {
+        const dim3 grid(wgs), block(512);
+        if (dtype == HP_BF16) {
+            if (d == 128) prefix_mfma16_pp_kernel<true, 128><<<grid, block, 0, s>>>(a);
+            else prefix_mfma16_pp_kernel<true, 64><<<grid, block, 0, s>>>(a);
+        } else {
+            if (d == 128) prefix_mfma16_pp_kernel<false, 128><<<grid, block, 0, s>>>(a);
+            else prefix_mfma16_pp_kernel<false, 64><<<grid, block, 0, s>>>(a);
+        }
+        return hipGetLastError();
+    }
+    if (wide) {  // 4 waves x 64 rows
         const dim3 grid(wgs), block(256);
         if (dtype == HP_BF16) {
             if (d == 128) prefix_mfma16_wide_kernel<true, 128><<<grid, block, 0, s>>>(a);
