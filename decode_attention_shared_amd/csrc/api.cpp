@@ -192,10 +192,11 @@ size_t node_ws_bytes(const NodePlan &np, int d) {
            round_up((size_t)np.nsplit * np.rows * sizeof(float), kWsAlign);
 }
 
-// Waves per (sequence, KV head) workgroup of the suffix pass: enough that each
-// wave walks only a few blocks of the longest suffix.
+// Waves per (sequence, KV head) workgroup of the suffix pass.  More waves
+// shorten each sequence's walk but leave more of them idle on short
+// sequences; two waves measured best for suffixes of up to 16 blocks.
 int suffix_waves(const hp_paged_kv &kv) {
-    return kv.max_blocks <= 2 ? 1 : kv.max_blocks <= 4 ? 2 : 4;
+    return kv.max_blocks <= 2 ? 1 : kv.max_blocks <= 16 ? 2 : 4;
 }
 
 PrefixArgs base_prefix_args(const hp_query &q) {

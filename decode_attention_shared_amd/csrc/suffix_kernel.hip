@@ -121,10 +121,12 @@ __global__ __launch_bounds__(64 * NWS) void suffix_kernel(SuffixArgs a) {
     const char *vp = (const char *)a.v_pool;
     const int *trow = a.table + (int64_t)b * a.max_blocks;
 
+    // Block ids are read one block-step ahead of their K/V loads, so the
+    // table lookup's latency never sits in front of a block's loads.
+    auto table_id = [&](int blk) { return blk < nblk ? trow[blk] : 0; };
     // Issue the loads of one block (keys past the sequence's end and blocks
     // with an out-of-range id are never read).
-    auto fetch = [&](int blk, u32x4 (&kr)[kPasses], u32x4 (&vr)[kPasses], int &valid) {
-        const int id = trow[blk];
+    auto fetch = [&](int blk, int id, u32x4 (&kr)[kPasses], u32x4 (&vr)[kPasses], int &valid) {
         const bool id_ok = id >= 0 && id < a.num_blocks;
         bad |= !id_ok;
         valid = id_ok ? min(kBlock, len - blk * kBlock) : 0;
@@ -185,13 +187,16 @@ __global__ __launch_bounds__(64 * NWS) void suffix_kernel(SuffixArgs a) {
         u32x4 k0[kPasses], v0[kPasses], k1[kPasses], v1[kPasses];
         int n0 = 0, n1 = 0;
         int blk = wave;
-        if (blk < nblk) fetch(blk, k0, v0, n0);
+        int id0 = table_id(blk), id1 = table_id(blk + NWS);
+        if (blk < nblk) fetch(blk, id0, k0, v0, n0);
 #pragma unroll 1
         for (; blk < nblk; blk += 2 * NWS) {
-            const int b1 = blk + NWS, b2 = blk + 2 * NWS;
-            if (b1 < nblk) fetch(b1, k1, v1, n1);
+            const int b1 = blk + NWS, b2 = blk + 2 * NWS, b3 = blk + 3 * NWS;
+            id0 = table_id(b2);
+            if (b1 < nblk) fetch(b1, id1, k1, v1, n1);
             if (n0 > 0) process(k0, v0, n0);
-            if (b2 < nblk) fetch(b2, k0, v0, n0);
+            id1 = table_id(b3);
+            if (b2 < nblk) fetch(b2, id0, k0, v0, n0);
             if (b1 < nblk && n1 > 0) process(k1, v1, n1);
         }
     }
