@@ -798,28 +798,45 @@ __global__ __launch_bounds__(512) void prefix_mfma16_pp_kernel(PrefixArgs args) 
     for (int db = 0; db < kDBlocks; ++db) oacc[db] = f32x16{};
     float m_run = -INFINITY, l_run = 0.f;
 
+    // Node fields the loop needs, read once (the compiler would otherwise
+    // reload them from the argument segment, a scalar-memory round trip, at
+    // every tile).
+    const int len = nd.len;
+    const int64_t stride_tok = nd.stride_tok;
     const uint16_t *kbase = (const uint16_t *)nd.k + (int64_t)task.g * nd.stride_head;
     const uint16_t *vbase = (const uint16_t *)nd.v + (int64_t)task.g * nd.stride_head;
-    int dma_row[kDmas], dma_ck[kDmas], dma_cv[kDmas];
+    // Per-lane element offsets of this wave's DMAs within a tile, in 32 bits
+    // (the launch picks this kernel only when kTile * stride_tok + d fits in
+    // int32); per tile only a wave-uniform tile offset is added.
+    int dma_row[kDmas];
+    uint32_t koff[kDmas], voff[kDmas];
 #pragma unroll
     for (int j = 0; j < kDmas; ++j) {
         const int r = (wave * kDmas + j) * kRowsPerDma + lane / kRowChunks;
         const int pos = lane % kRowChunks;
         dma_row[j] = r;
-        dma_ck[j] = (pos ^ (r % kRowChunks)) * 8;
-        dma_cv[j] = (pos ^ v_swizzle<D>(r)) * 8;
+        koff[j] = (uint32_t)(r * stride_tok) + (pos ^ (r % kRowChunks)) * 8;
+        voff[j] = (uint32_t)(r * stride_tok) + (pos ^ v_swizzle<D>(r)) * 8;
     }
     auto issue = [&](int tile) {
         const int st = (tile - tb) % kStages;
         const int key0 = tile * kTile;
-        const bool full = key0 + kTile <= nd.len;
+        const int64_t tile_off = (int64_t)key0 * stride_tok;
+        const uint16_t *kt = kbase + tile_off;
+        const uint16_t *vt = vbase + tile_off;
+        const bool full = key0 + kTile <= len;
 #pragma unroll
         for (int j = 0; j < kDmas; ++j) {
-            const int t = full ? key0 + dma_row[j] : min(key0 + dma_row[j], nd.len - 1);
-            const int64_t off = (int64_t)t * nd.stride_tok;
             uint16_t *dst = &lds[st][0][(wave * kDmas + j) * kRowsPerDma * D];
-            dma16(kbase + off + dma_ck[j], dst);
-            dma16(vbase + off + dma_cv[j], dst + kTileElems);
+            uint32_t ko = koff[j], vo = voff[j];
+            if (!full && key0 + dma_row[j] >= len) {
+                // keys past the node's end re-read its last key (masked to -inf)
+                const uint32_t back = (uint32_t)((key0 + dma_row[j] - (len - 1)) * stride_tok);
+                ko -= back;
+                vo -= back;
+            }
+            dma16(kt + ko, dst);
+            dma16(vt + vo, dst + kTileElems);
         }
     };
     const int k_swz = n % kRowChunks;
@@ -885,7 +902,7 @@ __global__ __launch_bounds__(512) void prefix_mfma16_pp_kernel(PrefixArgs args) 
     // Vector phase: online softmax of tile u (scores in s0/s1) into pk.  O
     // already holds every earlier tile, so a rescale applies to all of it.
     auto vphase = [&](int u) {
-        const int valid = nd.len - (tb + u) * kTile;
+        const int valid = len - (tb + u) * kTile;
         if (valid < kTile) {  // only the node's last tile can be partial
 #pragma unroll
             for (int i = 0; i < 16; ++i) {
@@ -1061,7 +1078,10 @@ hipError_t launch_prefix(const PrefixArgs &a, int dtype, int d, int nw, int wgs,
     bool wide = kWideEnabled && nw == kWideRows / 32 && dtype != HP_F32;
     for (int i = 0; wide && i < a.num_nodes; ++i)
         wide = (int64_t)kTile * a.nodes[i].stride_tok + d <= (int64_t)INT32_MAX;
-    if (kPingPongEnabled && nw == 8 && dtype != HP_F32) {
+    bool fits32 = true;  // per-lane DMA offsets within a tile fit in int32
+    for (int i = 0; i < a.num_nodes; ++i)
+        fits32 = fits32 && (int64_t)kTile * a.nodes[i].stride_tok + d <= (int64_t)INT32_MAX;
+    if (kPingPongEnabled && fits32 && nw == 8 && dtype != HP_F32) {
         const dim3 grid(wgs), block(512);
         if (dtype == HP_BF16) {
             if (d == 128) prefix_mfma16_pp_kernel<true, 128><<<grid, block, 0, s>>>(a);
