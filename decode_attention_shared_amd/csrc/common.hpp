@@ -37,9 +37,6 @@ struct RowDest {
 };
 
 constexpr int kMaxLaunchNodes = 16;
-// Rows per workgroup of the wide prefix kernel (4 waves x 64 rows); a launch
-// asks for it with nw = kWideRows / 32.
-constexpr int kWideRows = 256;
 
 struct PrefixNodeArg {
     const void *k;

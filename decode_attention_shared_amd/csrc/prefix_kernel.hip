@@ -181,10 +181,16 @@ __device__ __forceinline__ bool softmax_max(const f32x16 &s0, const f32x16 &s1, 
                                             float &m_run, float &l_run, float &alpha) {
     // maximum (not fmaxf): no NaN canonicalisation of every input, and
     // v_maximum3 takes two new scores per instruction.
-    float mt = __builtin_elementwise_maximum(s0[0], s1[0]);
+    // four independent chains, then a short tree (latency, not op count)
+    float mq[4];
 #pragma unroll
-    for (int i = 1; i < 16; ++i)
-        mt = __builtin_elementwise_maximum(mt, __builtin_elementwise_maximum(s0[i], s1[i]));
+    for (int r = 0; r < 4; ++r) mq[r] = __builtin_elementwise_maximum(s0[r], s1[r]);
+#pragma unroll
+    for (int i = 4; i < 16; ++i)
+        mq[i % 4] = __builtin_elementwise_maximum(mq[i % 4],
+                                                  __builtin_elementwise_maximum(s0[i], s1[i]));
+    float mt = __builtin_elementwise_maximum(__builtin_elementwise_maximum(mq[0], mq[1]),
+                                             __builtin_elementwise_maximum(mq[2], mq[3]));
     mt = fmaxf(mt, __shfl_xor(mt, 32, kWave));  // the other half-wave: the other keys of this query
     const float mts = mt * c;  // c > 0: the max commutes with the scaling
     const bool rescale = __any(mts > m_run + kLazy);
@@ -202,20 +208,20 @@ template <bool kBf16>
 __device__ __forceinline__ void softmax_exp(const f32x16 &s0, const f32x16 &s1, float c,
                                             float m_run, float &l_run, uint32_t (&pk)[16]) {
     const float neg_m = -m_run;
-    float sum = 0.f;
+    float sq[4] = {0.f, 0.f, 0.f, 0.f};  // independent accumulation chains
 #pragma unroll
     for (int i = 0; i < 8; ++i) {
         pk[i] = pack_p<kBf16>(fast_exp2(fmaf(s0[2 * i], c, neg_m)),
                               fast_exp2(fmaf(s0[2 * i + 1], c, neg_m)));
-        sum = add_packed<kBf16>(pk[i], sum);
+        sq[i % 4] = add_packed<kBf16>(pk[i], sq[i % 4]);
     }
 #pragma unroll
     for (int i = 0; i < 8; ++i) {
         pk[8 + i] = pack_p<kBf16>(fast_exp2(fmaf(s1[2 * i], c, neg_m)),
                                   fast_exp2(fmaf(s1[2 * i + 1], c, neg_m)));
-        sum = add_packed<kBf16>(pk[8 + i], sum);
+        sq[i % 4] = add_packed<kBf16>(pk[8 + i], sq[i % 4]);
     }
-    l_run += sum;
+    l_run += (sq[0] + sq[1]) + (sq[2] + sq[3]);
 }
 
 // Position of a V row's 16-byte chunks in LDS: chunk c of row r sits at
@@ -472,278 +478,13 @@ __global__ __launch_bounds__(64 * NW) void prefix_mfma16_kernel(PrefixArgs args)
 }
 
 // ---------------------------------------------------------------------------
-// Wide variant for many rows per KV head: 4 waves x 64 query rows.  Each wave
-// owns two 32-row blocks, so every K or V operand it reads from LDS feeds two
-// MFMAs: half the LDS traffic per FLOP of the 32-row layout, which at full
-// matrix-core rate would need about all of the LDS bandwidth.  One wave per
-// SIMD with the whole register file (O accumulators in AGPRs).
-//
-// Keys are handled in 32-key halves of the 64-key DMA tiles, which keeps the
-// live scores and probabilities small.  Iteration j overlaps, inside the
-// wave, the score product of half j+1 on the matrix cores with the
-// exponentials of half j on the vector ALUs, then the value product of half
-// j with the row max of half j+1.  That max can rise before half j's value
-// product is in O: the denominator is rescaled at once, the O rescale is
-// applied after the product, so every term of O and l is relative to the same
-// max when they meet.
-// ---------------------------------------------------------------------------
-template <bool kBf16, int D>
-__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1)))
-void prefix_mfma16_wide_kernel(PrefixArgs args) {
-    constexpr int NW = 4;
-    constexpr int kDSteps = D / 16;
-    constexpr int kDBlocks = D / 32;
-    constexpr int kRowChunks = D / 8;
-    constexpr int kRowsPerDma = kWave / kRowChunks;
-    constexpr int kDmas = kTile / kRowsPerDma / NW;
-    static_assert(kDmas >= 1 && kTile % (kRowsPerDma * NW) == 0, "tile split");
-    // A ring of 4 tiles: the one being consumed, and up to three in flight.
-    constexpr int kStages = 4;
-    constexpr int kTileElems = kTile * D;
-    __shared__ __attribute__((aligned(1024))) uint16_t lds[kStages][2][kTileElems];
-
-    const WgTask task = decode_wg(args);
-    if (!task.valid) return;
-    const PrefixNodeArg &nd = args.nodes[task.node];
-    const int G = args.G;
-    const int M = (nd.seq_end - nd.seq_begin) * G;
-    const int ntiles = (nd.len + kTile - 1) / kTile;
-    const int tb = task.split * nd.tiles_per_split;
-    const int te = min(tb + nd.tiles_per_split, ntiles);
-
-    const int tid = threadIdx.x;
-    const int wave = tid / kWave;
-    const int lane = tid % kWave;
-    const int n = lane & 31;
-    const int hi = lane >> 5;
-    const float c = args.scale_log2;
-    int rowi[2], bi[2], hq[2];
-    bool rok[2];
-#pragma unroll
-    for (int r = 0; r < 2; ++r) {
-        rowi[r] = task.rb * kWideRows + wave * 64 + r * 32 + n;
-        rok[r] = rowi[r] < M;
-        bi[r] = nd.seq_begin + (rok[r] ? rowi[r] / G : 0);
-        hq[r] = task.g * G + (rok[r] ? rowi[r] % G : 0);
-    }
-    u32x4 qf[2][kDSteps];
-#pragma unroll
-    for (int r = 0; r < 2; ++r) {
-        const uint16_t *qp =
-            (const uint16_t *)args.q + ((int64_t)bi[r] * args.Hq + hq[r]) * D + hi * 8;
-#pragma unroll
-        for (int kk = 0; kk < kDSteps; ++kk)
-            qf[r][kk] = rok[r] ? *(const u32x4 *)(qp + kk * 16) : u32x4{0, 0, 0, 0};
-    }
-    wait_vmcnt<0>();  // as in the 32-row kernel
-    f32x16 oacc[2][kDBlocks];
-#pragma unroll
-    for (int r = 0; r < 2; ++r)
-#pragma unroll
-        for (int db = 0; db < kDBlocks; ++db) oacc[r][db] = f32x16{};
-    float m_run[2] = {-INFINITY, -INFINITY}, l_run[2] = {0.f, 0.f};
-    float o_scale[2] = {1.f, 1.f};  // deferred O rescale (see above)
-
-    const uint16_t *kbase = (const uint16_t *)nd.k + (int64_t)task.g * nd.stride_head;
-    const uint16_t *vbase = (const uint16_t *)nd.v + (int64_t)task.g * nd.stride_head;
-    // Per-lane element offsets of this wave's DMAs within a tile (32-bit: the
-    // launch picks this kernel only when kTile * stride_tok + d fits in int32).
-    int dma_row[kDmas];
-    uint32_t koff[kDmas], voff[kDmas];
-#pragma unroll
-    for (int j = 0; j < kDmas; ++j) {
-        const int r = (wave * kDmas + j) * kRowsPerDma + lane / kRowChunks;
-        const int pos = lane % kRowChunks;
-        dma_row[j] = r;
-        koff[j] = (uint32_t)(r * nd.stride_tok) + (pos ^ (r % kRowChunks)) * 8;
-        voff[j] = (uint32_t)(r * nd.stride_tok) + (pos ^ (2 * (r % (kRowChunks / 2)))) * 8;
-    }
-    auto issue = [&](int tile) {
-        const int st = (tile - tb) % kStages;
-        const int key0 = tile * kTile;
-        const int64_t tile_off = (int64_t)key0 * nd.stride_tok;
-        const uint16_t *kt = kbase + tile_off;
-        const uint16_t *vt = vbase + tile_off;
-        const bool full = key0 + kTile <= nd.len;
-#pragma unroll
-        for (int j = 0; j < kDmas; ++j) {
-            uint16_t *dst = &lds[st][0][(wave * kDmas + j) * kRowsPerDma * D];
-            uint32_t ko = koff[j], vo = voff[j];
-            if (!full && key0 + dma_row[j] >= nd.len) {
-                // keys past the node's end re-read its last key (masked to -inf)
-                const uint32_t back =
-                    (uint32_t)((key0 + dma_row[j] - (nd.len - 1)) * nd.stride_tok);
-                ko -= back;
-                vo -= back;
-            }
-            dma16(kt + ko, dst);
-            dma16(vt + vo, dst + kTileElems);
-        }
-    };
-    // Stage and half of key half j (keys 32j .. 32j+31 of the node).
-    auto stage_of = [&](int j) { return (j / 2 - tb) % kStages; };
-
-    // S^T of one half for both row blocks: each K operand read feeds two MFMAs.
-    const int k_swz = n % kRowChunks;
-    auto qk = [&](int j, f32x16 (&s)[2]) {
-        const uint16_t *kb = &lds[stage_of(j)][0][(32 * (j & 1) + n) * D];
-        s[0] = f32x16{};
-        s[1] = f32x16{};
-#pragma unroll
-        for (int kk = 0; kk < kDSteps; ++kk) {
-            const int col = ((2 * kk + hi) ^ k_swz) * 8;
-            const u32x4 a = *(const u32x4 *)&kb[col];
-            s[0] = mfma32x32x16<kBf16>(a, qf[0][kk], s[0]);
-            s[1] = mfma32x32x16<kBf16>(a, qf[1][kk], s[1]);
-        }
-    };
-    // Mask keys past the node's end, then the lazy running-max update: l is
-    // rescaled now, O through o_scale after the pending value product.
-    auto max_step = [&](int j, f32x16 (&s)[2]) {
-        const int valid = nd.len - j * 32;
-        if (valid < 32) {
-#pragma unroll
-            for (int i = 0; i < 16; ++i) {
-                const int kr = 8 * (i / 4) + 4 * hi + (i % 4);
-                if (kr >= valid) {
-                    s[0][i] = -INFINITY;
-                    s[1][i] = -INFINITY;
-                }
-            }
-        }
-#pragma unroll
-        for (int r = 0; r < 2; ++r) {
-            float mt = s[r][0];
-#pragma unroll
-            for (int i = 1; i < 16; ++i) mt = fmaxf(mt, s[r][i]);
-            mt = fmaxf(mt, __shfl_xor(mt, 32, kWave)) * c;  // c > 0
-            if (__any(mt > m_run[r] + kLazy)) {
-                const float m_new = fmaxf(m_run[r], mt);
-                const float alpha = fast_exp2(m_run[r] - m_new);  // 0 the first time
-                l_run[r] *= alpha;
-                o_scale[r] *= alpha;
-                m_run[r] = m_new;
-            }
-        }
-    };
-    // Probabilities 2^(s*c - m) rounded to the 16-bit type, and the row sums
-    // of exactly those rounded values.
-    auto exp_step = [&](const f32x16 (&s)[2], uint32_t (&pk)[2][8]) {
-#pragma unroll
-        for (int r = 0; r < 2; ++r) {
-            const float neg_m = -m_run[r];
-            float sum = 0.f;
-#pragma unroll
-            for (int i = 0; i < 8; ++i) {
-                pk[r][i] = pack_p<kBf16>(fast_exp2(fmaf(s[r][2 * i], c, neg_m)),
-                                         fast_exp2(fmaf(s[r][2 * i + 1], c, neg_m)));
-                sum = add_packed<kBf16>(pk[r][i], sum);
-            }
-            l_run[r] += sum;
-        }
-    };
-    const int gi = lane >> 4, li = lane & 15;
-    const int v_key = 4 * hi + (li >> 2);
-    const int v_swz = 2 * (v_key % (kRowChunks / 2));
-    int v_col[kDBlocks];
-#pragma unroll
-    for (int db = 0; db < kDBlocks; ++db)
-        v_col[db] = v_key * D + ((4 * db + 2 * (gi & 1) + ((li & 3) >> 1)) ^ v_swz) * 8 +
-                    (li & 1) * 4;
-    // O += V P for one half and both row blocks; each V operand feeds two MFMAs.
-    auto pv = [&](int j, const uint32_t (&pk)[2][8]) {
-        const uint16_t *vb = &lds[stage_of(j)][1][32 * (j & 1) * D];
-#pragma unroll
-        for (int u = 0; u < 2; ++u) {
-            const u32x4 b0 = {pk[0][4 * u], pk[0][4 * u + 1], pk[0][4 * u + 2], pk[0][4 * u + 3]};
-            const u32x4 b1 = {pk[1][4 * u], pk[1][4 * u + 1], pk[1][4 * u + 2], pk[1][4 * u + 3]};
-#pragma unroll
-            for (int db = 0; db < kDBlocks; ++db) {
-                const uint16_t *vr = vb + 16 * u * D + v_col[db];
-                const u32x2 lo = lds_read_tr16(vr);
-                const u32x2 up = lds_read_tr16(vr + 8 * D);
-                const u32x4 aop = {lo.x, lo.y, up.x, up.y};
-                oacc[0][db] = mfma32x32x16<kBf16>(aop, b0, oacc[0][db]);
-                oacc[1][db] = mfma32x32x16<kBf16>(aop, b1, oacc[1][db]);
-            }
-        }
-    };
-    auto apply_scale = [&]() {
-#pragma unroll
-        for (int r = 0; r < 2; ++r) {
-            if (__any(o_scale[r] != 1.f)) {
-#pragma unroll
-                for (int db = 0; db < kDBlocks; ++db) oacc[r][db] *= o_scale[r];
-                o_scale[r] = 1.f;
-            }
-        }
-    };
-    const int jb = 2 * tb, je = 2 * te;  // key halves of this split
-    // Iteration for half j (scores in sc): when half j+1 starts a tile, wait
-    // for it (this wave's DMAs, then everyone's) and refill the ring; then
-    // S(j+1) || exp(j), and O += V P(j) || max(j+1).
-    auto step = [&](int j, f32x16 (&sc)[2], f32x16 (&sn)[2]) {
-        const bool has_next = j + 1 < je;
-        if (has_next && (j & 1)) {
-            const int t1 = (j + 1) / 2;
-            if (t1 + 1 < te) wait_vmcnt<2 * kDmas>();
-            else wait_vmcnt<0>();
-            block_sync();
-            // every wave is past the value product of tile t1-2, whose stage
-            // tile t1+2 takes
-            if (t1 + 2 < te) issue(t1 + 2);
-        }
-        if (has_next) qk(j + 1, sn);
-        uint32_t pk[2][8];
-        exp_step(sc, pk);
-#pragma unroll
-        for (int k = 0; k < 2 * kDSteps; ++k) {
-            __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);  // one MFMA
-            __builtin_amdgcn_sched_group_barrier(0x002, 5, 0);  // five VALU
-        }
-        pv(j, pk);
-        if (has_next) max_step(j + 1, sn);
-        apply_scale();
-    };
-
-    if (tb < te) {
-#pragma unroll
-        for (int k = 0; k < 3; ++k)
-            if (tb + k < te) issue(tb + k);
-        const int younger = min(2, te - tb - 1);
-        if (younger == 2) wait_vmcnt<4 * kDmas>();
-        else if (younger == 1) wait_vmcnt<2 * kDmas>();
-        else wait_vmcnt<0>();
-        block_sync();
-        f32x16 sa[2], sb[2];
-        qk(jb, sa);
-        max_step(jb, sa);
-        o_scale[0] = o_scale[1] = 1.f;  // O is still zero: nothing to rescale
-#pragma unroll 1
-        for (int j = jb; j < je; j += 2) {  // two halves per trip: the score sets alternate
-            step(j, sa, sb);
-            step(j + 1, sb, sa);
-        }
-    }
-
-#pragma unroll
-    for (int r = 0; r < 2; ++r) {
-        if (rok[r]) {
-            const int64_t ri = ((int64_t)(bi[r] - nd.dest.row_base)) * args.Hq + hq[r];
-            write_row<D>(nd.dest, task.split, ri, oacc[r], hi, m_run[r], l_run[r]);
-        }
-    }
-}
-
-// ---------------------------------------------------------------------------
 // Ping-pong variant for 256 rows per workgroup: 8 waves of 32 rows.  Waves w
 // and w+4 of a workgroup share a SIMD, so waves 0-3 and 4-7 form two groups
 // with one wave on every SIMD.  The groups run half a tile apart: while one
 // wave of a SIMD issues its matrix products (scores of tile u and the value
 // product of tile u-1) the other runs the softmax of its latest tile on the
-// vector ALUs, and the two swap roles at every workgroup barrier.  The matrix
-// cores and the vector ALUs of each SIMD are thus busy at the same time,
-// which a lockstep schedule of both waves cannot achieve.
+// vector ALUs, and the two swap roles at every workgroup barrier, so the
+// matrix core and the vector ALUs of a SIMD can work at the same time.
 // ---------------------------------------------------------------------------
 
 template <bool kBf16, int D>
@@ -1055,7 +796,6 @@ __global__ __launch_bounds__(64 * NW) void prefix_mfma32_kernel(PrefixArgs args)
 }
 
 constexpr bool kPingPongEnabled = true;
-constexpr bool kWideEnabled = false;  // slower than the 32-row kernel on gfx950 so far
 
 template <int NW>
 static hipError_t launch_nw(const PrefixArgs &a, int dtype, int d, int wgs, hipStream_t s) {
@@ -1074,10 +814,6 @@ static hipError_t launch_nw(const PrefixArgs &a, int dtype, int d, int wgs, hipS
 }
 
 hipError_t launch_prefix(const PrefixArgs &a, int dtype, int d, int nw, int wgs, hipStream_t s) {
-    // The wide kernel keeps per-lane DMA offsets within a tile in 32 bits.
-    bool wide = kWideEnabled && nw == kWideRows / 32 && dtype != HP_F32;
-    for (int i = 0; wide && i < a.num_nodes; ++i)
-        wide = (int64_t)kTile * a.nodes[i].stride_tok + d <= (int64_t)INT32_MAX;
     bool fits32 = true;  // per-lane DMA offsets within a tile fit in int32
     for (int i = 0; i < a.num_nodes; ++i)
         fits32 = fits32 && (int64_t)kTile * a.nodes[i].stride_tok + d <= (int64_t)INT32_MAX;
@@ -1089,17 +825,6 @@ hipError_t launch_prefix(const PrefixArgs &a, int dtype, int d, int nw, int wgs,
         } else {
             if (d == 128) prefix_mfma16_pp_kernel<false, 128><<<grid, block, 0, s>>>(a);
             else prefix_mfma16_pp_kernel<false, 64><<<grid, block, 0, s>>>(a);
-        }
-        return hipGetLastError();
-    }
-    if (wide) {  // 4 waves x 64 rows
-        const dim3 grid(wgs), block(256);
-        if (dtype == HP_BF16) {
-            if (d == 128) prefix_mfma16_wide_kernel<true, 128><<<grid, block, 0, s>>>(a);
-            else prefix_mfma16_wide_kernel<true, 64><<<grid, block, 0, s>>>(a);
-        } else {
-            if (d == 128) prefix_mfma16_wide_kernel<false, 128><<<grid, block, 0, s>>>(a);
-            else prefix_mfma16_wide_kernel<false, 64><<<grid, block, 0, s>>>(a);
         }
         return hipGetLastError();
     }
