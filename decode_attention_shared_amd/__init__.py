@@ -11,6 +11,11 @@ Entry points (same names as the C ABI):
   suffix_decode  per-sequence paged decode over private suffixes
   lse_merge      exact n-way merge of (O, LSE) partials
   cascade_step   a whole decode step over a prefix tree plus paged suffixes
+  tree_plan_build / TreeStep   a decode step over (C, i, j) chunk descriptors
+                 whose plan lives in device memory (any depth, forests)
+  kv_append      scatter of new tokens' K/V rows into the pool
+  Pakv           the host prefix-tree KV manager (insert, append, remove,
+                 context) that produces those descriptors
 """
 from __future__ import annotations
 
@@ -29,11 +34,16 @@ HP_MAX_LEVELS = 4
 HP_MAX_NODES = 32
 HP_MAX_MERGE = 16
 HP_BLOCK_SIZE = 16
+HP_CHUNK = 64
+HP_TREE_MAX_LAUNCHES = 4
 STATUS = {0: "HP_OK", 1: "HP_ERR_NULL", 2: "HP_ERR_INVALID_ARG", 3: "HP_ERR_UNSUPPORTED",
-          4: "HP_ERR_WORKSPACE", 5: "HP_ERR_HIP"}
+          4: "HP_ERR_WORKSPACE", 5: "HP_ERR_HIP", 6: "HP_ERR_CAPACITY"}
 EXPORTS = ["hp_prefix_attn_workspace_size", "hp_prefix_attn", "hp_suffix_decode_workspace_size",
            "hp_suffix_decode", "hp_lse_merge", "hp_cascade_workspace_size", "hp_cascade_step",
-           "hp_cascade_step_timed", "hp_status_string", "hp_last_hip_error", "hp_version"]
+           "hp_cascade_step_timed", "hp_tree_plan_build", "hp_tree_step", "hp_kv_append",
+           "hp_pakv_create", "hp_pakv_destroy", "hp_pakv_insert", "hp_pakv_append",
+           "hp_pakv_remove", "hp_pakv_context", "hp_pakv_seq_rows", "hp_pakv_get_stats",
+           "hp_status_string", "hp_last_hip_error", "hp_version"]
 
 _DTYPE = {torch.float32: HP_F32, torch.float16: HP_F16, torch.bfloat16: HP_BF16}
 
@@ -72,6 +82,32 @@ class PagedKV(ctypes.Structure):
                 ("block_table", ctypes.c_void_p), ("seq_lens", ctypes.c_void_p),
                 ("max_blocks", ctypes.c_int32), ("block_size", ctypes.c_int32),
                 ("num_blocks", ctypes.c_int32)]
+
+
+class ChunkDesc(ctypes.Structure):
+    _fields_ = [("row", ctypes.c_int32), ("count", ctypes.c_int32),
+                ("seq_begin", ctypes.c_int32), ("seq_end", ctypes.c_int32)]
+
+
+class TreePlan(ctypes.Structure):
+    _fields_ = [("B", ctypes.c_int32), ("Hq", ctypes.c_int32), ("Hkv", ctypes.c_int32),
+                ("d", ctypes.c_int32), ("dtype", ctypes.c_int32), ("share_min", ctypes.c_int32),
+                ("num_descs", ctypes.c_int32), ("num_segs", ctypes.c_int32),
+                ("num_pieces", ctypes.c_int32), ("num_srcs", ctypes.c_int32),
+                ("num_tok_rows", ctypes.c_int32), ("max_private", ctypes.c_int32),
+                ("num_launches", ctypes.c_int32),
+                ("launch_nw", ctypes.c_int32 * HP_TREE_MAX_LAUNCHES),
+                ("launch_wgs", ctypes.c_int32 * HP_TREE_MAX_LAUNCHES),
+                ("launch_wg0", ctypes.c_int32 * HP_TREE_MAX_LAUNCHES),
+                ("part_rows", ctypes.c_int64), ("pool_rows", ctypes.c_int64),
+                ("blob_bytes", ctypes.c_size_t), ("workspace_bytes", ctypes.c_size_t)]
+
+
+class PakvStats(ctypes.Structure):
+    _fields_ = [("num_chunks", ctypes.c_int32), ("chunks_used", ctypes.c_int32),
+                ("chunks_free", ctypes.c_int32), ("chunks_fresh", ctypes.c_int32),
+                ("nodes", ctypes.c_int32), ("seqs", ctypes.c_int32),
+                ("tokens_stored", ctypes.c_int64), ("tokens_logical", ctypes.c_int64)]
 
 
 _lib = None
@@ -122,6 +158,31 @@ def lib():
             L.hp_cascade_step_timed.argtypes = [ctypes.POINTER(Query), ctypes.POINTER(PrefixTree),
                                                 ctypes.POINTER(PagedKV), p, p, p,
                                                 ctypes.c_size_t, p, p, ctypes.c_int32]
+            i32, i64 = ctypes.c_int32, ctypes.c_int64
+            L.hp_tree_plan_build.restype = st
+            L.hp_tree_plan_build.argtypes = [ctypes.POINTER(Query), p, i32, i32, i64, p,
+                                             ctypes.c_size_t, ctypes.POINTER(TreePlan)]
+            L.hp_tree_step.restype = st
+            L.hp_tree_step.argtypes = [ctypes.POINTER(Query), ctypes.POINTER(TreePlan), p, p, p,
+                                       p, p, p, p, ctypes.c_size_t, p]
+            L.hp_kv_append.restype = st
+            L.hp_kv_append.argtypes = [p, p, p, i32, i32, i32, i32, p, p, i64, p, p, i32, p]
+            L.hp_pakv_create.restype = st
+            L.hp_pakv_create.argtypes = [i32, ctypes.POINTER(p)]
+            L.hp_pakv_destroy.restype = None
+            L.hp_pakv_destroy.argtypes = [p]
+            L.hp_pakv_insert.restype = st
+            L.hp_pakv_insert.argtypes = [p, i64, p, i32, p, p]
+            L.hp_pakv_append.restype = st
+            L.hp_pakv_append.argtypes = [p, i64, i32, p, p]
+            L.hp_pakv_remove.restype = st
+            L.hp_pakv_remove.argtypes = [p, i64]
+            L.hp_pakv_context.restype = st
+            L.hp_pakv_context.argtypes = [p, p, p, i32, p, i32, p, p]
+            L.hp_pakv_seq_rows.restype = st
+            L.hp_pakv_seq_rows.argtypes = [p, i64, p, i32, p]
+            L.hp_pakv_get_stats.restype = st
+            L.hp_pakv_get_stats.argtypes = [p, ctypes.POINTER(PakvStats)]
             _lib = L
     return _lib
 
@@ -320,3 +381,177 @@ def cascade_step(q: torch.Tensor, levels, k_pool=None, v_pool=None, block_table=
     """levels: root first, each a list of (k, v, seq_begin, seq_end) device tensors/ints;
     the pools, table and lengths describe the paged suffixes (or None for prefix only)."""
     return CascadeCall(q, levels, k_pool, v_pool, block_table, seq_lens, scale, out, lse)(stream)
+
+
+# ------------------------------------------------------------------------------
+# Chunked prefix tree: (C, i, j) descriptors, device-resident plans, append, PAKV
+# ------------------------------------------------------------------------------
+
+def _descs_array(descs) -> Tuple[ctypes.Array, int]:
+    """descs: an [n][4] int array-like of (row, count, seq_begin, seq_end)."""
+    import numpy as np
+    a = np.ascontiguousarray(np.asarray(descs, dtype=np.int32).reshape(-1, 4))
+    n = a.shape[0]
+    arr = (ChunkDesc * max(1, n))()
+    if n:
+        ctypes.memmove(arr, a.ctypes.data, a.nbytes)
+    return arr, n
+
+
+def tree_plan_build(B: int, Hq: int, Hkv: int, d: int, dtype: torch.dtype, descs,
+                    share_min: int, pool_rows: int):
+    """Plan a chunk-tree step.  Returns (TreePlan, blob) with blob a host uint8 tensor
+    holding the plan's device image (copy it to the GPU; see TreeStep)."""
+    L = lib()
+    geom = Query(None, B, Hq, Hkv, d, _DTYPE[dtype], 1.0)
+    arr, n = _descs_array(descs)
+    plan = TreePlan()
+    _check(L.hp_tree_plan_build(ctypes.byref(geom), ctypes.addressof(arr), n, share_min,
+                                pool_rows, None, 0, ctypes.byref(plan)), "hp_tree_plan_build")
+    blob = torch.zeros(max(16, plan.blob_bytes), dtype=torch.uint8)
+    _check(L.hp_tree_plan_build(ctypes.byref(geom), ctypes.addressof(arr), n, share_min,
+                                pool_rows, blob.data_ptr(), blob.numel(), ctypes.byref(plan)),
+           "hp_tree_plan_build")
+    return plan, blob
+
+
+class TreeStep:
+    """A planned chunk-tree step: the plan image copied to device memory once, its
+    workspace allocated once; each call is one hp_tree_step."""
+
+    def __init__(self, q_like: torch.Tensor, Hkv: int, descs, share_min: int, pool_rows: int,
+                 scale: Optional[float] = None):
+        _require_cuda(q_like, "q")
+        B, Hq, d = q_like.shape
+        self.plan, blob_host = tree_plan_build(B, Hq, Hkv, d, q_like.dtype, descs, share_min,
+                                               pool_rows)
+        self.blob = blob_host.to(q_like.device)  # the lazy context copy: once per tree shape
+        self.Hkv = Hkv
+        self.scale = scale
+        self.ws = _workspace(self.plan.workspace_bytes, q_like.device)
+
+    def __call__(self, q: torch.Tensor, k_pool: torch.Tensor, v_pool: torch.Tensor,
+                 seq_lens: Optional[torch.Tensor] = None, out=None, lse=None, stream=None):
+        L = lib()
+        qs = make_query(q, self.Hkv, self.scale)
+        for t, nm in ((k_pool, "k_pool"), (v_pool, "v_pool")):
+            _require_cuda(t, nm)
+            if t.dtype != q.dtype or not t.is_contiguous() or t.shape[-2:] != (self.Hkv, q.shape[2]):
+                raise ValueError(f"{nm} must be a contiguous [rows][Hkv][d] tensor of q's dtype")
+        if k_pool.shape[0] * (k_pool.numel() // max(1, k_pool.shape[0])) < \
+                self.plan.pool_rows * self.Hkv * q.shape[2]:
+            raise ValueError("pool has fewer rows than the plan was built for")
+        if seq_lens is not None:
+            _require_cuda(seq_lens, "seq_lens")
+            if seq_lens.dtype != torch.int32 or seq_lens.numel() != q.shape[0]:
+                raise ValueError("seq_lens must be int32 [B]")
+        out, lse = _out(q, out, lse, zero=False)
+        _check(L.hp_tree_step(ctypes.byref(qs), ctypes.byref(self.plan), self.blob.data_ptr(),
+                              k_pool.data_ptr(), v_pool.data_ptr(), _ptr(seq_lens),
+                              out.data_ptr(), _ptr(lse), _ptr(self.ws), self.plan.workspace_bytes,
+                              _stream(stream)), "hp_tree_step")
+        return out, lse
+
+
+def kv_append(k_new: torch.Tensor, v_new: torch.Tensor, rows: torch.Tensor,
+              k_pool: torch.Tensor, v_pool: torch.Tensor, seq_lens: Optional[torch.Tensor] = None,
+              seq_idx: Optional[torch.Tensor] = None, stream=None) -> None:
+    """Copy k_new[i], v_new[i] ([n][Hkv][d]) to pool row rows[i]; optionally
+    seq_lens[seq_idx[i]] += 1 (all device tensors)."""
+    L = lib()
+    for t, nm in ((k_new, "k_new"), (v_new, "v_new"), (rows, "rows"), (k_pool, "k_pool"),
+                  (v_pool, "v_pool")):
+        _require_cuda(t, nm)
+    if k_new.shape != v_new.shape or k_new.dim() != 3 or not k_new.is_contiguous() or \
+            not v_new.is_contiguous():
+        raise ValueError("k_new, v_new must be contiguous [n][Hkv][d]")
+    n, Hkv, d = k_new.shape
+    if k_pool.dtype != k_new.dtype or v_pool.dtype != k_new.dtype or \
+            not k_pool.is_contiguous() or not v_pool.is_contiguous() or \
+            k_pool.shape != v_pool.shape or k_pool.numel() % (Hkv * d):
+        raise ValueError("pools must be contiguous, of k_new's dtype, [rows][Hkv][d]")
+    if rows.dtype != torch.int32 or rows.numel() != n:
+        raise ValueError("rows must be int32 [n]")
+    num_seqs = 0
+    if seq_lens is not None:
+        _require_cuda(seq_lens, "seq_lens")
+        _require_cuda(seq_idx, "seq_idx")
+        if seq_lens.dtype != torch.int32 or seq_idx.dtype != torch.int32 or seq_idx.numel() != n:
+            raise ValueError("seq_lens and seq_idx must be int32, seq_idx [n]")
+        num_seqs = seq_lens.numel()
+    _check(L.hp_kv_append(k_new.data_ptr(), v_new.data_ptr(), rows.data_ptr(), n, Hkv, d,
+                          _DTYPE[k_new.dtype], k_pool.data_ptr(), v_pool.data_ptr(),
+                          k_pool.numel() // (Hkv * d), _ptr(seq_lens), _ptr(seq_idx), num_seqs,
+                          _stream(stream)), "hp_kv_append")
+
+
+class Pakv:
+    """Host prefix-tree KV cache manager over a pool of num_chunks * 64 rows."""
+
+    def __init__(self, num_chunks: int):
+        self._L = lib()
+        h = ctypes.c_void_p()
+        _check(self._L.hp_pakv_create(num_chunks, ctypes.byref(h)), "hp_pakv_create")
+        self._h = h
+        self.num_chunks = num_chunks
+
+    def close(self):
+        if self._h:
+            self._L.hp_pakv_destroy(self._h)
+            self._h = None
+
+    def __del__(self):
+        try:
+            self.close()
+        except Exception:
+            pass
+
+    def insert(self, seq_id: int, tokens: Sequence[int]):
+        """Returns (rows of every token, matched): tokens >= matched need K/V written."""
+        import numpy as np
+        t = np.ascontiguousarray(np.asarray(tokens, dtype=np.int32))
+        rows = np.zeros(max(1, t.shape[0]), dtype=np.int32)
+        m = ctypes.c_int32(0)
+        _check(self._L.hp_pakv_insert(self._h, seq_id, t.ctypes.data if t.size else None,
+                                      t.shape[0], rows.ctypes.data, ctypes.byref(m)),
+               "hp_pakv_insert")
+        return rows[:t.shape[0]], m.value
+
+    def append(self, seq_id: int, token: int):
+        """Returns (row for the token's K/V, changed): changed = the tree's shape moved."""
+        r, c = ctypes.c_int32(0), ctypes.c_int32(0)
+        _check(self._L.hp_pakv_append(self._h, seq_id, token, ctypes.byref(r), ctypes.byref(c)),
+               "hp_pakv_append")
+        return r.value, bool(c.value)
+
+    def remove(self, seq_id: int) -> None:
+        _check(self._L.hp_pakv_remove(self._h, seq_id), "hp_pakv_remove")
+
+    def stats(self) -> PakvStats:
+        st = PakvStats()
+        _check(self._L.hp_pakv_get_stats(self._h, ctypes.byref(st)), "hp_pakv_get_stats")
+        return st
+
+    def context(self):
+        """Returns (seq_order [B] int64, seq_lens [B] int32, descs [n][4] int32), numpy."""
+        import numpy as np
+        st = self.stats()
+        order = np.zeros(max(1, st.seqs), dtype=np.int64)
+        lens = np.zeros(max(1, st.seqs), dtype=np.int32)
+        descs = np.zeros((max(1, st.nodes), 4), dtype=np.int32)
+        ns, nd = ctypes.c_int32(0), ctypes.c_int32(0)
+        _check(self._L.hp_pakv_context(self._h, order.ctypes.data, lens.ctypes.data,
+                                       order.shape[0], descs.ctypes.data, descs.shape[0],
+                                       ctypes.byref(ns), ctypes.byref(nd)), "hp_pakv_context")
+        return order[:ns.value], lens[:ns.value], descs[:nd.value]
+
+    def seq_rows(self, seq_id: int):
+        import numpy as np
+        n = ctypes.c_int32(0)
+        st = self._L.hp_pakv_seq_rows(self._h, seq_id, None, 0, ctypes.byref(n))
+        if st not in (0, 6):
+            _check(st, "hp_pakv_seq_rows")
+        rows = np.zeros(max(1, n.value), dtype=np.int32)
+        _check(self._L.hp_pakv_seq_rows(self._h, seq_id, rows.ctypes.data, rows.shape[0],
+                                        ctypes.byref(n)), "hp_pakv_seq_rows")
+        return rows[:n.value]

@@ -19,7 +19,8 @@ CSRC = os.path.join(HERE, "csrc")
 INCLUDE = os.path.join(ROOT, "include")
 BUILD_DIR = os.path.join(ROOT, "_build")
 LIB_PATH = os.path.join(HERE, "libhp_attn.so")
-SOURCES = ["api.cpp", "prefix_kernel.hip", "suffix_kernel.hip", "merge_kernel.hip"]
+SOURCES = ["api.cpp", "tree.cpp", "pakv.cpp", "prefix_kernel.hip", "suffix_kernel.hip",
+           "merge_kernel.hip", "append_kernel.hip"]
 ARCH = "gfx950"
 
 COMMON_FLAGS = [

@@ -10,52 +10,70 @@
 #include <cstdint>
 #include <cstring>
 
-#include "common.hpp"
-#include "hp_attn.h"
-
-namespace hp {
-hipError_t launch_prefix(const PrefixArgs &a, int dtype, int d, int nw, int wgs, hipStream_t s);
-hipError_t launch_suffix(const SuffixArgs &a, int dtype, int d, int G, int nws, hipStream_t s);
-hipError_t launch_merge(const MergeArgs &a, int d, hipStream_t s);
-}  // namespace hp
+#include "host.hpp"
 
 namespace {
-
-using namespace hp;
-
 thread_local int32_t g_last_hip_error = 0;
+}  // namespace
 
-constexpr int kTileKeys = 64;           // keys per prefix tile (matches the kernels)
-constexpr int kCUs = 256;               // MI355X compute units
-constexpr int kWavesPerCU = 8;          // two waves per SIMD at the prefix kernels' register use
-// Cost of one byte of split partials (written once, read once by the merge),
-// in units of one tile of prefix work per resident workgroup (~1 us at
-// ~5 TB/s effective): used to trade scheduling rounds against partial traffic.
-constexpr double kPartialByteCost = 2e-7;
-constexpr size_t kWsAlign = 256;
-
-inline size_t round_up(size_t x, size_t a) { return (x + a - 1) / a * a; }
-inline int64_t cdiv(int64_t a, int64_t b) { return (a + b - 1) / b; }
-inline bool aligned16(const void *p) { return ((uintptr_t)p & 15u) == 0; }
-inline int esize(int dtype) { return dtype == HP_F32 ? 4 : 2; }
+namespace hp {
+namespace host {
 
 hp_status fail_hip(hipError_t e) {
     g_last_hip_error = (int32_t)e;
     return HP_ERR_HIP;
 }
 
-hp_status check_query(const hp_query *q) {
-    if (!q) return HP_ERR_NULL;
-    if (q->B < 0 || q->Hq <= 0 || q->Hkv <= 0 || q->Hq % q->Hkv != 0) return HP_ERR_INVALID_ARG;
-    if (q->dtype < HP_F32 || q->dtype > HP_BF16) return HP_ERR_INVALID_ARG;
-    if (!std::isfinite(q->scale)) return HP_ERR_INVALID_ARG;
-    if (q->d != 64 && q->d != 128) return HP_ERR_UNSUPPORTED;
-    const int G = q->Hq / q->Hkv;
-    if (G > 8 || (G & (G - 1)) != 0) return HP_ERR_UNSUPPORTED;
-    if (q->B > 0 && !q->q) return HP_ERR_NULL;
-    if (q->B > 0 && !aligned16(q->q)) return HP_ERR_INVALID_ARG;
-    return HP_OK;
+void plan_splits(const SplitItem *items, int count, int Hkv, int d, int nw, int64_t max_T,
+                 SplitPlan *out) {
+    const int64_t rows_per_wg = 32 * nw;
+    const int64_t slots = (int64_t)kCUs * kWavesPerCU / nw;
+    int64_t max_tiles = 0;
+    for (int i = 0; i < count; ++i) {
+        max_tiles = std::max<int64_t>(max_tiles, items[i].tiles);
+        out[i].rowblocks = (int)cdiv(std::max<int64_t>(items[i].M, 1), rows_per_wg);
+    }
+    const int64_t T_hi = std::max<int64_t>(1, std::min<int64_t>(max_T, max_tiles));
+    int64_t best_T = T_hi;
+    double best_cost = 1e300;
+    for (int64_t T = 1; T <= T_hi; ++T) {
+        int64_t wgs = 0;
+        double pbytes = 0;
+        for (int i = 0; i < count; ++i) {
+            const int64_t tiles = items[i].tiles;
+            const int64_t ns = tiles ? cdiv(tiles, T) : 1;
+            const int64_t units = (int64_t)Hkv * ns;
+            const int64_t rb = out[i].rowblocks;
+            wgs += (rb > 1 ? (int64_t)round_up(units, 8) : units) * rb;
+            pbytes += (double)ns * items[i].rows * (d + 1) * 4.0 * 2.0;
+        }
+        const double cost = (double)cdiv(wgs, slots) * T + kPartialByteCost * pbytes;
+        if (cost < best_cost) {
+            best_cost = cost;
+            best_T = T;
+        }
+    }
+    for (int i = 0; i < count; ++i) {
+        SplitPlan &sp = out[i];
+        const int64_t tiles = items[i].tiles;
+        const int64_t ns = tiles ? cdiv(tiles, best_T) : 1;
+        sp.tiles_per_split = tiles ? (int)cdiv(tiles, ns) : 0;
+        sp.nsplit = tiles ? (int)cdiv(tiles, sp.tiles_per_split) : 1;
+        const int64_t units = (int64_t)Hkv * sp.nsplit;
+        sp.units_padded = (int)(sp.rowblocks > 1 ? round_up(units, 8) : units);
+        sp.wgs = sp.units_padded * sp.rowblocks;
+    }
 }
+
+}  // namespace host
+}  // namespace hp
+
+namespace {
+
+using namespace hp;
+using namespace hp::host;
+
+hp_status check_query(const hp_query *q) { return check_geometry(q, true); }
 
 hp_status check_node(const hp_query *q, const hp_prefix_node *n) {
     if (!n) return HP_ERR_NULL;
@@ -120,8 +138,6 @@ hp_status check_out(const float *o, const float *lse) {
 // Work partitioning
 // ---------------------------------------------------------------------------
 
-int choose_nw(int64_t M) { return M <= 32 ? 1 : M <= 64 ? 2 : M <= 128 ? 4 : 8; }
-
 struct NodePlan {
     int nsplit = 1, tiles_per_split = 0, rowblocks = 1, units_padded = 0, wgs = 0;
     int64_t rows = 0;  // (seq_end - seq_begin) * Hq output rows
@@ -134,55 +150,27 @@ struct LevelPlan {
     NodePlan nodes[HP_MAX_NODES];
 };
 
-// Splits of the key range: every node of a level gets splits of (about) the
-// same number of tiles T, chosen to minimise
-//     rounds(T) * T + kPartialByteCost * partial_bytes(T)
-// where rounds(T) is how many times the launch fills the GPU's workgroup slots
-// (a partly filled last round costs a full round) and partial_bytes(T) the
-// split results written and read back by the merge.
+// Splits of every node of one level (one launch): plan_splits over the nodes.
 void plan_level(const hp_query &q, const hp_prefix_node *nodes, int count, LevelPlan &lp) {
     const int G = q.Hq / q.Hkv;
-    int64_t maxM = 1, max_tiles = 0;
+    SplitItem items[HP_MAX_NODES];
+    SplitPlan sp[HP_MAX_NODES];
+    int64_t maxM = 1;
     for (int i = 0; i < count; ++i) {
-        maxM = std::max<int64_t>(maxM, (int64_t)(nodes[i].seq_end - nodes[i].seq_begin) * G);
-        max_tiles = std::max<int64_t>(max_tiles, cdiv(nodes[i].len, kTileKeys));
+        const int64_t nseq = nodes[i].seq_end - nodes[i].seq_begin;
+        items[i] = SplitItem{nseq * G, nseq * q.Hq, cdiv(nodes[i].len, kTileKeys)};
+        maxM = std::max<int64_t>(maxM, nseq * G);
     }
     lp.nw = choose_nw(maxM);
-    const int64_t rows_per_wg = 32 * lp.nw;
-    const int64_t slots = (int64_t)kCUs * kWavesPerCU / lp.nw;
-    for (int i = 0; i < count; ++i) {
-        const int64_t M = (int64_t)(nodes[i].seq_end - nodes[i].seq_begin) * G;
-        lp.nodes[i].rowblocks = (int)cdiv(M, rows_per_wg);
-        lp.nodes[i].rows = (int64_t)(nodes[i].seq_end - nodes[i].seq_begin) * q.Hq;
-    }
-    int64_t best_T = std::max<int64_t>(1, max_tiles);
-    double best_cost = 1e300;
-    for (int64_t T = 1; T <= std::max<int64_t>(1, max_tiles); ++T) {
-        int64_t wgs = 0;
-        double pbytes = 0;
-        for (int i = 0; i < count; ++i) {
-            const int64_t tiles = cdiv(nodes[i].len, kTileKeys);
-            const int64_t ns = tiles ? cdiv(tiles, T) : 1;
-            const int64_t units = (int64_t)q.Hkv * ns;
-            const int64_t rb = lp.nodes[i].rowblocks;
-            wgs += (rb > 1 ? (int64_t)round_up(units, 8) : units) * rb;
-            pbytes += (double)ns * lp.nodes[i].rows * (q.d + 1) * 4.0 * 2.0;
-        }
-        const double cost = (double)cdiv(wgs, slots) * T + kPartialByteCost * pbytes;
-        if (cost < best_cost) {
-            best_cost = cost;
-            best_T = T;
-        }
-    }
+    plan_splits(items, count, q.Hkv, q.d, lp.nw, INT64_MAX, sp);
     for (int i = 0; i < count; ++i) {
         NodePlan &np = lp.nodes[i];
-        const int64_t tiles = cdiv(nodes[i].len, kTileKeys);
-        const int64_t ns = tiles ? cdiv(tiles, best_T) : 1;
-        np.tiles_per_split = tiles ? (int)cdiv(tiles, ns) : 0;
-        np.nsplit = tiles ? (int)cdiv(tiles, np.tiles_per_split) : 1;
-        const int64_t units = (int64_t)q.Hkv * np.nsplit;
-        np.units_padded = (int)(np.rowblocks > 1 ? round_up(units, 8) : units);
-        np.wgs = np.units_padded * np.rowblocks;
+        np.nsplit = sp[i].nsplit;
+        np.tiles_per_split = sp[i].tiles_per_split;
+        np.rowblocks = sp[i].rowblocks;
+        np.units_padded = sp[i].units_padded;
+        np.wgs = sp[i].wgs;
+        np.rows = items[i].rows;
     }
     lp.count = count;
 }
@@ -318,6 +306,7 @@ const char *hp_status_string(hp_status s) {
     case HP_ERR_UNSUPPORTED: return "unsupported (outside the implemented domain)";
     case HP_ERR_WORKSPACE: return "workspace missing or too small";
     case HP_ERR_HIP: return "HIP launch failed";
+    case HP_ERR_CAPACITY: return "capacity exceeded (pool, plan buffer or output array too small)";
     default: return "unknown status";
     }
 }

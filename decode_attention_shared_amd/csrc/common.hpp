@@ -54,12 +54,68 @@ struct PrefixNodeArg {
     RowDest dest;
 };
 
+// ---------------------------------------------------------------------------
+// Chunked-tree plan image: int32 arrays built on the host, copied to device
+// memory once per tree shape.  Word offsets of each array come from
+// tree_layout() (same on both sides).
+// ---------------------------------------------------------------------------
+struct TreeSeg {               // a run of batched descriptors sharing one range
+    int32_t piece_begin;       // first key tile in the piece table
+    int32_t ntiles;
+    int32_t seq_begin, seq_end;
+    int32_t nsplit, tiles_per_split, rowblocks, units_padded;
+    int32_t wg_begin;          // first workgroup of the segment in its launch
+    int32_t part_row0;         // first (sequence, split) partial row of the segment
+    int32_t pad0, pad1;
+};
+struct TreePiece {             // one key tile: `count` pool rows from `row`
+    int32_t row, count;
+};
+struct TreeSrc {               // one segment a sequence reads the partials of
+    int32_t part_row;          // partial row of (this sequence, split 0)
+    int32_t nsplit;
+    int32_t split_rows;        // partial rows between splits (= the segment's sequences)
+    int32_t pad;
+};
+constexpr int kTreeMaxTilesPerSplit = 64;  // one piece per lane of a wave
+
+struct TreeLayout {            // word offsets into the image
+    int64_t segs, pieces, wgseg, seq_tok, tok_rows, seq_src, srcs, shared, words;
+};
+
+__host__ __device__ inline int64_t tree_align4(int64_t w) { return (w + 3) & ~(int64_t)3; }
+
+__host__ __device__ inline TreeLayout tree_layout(int64_t num_segs, int64_t num_pieces,
+                                                  int64_t num_wgs, int64_t B,
+                                                  int64_t num_tok_rows, int64_t num_srcs) {
+    TreeLayout L;
+    int64_t w = 0;
+    L.segs = w;     w = tree_align4(w + num_segs * (int64_t)(sizeof(TreeSeg) / 4));
+    L.pieces = w;   w = tree_align4(w + num_pieces * 2);
+    L.wgseg = w;    w = tree_align4(w + num_wgs);
+    L.seq_tok = w;  w = tree_align4(w + B + 1);
+    L.tok_rows = w; w = tree_align4(w + num_tok_rows);
+    L.seq_src = w;  w = tree_align4(w + B + 1);
+    L.srcs = w;     w = tree_align4(w + num_srcs * 4);
+    L.shared = w;   w = tree_align4(w + B);
+    L.words = w;
+    return L;
+}
+
 struct PrefixArgs {
     const void *q;
     int32_t B, Hq, Hkv, G;
     float scale_log2;         // scale * log2(e): scores go straight to the exp2 domain
     int32_t num_nodes;
     PrefixNodeArg nodes[kMaxLaunchNodes];
+    // Chunk-tree launches only: segments come from the plan image.
+    const int32_t *tree;      // plan image (device)
+    int64_t seg_off, piece_off, wgseg_off;  // word offsets of its arrays
+    int32_t wg0;              // this launch's first entry of the workgroup table
+    const void *k_pool, *v_pool;
+    int64_t row_stride;       // elements between pool rows (Hkv * d)
+    int32_t d;
+    float *part_o, *part_lse; // partial results, [part_rows][Hq][d] and [part_rows][Hq]
 };
 
 constexpr int kMaxMergeSrc = HP_MAX_NODES + 1;
@@ -84,8 +140,8 @@ struct SuffixArgs {
     const void *q;
     const void *k_pool;
     const void *v_pool;
-    const int32_t *table;
-    const int32_t *lens;
+    const int32_t *table;     // block table; chunk-tree mode: unused
+    const int32_t *lens;      // chunk-tree mode: total tokens of each sequence, may be null
     int32_t B, Hq, Hkv;
     int32_t max_blocks, num_blocks;
     int32_t has_suffix;       // 0: no paged suffix (only the sources are merged)
@@ -93,6 +149,11 @@ struct SuffixArgs {
     RowDest dest;             // final O and LSE (o_split, lse_split unused)
     int32_t nsrc;
     MergeSrc src[kMaxMergeSrc];
+    // Chunk-tree mode: private rows and segment partials from the plan image.
+    const int32_t *tree;
+    int64_t seq_tok_off, tok_rows_off, seq_src_off, srcs_off, shared_off;
+    int64_t pool_rows;
+    const float *part_o, *part_lse;
 };
 
 struct MergeArgs {

@@ -1,0 +1,83 @@
+// Host-side helpers shared by the C-ABI translation units (validation,
+// sizes and the split planner).  Internal to the library.
+#pragma once
+
+#include <hip/hip_runtime.h>
+
+#include <cmath>
+#include <cstddef>
+#include <cstdint>
+
+#include "common.hpp"
+#include "hp_attn.h"
+
+namespace hp {
+
+hipError_t launch_prefix(const PrefixArgs &a, int dtype, int d, int nw, int wgs, hipStream_t s);
+hipError_t launch_tree_prefix(const PrefixArgs &a, int dtype, int d, int nw, int wgs,
+                              hipStream_t s);
+hipError_t launch_suffix(const SuffixArgs &a, int dtype, int d, int G, int nws, hipStream_t s);
+hipError_t launch_tree_suffix(const SuffixArgs &a, int dtype, int d, int G, int nws,
+                              hipStream_t s);
+hipError_t launch_merge(const MergeArgs &a, int d, hipStream_t s);
+hipError_t launch_kv_append(const void *k_new, const void *v_new, const int32_t *rows, int32_t n,
+                            int64_t row_bytes, void *k_pool, void *v_pool, int64_t pool_rows,
+                            int32_t *seq_lens, const int32_t *seq_idx, int32_t num_seqs,
+                            hipStream_t s);
+
+namespace host {
+
+constexpr int kTileKeys = 64;           // keys per prefix tile (matches the kernels)
+constexpr int kCUs = 256;               // MI355X compute units
+constexpr int kWavesPerCU = 8;          // two waves per SIMD at the prefix kernels' register use
+// Cost of one byte of split partials (written once, read once by the merge),
+// in units of one tile of prefix work per resident workgroup (~1 us at
+// ~5 TB/s effective): used to trade scheduling rounds against partial traffic.
+constexpr double kPartialByteCost = 2e-7;
+constexpr size_t kWsAlign = 256;
+
+inline size_t round_up(size_t x, size_t a) { return (x + a - 1) / a * a; }
+inline int64_t cdiv(int64_t a, int64_t b) { return (a + b - 1) / b; }
+inline bool aligned16(const void *p) { return ((uintptr_t)p & 15u) == 0; }
+inline int esize(int dtype) { return dtype == HP_F32 ? 4 : 2; }
+
+// hipError_t of the calling thread's last failed launch.
+hp_status fail_hip(hipError_t e);
+
+// Geometry checks of a query (q may be NULL when need_q is false).
+inline hp_status check_geometry(const hp_query *q, bool need_q) {
+    if (!q) return HP_ERR_NULL;
+    if (q->B < 0 || q->Hq <= 0 || q->Hkv <= 0 || q->Hq % q->Hkv != 0) return HP_ERR_INVALID_ARG;
+    if (q->dtype < HP_F32 || q->dtype > HP_BF16) return HP_ERR_INVALID_ARG;
+    if (need_q && !std::isfinite(q->scale)) return HP_ERR_INVALID_ARG;
+    if (q->d != 64 && q->d != 128) return HP_ERR_UNSUPPORTED;
+    const int G = q->Hq / q->Hkv;
+    if (G > 8 || (G & (G - 1)) != 0) return HP_ERR_UNSUPPORTED;
+    if (need_q && q->B > 0 && !q->q) return HP_ERR_NULL;
+    if (need_q && q->B > 0 && !aligned16(q->q)) return HP_ERR_INVALID_ARG;
+    return HP_OK;
+}
+
+inline int choose_nw(int64_t M) { return M <= 32 ? 1 : M <= 64 ? 2 : M <= 128 ? 4 : 8; }
+
+// One unit of prefix work for the split planner: M stacked query rows per
+// KV head, `rows` output rows ((sequences) * Hq) and `tiles` 64-key tiles.
+struct SplitItem {
+    int64_t M, rows, tiles;
+};
+struct SplitPlan {
+    int nsplit = 1, tiles_per_split = 0, rowblocks = 1, units_padded = 0, wgs = 0;
+};
+
+// Splits of the key range for items launched together (one row-block width
+// nw): every item gets splits of (about) the same number of tiles T <= max_T,
+// chosen to minimise
+//     rounds(T) * T + kPartialByteCost * partial_bytes(T)
+// where rounds(T) is how many times the launch fills the GPU's workgroup slots
+// (a partly filled last round costs a full round) and partial_bytes(T) the
+// split results written and read back by the merge.
+void plan_splits(const SplitItem *items, int count, int Hkv, int d, int nw, int64_t max_T,
+                 SplitPlan *out);
+
+}  // namespace host
+}  // namespace hp

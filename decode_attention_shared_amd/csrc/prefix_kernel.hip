@@ -58,15 +58,8 @@ struct WgTask {
     bool valid;
 };
 
-__device__ __forceinline__ WgTask decode_wg(const PrefixArgs &args) {
+__device__ __forceinline__ WgTask decode_local(const PrefixNodeArg &nd, int local, int Hkv) {
     WgTask t;
-    const int wg = blockIdx.x;
-    int ni = 0;
-#pragma unroll 1
-    for (int i = 1; i < args.num_nodes; ++i)
-        if (wg >= args.nodes[i].wg_begin) ni = i;
-    const PrefixNodeArg &nd = args.nodes[ni];
-    const int local = wg - nd.wg_begin;
     int unit, rb;
     if (nd.rowblocks == 1) {
         unit = local;
@@ -77,12 +70,94 @@ __device__ __forceinline__ WgTask decode_wg(const PrefixArgs &args) {
         rb = rem / 8;
         unit = chunk * 8 + rem % 8;
     }
-    t.node = ni;
+    t.node = 0;
     t.g = unit / nd.nsplit;
     t.split = unit % nd.nsplit;
     t.rb = rb;
-    t.valid = unit < args.Hkv * nd.nsplit;
+    t.valid = unit < Hkv * nd.nsplit;
     return t;
+}
+
+__device__ __forceinline__ WgTask decode_wg(const PrefixArgs &args) {
+    const int wg = blockIdx.x;
+    int ni = 0;
+#pragma unroll 1
+    for (int i = 1; i < args.num_nodes; ++i)
+        if (wg >= args.nodes[i].wg_begin) ni = i;
+    WgTask t = decode_local(args.nodes[ni], wg - args.nodes[ni].wg_begin, args.Hkv);
+    t.node = ni;
+    return t;
+}
+
+// Chunk-tree launches: the workgroup table of the plan image names this
+// workgroup's segment; the segment record gives the same fields as a node
+// (its keys are pool rows, its results go to the partial buffers).
+__device__ __forceinline__ WgTask decode_tree_wg(const PrefixArgs &args, PrefixNodeArg &nd,
+                                                 int &piece_begin) {
+    const int32_t *tr = args.tree;
+    const int si = tr[args.wgseg_off + args.wg0 + blockIdx.x];
+    const TreeSeg sg = *(const TreeSeg *)(tr + args.seg_off + (int64_t)si * (sizeof(TreeSeg) / 4));
+    const int64_t nseq = sg.seq_end - sg.seq_begin;
+    nd.k = args.k_pool;
+    nd.v = args.v_pool;
+    nd.stride_tok = args.row_stride;
+    nd.stride_head = args.d;
+    nd.len = sg.ntiles * kTile;
+    nd.seq_begin = sg.seq_begin;
+    nd.seq_end = sg.seq_end;
+    nd.nsplit = sg.nsplit;
+    nd.tiles_per_split = sg.tiles_per_split;
+    nd.rowblocks = sg.rowblocks;
+    nd.units_padded = sg.units_padded;
+    nd.wg_begin = sg.wg_begin;
+    nd.dest.o = args.part_o + (int64_t)sg.part_row0 * args.Hq * args.d;
+    nd.dest.lse = args.part_lse + (int64_t)sg.part_row0 * args.Hq;
+    nd.dest.o_split = nseq * args.Hq * args.d;
+    nd.dest.lse_split = nseq * args.Hq;
+    nd.dest.row_base = sg.seq_begin;
+    piece_begin = sg.piece_begin;
+    return decode_local(nd, (int)blockIdx.x - sg.wg_begin, args.Hkv);
+}
+
+// Where the keys of a tile come from.  key0(t): row offset of tile t's first
+// key from the node's base (in rows of stride_tok); valid(t): keys the tile
+// holds (values of 64 or more mean a full tile).
+//
+// A node stored contiguously: tile t holds keys 64t .. 64t + 63, and only the
+// node's last tile can be partial.
+struct ContigTiles {
+    int len;
+    __device__ __forceinline__ int key0(int tile) const { return tile * kTile; }
+    __device__ __forceinline__ int valid(int tile) const { return len - tile * kTile; }
+};
+// A chunk-tree segment: tile t is one piece (up to 64 consecutive pool rows),
+// and any piece may be partial.  Lane l holds piece tb + l of this split;
+// a tile's fields are read from that lane into scalar registers.
+struct ChunkTiles {
+    int tb;
+    int row_l, cnt_l;
+    __device__ __forceinline__ int key0(int tile) const {
+        return __builtin_amdgcn_readlane(row_l, tile - tb);
+    }
+    __device__ __forceinline__ int valid(int tile) const {
+        return __builtin_amdgcn_readlane(cnt_l, tile - tb);
+    }
+};
+
+__device__ __forceinline__ ChunkTiles load_pieces(const PrefixArgs &args, int piece_begin, int tb,
+                                                  int te) {
+    ChunkTiles src;
+    src.tb = tb;
+    const int l = threadIdx.x % kWave;
+    src.row_l = 0;
+    src.cnt_l = 0;
+    if (tb + l < te) {
+        const TreePiece p =
+            *(const TreePiece *)(args.tree + args.piece_off + 2 * ((int64_t)piece_begin + tb + l));
+        src.row_l = p.row;
+        src.cnt_l = p.count;
+    }
+    return src;
 }
 
 // Online-softmax update for one 64-key tile held as two 32x32 score blocks.
@@ -270,8 +345,10 @@ __device__ __forceinline__ void block_sync() {
     __builtin_amdgcn_sched_barrier(0);
 }
 
-template <bool kBf16, int D, int NW>
-__global__ __launch_bounds__(64 * NW) void prefix_mfma16_kernel(PrefixArgs args) {
+template <bool kBf16, int D, int NW, class Tiles>
+__device__ __forceinline__ void mfma16_body(const PrefixArgs &args, const WgTask &task,
+                                            const PrefixNodeArg &nd, const Tiles &src, int tb,
+                                            int te) {
     constexpr int kDSteps = D / 16;
     constexpr int kDBlocks = D / 32;
     constexpr int kRowChunks = D / 8;                     // 16-byte chunks per K/V row
@@ -295,14 +372,8 @@ __global__ __launch_bounds__(64 * NW) void prefix_mfma16_kernel(PrefixArgs args)
     // group of the transposing read touches land 2 chunks apart.
     __shared__ __attribute__((aligned(1024))) uint16_t lds[kStages][2][kTileElems];
 
-    const WgTask task = decode_wg(args);
-    if (!task.valid) return;
-    const PrefixNodeArg &nd = args.nodes[task.node];
     const int G = args.G;
     const int M = (nd.seq_end - nd.seq_begin) * G;
-    const int ntiles = (nd.len + kTile - 1) / kTile;
-    const int tb = task.split * nd.tiles_per_split;  // first tile of this split
-    const int te = min(tb + nd.tiles_per_split, ntiles);
 
     const int tid = threadIdx.x;
     const int wave = tid / kWave;
@@ -349,13 +420,14 @@ __global__ __launch_bounds__(64 * NW) void prefix_mfma16_kernel(PrefixArgs args)
     }
     auto issue = [&](int tile) {
         const int st = (tile - tb) % kStages;
-        const int key0 = tile * kTile;
-        const bool full = key0 + kTile <= nd.len;
+        const int key0 = src.key0(tile);
+        const int valid = src.valid(tile);
+        const bool full = valid >= kTile;
 #pragma unroll
         for (int j = 0; j < kDmas; ++j) {
-            // keys past the node's end re-read its last key (finite data whose
+            // keys past the tile's end re-read its last key (finite data whose
             // scores are masked to -inf)
-            const int t = full ? key0 + dma_row[j] : min(key0 + dma_row[j], nd.len - 1);
+            const int t = key0 + (full ? dma_row[j] : min(dma_row[j], valid - 1));
             const int64_t off = (int64_t)t * nd.stride_tok;
             uint16_t *dst = &lds[st][0][(wave * kDmas + j) * kRowsPerDma * D];
             dma16(kbase + off + dma_ck[j], dst);
@@ -420,8 +492,8 @@ __global__ __launch_bounds__(64 * NW) void prefix_mfma16_kernel(PrefixArgs args)
         if (tile + kStages - 1 < te) issue(tile + kStages - 1);
 
         // Accumulator i of a 32x32 block holds key 8*(i/4) + 4*hi + i%4.
-        const int valid = nd.len - tile * kTile;
-        if (valid < kTile) {  // only the node's last tile can be partial
+        const int valid = src.valid(tile);
+        if (valid < kTile) {
 #pragma unroll
             for (int i = 0; i < 16; ++i) {
                 const int kr = 8 * (i / 4) + 4 * hi + (i % 4);
@@ -477,6 +549,29 @@ __global__ __launch_bounds__(64 * NW) void prefix_mfma16_kernel(PrefixArgs args)
     }
 }
 
+template <bool kBf16, int D, int NW>
+__global__ __launch_bounds__(64 * NW) void prefix_mfma16_kernel(PrefixArgs args) {
+    const WgTask task = decode_wg(args);
+    if (!task.valid) return;
+    const PrefixNodeArg &nd = args.nodes[task.node];
+    const int ntiles = (nd.len + kTile - 1) / kTile;
+    const int tb = task.split * nd.tiles_per_split;  // first tile of this split
+    const int te = min(tb + nd.tiles_per_split, ntiles);
+    mfma16_body<kBf16, D, NW>(args, task, nd, ContigTiles{nd.len}, tb, te);
+}
+
+template <bool kBf16, int D, int NW>
+__global__ __launch_bounds__(64 * NW) void tree_mfma16_kernel(PrefixArgs args) {
+    PrefixNodeArg nd;
+    int piece_begin;
+    const WgTask task = decode_tree_wg(args, nd, piece_begin);
+    if (!task.valid) return;
+    const int ntiles = nd.len / kTile;
+    const int tb = task.split * nd.tiles_per_split;
+    const int te = min(tb + nd.tiles_per_split, ntiles);
+    mfma16_body<kBf16, D, NW>(args, task, nd, load_pieces(args, piece_begin, tb, te), tb, te);
+}
+
 // ---------------------------------------------------------------------------
 // Ping-pong variant for 256 rows per workgroup: 8 waves of 32 rows.  Waves w
 // and w+4 of a workgroup share a SIMD, so waves 0-3 and 4-7 form two groups
@@ -487,8 +582,10 @@ __global__ __launch_bounds__(64 * NW) void prefix_mfma16_kernel(PrefixArgs args)
 // matrix core and the vector ALUs of a SIMD can work at the same time.
 // ---------------------------------------------------------------------------
 
-template <bool kBf16, int D>
-__global__ __launch_bounds__(512) void prefix_mfma16_pp_kernel(PrefixArgs args) {
+template <bool kBf16, int D, class Tiles>
+__device__ __forceinline__ void pp_body(const PrefixArgs &args, const WgTask &task,
+                                        const PrefixNodeArg &nd, const Tiles &src, int tb,
+                                        int te) {
     constexpr int NW = 8;
     constexpr int kDSteps = D / 16;
     constexpr int kDBlocks = D / 32;
@@ -503,14 +600,8 @@ __global__ __launch_bounds__(512) void prefix_mfma16_pp_kernel(PrefixArgs args) 
     constexpr int kTileElems = kTile * D;
     __shared__ __attribute__((aligned(1024))) uint16_t lds[kStages][2][kTileElems];
 
-    const WgTask task = decode_wg(args);
-    if (!task.valid) return;
-    const PrefixNodeArg &nd = args.nodes[task.node];
     const int G = args.G;
     const int M = (nd.seq_end - nd.seq_begin) * G;
-    const int ntiles = (nd.len + kTile - 1) / kTile;
-    const int tb = task.split * nd.tiles_per_split;
-    const int te = min(tb + nd.tiles_per_split, ntiles);
 
     const int tid = threadIdx.x;
     const int wave = tid / kWave;
@@ -542,7 +633,6 @@ __global__ __launch_bounds__(512) void prefix_mfma16_pp_kernel(PrefixArgs args) 
     // Node fields the loop needs, read once (the compiler would otherwise
     // reload them from the argument segment, a scalar-memory round trip, at
     // every tile).
-    const int len = nd.len;
     const int64_t stride_tok = nd.stride_tok;
     const uint16_t *kbase = (const uint16_t *)nd.k + (int64_t)task.g * nd.stride_head;
     const uint16_t *vbase = (const uint16_t *)nd.v + (int64_t)task.g * nd.stride_head;
@@ -561,18 +651,19 @@ __global__ __launch_bounds__(512) void prefix_mfma16_pp_kernel(PrefixArgs args) 
     }
     auto issue = [&](int tile) {
         const int st = (tile - tb) % kStages;
-        const int key0 = tile * kTile;
+        const int key0 = src.key0(tile);
+        const int valid = src.valid(tile);
         const int64_t tile_off = (int64_t)key0 * stride_tok;
         const uint16_t *kt = kbase + tile_off;
         const uint16_t *vt = vbase + tile_off;
-        const bool full = key0 + kTile <= len;
+        const bool full = valid >= kTile;
 #pragma unroll
         for (int j = 0; j < kDmas; ++j) {
             uint16_t *dst = &lds[st][0][(wave * kDmas + j) * kRowsPerDma * D];
             uint32_t ko = koff[j], vo = voff[j];
-            if (!full && key0 + dma_row[j] >= len) {
-                // keys past the node's end re-read its last key (masked to -inf)
-                const uint32_t back = (uint32_t)((key0 + dma_row[j] - (len - 1)) * stride_tok);
+            if (!full && dma_row[j] >= valid) {
+                // keys past the tile's end re-read its last key (masked to -inf)
+                const uint32_t back = (uint32_t)((dma_row[j] - (valid - 1)) * stride_tok);
                 ko -= back;
                 vo -= back;
             }
@@ -643,8 +734,8 @@ __global__ __launch_bounds__(512) void prefix_mfma16_pp_kernel(PrefixArgs args) 
     // Vector phase: online softmax of tile u (scores in s0/s1) into pk.  O
     // already holds every earlier tile, so a rescale applies to all of it.
     auto vphase = [&](int u) {
-        const int valid = len - (tb + u) * kTile;
-        if (valid < kTile) {  // only the node's last tile can be partial
+        const int valid = src.valid(tb + u);
+        if (valid < kTile) {
 #pragma unroll
             for (int i = 0; i < 16; ++i) {
                 const int kr = 8 * (i / 4) + 4 * hi + (i % 4);
@@ -687,25 +778,44 @@ __global__ __launch_bounds__(512) void prefix_mfma16_pp_kernel(PrefixArgs args) 
     }
 }
 
+template <bool kBf16, int D>
+__global__ __launch_bounds__(512) void prefix_mfma16_pp_kernel(PrefixArgs args) {
+    const WgTask task = decode_wg(args);
+    if (!task.valid) return;
+    const PrefixNodeArg &nd = args.nodes[task.node];
+    const int ntiles = (nd.len + kTile - 1) / kTile;
+    const int tb = task.split * nd.tiles_per_split;
+    const int te = min(tb + nd.tiles_per_split, ntiles);
+    pp_body<kBf16, D>(args, task, nd, ContigTiles{nd.len}, tb, te);
+}
+
+template <bool kBf16, int D>
+__global__ __launch_bounds__(512) void tree_mfma16_pp_kernel(PrefixArgs args) {
+    PrefixNodeArg nd;
+    int piece_begin;
+    const WgTask task = decode_tree_wg(args, nd, piece_begin);
+    if (!task.valid) return;
+    const int ntiles = nd.len / kTile;
+    const int tb = task.split * nd.tiles_per_split;
+    const int te = min(tb + nd.tiles_per_split, ntiles);
+    pp_body<kBf16, D>(args, task, nd, load_pieces(args, piece_begin, tb, te), tb, te);
+}
+
 // ---------------------------------------------------------------------------
 // fp32 inputs: v_mfma_f32_32x32x2f32 (no down-conversion anywhere)
 // ---------------------------------------------------------------------------
-template <int D, int NW>
-__global__ __launch_bounds__(64 * NW) void prefix_mfma32_kernel(PrefixArgs args) {
+template <int D, int NW, class Tiles>
+__device__ __forceinline__ void mfma32_body(const PrefixArgs &args, const WgTask &task,
+                                            const PrefixNodeArg &nd, const Tiles &src,
+                                            int tile_begin, int tile_end) {
     constexpr int kThreads = 64 * NW;
     constexpr int kKStride = D + 1;  // odd stride: rows fall in different banks
     constexpr int kDBlocks = D / 32;
     __shared__ float ks[kTile * kKStride];
     __shared__ __attribute__((aligned(16))) float vs[kTile * D];
 
-    const WgTask task = decode_wg(args);
-    if (!task.valid) return;
-    const PrefixNodeArg &nd = args.nodes[task.node];
     const int G = args.G;
     const int M = (nd.seq_end - nd.seq_begin) * G;
-    const int ntiles = (nd.len + kTile - 1) / kTile;
-    const int tile_begin = task.split * nd.tiles_per_split;
-    const int tile_end = min(tile_begin + nd.tiles_per_split, ntiles);
 
     const int wave = threadIdx.x / kWave;
     const int lane = threadIdx.x % kWave;
@@ -733,7 +843,8 @@ __global__ __launch_bounds__(64 * NW) void prefix_mfma32_kernel(PrefixArgs args)
 
 #pragma unroll 1
     for (int tile = tile_begin; tile < tile_end; ++tile) {
-        const int key0 = tile * kTile;
+        const int key0 = src.key0(tile);
+        const int valid = src.valid(tile);
         __syncthreads();
         static_assert((kTile * D / 4) % kThreads == 0, "tile chunks must divide evenly");
 #pragma unroll
@@ -743,7 +854,7 @@ __global__ __launch_bounds__(64 * NW) void prefix_mfma32_kernel(PrefixArgs args)
             const int dc = c % (D / 4);
             const int t = key0 + key;
             f32x4 kv = {0.f, 0.f, 0.f, 0.f}, vv = {0.f, 0.f, 0.f, 0.f};
-            if (t < nd.len) {
+            if (key < valid) {
                 const int64_t off = (int64_t)t * nd.stride_tok + dc * 4;
                 kv = *(const f32x4 *)(kbase + off);
                 vv = *(const f32x4 *)(vbase + off);
@@ -763,7 +874,6 @@ __global__ __launch_bounds__(64 * NW) void prefix_mfma32_kernel(PrefixArgs args)
                                                       qf[kk], s1, 0, 0, 0);
         }
         float x[32];
-        const int valid = nd.len - key0;
 #pragma unroll
         for (int i = 0; i < 16; ++i) {
             const int kr = 8 * (i / 4) + 4 * hi + (i % 4);
@@ -793,6 +903,29 @@ __global__ __launch_bounds__(64 * NW) void prefix_mfma32_kernel(PrefixArgs args)
         const int64_t ri = ((int64_t)(b - nd.dest.row_base)) * args.Hq + h;
         write_row<D>(nd.dest, task.split, ri, oacc, hi, m_run, l_run);
     }
+}
+
+template <int D, int NW>
+__global__ __launch_bounds__(64 * NW) void prefix_mfma32_kernel(PrefixArgs args) {
+    const WgTask task = decode_wg(args);
+    if (!task.valid) return;
+    const PrefixNodeArg &nd = args.nodes[task.node];
+    const int ntiles = (nd.len + kTile - 1) / kTile;
+    const int tb = task.split * nd.tiles_per_split;
+    const int te = min(tb + nd.tiles_per_split, ntiles);
+    mfma32_body<D, NW>(args, task, nd, ContigTiles{nd.len}, tb, te);
+}
+
+template <int D, int NW>
+__global__ __launch_bounds__(64 * NW) void tree_mfma32_kernel(PrefixArgs args) {
+    PrefixNodeArg nd;
+    int piece_begin;
+    const WgTask task = decode_tree_wg(args, nd, piece_begin);
+    if (!task.valid) return;
+    const int ntiles = nd.len / kTile;
+    const int tb = task.split * nd.tiles_per_split;
+    const int te = min(tb + nd.tiles_per_split, ntiles);
+    mfma32_body<D, NW>(args, task, nd, load_pieces(args, piece_begin, tb, te), tb, te);
 }
 
 constexpr bool kPingPongEnabled = true;
@@ -833,6 +966,45 @@ hipError_t launch_prefix(const PrefixArgs &a, int dtype, int d, int nw, int wgs,
     case 2: return launch_nw<2>(a, dtype, d, wgs, s);
     case 4: return launch_nw<4>(a, dtype, d, wgs, s);
     default: return launch_nw<8>(a, dtype, d, wgs, s);
+    }
+}
+
+template <int NW>
+static hipError_t launch_tree_nw(const PrefixArgs &a, int dtype, int d, int wgs, hipStream_t s) {
+    const dim3 grid(wgs), block(64 * NW);
+    if (dtype == HP_BF16) {
+        if (d == 128) tree_mfma16_kernel<true, 128, NW><<<grid, block, 0, s>>>(a);
+        else tree_mfma16_kernel<true, 64, NW><<<grid, block, 0, s>>>(a);
+    } else if (dtype == HP_F16) {
+        if (d == 128) tree_mfma16_kernel<false, 128, NW><<<grid, block, 0, s>>>(a);
+        else tree_mfma16_kernel<false, 64, NW><<<grid, block, 0, s>>>(a);
+    } else {
+        if (d == 128) tree_mfma32_kernel<128, NW><<<grid, block, 0, s>>>(a);
+        else tree_mfma32_kernel<64, NW><<<grid, block, 0, s>>>(a);
+    }
+    return hipGetLastError();
+}
+
+// Chunk-tree segments of one row-block width (the caller checks that
+// kTile * row_stride + d fits in int32).
+hipError_t launch_tree_prefix(const PrefixArgs &a, int dtype, int d, int nw, int wgs,
+                              hipStream_t s) {
+    if (kPingPongEnabled && nw == 8 && dtype != HP_F32) {
+        const dim3 grid(wgs), block(512);
+        if (dtype == HP_BF16) {
+            if (d == 128) tree_mfma16_pp_kernel<true, 128><<<grid, block, 0, s>>>(a);
+            else tree_mfma16_pp_kernel<true, 64><<<grid, block, 0, s>>>(a);
+        } else {
+            if (d == 128) tree_mfma16_pp_kernel<false, 128><<<grid, block, 0, s>>>(a);
+            else tree_mfma16_pp_kernel<false, 64><<<grid, block, 0, s>>>(a);
+        }
+        return hipGetLastError();
+    }
+    switch (nw) {
+    case 1: return launch_tree_nw<1>(a, dtype, d, wgs, s);
+    case 2: return launch_tree_nw<2>(a, dtype, d, wgs, s);
+    case 4: return launch_tree_nw<4>(a, dtype, d, wgs, s);
+    default: return launch_tree_nw<8>(a, dtype, d, wgs, s);
     }
 }
 

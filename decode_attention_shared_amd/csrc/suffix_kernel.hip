@@ -67,7 +67,11 @@ __device__ __forceinline__ float group_sum(float x) {
     return x;
 }
 
-template <int kDt, int D, int G, int NWS>
+// kTree: chunk-tree mode.  The private keys of sequence b are the pool rows
+// tok_rows[seq_tok[b] ..] (one row per token: tree pieces start at any row),
+// and the partials to merge are the sequence's entries in the plan's source
+// list, instead of a block table and by-value sources.
+template <int kDt, int D, int G, int NWS, bool kTree>
 __global__ __launch_bounds__(64 * NWS) void suffix_kernel(SuffixArgs a) {
     using E = Elem<kDt>;
     constexpr int kEpl = 16 / E::kSize;  // elements per lane per token
@@ -101,7 +105,16 @@ __global__ __launch_bounds__(64 * NWS) void suffix_kernel(SuffixArgs a) {
 
     int len = 0;
     bool bad = false;
-    if (a.has_suffix) {
+    int tok0 = 0;  // chunk-tree mode: first private row entry of this sequence
+    if constexpr (kTree) {
+        tok0 = a.tree[a.seq_tok_off + b];
+        const int cap = a.tree[a.seq_tok_off + b + 1] - tok0;
+        len = cap;
+        if (a.lens != nullptr) {
+            len = a.lens[b] - a.tree[a.shared_off + b];
+            bad = len < 0 || len > cap;
+        }
+    } else if (a.has_suffix) {
         len = a.lens[b];
         bad = len < 0 || len > a.max_blocks * kBlock;
     }
@@ -119,26 +132,61 @@ __global__ __launch_bounds__(64 * NWS) void suffix_kernel(SuffixArgs a) {
     const int64_t tok_stride = (int64_t)a.Hkv * D * E::kSize;  // bytes between tokens of a block
     const char *kp = (const char *)a.k_pool;
     const char *vp = (const char *)a.v_pool;
-    const int *trow = a.table + (int64_t)b * a.max_blocks;
+    const int *trow = kTree ? a.tree + a.tok_rows_off + tok0 : a.table + (int64_t)b * a.max_blocks;
 
-    // Block ids are read one block-step ahead of their K/V loads, so the
-    // table lookup's latency never sits in front of a block's loads.
-    auto table_id = [&](int blk) { return blk < nblk ? trow[blk] : 0; };
+    // Where a block's keys are: its block id (block table), or in chunk-tree
+    // mode the pool row of each token this lane loads.  Read one block-step
+    // ahead of the K/V loads, so the lookup's latency never sits in front of
+    // a block's loads.
+    struct Ref {
+        int v[kTree ? kPasses : 1];
+    };
+    auto table_id = [&](int blk) {
+        Ref r;
+        if constexpr (kTree) {
+#pragma unroll
+            for (int p = 0; p < kPasses; ++p) {
+                const int t = blk * kBlock + p * kTpp + tg;
+                r.v[p] = blk < nblk && t < len ? trow[t] : 0;  // nblk = 0 when len is bad
+            }
+        } else {
+            r.v[0] = blk < nblk ? trow[blk] : 0;
+        }
+        return r;
+    };
     // Issue the loads of one block (keys past the sequence's end and blocks
     // with an out-of-range id are never read).
-    auto fetch = [&](int blk, int id, u32x4 (&kr)[kPasses], u32x4 (&vr)[kPasses], int &valid) {
-        const bool id_ok = id >= 0 && id < a.num_blocks;
-        bad |= !id_ok;
-        valid = id_ok ? min(kBlock, len - blk * kBlock) : 0;
-        const int64_t base = ((int64_t)(id_ok ? id : 0) * kBlock * a.Hkv + g) * D * E::kSize +
-                             d0 * E::kSize;
+    auto fetch = [&](int blk, const Ref &ref, u32x4 (&kr)[kPasses], u32x4 (&vr)[kPasses],
+                     int &valid) {
+        if constexpr (kTree) {
+            valid = min(kBlock, len - blk * kBlock);
 #pragma unroll
-        for (int p = 0; p < kPasses; ++p) {
-            const int t = p * kTpp + tg;
-            const bool ok = t < valid;
-            const int64_t off = base + t * tok_stride;
-            kr[p] = ok ? *(const u32x4 *)(kp + off) : u32x4{0, 0, 0, 0};
-            vr[p] = ok ? *(const u32x4 *)(vp + off) : u32x4{0, 0, 0, 0};
+            for (int p = 0; p < kPasses; ++p) {
+                const int t = p * kTpp + tg;
+                const int row = ref.v[p];
+                const bool row_ok = row >= 0 && row < a.pool_rows;
+                bad |= t < valid && !row_ok;
+                const bool ok = t < valid && row_ok;
+                const int64_t off = ((int64_t)(ok ? row : 0) * a.Hkv + g) * D * E::kSize +
+                                    d0 * E::kSize;
+                kr[p] = ok ? *(const u32x4 *)(kp + off) : u32x4{0, 0, 0, 0};
+                vr[p] = ok ? *(const u32x4 *)(vp + off) : u32x4{0, 0, 0, 0};
+            }
+        } else {
+            const int id = ref.v[0];
+            const bool id_ok = id >= 0 && id < a.num_blocks;
+            bad |= !id_ok;
+            valid = id_ok ? min(kBlock, len - blk * kBlock) : 0;
+            const int64_t base = ((int64_t)(id_ok ? id : 0) * kBlock * a.Hkv + g) * D * E::kSize +
+                                 d0 * E::kSize;
+#pragma unroll
+            for (int p = 0; p < kPasses; ++p) {
+                const int t = p * kTpp + tg;
+                const bool ok = t < valid;
+                const int64_t off = base + t * tok_stride;
+                kr[p] = ok ? *(const u32x4 *)(kp + off) : u32x4{0, 0, 0, 0};
+                vr[p] = ok ? *(const u32x4 *)(vp + off) : u32x4{0, 0, 0, 0};
+            }
         }
     };
     // Online-softmax update with one block (exp2 domain, scale folded in).
@@ -187,7 +235,7 @@ __global__ __launch_bounds__(64 * NWS) void suffix_kernel(SuffixArgs a) {
         u32x4 k0[kPasses], v0[kPasses], k1[kPasses], v1[kPasses];
         int n0 = 0, n1 = 0;
         int blk = wave;
-        int id0 = table_id(blk), id1 = table_id(blk + NWS);
+        Ref id0 = table_id(blk), id1 = table_id(blk + NWS);
         if (blk < nblk) fetch(blk, id0, k0, v0, n0);
 #pragma unroll 1
         for (; blk < nblk; blk += 2 * NWS) {
@@ -245,16 +293,32 @@ __global__ __launch_bounds__(64 * NWS) void suffix_kernel(SuffixArgs a) {
         // prefix parts: normalised O_i with natural-log LSE_i
         float mx = sl > 0.f ? ms : -INFINITY;
         bool nan_seen = false;
+        if constexpr (kTree) {
+            const int s0 = a.tree[a.seq_src_off + b], s1 = a.tree[a.seq_src_off + b + 1];
 #pragma unroll 1
-        for (int si = 0; si < a.nsrc; ++si) {
-            const MergeSrc &s = a.src[si];
-            if (b < s.b0 || b >= s.b1) continue;
-            const int64_t ri = (b - s.b0) * a.Hq + h;
+            for (int si = s0; si < s1; ++si) {
+                const TreeSrc sr = *(const TreeSrc *)(a.tree + a.srcs_off + 4 * (int64_t)si);
 #pragma unroll 4
-            for (int i = 0; i < s.nsplit; ++i) {
-                const float L = s.lse[(int64_t)i * s.lse_split + ri] * kLog2e;
-                nan_seen |= (L != L);
-                mx = fmaxf(mx, L);
+                for (int i = 0; i < sr.nsplit; ++i) {
+                    const float L =
+                        a.part_lse[((int64_t)sr.part_row + (int64_t)i * sr.split_rows) * a.Hq + h] *
+                        kLog2e;
+                    nan_seen |= (L != L);
+                    mx = fmaxf(mx, L);
+                }
+            }
+        } else {
+#pragma unroll 1
+            for (int si = 0; si < a.nsrc; ++si) {
+                const MergeSrc &s = a.src[si];
+                if (b < s.b0 || b >= s.b1) continue;
+                const int64_t ri = (b - s.b0) * a.Hq + h;
+#pragma unroll 4
+                for (int i = 0; i < s.nsplit; ++i) {
+                    const float L = s.lse[(int64_t)i * s.lse_split + ri] * kLog2e;
+                    nan_seen |= (L != L);
+                    mx = fmaxf(mx, L);
+                }
             }
         }
         f32x4 out;
@@ -273,17 +337,33 @@ __global__ __launch_bounds__(64 * NWS) void suffix_kernel(SuffixArgs a) {
                 den = sl * f;
                 num = so * f;
             }
+            if constexpr (kTree) {
+                const int s0 = a.tree[a.seq_src_off + b], s1 = a.tree[a.seq_src_off + b + 1];
 #pragma unroll 1
-            for (int si = 0; si < a.nsrc; ++si) {
-                const MergeSrc &s = a.src[si];
-                if (b < s.b0 || b >= s.b1) continue;
-                const int64_t ri = (b - s.b0) * a.Hq + h;
+                for (int si = s0; si < s1; ++si) {
+                    const TreeSrc sr = *(const TreeSrc *)(a.tree + a.srcs_off + 4 * (int64_t)si);
 #pragma unroll 4
-                for (int i = 0; i < s.nsplit; ++i) {
-                    const float w =
-                        fast_exp2(s.lse[(int64_t)i * s.lse_split + ri] * kLog2e - mx);
-                    num += w * *(const f32x4 *)(s.o + (int64_t)i * s.o_split + ri * D + c4);
-                    den += w;
+                    for (int i = 0; i < sr.nsplit; ++i) {
+                        const int64_t ri =
+                            ((int64_t)sr.part_row + (int64_t)i * sr.split_rows) * a.Hq + h;
+                        const float w = fast_exp2(a.part_lse[ri] * kLog2e - mx);
+                        num += w * *(const f32x4 *)(a.part_o + ri * D + c4);
+                        den += w;
+                    }
+                }
+            } else {
+#pragma unroll 1
+                for (int si = 0; si < a.nsrc; ++si) {
+                    const MergeSrc &s = a.src[si];
+                    if (b < s.b0 || b >= s.b1) continue;
+                    const int64_t ri = (b - s.b0) * a.Hq + h;
+#pragma unroll 4
+                    for (int i = 0; i < s.nsplit; ++i) {
+                        const float w =
+                            fast_exp2(s.lse[(int64_t)i * s.lse_split + ri] * kLog2e - mx);
+                        num += w * *(const f32x4 *)(s.o + (int64_t)i * s.o_split + ri * D + c4);
+                        den += w;
+                    }
                 }
             }
             out = num * (1.f / den);
@@ -295,38 +375,50 @@ __global__ __launch_bounds__(64 * NWS) void suffix_kernel(SuffixArgs a) {
     }
 }
 
-template <int kDt, int D, int NWS>
+template <int kDt, int D, int NWS, bool kTree>
 static void launch_g(const SuffixArgs &a, int G, dim3 grid, hipStream_t s) {
     constexpr int T = 64 * NWS;
     switch (G) {
-    case 1: suffix_kernel<kDt, D, 1, NWS><<<grid, T, 0, s>>>(a); break;
-    case 2: suffix_kernel<kDt, D, 2, NWS><<<grid, T, 0, s>>>(a); break;
-    case 4: suffix_kernel<kDt, D, 4, NWS><<<grid, T, 0, s>>>(a); break;
-    default: suffix_kernel<kDt, D, 8, NWS><<<grid, T, 0, s>>>(a); break;
+    case 1: suffix_kernel<kDt, D, 1, NWS, kTree><<<grid, T, 0, s>>>(a); break;
+    case 2: suffix_kernel<kDt, D, 2, NWS, kTree><<<grid, T, 0, s>>>(a); break;
+    case 4: suffix_kernel<kDt, D, 4, NWS, kTree><<<grid, T, 0, s>>>(a); break;
+    default: suffix_kernel<kDt, D, 8, NWS, kTree><<<grid, T, 0, s>>>(a); break;
     }
 }
 
-template <int kDt, int NWS>
+template <int kDt, int NWS, bool kTree>
 static void launch_d(const SuffixArgs &a, int d, int G, dim3 grid, hipStream_t s) {
-    if (d == 128) launch_g<kDt, 128, NWS>(a, G, grid, s);
-    else launch_g<kDt, 64, NWS>(a, G, grid, s);
+    if (d == 128) launch_g<kDt, 128, NWS, kTree>(a, G, grid, s);
+    else launch_g<kDt, 64, NWS, kTree>(a, G, grid, s);
 }
 
-template <int kDt>
+template <int kDt, bool kTree>
 static void launch_dt(const SuffixArgs &a, int d, int G, int nws, dim3 grid, hipStream_t s) {
     switch (nws) {
-    case 1: launch_d<kDt, 1>(a, d, G, grid, s); break;
-    case 2: launch_d<kDt, 2>(a, d, G, grid, s); break;
-    default: launch_d<kDt, 4>(a, d, G, grid, s); break;
+    case 1: launch_d<kDt, 1, kTree>(a, d, G, grid, s); break;
+    case 2: launch_d<kDt, 2, kTree>(a, d, G, grid, s); break;
+    default: launch_d<kDt, 4, kTree>(a, d, G, grid, s); break;
     }
+}
+
+template <bool kTree>
+static hipError_t launch_mode(const SuffixArgs &a, int dtype, int d, int G, int nws,
+                              hipStream_t s) {
+    const dim3 grid((unsigned)((int64_t)a.B * a.Hkv));
+    if (dtype == HP_BF16) launch_dt<HP_BF16, kTree>(a, d, G, nws, grid, s);
+    else if (dtype == HP_F16) launch_dt<HP_F16, kTree>(a, d, G, nws, grid, s);
+    else launch_dt<HP_F32, kTree>(a, d, G, nws, grid, s);
+    return hipGetLastError();
 }
 
 hipError_t launch_suffix(const SuffixArgs &a, int dtype, int d, int G, int nws, hipStream_t s) {
-    const dim3 grid((unsigned)((int64_t)a.B * a.Hkv));
-    if (dtype == HP_BF16) launch_dt<HP_BF16>(a, d, G, nws, grid, s);
-    else if (dtype == HP_F16) launch_dt<HP_F16>(a, d, G, nws, grid, s);
-    else launch_dt<HP_F32>(a, d, G, nws, grid, s);
-    return hipGetLastError();
+    return launch_mode<false>(a, dtype, d, G, nws, s);
+}
+
+// Sequence-first pass of a chunk-tree step (a.tree set).
+hipError_t launch_tree_suffix(const SuffixArgs &a, int dtype, int d, int G, int nws,
+                              hipStream_t s) {
+    return launch_mode<true>(a, dtype, d, G, nws, s);
 }
 
 }  // namespace hp

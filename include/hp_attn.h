@@ -67,6 +67,7 @@ extern "C" {
 #define HP_MAX_NODES 32   /* prefix nodes per call, all levels together */
 #define HP_MAX_MERGE 16   /* partials per hp_lse_merge call */
 #define HP_BLOCK_SIZE 16  /* tokens per paged KV block */
+#define HP_CHUNK 64       /* tokens per chunk of the prefix-tree KV pool */
 
 typedef enum hp_dtype { HP_F32 = 0, HP_F16 = 1, HP_BF16 = 2 } hp_dtype;
 
@@ -76,7 +77,8 @@ typedef enum hp_status {
     HP_ERR_INVALID_ARG = 2, /* sizes, ranges or alignment are inconsistent */
     HP_ERR_UNSUPPORTED = 3, /* valid, but outside the implemented domain */
     HP_ERR_WORKSPACE = 4,   /* workspace NULL or smaller than the size query's answer */
-    HP_ERR_HIP = 5          /* a HIP launch failed; see hp_last_hip_error() */
+    HP_ERR_HIP = 5,         /* a HIP launch failed; see hp_last_hip_error() */
+    HP_ERR_CAPACITY = 6     /* a pool, plan buffer or output array is too small */
 } hp_status;
 
 /* The query side of one decode step. */
@@ -196,6 +198,166 @@ hp_status hp_cascade_step_timed(const hp_query *query, const hp_prefix_tree *tre
                                 const hp_paged_kv *kv, float *o, float *lse, void *workspace,
                                 size_t workspace_bytes, void *stream, void *const *events,
                                 int32_t n_events);
+
+/* ------------------------------------------------------------------------
+ * Chunked prefix tree: device-resident (C, i, j) plans
+ * ------------------------------------------------------------------------
+ * Keys and values live in a pool of rows: row r holds one token, its key for
+ * KV head g at k_pool + (r*Hkv + g)*d (elements); same for v_pool.  A chunk
+ * is HP_CHUNK consecutive rows.  A descriptor names `count` consecutive rows
+ * and the sequences [seq_begin, seq_end) that attend them: the chunk
+ * descriptor (C, i, j) of the ChunkAttention page, section "Context
+ * Generation and GPU-CPU Coordination".  Any set of descriptors is a valid
+ * step (a tree of any depth, a forest, or ranges that cover only some
+ * sequences); sequence b attends the union of the rows of every descriptor
+ * whose range holds b.
+ */
+typedef struct hp_chunk_desc {
+    int32_t row;        /* first pool row */
+    int32_t count;      /* rows, 1..HP_CHUNK */
+    int32_t seq_begin, seq_end;
+} hp_chunk_desc;
+
+/*
+ * Host summary of a plan built by hp_tree_plan_build().  The plan itself is a
+ * byte image ("blob") that the caller copies to device memory and passes to
+ * hp_tree_step(); it only changes when the descriptors change, so a caller
+ * copies it again only then (the page's lazy context copy, same section).
+ * Every field is written by hp_tree_plan_build(); pass the struct unchanged.
+ */
+#define HP_TREE_MAX_LAUNCHES 4
+typedef struct hp_tree_plan {
+    int32_t B, Hq, Hkv, d, dtype;
+    int32_t share_min;          /* descriptors with seq_end - seq_begin >= share_min are batched */
+    int32_t num_descs;
+    int32_t num_segs;           /* batched segments (runs of descriptors with one range) */
+    int32_t num_pieces;         /* key tiles of the segments */
+    int32_t num_srcs;           /* (sequence, segment) pairs */
+    int32_t num_tok_rows;       /* private rows over all sequences */
+    int32_t max_private;        /* longest private row list of one sequence */
+    int32_t num_launches;       /* chunk-first launches (one per row-block width) */
+    int32_t launch_nw[HP_TREE_MAX_LAUNCHES];   /* waves per workgroup */
+    int32_t launch_wgs[HP_TREE_MAX_LAUNCHES];  /* workgroups */
+    int32_t launch_wg0[HP_TREE_MAX_LAUNCHES];  /* first entry of the launch in the blob's workgroup table */
+    int64_t part_rows;          /* (sequence, split) partial rows of all segments */
+    int64_t pool_rows;          /* rows the descriptors were checked against */
+    size_t blob_bytes;          /* size of the device image */
+    size_t workspace_bytes;     /* workspace hp_tree_step needs */
+} hp_tree_plan;
+
+/*
+ * Plan one decode step over chunk descriptors (ChunkAttention page, sections
+ * "Two-Phase Partition (TPP): Algorithm Overview" and "The Chunk-First Phase
+ * Kernel in Detail").  Descriptors with seq_end - seq_begin >= share_min
+ * (>= 2) are batched: consecutive ones with the same range form a segment
+ * whose keys stream once through the matrix cores for all the range's query
+ * rows (chunk-first phase).  The others are private: each sequence they cover
+ * reads them in the per-sequence pass (sequence-first phase).  Descriptors are
+ * given in tree pre-order, as hp_pakv_context() emits them, so that a path of
+ * chunks shared by one range is one segment; any order is still correct.
+ *
+ * geom: B, Hq, Hkv, d, dtype (geom->q and geom->scale are not used).  descs:
+ * host array of n descriptors.  pool_rows: rows of the pool the step will
+ * read (every descriptor must lie inside it).  blob: host buffer of
+ * blob_capacity bytes that receives the device image, or NULL to only fill
+ * `plan` (the size query).  Returns HP_ERR_CAPACITY when blob is too small.
+ */
+hp_status hp_tree_plan_build(const hp_query *geom, const hp_chunk_desc *descs, int32_t n,
+                             int32_t share_min, int64_t pool_rows, void *blob,
+                             size_t blob_capacity, hp_tree_plan *plan);
+
+/*
+ * One decode step over a plan: every row (b, h) attends the rows of every
+ * descriptor covering b.  Runs the chunk-first launches (MFMA, one per
+ * row-block width), then the sequence-first pass, which walks each sequence's
+ * private rows and merges them with the partials of its segments in one
+ * epilogue (ChunkAttention page, "The Sequence-First Phase Kernel in
+ * Detail" and "The attn_reduce Function", Eq. 2, in LSE form).
+ *
+ * blob_dev: the plan's image in device memory (16-byte aligned).  k_pool,
+ * v_pool: device [pool_rows][Hkv][d].  seq_lens: device [B] total tokens of
+ * each sequence (batched + private), or NULL to read every private row the
+ * descriptors give.  With seq_lens, a sequence reads the first seq_lens[b] -
+ * (its batched rows) of its private rows, so the last private descriptor of a
+ * sequence may name rows not yet written (room to append into without a new
+ * plan); a length outside [batched rows, batched + private rows] makes the
+ * row's O and LSE NaN.  q must match the plan's geometry.  lse may be NULL.
+ */
+hp_status hp_tree_step(const hp_query *q, const hp_tree_plan *plan, const void *blob_dev,
+                       const void *k_pool, const void *v_pool, const int32_t *seq_lens,
+                       float *o, float *lse, void *workspace, size_t workspace_bytes,
+                       void *stream);
+
+/*
+ * Decode-step KV append: token i's key and value rows (k_new, v_new: device
+ * [n][Hkv][d]) are copied to pool row rows[i] (ChunkAttention page, section
+ * "Prefix-Aware KV Cache (PAKV): The Prefix Tree Structure", the Append
+ * operation: the new token's K/V
+ * go into its sequence's leaf chunk).  rows: device [n]; an entry outside
+ * [0, pool_rows) is skipped (nothing written, no length advanced).  If seq_idx
+ * is not NULL, seq_lens[seq_idx[i]] is incremented for every token that was
+ * written (device arrays; an index outside [0, num_seqs) is skipped), so a
+ * captured step can advance its lengths without a host copy.  Rows of one
+ * call must be distinct.  Exact copy.
+ */
+hp_status hp_kv_append(const void *k_new, const void *v_new, const int32_t *rows, int32_t n,
+                       int32_t Hkv, int32_t d, int32_t dtype, void *k_pool, void *v_pool,
+                       int64_t pool_rows, int32_t *seq_lens, const int32_t *seq_idx,
+                       int32_t num_seqs, void *stream);
+
+/*
+ * Prefix-aware KV cache manager (host only; ChunkAttention page, section
+ * "Prefix-Aware KV Cache (PAKV): The Prefix Tree Structure", its Insert,
+ * Append and Delete operations and its memory allocator; section "Design
+ * Choices and Their Justifications" on the pool): a prefix tree whose nodes
+ * hold token runs of at most HP_CHUNK tokens, each in one pool chunk, plus a
+ * chunk allocator with a free list (freed chunks are reused, never returned).  It owns chunk
+ * ids only; the caller owns the device pool of num_chunks * HP_CHUNK rows and
+ * writes K/V where the manager says (hp_kv_append).
+ *
+ *   insert  the longest prefix of `tokens` already in the tree is shared (a
+ *           node matched part-way is split, without copying); the remaining
+ *           tokens get new chunks.  rows[t] receives the pool row of token t;
+ *           rows of tokens >= *matched must be written by the caller.
+ *   append  one new token at the end of a sequence: into its leaf chunk when
+ *           the sequence alone owns that chunk's tail, else into a new chunk.
+ *           *changed is 1 when the tree's shape changed (a new plan is due).
+ *   remove  the sequence leaves; nodes no sequence passes through are freed
+ *           and chunks no node uses return to the free list.
+ *   context the (C, i, j) descriptors of the live tree in pre-order, with
+ *           sequences numbered so that every node covers a contiguous range
+ *           (the page's contiguity property); seq_order[b] is the id of batch
+ *           row b and seq_lens[b] its token count.  A sequence's leaf chunk is
+ *           reported with its remaining room, so the plan stays valid while
+ *           tokens are appended into it.
+ * Sequence ids are caller-chosen int64 values.  A handle is not thread-safe.
+ */
+typedef struct hp_pakv hp_pakv;
+typedef struct hp_pakv_stats {
+    int32_t num_chunks;     /* capacity */
+    int32_t chunks_used;    /* referenced by a node */
+    int32_t chunks_free;    /* on the free list */
+    int32_t chunks_fresh;   /* never handed out */
+    int32_t nodes;          /* tree nodes, root excluded */
+    int32_t seqs;           /* live sequences */
+    int64_t tokens_stored;  /* tokens held by nodes (shared tokens once) */
+    int64_t tokens_logical; /* sum of sequence lengths */
+} hp_pakv_stats;
+
+hp_status hp_pakv_create(int32_t num_chunks, hp_pakv **out);
+void hp_pakv_destroy(hp_pakv *p);
+hp_status hp_pakv_insert(hp_pakv *p, int64_t seq_id, const int32_t *tokens, int32_t n,
+                         int32_t *rows, int32_t *matched);
+hp_status hp_pakv_append(hp_pakv *p, int64_t seq_id, int32_t token, int32_t *row,
+                         int32_t *changed);
+hp_status hp_pakv_remove(hp_pakv *p, int64_t seq_id);
+hp_status hp_pakv_context(hp_pakv *p, int64_t *seq_order, int32_t *seq_lens,
+                          int32_t seq_capacity, hp_chunk_desc *descs, int32_t desc_capacity,
+                          int32_t *num_seqs, int32_t *num_descs);
+/* Pool rows of every token of one sequence, in order (n = its length). */
+hp_status hp_pakv_seq_rows(hp_pakv *p, int64_t seq_id, int32_t *rows, int32_t capacity,
+                           int32_t *n);
+hp_status hp_pakv_get_stats(hp_pakv *p, hp_pakv_stats *stats);
 
 /* Static description of a status code. */
 const char *hp_status_string(hp_status status);

@@ -18,6 +18,15 @@ Functions:
   step_attention(step, part, rows)  the above over a generated ``workloads.Step``:
       "all" = every prefix node of the sequence then its suffix, "prefix" = its
       prefix nodes only, "suffix" = its suffix only, or ("level", i).
+  tree_attention(step, rows)  the same definition over a ``workloads.ChunkTreeStep``:
+      sequence b attends the pool rows of every descriptor holding it, cut at
+      its length ("ChunkAttention: Efficient Self-Attention with Prefix-Aware
+      KV Cache and Two-Phase Partition", section "Context Generation and
+      GPU-CPU Coordination": a chunk descriptor (C, i, j) gives chunk C's keys
+      to sequences i .. j-1).
+  kv_append(pool, rows, new)  the decode-step append of that page's section
+      "Prefix-Aware KV Cache (PAKV): The Prefix Tree Structure": row i of
+      ``new`` is stored at pool row rows[i] (entries outside the pool skipped).
 """
 from __future__ import annotations
 
@@ -198,3 +207,21 @@ def step_attention(step, part="all", rows: Optional[Sequence[int]] = None,
                    nthreads: int = 0, lib=None) -> Tuple[np.ndarray, np.ndarray]:
     return attention(step.q, step_segments(step, part), step.cfg.Hkv, step.scale, rows,
                      nthreads, lib)
+
+
+def tree_attention(step, rows: Optional[Sequence[int]] = None, nthreads: int = 0,
+                   lib=None) -> Tuple[np.ndarray, np.ndarray]:
+    """fp64 attention of a ``workloads.ChunkTreeStep`` (every row, or ``rows``)."""
+    need = set(range(step.B)) if rows is None else {int(r) // step.Hq for r in rows}
+    segs = [step.keys_of(b) if b in need else [] for b in range(step.B)]
+    return attention(step.q, segs, step.Hkv, step.scale, rows, nthreads, lib)
+
+
+def kv_append(pool: torch.Tensor, rows: Sequence[int], new: torch.Tensor) -> torch.Tensor:
+    """A copy of ``pool`` ([rows][...]) with new[i] stored at row rows[i]; rows
+    outside [0, len(pool)) are skipped.  Plain element copy, no arithmetic."""
+    out = pool.clone()
+    for i, r in enumerate(list(rows)):
+        if 0 <= int(r) < out.shape[0]:
+            out[int(r)] = new[i]
+    return out

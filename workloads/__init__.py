@@ -326,3 +326,187 @@ def prefix_flops(cfg: Config) -> int:
         for (ln, b0, b1) in level:
             total += 4 * (b1 - b0) * cfg.Hq * ln * cfg.d
     return total
+
+
+# ----------------------------------------------------------------------------------------
+# Chunk-tree steps: keys in a pool of rows named by (C, i, j) descriptors
+# ----------------------------------------------------------------------------------------
+
+CHUNK = 64  # tokens per pool chunk
+
+
+@dataclasses.dataclass
+class ChunkTreeStep:
+    """One decode step over chunk descriptors, on the CPU.
+
+    ``descs[k] = (row, count, seq_begin, seq_end)``: sequences [seq_begin,
+    seq_end) attend pool rows row .. row + count - 1.  Sequence b attends the
+    rows of every descriptor holding b, in descriptor order, up to
+    ``seq_lens[b]`` rows in total (a sequence's last descriptor may name rows
+    past that: room to append into, NaN-filled).  Rows no descriptor names are
+    NaN too.
+    """
+    B: int
+    Hq: int
+    Hkv: int
+    d: int
+    dtype: str
+    scale: float
+    q: torch.Tensor            # [B][Hq][d]
+    k_pool: torch.Tensor       # [rows][Hkv][d]
+    v_pool: torch.Tensor
+    descs: np.ndarray          # [n][4] int32
+    seq_lens: np.ndarray       # [B] int32: rows each sequence attends
+
+    @property
+    def pool_rows(self) -> int:
+        return int(self.k_pool.shape[0])
+
+    def rows_of(self, b: int) -> List[int]:
+        rows: List[int] = []
+        for (r, c, b0, b1) in self.descs.tolist():
+            if b0 <= b < b1:
+                rows.extend(range(r, r + c))
+        return rows[:int(self.seq_lens[b])]
+
+    def keys_of(self, b: int) -> List[Tuple[torch.Tensor, torch.Tensor]]:
+        idx = torch.as_tensor(self.rows_of(b), dtype=torch.int64)
+        return [(self.k_pool[idx], self.v_pool[idx])]
+
+
+def _pool_from_descs(g: torch.Generator, num_chunks: int, Hkv: int, d: int, dt: torch.dtype,
+                     live_rows: Sequence[int]) -> Tuple[torch.Tensor, torch.Tensor]:
+    rows = num_chunks * CHUNK
+    k_pool = torch.full((rows, Hkv, d), float("nan"), dtype=dt)
+    v_pool = torch.full((rows, Hkv, d), float("nan"), dtype=dt)
+    idx = torch.as_tensor(list(live_rows), dtype=torch.int64)
+    if idx.numel():
+        k_pool[idx] = _randn(g, (idx.numel(), Hkv, d), dt)
+        v_pool[idx] = _randn(g, (idx.numel(), Hkv, d), dt)
+    return k_pool, v_pool
+
+
+def random_chunk_tree(seed: int, B: int, Hq: int, Hkv: int, d: int, dtype: str,
+                      depth: int = 4, max_chunks: int = 3, root_chunks: int = 4,
+                      p_partial: float = 0.3, p_gap: float = 0.2, private_chunks: int = 2,
+                      room: bool = True, q_mult: float = 1.0) -> ChunkTreeStep:
+    """A random forest of chunk descriptors in tree pre-order.
+
+    Every node covers a contiguous sequence range and holds 1..max_chunks
+    pieces (root_chunks at depth 0), each a full 64-row chunk or, with
+    probability p_partial, a run of 1..64 rows at a random offset inside one.
+    A range of several sequences is cut into 1..4 contiguous parts; each part
+    gets a child subtree, or with probability p_gap nothing.  Single sequences
+    get 0..private_chunks private pieces.  With ``room``, each sequence's
+    last private piece names the rest of its chunk (NaN rows past the
+    sequence's length).  Chunks are placed at a random permutation of the
+    pool.  Draw order: structure (torch.randint), chunk permutation, Q, then
+    K and V of every named row in row order.
+    """
+    g = torch.Generator().manual_seed(int(seed))
+    dt = _TORCH_DTYPES[dtype]
+
+    def ri(lo: int, hi: int) -> int:  # inclusive
+        return int(torch.randint(lo, hi + 1, (1,), generator=g))
+
+    def rf() -> float:
+        return float(torch.rand((1,), generator=g))
+
+    # (chunk placeholder, slot, count, b0, b1, is_private_leaf_piece)
+    pieces: List[List[int]] = []
+
+    def piece(b0: int, b1: int, private: bool) -> None:
+        if rf() < p_partial:
+            cnt = ri(1, CHUNK)
+            slot = ri(0, CHUNK - cnt)
+        else:
+            cnt, slot = CHUNK, 0
+        pieces.append([len(pieces), slot, cnt, b0, b1, int(private)])
+
+    def node(b0: int, b1: int, level: int) -> None:
+        n = root_chunks if level == 0 else ri(1, max_chunks)
+        for _ in range(n):
+            piece(b0, b1, False)
+        if b1 - b0 == 1:
+            for _ in range(ri(0, private_chunks)):
+                piece(b0, b1, True)
+            return
+        if level + 1 > depth:
+            return
+        parts = min(b1 - b0, ri(1, 4))
+        cuts = sorted(set([b0, b1] + [ri(b0 + 1, b1 - 1) for _ in range(parts - 1)]))
+        for lo, hi in zip(cuts[:-1], cuts[1:]):
+            if rf() < p_gap:
+                continue
+            node(lo, hi, level + 1)
+
+    node(0, B, 0)
+    num_chunks = len(pieces) + max(1, len(pieces) // 8)
+    perm = torch.randperm(num_chunks, generator=g).tolist()
+    q = _randn(g, (B, Hq, d), dt, q_mult)
+
+    descs = []
+    real = np.zeros(B, dtype=np.int64)
+    last_private = {}
+    for p in pieces:
+        chunk, slot, cnt, b0, b1, priv = p
+        row = perm[chunk] * CHUNK + slot
+        descs.append([row, cnt, b0, b1])
+        for b in range(b0, b1):
+            real[b] += cnt
+        if b1 - b0 == 1:
+            last_private[b0] = len(descs) - 1
+    live = sorted({r for (r, c, _, _) in descs for r in range(r, r + c)})
+    k_pool, v_pool = _pool_from_descs(g, num_chunks, Hkv, d, dt, live)
+    if room:
+        for b, k in last_private.items():
+            r, c, b0, b1 = descs[k]
+            descs[k][1] = CHUNK - (r % CHUNK)  # the rest of the chunk: not yet written
+    return ChunkTreeStep(B=B, Hq=Hq, Hkv=Hkv, d=d, dtype=dtype, scale=scale_for(d), q=q,
+                         k_pool=k_pool, v_pool=v_pool,
+                         descs=np.asarray(descs, dtype=np.int32).reshape(-1, 4),
+                         seq_lens=real.astype(np.int32))
+
+
+def chunked_config(cfg: Config, seed: int = 0, seq_lens: Optional[Sequence[int]] = None
+                   ) -> ChunkTreeStep:
+    """A Config's step laid out as chunk descriptors: every prefix node's keys in
+    full 64-row chunks (one descriptor per chunk over the node's range, root
+    level first), then each sequence's suffix in private chunks, the last one
+    named whole (room to append).  Chunks sit at a random permutation of the
+    pool.  Suffix lengths are drawn as in ``generate``; draw order: lengths, Q,
+    chunk permutation, K and V of every named row in row order."""
+    _validate_config(cfg)
+    g = torch.Generator().manual_seed(int(seed))
+    dt = cfg.torch_dtype
+    lens = torch.randint(cfg.suffix_lo, cfg.suffix_hi + 1, (cfg.B,), generator=g,
+                         dtype=torch.int64)
+    if seq_lens is not None:
+        lens = torch.as_tensor([int(x) for x in seq_lens], dtype=torch.int64)
+    q = _randn(g, (cfg.B, cfg.Hq, cfg.d), dt)
+    plan = []  # (b0, b1, count, real)
+    for level in cfg.levels:
+        for (ln, b0, b1) in level:
+            for t in range(0, ln, CHUNK):
+                c = min(CHUNK, ln - t)
+                plan.append((b0, b1, c, c))
+    for b in range(cfg.B):
+        s = int(lens[b])
+        for t in range(0, s, CHUNK):
+            c = min(CHUNK, s - t)
+            last = t + CHUNK >= s
+            plan.append((b, b + 1, CHUNK if last else c, c))
+    num_chunks = len(plan) + max(1, len(plan) // 8)
+    perm = torch.randperm(num_chunks, generator=g).tolist()
+    descs, live = [], []
+    real = np.zeros(cfg.B, dtype=np.int64)
+    for i, (b0, b1, cnt, rl) in enumerate(plan):
+        row = perm[i] * CHUNK
+        descs.append([row, cnt, b0, b1])
+        live.extend(range(row, row + rl))
+        real[b0:b1] += rl
+    k_pool, v_pool = _pool_from_descs(g, num_chunks, cfg.Hkv, cfg.d, dt, sorted(live))
+    return ChunkTreeStep(B=cfg.B, Hq=cfg.Hq, Hkv=cfg.Hkv, d=cfg.d, dtype=cfg.dtype,
+                         scale=scale_for(cfg.d), q=q, k_pool=k_pool, v_pool=v_pool,
+                         descs=np.asarray(descs, dtype=np.int32).reshape(-1, 4),
+                         seq_lens=real.astype(np.int32))
