@@ -223,4 +223,40 @@ __device__ __forceinline__ float xor_sum_from(float x) {
     return x;
 }
 
+// Global memory straight into LDS (gfx950 global_load_lds_dword{,x4}): lane i
+// writes lds_base + 16*i (dma16) or lds_base + 4*i (dma4); lds_base is
+// wave-uniform (M0).  Issued as inline assembly so that the compiler does not
+// track it: it cannot prove that later LDS reads do not alias a transfer in
+// flight, and would otherwise wait for every transfer before each of them.
+// Completion is the caller's business: a vmcnt wait, then a barrier.
+template <int kBytes>
+__device__ __forceinline__ void lds_dma(const void *g, void *lds_base) {
+    static_assert(kBytes == 4 || kBytes == 16, "dword or dwordx4");
+    const uint32_t l = __builtin_amdgcn_readfirstlane(
+        (uint32_t)(uintptr_t)(__attribute__((address_space(3))) void *)lds_base);
+    uint32_t saved;  // M0 is reserved by the compiler: restore it
+    if constexpr (kBytes == 16)
+        asm volatile(
+            "s_mov_b32 %0, m0\n\ts_mov_b32 m0, %2\n\tglobal_load_lds_dwordx4 %1, off\n\t"
+            "s_mov_b32 m0, %0"
+            : "=&s"(saved)
+            : "v"(g), "s"(l)
+            : "memory");
+    else
+        asm volatile(
+            "s_mov_b32 %0, m0\n\ts_mov_b32 m0, %2\n\tglobal_load_lds_dword %1, off\n\t"
+            "s_mov_b32 m0, %0"
+            : "=&s"(saved)
+            : "v"(g), "s"(l)
+            : "memory");
+}
+__device__ __forceinline__ void dma16(const void *g, void *lds_base) { lds_dma<16>(g, lds_base); }
+
+// s_waitcnt with only vmcnt = n (expcnt and lgkmcnt left unconstrained).
+template <int n>
+__device__ __forceinline__ void wait_vmcnt() {
+    static_assert(n >= 0 && n < 64, "vmcnt range");
+    __builtin_amdgcn_s_waitcnt((n & 15) | (7 << 4) | (15 << 8) | ((n >> 4) << 14));
+}
+
 }  // namespace hp

@@ -308,31 +308,6 @@ __device__ __forceinline__ int v_swizzle(int r) {
     return 4 * ((r / (128 / D)) % (D / 32));
 }
 
-// s_waitcnt with only vmcnt = n (expcnt and lgkmcnt left unconstrained).
-template <int n>
-__device__ __forceinline__ void wait_vmcnt() {
-    static_assert(n >= 0 && n < 64, "vmcnt range");
-    __builtin_amdgcn_s_waitcnt((n & 15) | (7 << 4) | (15 << 8) | ((n >> 4) << 14));
-}
-
-// 16 bytes from global memory straight into LDS (gfx950 global_load_lds_dwordx4):
-// lane i writes lds_base + 16*i; lds_base is wave-uniform (M0).  Issued as
-// inline assembly so that the compiler does not track it: it cannot prove
-// that the transposing LDS reads of other stages do not alias the transfer,
-// and would otherwise wait for every transfer in flight before each of them.
-// Completion is this code's business: wait_vmcnt before block_sync.
-__device__ __forceinline__ void dma16(const void *g, void *lds_base) {
-    const uint32_t l = __builtin_amdgcn_readfirstlane(
-        (uint32_t)(uintptr_t)(__attribute__((address_space(3))) void *)lds_base);
-    uint32_t saved;  // M0 is reserved by the compiler: restore it
-    asm volatile(
-        "s_mov_b32 %0, m0\n\ts_mov_b32 m0, %2\n\tglobal_load_lds_dwordx4 %1, off\n\t"
-        "s_mov_b32 m0, %0"
-        : "=&s"(saved)
-        : "v"(g), "s"(l)
-        : "memory");
-}
-
 // Workgroup barrier that the compiler may not move memory accesses across
 // (LDS is written by DMA outside its view), taken after this wave's own LDS
 // reads have returned.

@@ -120,6 +120,59 @@ __global__ __launch_bounds__(64 * NWS) void suffix_kernel(SuffixArgs a) {
     }
     const int nblk = bad ? 0 : (len + kBlock - 1) / kBlock;
 
+    // The prefix partials this row merges (splits of the by-value sources
+    // covering sequence b) are copied into LDS by DMA right away, so their
+    // latency hides behind the suffix stream and the epilogue reads them
+    // from LDS.  Part p holds G rows of D floats and G LSEs; rows whose
+    // parts do not fit the stage are read from memory in the epilogue.
+    constexpr int kStageO = G == 1 ? 2048 : 8192;  // floats; a multiple of 4 * kWave
+    constexpr int kCpp = G * D / 4;                 // 16-byte chunks per part
+    __shared__ __attribute__((aligned(16))) float sm_po[kTree ? 4 : kStageO];
+    __shared__ float sm_pl[kWave];
+    int nparts = 0;
+    if constexpr (!kTree) {
+#pragma unroll 1
+        for (int si = 0; si < a.nsrc; ++si)
+            if (b >= a.src[si].b0 && b < a.src[si].b1) nparts += a.src[si].nsplit;
+    }
+    const bool staged = !kTree && nparts > 0 && nparts * kCpp * 4 <= kStageO && nparts * G <= kWave;
+    if constexpr (!kTree) {
+        if (staged) {
+            // Locate part p of this row: pointers to its first O float and LSE.
+            auto part = [&](int p, const float *&po, const float *&pl) {
+                po = a.src[0].o;  // replaced below: p < nparts always matches one source
+                pl = a.src[0].lse;
+                int pb = 0;
+#pragma unroll 1
+                for (int si = 0; si < a.nsrc; ++si) {
+                    const MergeSrc &sr = a.src[si];
+                    if (b < sr.b0 || b >= sr.b1) continue;
+                    const int i = p - pb;
+                    if (i >= 0 && i < sr.nsplit) {
+                        const int64_t ri = (b - sr.b0) * a.Hq + (int64_t)g * G;
+                        po = sr.o + (int64_t)i * sr.o_split + ri * D;
+                        pl = sr.lse + (int64_t)i * sr.lse_split + ri;
+                    }
+                    pb += sr.nsplit;
+                }
+            };
+            const int chunks = nparts * kCpp;
+#pragma unroll 1
+            for (int c0 = wave * kWave; c0 < chunks; c0 += NWS * kWave) {
+                const int c = min(c0 + lane, chunks - 1);  // lanes past the end re-read the last chunk
+                const float *po, *pl;
+                part(c / kCpp, po, pl);
+                lds_dma<16>(po + (c % kCpp) * 4, &sm_po[c0 * 4]);
+            }
+            if (wave == 0) {
+                const int e = min(lane, nparts * G - 1);
+                const float *po, *pl;
+                part(e / G, po, pl);
+                lds_dma<4>(pl + e % G, sm_pl);
+            }
+        }
+    }
+
     float m[G], l[G], acc[G][kEpl];
 #pragma unroll
     for (int j = 0; j < G; ++j) {
@@ -264,6 +317,7 @@ __global__ __launch_bounds__(64 * NWS) void suffix_kernel(SuffixArgs a) {
         }
     }
     if (lane == 0) sm_bad[wave] = bad ? 1 : 0;
+    if (staged) wait_vmcnt<0>();  // this wave's partial DMAs have landed (the barrier publishes them)
     __syncthreads();
 
     // Final merge: this row's suffix (the waves' states) and every prefix
@@ -306,6 +360,13 @@ __global__ __launch_bounds__(64 * NWS) void suffix_kernel(SuffixArgs a) {
                     nan_seen |= (L != L);
                     mx = fmaxf(mx, L);
                 }
+            }
+        } else if (staged) {
+#pragma unroll 4
+            for (int p = 0; p < nparts; ++p) {
+                const float L = sm_pl[p * G + j] * kLog2e;
+                nan_seen |= (L != L);
+                mx = fmaxf(mx, L);
             }
         } else {
 #pragma unroll 1
@@ -350,6 +411,13 @@ __global__ __launch_bounds__(64 * NWS) void suffix_kernel(SuffixArgs a) {
                         num += w * *(const f32x4 *)(a.part_o + ri * D + c4);
                         den += w;
                     }
+                }
+            } else if (staged) {
+#pragma unroll 4
+                for (int p = 0; p < nparts; ++p) {
+                    const float w = fast_exp2(sm_pl[p * G + j] * kLog2e - mx);
+                    num += w * *(const f32x4 *)&sm_po[(p * G + j) * D + c4];
+                    den += w;
                 }
             } else {
 #pragma unroll 1
