@@ -13,6 +13,9 @@ Entry points (same names as the C ABI):
   cascade_step   a whole decode step over a prefix tree plus paged suffixes
   tree_plan_build / TreeStep   a decode step over (C, i, j) chunk descriptors
                  whose plan lives in device memory (any depth, forests)
+  stream_decode / StreamCall   shared-context requests: P streams per request
+                 read their document once; a stream-id mask picks each
+                 stream's own tokens from the request's KV row
   kv_append      scatter of new tokens' K/V rows into the pool
   Pakv           the host prefix-tree KV manager (insert, append, remove,
                  context) that produces those descriptors
@@ -40,7 +43,8 @@ STATUS = {0: "HP_OK", 1: "HP_ERR_NULL", 2: "HP_ERR_INVALID_ARG", 3: "HP_ERR_UNSU
           4: "HP_ERR_WORKSPACE", 5: "HP_ERR_HIP", 6: "HP_ERR_CAPACITY"}
 EXPORTS = ["hp_prefix_attn_workspace_size", "hp_prefix_attn", "hp_suffix_decode_workspace_size",
            "hp_suffix_decode", "hp_lse_merge", "hp_cascade_workspace_size", "hp_cascade_step",
-           "hp_cascade_step_timed", "hp_tree_plan_build", "hp_tree_step", "hp_kv_append",
+           "hp_cascade_step_timed", "hp_stream_decode_workspace_size", "hp_stream_decode",
+           "hp_tree_plan_build", "hp_tree_step", "hp_kv_append",
            "hp_pakv_create", "hp_pakv_destroy", "hp_pakv_insert", "hp_pakv_append",
            "hp_pakv_remove", "hp_pakv_context", "hp_pakv_seq_rows", "hp_pakv_get_stats",
            "hp_status_string", "hp_last_hip_error", "hp_version"]
@@ -82,6 +86,14 @@ class PagedKV(ctypes.Structure):
                 ("block_table", ctypes.c_void_p), ("seq_lens", ctypes.c_void_p),
                 ("max_blocks", ctypes.c_int32), ("block_size", ctypes.c_int32),
                 ("num_blocks", ctypes.c_int32)]
+
+
+class StreamRows(ctypes.Structure):
+    _fields_ = [("k_pool", ctypes.c_void_p), ("v_pool", ctypes.c_void_p),
+                ("row_slots", ctypes.c_void_p), ("slot_sid", ctypes.c_void_p),
+                ("row_len", ctypes.c_void_p), ("q_req", ctypes.c_void_p),
+                ("q_sid", ctypes.c_void_p), ("num_requests", ctypes.c_int32),
+                ("row_cap", ctypes.c_int32), ("pool_rows", ctypes.c_int64)]
 
 
 class ChunkDesc(ctypes.Structure):
@@ -159,6 +171,15 @@ def lib():
                                                 ctypes.POINTER(PagedKV), p, p, p,
                                                 ctypes.c_size_t, p, p, ctypes.c_int32]
             i32, i64 = ctypes.c_int32, ctypes.c_int64
+            L.hp_stream_decode_workspace_size.restype = st
+            L.hp_stream_decode_workspace_size.argtypes = [ctypes.POINTER(Query),
+                                                          ctypes.POINTER(PrefixTree),
+                                                          ctypes.POINTER(StreamRows),
+                                                          ctypes.POINTER(ctypes.c_size_t)]
+            L.hp_stream_decode.restype = st
+            L.hp_stream_decode.argtypes = [ctypes.POINTER(Query), ctypes.POINTER(PrefixTree),
+                                           ctypes.POINTER(StreamRows), p, p, p,
+                                           ctypes.c_size_t, p]
             L.hp_tree_plan_build.restype = st
             L.hp_tree_plan_build.argtypes = [ctypes.POINTER(Query), p, i32, i32, i64, p,
                                              ctypes.c_size_t, ctypes.POINTER(TreePlan)]
@@ -386,6 +407,71 @@ def cascade_step(q: torch.Tensor, levels, k_pool=None, v_pool=None, block_table=
 # ------------------------------------------------------------------------------
 # Chunked prefix tree: (C, i, j) descriptors, device-resident plans, append, PAKV
 # ------------------------------------------------------------------------------
+
+def make_stream_rows(k_pool: torch.Tensor, v_pool: torch.Tensor, row_slots: torch.Tensor,
+                     slot_sid: torch.Tensor, row_len: torch.Tensor, q_req: torch.Tensor,
+                     q_sid: torch.Tensor) -> StreamRows:
+    """Pools [pool_rows][Hkv][d]; row_slots / slot_sid [R][row_cap], row_len [R],
+    q_req / q_sid [B]: contiguous int32 device tensors."""
+    for t, nm in ((k_pool, "k_pool"), (v_pool, "v_pool"), (row_slots, "row_slots"),
+                  (slot_sid, "slot_sid"), (row_len, "row_len"), (q_req, "q_req"),
+                  (q_sid, "q_sid")):
+        _require_cuda(t, nm)
+    if k_pool.dim() != 3 or k_pool.shape != v_pool.shape or not k_pool.is_contiguous() \
+            or not v_pool.is_contiguous():
+        raise ValueError("pools must be contiguous [pool_rows][Hkv][d]")
+    for t, nm in ((row_slots, "row_slots"), (slot_sid, "slot_sid"), (row_len, "row_len"),
+                  (q_req, "q_req"), (q_sid, "q_sid")):
+        if t.dtype != torch.int32 or not t.is_contiguous():
+            raise ValueError(f"{nm} must be a contiguous int32 tensor")
+    if row_slots.dim() != 2 or row_slots.shape != slot_sid.shape or \
+            row_len.shape != (row_slots.shape[0],) or q_req.shape != q_sid.shape:
+        raise ValueError("row_slots/slot_sid [R][row_cap], row_len [R], q_req/q_sid [B]")
+    return StreamRows(k_pool.data_ptr(), v_pool.data_ptr(), row_slots.data_ptr(),
+                      slot_sid.data_ptr(), row_len.data_ptr(), q_req.data_ptr(),
+                      q_sid.data_ptr(), row_slots.shape[0], row_slots.shape[1],
+                      k_pool.shape[0])
+
+
+class StreamCall:
+    """A prepared hp_stream_decode: every stream query attends its document (the
+    prefix tree ``doc_levels``, as in CascadeCall) and the positions of its
+    request's KV row whose stream id is -1 or its own."""
+
+    def __init__(self, q: torch.Tensor, doc_levels, k_pool: torch.Tensor, v_pool: torch.Tensor,
+                 row_slots: torch.Tensor, slot_sid: torch.Tensor, row_len: torch.Tensor,
+                 q_req: torch.Tensor, q_sid: torch.Tensor, scale: Optional[float] = None,
+                 out=None, lse=None):
+        L = lib()
+        self._L = L
+        if q_req.shape != (q.shape[0],):
+            raise ValueError("q_req and q_sid need one entry per query")
+        self.query = make_query(q, k_pool.shape[1], scale)
+        self.tree, self._keep = make_tree(doc_levels) if doc_levels else (None, None)
+        self.rows = make_stream_rows(k_pool, v_pool, row_slots, slot_sid, row_len, q_req, q_sid)
+        self.out, self.lse = _out(q, out, lse, zero=False)
+        self._tree_p = ctypes.byref(self.tree) if self.tree is not None else None
+        nbytes = ctypes.c_size_t(0)
+        _check(L.hp_stream_decode_workspace_size(ctypes.byref(self.query), self._tree_p,
+                                                 ctypes.byref(self.rows), ctypes.byref(nbytes)),
+               "hp_stream_decode_workspace_size")
+        self.workspace_bytes = nbytes.value
+        self.ws = _workspace(nbytes.value, q.device)
+        self._refs = (q, doc_levels, k_pool, v_pool, row_slots, slot_sid, row_len, q_req, q_sid)
+
+    def __call__(self, stream=None):
+        _check(self._L.hp_stream_decode(ctypes.byref(self.query), self._tree_p,
+                                        ctypes.byref(self.rows), self.out.data_ptr(),
+                                        _ptr(self.lse), _ptr(self.ws), self.workspace_bytes,
+                                        _stream(stream)), "hp_stream_decode")
+        return self.out, self.lse
+
+
+def stream_decode(q: torch.Tensor, doc_levels, k_pool, v_pool, row_slots, slot_sid, row_len,
+                  q_req, q_sid, scale: Optional[float] = None, out=None, lse=None, stream=None):
+    return StreamCall(q, doc_levels, k_pool, v_pool, row_slots, slot_sid, row_len, q_req,
+                      q_sid, scale, out, lse)(stream)
+
 
 def _descs_array(descs) -> Tuple[ctypes.Array, int]:
     """descs: an [n][4] int array-like of (row, count, seq_begin, seq_end)."""

@@ -455,6 +455,29 @@ hp_status record(void *const *events, int i, hipStream_t s) {
     return e == hipSuccess ? HP_OK : fail_hip(e);
 }
 
+// Prefix pass of every tree level (root first), results into the cascade
+// plan's workspace slots; m receives one merge source per node.
+hp_status run_prefix_levels(const hp_query *q, const hp_prefix_tree *tree, const CascadePlan &cp,
+                            char *base, MergeArgs &m, hipStream_t s) {
+    for (int l = 0; l < cp.num_levels; ++l) {
+        const LevelPlan &lp = cp.levels[l];
+        RowDest dests[HP_MAX_NODES];
+        for (int i = 0; i < lp.count; ++i) {
+            const NodePlan &np = lp.nodes[i];
+            const hp_prefix_node &nd = tree->nodes[lp.first + i];
+            float *wo = (float *)(base + cp.node_off[lp.first + i]);
+            float *wl = (float *)((char *)wo +
+                                  round_up((size_t)np.nsplit * np.rows * q->d * 4, kWsAlign));
+            dests[i] = RowDest{wo, wl, np.rows * q->d, np.rows, nd.seq_begin};
+            m.src[m.nsrc++] = MergeSrc{wo, wl, np.rows * q->d, np.rows, np.nsplit, 0,
+                                       nd.seq_begin, nd.seq_end};
+        }
+        hp_status st = run_level(*q, tree->nodes + lp.first, lp, dests, s);
+        if (st != HP_OK) return st;
+    }
+    return HP_OK;
+}
+
 hp_status cascade_impl(const hp_query *q, const hp_prefix_tree *tree, const hp_paged_kv *kv,
                        float *o, float *lse, void *ws, size_t ws_bytes, void *stream,
                        void *const *events) {
@@ -471,23 +494,7 @@ hp_status cascade_impl(const hp_query *q, const hp_prefix_tree *tree, const hp_p
 
     MergeArgs m;
     std::memset(&m, 0, sizeof m);
-    // Prefix pass, level by level (root first).
-    for (int l = 0; l < cp.num_levels; ++l) {
-        const LevelPlan &lp = cp.levels[l];
-        RowDest dests[HP_MAX_NODES];
-        for (int i = 0; i < lp.count; ++i) {
-            const NodePlan &np = lp.nodes[i];
-            const hp_prefix_node &nd = tree->nodes[lp.first + i];
-            float *wo = (float *)(base + cp.node_off[lp.first + i]);
-            float *wl = (float *)((char *)wo +
-                                  round_up((size_t)np.nsplit * np.rows * q->d * 4, kWsAlign));
-            dests[i] = RowDest{wo, wl, np.rows * q->d, np.rows, nd.seq_begin};
-            m.src[m.nsrc++] = MergeSrc{wo, wl, np.rows * q->d, np.rows, np.nsplit, 0,
-                                       nd.seq_begin, nd.seq_end};
-        }
-        st = run_level(*q, tree->nodes + lp.first, lp, dests, s);
-        if (st != HP_OK) return st;
-    }
+    if ((st = run_prefix_levels(q, tree, cp, base, m, s)) != HP_OK) return st;
     if ((st = record(events, 1, s)) != HP_OK) return st;
     if (cp.has_suffix) {
         // Suffix pass with the merge of every level's partials fused in.
@@ -511,9 +518,111 @@ hp_status cascade_impl(const hp_query *q, const hp_prefix_tree *tree, const hp_p
     return record(events, 3, s);
 }
 
+// ------------------------- shared-context streams -------------------------
+
+hp_status check_stream_rows(const hp_query *q, const hp_stream_rows *r) {
+    if (!r) return HP_ERR_NULL;
+    if (r->num_requests < 1 || r->row_cap < 1 || r->pool_rows < 1) return HP_ERR_INVALID_ARG;
+    if (r->pool_rows > INT32_MAX) return HP_ERR_INVALID_ARG;  // pool rows are int32 entries
+    if (!r->k_pool || !r->v_pool || !r->row_slots || !r->slot_sid || !r->row_len || !r->q_req ||
+        !r->q_sid)
+        return HP_ERR_NULL;
+    if (!aligned16(r->k_pool) || !aligned16(r->v_pool)) return HP_ERR_INVALID_ARG;
+    for (const void *p : {(const void *)r->row_slots, (const void *)r->slot_sid,
+                          (const void *)r->row_len, (const void *)r->q_req,
+                          (const void *)r->q_sid})
+        if ((uintptr_t)p & 3u) return HP_ERR_INVALID_ARG;
+    (void)q;
+    return HP_OK;
+}
+
+// Workspace of a stream step: the cascade plan's prefix partials, then the
+// per-query visible-row counts and tables.
+struct StreamPlan {
+    CascadePlan cp;
+    size_t len_off = 0, table_off = 0, bytes = 0;
+};
+
+hp_status plan_stream(const hp_query *q, const hp_prefix_tree *doc, const hp_stream_rows *r,
+                      StreamPlan &sp) {
+    hp_status st = plan_cascade(q, doc, nullptr, sp.cp);
+    if (st != HP_OK) return st;
+    if ((st = check_stream_rows(q, r)) != HP_OK) return st;
+    sp.len_off = round_up(sp.cp.bytes, kWsAlign);
+    sp.table_off = sp.len_off + round_up((size_t)q->B * 4, kWsAlign);
+    sp.bytes = sp.table_off + round_up((size_t)q->B * (size_t)r->row_cap * 4, kWsAlign);
+    return HP_OK;
+}
+
 }  // namespace
 
 extern "C" {
+
+hp_status hp_stream_decode_workspace_size(const hp_query *q, const hp_prefix_tree *doc,
+                                          const hp_stream_rows *rows, size_t *bytes) {
+    if (!bytes) return HP_ERR_NULL;
+    StreamPlan sp;
+    hp_status st = plan_stream(q, doc, rows, sp);
+    if (st != HP_OK) return st;
+    *bytes = sp.bytes;
+    return HP_OK;
+}
+
+hp_status hp_stream_decode(const hp_query *q, const hp_prefix_tree *doc,
+                           const hp_stream_rows *rows, float *o, float *lse, void *ws,
+                           size_t ws_bytes, void *stream) {
+    StreamPlan sp;
+    hp_status st = plan_stream(q, doc, rows, sp);
+    if (st != HP_OK) return st;
+    if ((st = check_out(o, lse)) != HP_OK) return st;
+    if (q->B == 0) return HP_OK;
+    if (!ws || ws_bytes < sp.bytes || !aligned16(ws)) return HP_ERR_WORKSPACE;
+    hipStream_t s = (hipStream_t)stream;
+    char *base = (char *)ws;
+    int32_t *tok_len = (int32_t *)(base + sp.len_off);
+    int32_t *tok_table = (int32_t *)(base + sp.table_off);
+
+    MergeArgs m;
+    std::memset(&m, 0, sizeof m);
+    if ((st = run_prefix_levels(q, doc, sp.cp, base, m, s)) != HP_OK) return st;
+
+    StreamSelectArgs sel;
+    std::memset(&sel, 0, sizeof sel);
+    sel.row_slots = rows->row_slots;
+    sel.slot_sid = rows->slot_sid;
+    sel.row_len = rows->row_len;
+    sel.q_req = rows->q_req;
+    sel.q_sid = rows->q_sid;
+    sel.B = q->B;
+    sel.R = rows->num_requests;
+    sel.row_cap = rows->row_cap;
+    sel.tok_table = tok_table;
+    sel.tok_len = tok_len;
+    hipError_t e = launch_stream_select(sel, s);
+    if (e != hipSuccess) return fail_hip(e);
+
+    SuffixArgs a;
+    std::memset(&a, 0, sizeof a);
+    a.q = q->q;
+    a.k_pool = rows->k_pool;
+    a.v_pool = rows->v_pool;
+    a.table = tok_table;
+    a.lens = tok_len;
+    a.B = q->B;
+    a.Hq = q->Hq;
+    a.Hkv = q->Hkv;
+    a.max_blocks = rows->row_cap;  // capacity of each query's table
+    a.has_suffix = 1;
+    a.scale_log2 = (float)((double)q->scale * 1.4426950408889634);
+    a.dest = RowDest{o, lse, 0, 0, 0};
+    a.pool_rows = rows->pool_rows;
+    a.nsrc = m.nsrc;
+    for (int i = 0; i < m.nsrc; ++i) a.src[i] = m.src[i];
+    const int blocks = (int)cdiv(rows->row_cap, HP_BLOCK_SIZE);
+    const int nws = blocks <= 2 ? 1 : blocks <= 16 ? 2 : 4;
+    e = launch_token_suffix(a, q->dtype, q->d, q->Hq / q->Hkv, nws, s);
+    return e == hipSuccess ? HP_OK : fail_hip(e);
+}
 
 hp_status hp_cascade_step(const hp_query *q, const hp_prefix_tree *tree, const hp_paged_kv *kv,
                           float *o, float *lse, void *ws, size_t ws_bytes, void *stream) {

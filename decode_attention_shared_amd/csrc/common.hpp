@@ -156,6 +156,20 @@ struct SuffixArgs {
     const float *part_o, *part_lse;
 };
 
+// Stream selection of a shared-context step: query b (request q_req[b],
+// stream q_sid[b]) gets the pool rows of the visible positions of its
+// request's KV row, in row order.
+struct StreamSelectArgs {
+    const int32_t *row_slots;  // [R][row_cap] pool row of each position
+    const int32_t *slot_sid;   // [R][row_cap] stream id of each position (-1: every stream)
+    const int32_t *row_len;    // [R]
+    const int32_t *q_req;      // [B]
+    const int32_t *q_sid;      // [B]
+    int32_t B, R, row_cap;
+    int32_t *tok_table;        // [B][row_cap] out: visible pool rows
+    int32_t *tok_len;          // [B] out: their count, -1 when the metadata is out of range
+};
+
 struct MergeArgs {
     MergeSrc src[kMaxMergeSrc];
     int32_t nsrc;

@@ -67,12 +67,20 @@ __device__ __forceinline__ float group_sum(float x) {
     return x;
 }
 
-// kTree: chunk-tree mode.  The private keys of sequence b are the pool rows
-// tok_rows[seq_tok[b] ..] (one row per token: tree pieces start at any row),
-// and the partials to merge are the sequence's entries in the plan's source
-// list, instead of a block table and by-value sources.
-template <int kDt, int D, int G, int NWS, bool kTree>
+// Where a sequence's keys are (kMode):
+//   kBlocks  paged: token t in slot t % 16 of block table[b][t / 16];
+//   kTree    chunk-tree: pool row tok_rows[seq_tok[b] + t] (one row per token:
+//            tree pieces start at any row), partials from the plan's source
+//            list instead of the by-value sources;
+//   kTokens  token table: pool row table[b * cap + t] (cap = max_blocks) for
+//            t < lens[b] (the visible positions of a stream of a
+//            shared-context request, gathered by the stream selection
+//            kernel; its document is merged in as a by-value source).
+constexpr int kBlocks = 0, kTree = 1, kTokens = 2;
+
+template <int kDt, int D, int G, int NWS, int kMode>
 __global__ __launch_bounds__(64 * NWS) void suffix_kernel(SuffixArgs a) {
+    constexpr bool kRows = kMode != kBlocks;  // one pool row per token
     using E = Elem<kDt>;
     constexpr int kEpl = 16 / E::kSize;  // elements per lane per token
     constexpr int kLpt = D / kEpl;       // lanes per token
@@ -105,16 +113,24 @@ __global__ __launch_bounds__(64 * NWS) void suffix_kernel(SuffixArgs a) {
 
     int len = 0;
     bool bad = false;
-    int tok0 = 0;  // chunk-tree mode: first private row entry of this sequence
-    if constexpr (kTree) {
-        tok0 = a.tree[a.seq_tok_off + b];
+    const int *trow;
+    if constexpr (kMode == kTree) {
+        const int tok0 = a.tree[a.seq_tok_off + b];
         const int cap = a.tree[a.seq_tok_off + b + 1] - tok0;
+        trow = a.tree + a.tok_rows_off + tok0;
         len = cap;
         if (a.lens != nullptr) {
             len = a.lens[b] - a.tree[a.shared_off + b];
             bad = len < 0 || len > cap;
         }
-    } else if (a.has_suffix) {
+    } else if constexpr (kMode == kTokens) {
+        trow = a.table + (int64_t)b * a.max_blocks;
+        len = a.lens[b];
+        bad = len < 0 || len > a.max_blocks;
+    } else {
+        trow = a.table + (int64_t)b * a.max_blocks;
+    }
+    if (kMode == kBlocks && a.has_suffix) {
         len = a.lens[b];
         bad = len < 0 || len > a.max_blocks * kBlock;
     }
@@ -127,16 +143,16 @@ __global__ __launch_bounds__(64 * NWS) void suffix_kernel(SuffixArgs a) {
     // parts do not fit the stage are read from memory in the epilogue.
     constexpr int kStageO = G == 1 ? 2048 : 8192;  // floats; a multiple of 4 * kWave
     constexpr int kCpp = G * D / 4;                 // 16-byte chunks per part
-    __shared__ __attribute__((aligned(16))) float sm_po[kTree ? 4 : kStageO];
+    __shared__ __attribute__((aligned(16))) float sm_po[kMode == kTree ? 4 : kStageO];
     __shared__ float sm_pl[kWave];
     int nparts = 0;
-    if constexpr (!kTree) {
+    if constexpr (kMode != kTree) {
 #pragma unroll 1
         for (int si = 0; si < a.nsrc; ++si)
             if (b >= a.src[si].b0 && b < a.src[si].b1) nparts += a.src[si].nsplit;
     }
-    const bool staged = !kTree && nparts > 0 && nparts * kCpp * 4 <= kStageO && nparts * G <= kWave;
-    if constexpr (!kTree) {
+    const bool staged = kMode != kTree && nparts > 0 && nparts * kCpp * 4 <= kStageO && nparts * G <= kWave;
+    if constexpr (kMode != kTree) {
         if (staged) {
             // Locate part p of this row: pointers to its first O float and LSE.
             auto part = [&](int p, const float *&po, const float *&pl) {
@@ -185,18 +201,17 @@ __global__ __launch_bounds__(64 * NWS) void suffix_kernel(SuffixArgs a) {
     const int64_t tok_stride = (int64_t)a.Hkv * D * E::kSize;  // bytes between tokens of a block
     const char *kp = (const char *)a.k_pool;
     const char *vp = (const char *)a.v_pool;
-    const int *trow = kTree ? a.tree + a.tok_rows_off + tok0 : a.table + (int64_t)b * a.max_blocks;
 
     // Where a block's keys are: its block id (block table), or in chunk-tree
     // mode the pool row of each token this lane loads.  Read one block-step
     // ahead of the K/V loads, so the lookup's latency never sits in front of
     // a block's loads.
     struct Ref {
-        int v[kTree ? kPasses : 1];
+        int v[kRows ? kPasses : 1];
     };
     auto table_id = [&](int blk) {
         Ref r;
-        if constexpr (kTree) {
+        if constexpr (kRows) {
 #pragma unroll
             for (int p = 0; p < kPasses; ++p) {
                 const int t = blk * kBlock + p * kTpp + tg;
@@ -211,7 +226,7 @@ __global__ __launch_bounds__(64 * NWS) void suffix_kernel(SuffixArgs a) {
     // with an out-of-range id are never read).
     auto fetch = [&](int blk, const Ref &ref, u32x4 (&kr)[kPasses], u32x4 (&vr)[kPasses],
                      int &valid) {
-        if constexpr (kTree) {
+        if constexpr (kRows) {
             valid = min(kBlock, len - blk * kBlock);
 #pragma unroll
             for (int p = 0; p < kPasses; ++p) {
@@ -316,7 +331,10 @@ __global__ __launch_bounds__(64 * NWS) void suffix_kernel(SuffixArgs a) {
             sm_l[wave][j] = lt;
         }
     }
-    if (lane == 0) sm_bad[wave] = bad ? 1 : 0;
+    // A bad pool row is seen by the lanes that hold its token (row modes): any lane
+    // of the wave marks it.
+    const bool wave_bad = __any(bad);
+    if (lane == 0) sm_bad[wave] = wave_bad ? 1 : 0;
     if (staged) wait_vmcnt<0>();  // this wave's partial DMAs have landed (the barrier publishes them)
     __syncthreads();
 
@@ -347,7 +365,7 @@ __global__ __launch_bounds__(64 * NWS) void suffix_kernel(SuffixArgs a) {
         // prefix parts: normalised O_i with natural-log LSE_i
         float mx = sl > 0.f ? ms : -INFINITY;
         bool nan_seen = false;
-        if constexpr (kTree) {
+        if constexpr (kMode == kTree) {
             const int s0 = a.tree[a.seq_src_off + b], s1 = a.tree[a.seq_src_off + b + 1];
 #pragma unroll 1
             for (int si = s0; si < s1; ++si) {
@@ -398,7 +416,7 @@ __global__ __launch_bounds__(64 * NWS) void suffix_kernel(SuffixArgs a) {
                 den = sl * f;
                 num = so * f;
             }
-            if constexpr (kTree) {
+            if constexpr (kMode == kTree) {
                 const int s0 = a.tree[a.seq_src_off + b], s1 = a.tree[a.seq_src_off + b + 1];
 #pragma unroll 1
                 for (int si = s0; si < s1; ++si) {
@@ -443,50 +461,56 @@ __global__ __launch_bounds__(64 * NWS) void suffix_kernel(SuffixArgs a) {
     }
 }
 
-template <int kDt, int D, int NWS, bool kTree>
+template <int kDt, int D, int NWS, int kMode>
 static void launch_g(const SuffixArgs &a, int G, dim3 grid, hipStream_t s) {
     constexpr int T = 64 * NWS;
     switch (G) {
-    case 1: suffix_kernel<kDt, D, 1, NWS, kTree><<<grid, T, 0, s>>>(a); break;
-    case 2: suffix_kernel<kDt, D, 2, NWS, kTree><<<grid, T, 0, s>>>(a); break;
-    case 4: suffix_kernel<kDt, D, 4, NWS, kTree><<<grid, T, 0, s>>>(a); break;
-    default: suffix_kernel<kDt, D, 8, NWS, kTree><<<grid, T, 0, s>>>(a); break;
+    case 1: suffix_kernel<kDt, D, 1, NWS, kMode><<<grid, T, 0, s>>>(a); break;
+    case 2: suffix_kernel<kDt, D, 2, NWS, kMode><<<grid, T, 0, s>>>(a); break;
+    case 4: suffix_kernel<kDt, D, 4, NWS, kMode><<<grid, T, 0, s>>>(a); break;
+    default: suffix_kernel<kDt, D, 8, NWS, kMode><<<grid, T, 0, s>>>(a); break;
     }
 }
 
-template <int kDt, int NWS, bool kTree>
+template <int kDt, int NWS, int kMode>
 static void launch_d(const SuffixArgs &a, int d, int G, dim3 grid, hipStream_t s) {
-    if (d == 128) launch_g<kDt, 128, NWS, kTree>(a, G, grid, s);
-    else launch_g<kDt, 64, NWS, kTree>(a, G, grid, s);
+    if (d == 128) launch_g<kDt, 128, NWS, kMode>(a, G, grid, s);
+    else launch_g<kDt, 64, NWS, kMode>(a, G, grid, s);
 }
 
-template <int kDt, bool kTree>
+template <int kDt, int kMode>
 static void launch_dt(const SuffixArgs &a, int d, int G, int nws, dim3 grid, hipStream_t s) {
     switch (nws) {
-    case 1: launch_d<kDt, 1, kTree>(a, d, G, grid, s); break;
-    case 2: launch_d<kDt, 2, kTree>(a, d, G, grid, s); break;
-    default: launch_d<kDt, 4, kTree>(a, d, G, grid, s); break;
+    case 1: launch_d<kDt, 1, kMode>(a, d, G, grid, s); break;
+    case 2: launch_d<kDt, 2, kMode>(a, d, G, grid, s); break;
+    default: launch_d<kDt, 4, kMode>(a, d, G, grid, s); break;
     }
 }
 
-template <bool kTree>
+template <int kMode>
 static hipError_t launch_mode(const SuffixArgs &a, int dtype, int d, int G, int nws,
                               hipStream_t s) {
     const dim3 grid((unsigned)((int64_t)a.B * a.Hkv));
-    if (dtype == HP_BF16) launch_dt<HP_BF16, kTree>(a, d, G, nws, grid, s);
-    else if (dtype == HP_F16) launch_dt<HP_F16, kTree>(a, d, G, nws, grid, s);
-    else launch_dt<HP_F32, kTree>(a, d, G, nws, grid, s);
+    if (dtype == HP_BF16) launch_dt<HP_BF16, kMode>(a, d, G, nws, grid, s);
+    else if (dtype == HP_F16) launch_dt<HP_F16, kMode>(a, d, G, nws, grid, s);
+    else launch_dt<HP_F32, kMode>(a, d, G, nws, grid, s);
     return hipGetLastError();
 }
 
 hipError_t launch_suffix(const SuffixArgs &a, int dtype, int d, int G, int nws, hipStream_t s) {
-    return launch_mode<false>(a, dtype, d, G, nws, s);
+    return launch_mode<kBlocks>(a, dtype, d, G, nws, s);
 }
 
 // Sequence-first pass of a chunk-tree step (a.tree set).
 hipError_t launch_tree_suffix(const SuffixArgs &a, int dtype, int d, int G, int nws,
                               hipStream_t s) {
-    return launch_mode<true>(a, dtype, d, G, nws, s);
+    return launch_mode<kTree>(a, dtype, d, G, nws, s);
+}
+
+// Per-stream token tables of a shared-context request (a.table [B][cap]).
+hipError_t launch_token_suffix(const SuffixArgs &a, int dtype, int d, int G, int nws,
+                               hipStream_t s) {
+    return launch_mode<kTokens>(a, dtype, d, G, nws, s);
 }
 
 }  // namespace hp

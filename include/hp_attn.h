@@ -200,6 +200,55 @@ hp_status hp_cascade_step_timed(const hp_query *query, const hp_prefix_tree *tre
                                 int32_t n_events);
 
 /* ------------------------------------------------------------------------
+ * Shared-context requests: stream-id masked decode
+ * ------------------------------------------------------------------------
+ * A request decodes P independent questions about one document as P streams
+ * of one KV row ("Read Once, Answer Many: Parallel Prompting for
+ * Shared-Context LLM Inference", section "Parallel Prompting").  The document
+ * is a prefix node (read once for every stream of every request that shares
+ * it, by the prefix pass).  The rest of a request's row -- its questions and
+ * the streams' answer tokens, in whatever order the engine appends them --
+ * lives in a pool with one token per row, each position tagged with a stream
+ * id; -1 marks a position every stream of the request sees.  Query b, of
+ * stream q_sid[b] in request q_req[b], attends the document and exactly the
+ * positions of its request's row whose id is -1 or q_sid[b] (the page's
+ * Eq. 2 and Figure 2: the answer of a stream depends only on the document and
+ * its own question), in row order.
+ *
+ * Key of pool row p, KV head g at k_pool + (p*Hkv + g)*d (elements).
+ * row_slots / slot_sid: device [num_requests][row_cap]; row_len: device
+ * [num_requests]; q_req / q_sid: device [B].  All are read on the device, so
+ * they may change between graph replays.  A request index or row length out
+ * of range, or a visible position whose pool row is outside [0, pool_rows),
+ * makes that query's O and LSE NaN (nothing out of range is dereferenced).
+ */
+typedef struct hp_stream_rows {
+    const void *k_pool, *v_pool;   /* device [pool_rows][Hkv][d] of dtype */
+    const int32_t *row_slots;      /* device [num_requests][row_cap] */
+    const int32_t *slot_sid;       /* device [num_requests][row_cap] */
+    const int32_t *row_len;        /* device [num_requests], each in [0, row_cap] */
+    const int32_t *q_req;          /* device [B] */
+    const int32_t *q_sid;          /* device [B] */
+    int32_t num_requests;          /* >= 1 */
+    int32_t row_cap;               /* >= 1 */
+    int64_t pool_rows;             /* >= 1 */
+} hp_stream_rows;
+
+/*
+ * One decode step of shared-context requests: the prefix pass over every node
+ * of `doc` (a prefix tree as in hp_cascade_step; NULL for none), the stream
+ * selection (the mask of Eq. 2 evaluated on the stream ids, writing each
+ * query's visible pool rows into the workspace), and the sequence-first pass
+ * over those rows with the merge of the document partials fused in.  lse may
+ * be NULL.  Workspace: hp_stream_decode_workspace_size().
+ */
+hp_status hp_stream_decode_workspace_size(const hp_query *query, const hp_prefix_tree *doc,
+                                          const hp_stream_rows *rows, size_t *bytes);
+hp_status hp_stream_decode(const hp_query *query, const hp_prefix_tree *doc,
+                           const hp_stream_rows *rows, float *o, float *lse, void *workspace,
+                           size_t workspace_bytes, void *stream);
+
+/* ------------------------------------------------------------------------
  * Chunked prefix tree: device-resident (C, i, j) plans
  * ------------------------------------------------------------------------
  * Keys and values live in a pool of rows: row r holds one token, its key for

@@ -24,6 +24,12 @@ Functions:
       KV Cache and Two-Phase Partition", section "Context Generation and
       GPU-CPU Coordination": a chunk descriptor (C, i, j) gives chunk C's keys
       to sequences i .. j-1).
+  visible_positions(slot_sid, q_sid) / stream_attention(step, rows)  the
+      stream-id mask of "Read Once, Answer Many: Parallel Prompting for
+      Shared-Context LLM Inference" (section "Parallel Prompting", Eq. 2): a
+      query of stream s attends the document and the positions of its
+      request's KV row tagged -1 or s; the masked softmax is the plain softmax
+      over those positions (a masked score contributes e^-inf = 0).
   kv_append(pool, rows, new)  the decode-step append of that page's section
       "Prefix-Aware KV Cache (PAKV): The Prefix Tree Structure": row i of
       ``new`` is stored at pool row rows[i] (entries outside the pool skipped).
@@ -215,6 +221,49 @@ def tree_attention(step, rows: Optional[Sequence[int]] = None, nthreads: int = 0
     need = set(range(step.B)) if rows is None else {int(r) // step.Hq for r in rows}
     segs = [step.keys_of(b) if b in need else [] for b in range(step.B)]
     return attention(step.q, segs, step.Hkv, step.scale, rows, nthreads, lib)
+
+
+def visible_positions(slot_sid: Sequence[int], q_sid: int) -> np.ndarray:
+    """Row positions a query of stream ``q_sid`` may attend: those whose stream id is
+    -1 (every stream) or ``q_sid`` ("Read Once, Answer Many: Parallel Prompting for
+    Shared-Context LLM Inference", section "Parallel Prompting", Eq. 2; the causal
+    term holds for every position of a decode step's row, which ends at the new
+    tokens).  In row order."""
+    sid = np.asarray(slot_sid, dtype=np.int64)
+    return np.nonzero((sid == -1) | (sid == int(q_sid)))[0]
+
+
+def stream_segments(step, rows: Optional[Sequence[int]] = None
+                    ) -> List[List[Tuple[torch.Tensor, torch.Tensor]]]:
+    """Key segments of every query of a ``workloads.StreamStep``: its document nodes
+    (root first), then the visible positions of its request's row, read from the
+    logical row arrays (never through the pool)."""
+    cfg = step.cfg
+    need = set(range(cfg.B)) if rows is None else {int(r) // cfg.Hq for r in rows}
+    out = []
+    for b in range(cfg.B):
+        if b not in need:
+            out.append([])
+            continue
+        segs = []
+        for level in step.levels:
+            for node in level:
+                if node.seq_begin <= b < node.seq_end:
+                    segs.append((node.k, node.v))
+        r = int(step.q_req[b])
+        n = int(step.row_len[r])
+        vis = torch.as_tensor(visible_positions(step.row_sid[r, :n].tolist(),
+                                                int(step.q_sid[b])), dtype=torch.int64)
+        segs.append((step.row_k[r][vis], step.row_v[r][vis]))
+        out.append(segs)
+    return out
+
+
+def stream_attention(step, rows: Optional[Sequence[int]] = None, nthreads: int = 0,
+                     lib=None) -> Tuple[np.ndarray, np.ndarray]:
+    """fp64 attention of a ``workloads.StreamStep`` (every row, or ``rows``)."""
+    return attention(step.q, stream_segments(step, rows), step.cfg.Hkv, step.scale, rows,
+                     nthreads, lib)
 
 
 def kv_append(pool: torch.Tensor, rows: Sequence[int], new: torch.Tensor) -> torch.Tensor:

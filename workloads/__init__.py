@@ -510,3 +510,155 @@ def chunked_config(cfg: Config, seed: int = 0, seq_lens: Optional[Sequence[int]]
                          scale=scale_for(cfg.d), q=q, k_pool=k_pool, v_pool=v_pool,
                          descs=np.asarray(descs, dtype=np.int32).reshape(-1, 4),
                          seq_lens=real.astype(np.int32))
+
+
+# ----------------------------------------------------------------------------------------
+# Shared-context requests: P streams per request, stream-id tagged KV rows
+# ----------------------------------------------------------------------------------------
+
+@dataclasses.dataclass
+class StreamStep:
+    """One decode step of shared-context requests, on the CPU.
+
+    The B queries are the streams: query b is stream ``q_sid[b]`` of request
+    ``q_req[b]`` (requests hold P consecutive queries; the last may hold
+    fewer).  Every query attends the document nodes ``levels`` (as a Step's
+    prefix) and the positions of its request's KV row whose stream id is -1
+    or its own.  Request r's row, position i < row_len[r]: stream id
+    ``row_sid[r][i]``, logical key/value ``row_k[r][i]`` / ``row_v[r][i]`` (the
+    oracle reads these), stored at pool row ``row_slots[r][i]`` of
+    ``k_pool`` / ``v_pool`` (the GPU reads these).  Row layout, as the
+    Parallel Prompting page lays a request out: ``shared_len`` tokens every
+    stream sees (id -1), then each stream's question tokens, then the
+    streams' answer tokens interleaved step by step.  Unused pool rows are
+    NaN; row padding points at a NaN row with id -3 (never visible).
+    """
+    cfg: Config
+    P: int
+    seed: int
+    scale: float
+    q: torch.Tensor            # [B][Hq][d]
+    levels: List[List[Node]]
+    q_req: torch.Tensor        # [B] int32
+    q_sid: torch.Tensor        # [B] int32
+    own_lens: torch.Tensor     # [B] int64: question + answer tokens of each stream
+    answer_len: int
+    shared_len: int
+    row_len: torch.Tensor      # [R] int32
+    row_sid: torch.Tensor      # [R][row_cap] int32
+    row_slots: torch.Tensor    # [R][row_cap] int32
+    row_k: List[torch.Tensor]  # per request [row_len][Hkv][d]
+    row_v: List[torch.Tensor]
+    k_pool: torch.Tensor       # [pool_rows][Hkv][d]
+    v_pool: torch.Tensor
+
+    @property
+    def R(self) -> int:
+        return int(self.row_len.shape[0])
+
+    @property
+    def row_cap(self) -> int:
+        return int(self.row_sid.shape[1])
+
+    def own_positions(self, b: int) -> List[int]:
+        """Row positions of stream b's own tokens and the shared tokens, from the
+        layout rule (not from the ids): what the stream would hold if decoded alone."""
+        r, s = int(self.q_req[b]), int(self.q_sid[b])
+        b0 = r * self.P
+        n = min(self.P, self.cfg.B - b0)
+        qlens = [int(self.own_lens[x]) - self.answer_len for x in range(b0, b0 + n)]
+        pos = list(range(self.shared_len))
+        start = self.shared_len + sum(qlens[:s])
+        pos += list(range(start, start + qlens[s]))
+        ans0 = self.shared_len + sum(qlens)
+        pos += [ans0 + t * n + s for t in range(self.answer_len)]
+        return pos
+
+
+def docqa_streams(P: int = 32) -> Config:
+    """Parallel Prompting's shared-document workload at the docqa_codellama7b shape: one
+    16384-token document, 256 question streams in requests of P, each stream with
+    question + answer tokens U[64, 512]."""
+    base = docqa_codellama7b()
+    return dataclasses.replace(base, name=f"docqa_streams_p{P}",
+                               description=base.description + f", requests of {P} streams, "
+                               "stream-id tagged rows")
+
+
+def stream_step(cfg: Config, P: int, seed: int = 0, answer_len: int = 32, shared_len: int = 0,
+                q_mult: float = 1.0) -> StreamStep:
+    """Draw one shared-context step: cfg.B streams in requests of P, document = cfg's
+    prefix nodes, each stream's own token count (question + answer) drawn from
+    U[cfg.suffix_lo, cfg.suffix_hi] (at least answer_len).  Draw order: own token
+    counts, Q, each prefix node's K then V, each request's row K then V in row
+    order, then a permutation of the pool rows."""
+    _validate_config(cfg)
+    if P < 1 or answer_len < 0 or shared_len < 0 or cfg.suffix_lo < answer_len:
+        raise ValueError("need P >= 1 and suffix_lo >= answer_len >= 0")
+    g = torch.Generator().manual_seed(int(seed))
+    dt = cfg.torch_dtype
+    B = cfg.B
+    own = torch.randint(cfg.suffix_lo, cfg.suffix_hi + 1, (B,), generator=g, dtype=torch.int64)
+    q = _randn(g, (B, cfg.Hq, cfg.d), dt, q_mult)
+    levels: List[List[Node]] = []
+    for level in cfg.levels:
+        nodes = []
+        for (ln, b0, b1) in level:
+            nodes.append(Node(_randn(g, (ln, cfg.Hkv, cfg.d), dt),
+                              _randn(g, (ln, cfg.Hkv, cfg.d), dt), b0, b1))
+        levels.append(nodes)
+    R = -(-B // P)
+    sids, row_k, row_v = [], [], []
+    for r in range(R):
+        b0 = r * P
+        n = min(P, B - b0)
+        qlens = [int(own[b]) - answer_len for b in range(b0, b0 + n)]
+        sid = [-1] * shared_len
+        for s in range(n):
+            sid += [s] * qlens[s]
+        for _ in range(answer_len):
+            sid += list(range(n))
+        sids.append(sid)
+        row_k.append(_randn(g, (len(sid), cfg.Hkv, cfg.d), dt))
+        row_v.append(_randn(g, (len(sid), cfg.Hkv, cfg.d), dt))
+    lens = [len(s) for s in sids]
+    cap = max(1, max(lens))
+    used = sum(lens)
+    pool_rows = used + max(1, int(math.ceil(used * SPARE_FRACTION)))
+    perm = torch.randperm(pool_rows, generator=g).to(torch.int64)
+    pad_row = int(perm[used])
+    k_pool = torch.full((pool_rows, cfg.Hkv, cfg.d), float("nan"), dtype=dt)
+    v_pool = torch.full((pool_rows, cfg.Hkv, cfg.d), float("nan"), dtype=dt)
+    row_sid = torch.full((R, cap), -3, dtype=torch.int32)
+    row_slots = torch.full((R, cap), pad_row, dtype=torch.int32)
+    off = 0
+    for r in range(R):
+        n = lens[r]
+        dest = perm[off:off + n]
+        off += n
+        row_sid[r, :n] = torch.as_tensor(sids[r], dtype=torch.int32)
+        row_slots[r, :n] = dest.to(torch.int32)
+        if n:
+            k_pool[dest] = row_k[r]
+            v_pool[dest] = row_v[r]
+    q_req = (torch.arange(B) // P).to(torch.int32)
+    q_sid = (torch.arange(B) % P).to(torch.int32)
+    return StreamStep(cfg=cfg, P=P, seed=int(seed), scale=scale_for(cfg.d), q=q, levels=levels,
+                      q_req=q_req, q_sid=q_sid, own_lens=own, answer_len=answer_len,
+                      shared_len=shared_len, row_len=torch.as_tensor(lens, dtype=torch.int32),
+                      row_sid=row_sid, row_slots=row_slots, row_k=row_k, row_v=row_v,
+                      k_pool=k_pool, v_pool=v_pool)
+
+
+def stream_bytes(step: StreamStep) -> dict:
+    """Bytes a shared-context step must move: each document node's KV once, each
+    stream's visible row tokens (its own and the shared ones), the stream ids of
+    every row position each query's selection reads, Q in, fp32 O and LSE out."""
+    cfg = step.cfg
+    tok = kv_bytes_per_token(cfg.Hkv, cfg.d, cfg.esize)
+    prefix = sum(ln for level in cfg.levels for (ln, _, _) in level) * tok
+    visible = sum(len(step.own_positions(b)) for b in range(cfg.B))
+    q = cfg.B * cfg.Hq * cfg.d * cfg.esize
+    out = cfg.B * cfg.Hq * cfg.d * 4 + cfg.B * cfg.Hq * 4
+    return {"prefix": prefix, "streams": visible * tok, "q": q, "out": out,
+            "total": prefix + visible * tok + q + out}
