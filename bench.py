@@ -186,6 +186,61 @@ def cpu_baseline(step, target_s: float):
                       f"{el:.1f} s of fp64 work; steps/s scaled by rows"}
 
 
+SHARE_SEQS = (2, 4, 8, 16, 32, 64, 128, 256)
+SHARE_TOKENS = (64, 128, 256, 512, 1024, 2048, 4096, 16384)
+SHARE_PRIVATE = 64  # private tokens per sequence beside the shared run
+
+
+def share_sweep(reps: int = 20):
+    """Batched vs private reading of one shared run of keys, through the chunk-tree step:
+    the run's descriptors cover sequences [0, nseq); each sequence also owns SHARE_PRIVATE
+    private rows.  share_min = 2 batches the run (prefix pass + merge), share_min =
+    nseq + 1 makes every descriptor private (each sequence reads the run itself)."""
+    import torch
+    import decode_attention_shared_amd as hp
+    out = []
+    dev = "cuda:0"
+    for (Hq, Hkv) in ((32, 32), (32, 8)):
+        d = 128
+        B = max(SHARE_SEQS)
+        rows = max(SHARE_TOKENS) + B * SHARE_PRIVATE
+        g = torch.Generator(device=dev).manual_seed(0)
+        kp = torch.randn(rows, Hkv, d, generator=g, device=dev).to(torch.bfloat16)
+        vp = torch.randn(rows, Hkv, d, generator=g, device=dev).to(torch.bfloat16)
+        for nseq in SHARE_SEQS:
+            q = torch.randn(nseq, Hq, d, generator=g, device=dev).to(torch.bfloat16)
+            for tok in SHARE_TOKENS:
+                descs = [(r, min(64, tok - r), 0, nseq) for r in range(0, tok, 64)]
+                base = max(SHARE_TOKENS)
+                descs += [(base + b * SHARE_PRIVATE + r, 64, b, b + 1)
+                          for b in range(nseq) for r in range(0, SHARE_PRIVATE, 64)]
+                res = {"Hq": Hq, "Hkv": Hkv, "nseq": nseq, "tokens": tok}
+                for mode, smin in (("batched", 2), ("private", nseq + 1)):
+                    ts = hp.TreeStep(q, Hkv, descs, smin, rows, 1.0 / d ** 0.5)
+                    o, l = ts(q, kp, vp)
+                    for _ in range(5):
+                        ts(q, kp, vp, out=o, lse=l)
+                    torch.cuda.synchronize()
+                    times = []
+                    for _ in range(reps):
+                        a = torch.cuda.Event(enable_timing=True)
+                        e = torch.cuda.Event(enable_timing=True)
+                        a.record()
+                        ts(q, kp, vp, out=o, lse=l)
+                        e.record()
+                        e.synchronize()
+                        times.append(a.elapsed_time(e) * 1e3)
+                    times.sort()
+                    res[mode + "_us"] = round(times[len(times) // 2], 2)
+                res["batched_wins"] = res["batched_us"] < res["private_us"]
+                out.append(res)
+                print(f"[share] Hq {Hq} Hkv {Hkv} nseq {nseq:3d} tokens {tok:5d}: batched "
+                      f"{res['batched_us']:8.1f} us  private {res['private_us']:8.1f} us",
+                      file=sys.stderr, flush=True)
+    return {"share_sweep": out, "private_tokens_per_seq": SHARE_PRIVATE, "dtype": "bf16",
+            "d": 128}
+
+
 def load_traffic(name: str, khash: str):
     path = os.path.join(ROOT, "profiles", "traffic.json")
     if not os.path.exists(path):
@@ -211,6 +266,11 @@ def main():
     ap.add_argument("--sweep-steps", type=int, default=50)
     ap.add_argument("--profile-only", action="store_true",
                     help="only run warmup + timed steps (for rocprofv3); no sweep or CPU leg")
+    ap.add_argument("--share-sweep", action="store_true",
+                    help="instead of the step, time one shared run of keys read once for all its "
+                         "sequences (batched) against each sequence reading it (private), over a "
+                         "grid of sequence counts and run lengths (the data the batching policy "
+                         "is fitted to)")
     ap.add_argument("--copy-probe", type=int, default=0, metavar="MIB",
                     help="instead of the step, run --steps device-to-device copies of MIB MiB "
                          "(a plain copy of known size, to calibrate HBM byte counters)")
@@ -227,6 +287,10 @@ def main():
     import workloads
     if not torch.cuda.is_available():
         raise SystemExit("bench.py needs a GPU")
+
+    if args.share_sweep:
+        print(json.dumps(share_sweep()), flush=True)
+        return
 
     if args.copy_probe:
         n = args.copy_probe << 20

@@ -44,7 +44,7 @@ STATUS = {0: "HP_OK", 1: "HP_ERR_NULL", 2: "HP_ERR_INVALID_ARG", 3: "HP_ERR_UNSU
 EXPORTS = ["hp_prefix_attn_workspace_size", "hp_prefix_attn", "hp_suffix_decode_workspace_size",
            "hp_suffix_decode", "hp_lse_merge", "hp_cascade_workspace_size", "hp_cascade_step",
            "hp_cascade_step_timed", "hp_stream_decode_workspace_size", "hp_stream_decode",
-           "hp_tree_plan_build", "hp_tree_step", "hp_kv_append",
+           "hp_tree_plan_build", "hp_share_decision", "hp_tree_step", "hp_kv_append",
            "hp_pakv_create", "hp_pakv_destroy", "hp_pakv_insert", "hp_pakv_append",
            "hp_pakv_remove", "hp_pakv_context", "hp_pakv_seq_rows", "hp_pakv_get_stats",
            "hp_status_string", "hp_last_hip_error", "hp_version"]
@@ -183,6 +183,9 @@ def lib():
             L.hp_tree_plan_build.restype = st
             L.hp_tree_plan_build.argtypes = [ctypes.POINTER(Query), p, i32, i32, i64, p,
                                              ctypes.c_size_t, ctypes.POINTER(TreePlan)]
+            L.hp_share_decision.restype = st
+            L.hp_share_decision.argtypes = [ctypes.POINTER(Query), i64, i32,
+                                            ctypes.POINTER(ctypes.c_int32)]
             L.hp_tree_step.restype = st
             L.hp_tree_step.argtypes = [ctypes.POINTER(Query), ctypes.POINTER(TreePlan), p, p, p,
                                        p, p, p, p, ctypes.c_size_t, p]
@@ -499,6 +502,18 @@ def tree_plan_build(B: int, Hq: int, Hkv: int, d: int, dtype: torch.dtype, descs
                                 pool_rows, blob.data_ptr(), blob.numel(), ctypes.byref(plan)),
            "hp_tree_plan_build")
     return plan, blob
+
+
+def share_decision(Hq: int, Hkv: int, tokens: int, nseq: int, d: int = 128,
+                   dtype: torch.dtype = torch.bfloat16) -> bool:
+    """True when `tokens` keys shared by `nseq` sequences are better read once for all of
+    them (prefix pass plus merge) than by each sequence (hp_share_decision)."""
+    L = lib()
+    geom = Query(None, max(1, nseq), Hq, Hkv, d, _DTYPE[dtype], 1.0)
+    out = ctypes.c_int32(0)
+    _check(L.hp_share_decision(ctypes.byref(geom), tokens, nseq, ctypes.byref(out)),
+           "hp_share_decision")
+    return bool(out.value)
 
 
 class TreeStep:

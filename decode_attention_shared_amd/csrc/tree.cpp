@@ -48,6 +48,27 @@ hp_status check_descs(const hp_query &g, const hp_chunk_desc *descs, int32_t n,
     return HP_OK;
 }
 
+// Batching policy: read a run of `tokens` shared keys once for its `nseq`
+// sequences (the chunk-first phase, plus the partial merge) only when that is
+// faster than every sequence reading the run in its own pass.  Under a few
+// hundred shared tokens, or with few sequences, the extra launch and merge
+// cost more than the shared read saves ("Shared Prefix KV Caching, in depth",
+// section "Trade-offs"; the boundary conditions listed in "Hydragen:
+// High-Throughput LLM Inference with Shared Prefixes", section "How Hydragen
+// Positions Itself": long shared prefixes and large batches).  The thresholds are the smallest run lengths at which the
+// batched step measured faster than the private one on MI355X (bf16, d = 128,
+// 32 query heads with 32 or 8 KV heads, 2..256 sequences, 64 private rows per
+// sequence; the run length doubled from 64 to 16384).  With one query head
+// per KV head the private pass keeps up longer, as each (sequence, KV head)
+// workgroup then streams its keys for a single query.
+bool share_decision(int G, int64_t tokens, int64_t nseq) {
+    if (nseq < 2 || tokens <= 0) return false;
+    int64_t t;
+    if (G == 1) t = nseq <= 8 ? 1024 : nseq <= 32 ? 512 : nseq <= 128 ? 256 : 128;
+    else t = nseq <= 64 ? 512 : nseq <= 128 ? 256 : 128;
+    return tokens >= t;
+}
+
 // Everything of the plan but the image bytes; fills `plan` and `img`.
 hp_status build(const hp_query &g, const hp_chunk_desc *descs, int32_t n, int32_t share_min,
                 int64_t pool_rows, hp_tree_plan &plan, Image &img) {
@@ -63,12 +84,35 @@ hp_status build(const hp_query &g, const hp_chunk_desc *descs, int32_t n, int32_
     plan.num_descs = n;
     plan.pool_rows = pool_rows;
 
+    // Which descriptors are batched: by range size (share_min >= 2), or, with
+    // share_min == 0, run by run (consecutive descriptors with one range of at
+    // least two sequences) by the measured batching policy on the run's
+    // total rows.
+    std::vector<char> is_batched(n > 0 ? n : 1, 0);
+    for (int32_t k = 0; k < n;) {
+        int32_t e = k + 1;
+        while (e < n && descs[e].seq_begin == descs[k].seq_begin &&
+               descs[e].seq_end == descs[k].seq_end)
+            ++e;
+        const int32_t nseq = descs[k].seq_end - descs[k].seq_begin;
+        bool batch;
+        if (share_min == 0) {
+            int64_t tokens = 0;
+            for (int32_t j = k; j < e; ++j) tokens += descs[j].count;
+            batch = share_decision(G, tokens, nseq);
+        } else {
+            batch = nseq >= share_min;
+        }
+        for (int32_t j = k; j < e; ++j) is_batched[j] = batch;
+        k = e;
+    }
+
     // Segments: runs of consecutive batched descriptors with one range.
     std::vector<int64_t> seg_tokens;
     bool open = false;
     for (int32_t k = 0; k < n; ++k) {
         const hp_chunk_desc &c = descs[k];
-        const bool batched = c.seq_end - c.seq_begin >= share_min;
+        const bool batched = is_batched[k];
         if (!batched) {
             open = false;
             continue;
@@ -164,7 +208,7 @@ hp_status build(const hp_query &g, const hp_chunk_desc *descs, int32_t n, int32_
     std::vector<int64_t> ntok(B + 1, 0);
     for (int32_t k = 0; k < n; ++k) {
         const hp_chunk_desc &c = descs[k];
-        if (c.seq_end - c.seq_begin >= share_min) continue;
+        if (is_batched[k]) continue;
         for (int b = c.seq_begin; b < c.seq_end; ++b) ntok[b + 1] += c.count;
     }
     int64_t max_private = 0;
@@ -178,7 +222,7 @@ hp_status build(const hp_query &g, const hp_chunk_desc *descs, int32_t n, int32_
         std::vector<int64_t> fill(ntok.begin(), ntok.end() - 1);
         for (int32_t k = 0; k < n; ++k) {
             const hp_chunk_desc &c = descs[k];
-            if (c.seq_end - c.seq_begin >= share_min) continue;
+            if (is_batched[k]) continue;
             for (int b = c.seq_begin; b < c.seq_end; ++b)
                 for (int r = 0; r < c.count; ++r) img.tok_rows[(size_t)fill[b]++] = c.row + r;
         }
@@ -236,7 +280,7 @@ hp_status hp_tree_plan_build(const hp_query *geom, const hp_chunk_desc *descs, i
     if (!plan) return HP_ERR_NULL;
     hp_status st = check_geometry(geom, false);
     if (st != HP_OK) return st;
-    if (share_min < 2) return HP_ERR_INVALID_ARG;
+    if (share_min != 0 && share_min < 2) return HP_ERR_INVALID_ARG;
     st = check_descs(*geom, descs, n, pool_rows);
     if (st != HP_OK) return st;
     hp_tree_plan p;
@@ -248,6 +292,16 @@ hp_status hp_tree_plan_build(const hp_query *geom, const hp_chunk_desc *descs, i
         write_image(p, img, blob);
     }
     *plan = p;
+    return HP_OK;
+}
+
+hp_status hp_share_decision(const hp_query *geom, int64_t tokens, int32_t nseq,
+                            int32_t *batch) {
+    if (!batch) return HP_ERR_NULL;
+    hp_status st = check_geometry(geom, false);
+    if (st != HP_OK) return st;
+    if (tokens < 0 || nseq < 0 || nseq > geom->B) return HP_ERR_INVALID_ARG;
+    *batch = share_decision(geom->Hq / geom->Hkv, tokens, nseq) ? 1 : 0;
     return HP_OK;
 }
 

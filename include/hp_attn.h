@@ -301,7 +301,9 @@ typedef struct hp_tree_plan {
  * (>= 2) are batched: consecutive ones with the same range form a segment
  * whose keys stream once through the matrix cores for all the range's query
  * rows (chunk-first phase).  The others are private: each sequence they cover
- * reads them in the per-sequence pass (sequence-first phase).  Descriptors are
+ * reads them in the per-sequence pass (sequence-first phase).  share_min = 0
+ * decides run by run (consecutive descriptors with one range) with
+ * hp_share_decision() on the run's total rows and range size.  Descriptors are
  * given in tree pre-order, as hp_pakv_context() emits them, so that a path of
  * chunks shared by one range is one segment; any order is still correct.
  *
@@ -314,6 +316,19 @@ typedef struct hp_tree_plan {
 hp_status hp_tree_plan_build(const hp_query *geom, const hp_chunk_desc *descs, int32_t n,
                              int32_t share_min, int64_t pool_rows, void *blob,
                              size_t blob_capacity, hp_tree_plan *plan);
+
+/*
+ * Batching policy: *batch = 1 when `tokens` keys shared by `nseq` sequences
+ * are better read once for all of them (prefix pass plus merge) than by each
+ * sequence in its own pass, else 0 ("Shared Prefix KV Caching, in depth",
+ * section "Trade-offs": under a few hundred shared tokens or with few
+ * sequences the extra launch and merge cost more than they save; Hydragen
+ * page, section "How Hydragen Positions Itself", on its boundary conditions).  The rule is
+ * a threshold on `tokens` that falls as `nseq` grows, fitted to timings of
+ * both passes on MI355X; it depends on geom's Hq / Hkv (geom->q and
+ * geom->scale are not used).  nseq in [0, geom->B], tokens >= 0.
+ */
+hp_status hp_share_decision(const hp_query *geom, int64_t tokens, int32_t nseq, int32_t *batch);
 
 /*
  * One decode step over a plan: every row (b, h) attends the rows of every

@@ -48,6 +48,8 @@ TREE_CASES = [
     ("bf16", 128, 12, 8, 8, 5, 64, 5),    # threshold above B: everything private
     ("f32", 64, 10, 2, 1, 3, 2, 6),       # fp32 matrix path
     ("f32", 128, 33, 4, 2, 4, 4, 7),      # fp32, d=128
+    ("bf16", 128, 160, 8, 2, 3, 0, 8),    # automatic batching policy, run by run
+    ("f16", 128, 96, 4, 4, 4, 0, 9),      # automatic, MHA
 ]
 
 
