@@ -241,6 +241,58 @@ def share_sweep(reps: int = 20):
             "d": 128}
 
 
+def other_configs(ev, seed: int, steps: int):
+    """Step time of every other workload shape (cascade) and of the shared-document
+    workload laid out as Parallel Prompting requests (stream decode), hot, inputs
+    resident in HBM.  Effective GB/s = algorithmic bytes / wall time per step."""
+    import torch
+    import workloads
+    import decode_attention_shared_amd as hp
+    out = []
+    for cfg in (workloads.tiny_f32(), workloads.llama3_8b_gqa(), workloads.docqa_codellama7b(),
+                workloads.two_level_gqa()):
+        print(f"[bench] config {cfg.name}", file=sys.stderr, flush=True)
+        st, cl = prepare(cfg, seed)
+        w, ps = time_steps(cl, ev, steps, 5)
+        b = workloads.algorithmic_bytes(cfg, st.seq_lens.tolist())["total"]
+        wms = w / steps * 1e3
+        out.append({"workload": cfg.name, "path": "cascade", "steps_per_s": round(steps / w, 1),
+                    "ms_per_step": round(wms, 4), "algorithmic_bytes": b,
+                    "effective_gbps": round(b / (wms * 1e-3) / 1e9, 1),
+                    "hbm_roofline_frac": round(b / (wms * 1e-3) / 1e9 / HBM_PEAK_GBPS, 4),
+                    "pass_ms": {k: round(mean(ps[k]), 4) for k in ("prefix", "suffix", "merge")}})
+        del cl, st
+        torch.cuda.empty_cache()
+    cfg = workloads.docqa_streams(32)
+    print(f"[bench] config {cfg.name}", file=sys.stderr, flush=True)
+    st = workloads.stream_step(cfg, P=32, seed=seed)
+    dev = "cuda:0"
+    levels = [[(n.k.to(dev), n.v.to(dev), n.seq_begin, n.seq_end) for n in lvl]
+              for lvl in st.levels]
+    call = hp.StreamCall(st.q.to(dev), levels, st.k_pool.to(dev), st.v_pool.to(dev),
+                         st.row_slots.to(dev), st.row_sid.to(dev), st.row_len.to(dev),
+                         st.q_req.to(dev), st.q_sid.to(dev), st.scale)
+    for _ in range(5):
+        call()
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for _ in range(steps):
+        call()
+    torch.cuda.synchronize()
+    w = time.perf_counter() - t0
+    b = workloads.stream_bytes(st)["total"]
+    wms = w / steps * 1e3
+    out.append({"workload": cfg.name, "path": "stream_decode", "steps_per_s": round(steps / w, 1),
+                "ms_per_step": round(wms, 4), "algorithmic_bytes": b,
+                "effective_gbps": round(b / (wms * 1e-3) / 1e9, 1),
+                "hbm_roofline_frac": round(b / (wms * 1e-3) / 1e9 / HBM_PEAK_GBPS, 4),
+                "requests": st.R, "streams_per_request": 32,
+                "row_positions": int(st.row_len.sum())})
+    del call, st
+    torch.cuda.empty_cache()
+    return out
+
+
 def load_traffic(name: str, khash: str):
     path = os.path.join(ROOT, "profiles", "traffic.json")
     if not os.path.exists(path):
@@ -263,6 +315,8 @@ def main():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-seconds", type=float, default=15.0)
     ap.add_argument("--no-sweep", action="store_true")
+    ap.add_argument("--no-configs", action="store_true",
+                    help="skip the other workload shapes and the stream-decode workload")
     ap.add_argument("--sweep-steps", type=int, default=50)
     ap.add_argument("--profile-only", action="store_true",
                     help="only run warmup + timed steps (for rocprofv3); no sweep or CPU leg")
@@ -387,6 +441,8 @@ def main():
             del cl, st
             torch.cuda.empty_cache()
         result["prefix_sweep"] = sweep
+    if not args.profile_only and not args.no_configs:
+        result["configs"] = other_configs(ev, args.seed, args.sweep_steps)
     if not args.profile_only and not args.no_cpu_baseline:
         print("[bench] CPU oracle baseline", file=sys.stderr, flush=True)
         result["cpu_baseline"] = cpu_baseline(step, args.cpu_seconds)

@@ -154,6 +154,7 @@ struct SuffixArgs {
     int64_t seq_tok_off, tok_rows_off, seq_src_off, srcs_off, shared_off;
     int64_t pool_rows;
     const float *part_o, *part_lse;
+    int32_t stage_floats;     // dynamic LDS for staged partials (0: read them from memory)
 };
 
 // Stream selection of a shared-context step: query b (request q_req[b],

@@ -28,10 +28,27 @@ namespace hp {
 
 template <int kDt>
 struct Elem;
+// get: element e of a lane's 16-byte slice, widened to fp32.  dot: the dot
+// product of two such slices in fp32 (16-bit pairs through v_dot2 with fp32
+// accumulation; every product of two 16-bit values is exact in fp32).  The
+// pairs are taken from a whole-vector cast by shuffles: this toolchain
+// miscompiles __builtin_bit_cast of a single vector element (it reads element
+// 0 whatever the index).
+typedef _Float16 sf16x2 __attribute__((ext_vector_type(2)));
+typedef __bf16 sbf16x2 __attribute__((ext_vector_type(2)));
+typedef _Float16 sf16x8 __attribute__((ext_vector_type(8)));
+typedef __bf16 sbf16x8 __attribute__((ext_vector_type(8)));
 template <>
 struct Elem<HP_F32> {
     static constexpr int kSize = 4;
     __device__ static float get(const u32x4 &w, int e) { return __uint_as_float(w[e]); }
+    __device__ static float dot(const u32x4 &a, const u32x4 &b) {
+        const f32x4 x = __builtin_bit_cast(f32x4, a), y = __builtin_bit_cast(f32x4, b);
+        float s = x[0] * y[0];
+        s = fmaf(x[1], y[1], s);
+        s = fmaf(x[2], y[2], s);
+        return fmaf(x[3], y[3], s);
+    }
 };
 template <>
 struct Elem<HP_F16> {
@@ -39,12 +56,38 @@ struct Elem<HP_F16> {
     __device__ static float get(const u32x4 &w, int e) {
         return f16_bits_to_float((w[e >> 1] >> (16 * (e & 1))) & 0xffffu);
     }
+    __device__ static float dot(const u32x4 &a, const u32x4 &b) {
+        const sf16x8 x = __builtin_bit_cast(sf16x8, a), y = __builtin_bit_cast(sf16x8, b);
+        float s0 = __builtin_amdgcn_fdot2(__builtin_shufflevector(x, x, 0, 1),
+                                          __builtin_shufflevector(y, y, 0, 1), 0.f, false);
+        float s1 = __builtin_amdgcn_fdot2(__builtin_shufflevector(x, x, 2, 3),
+                                          __builtin_shufflevector(y, y, 2, 3), 0.f, false);
+        s0 = __builtin_amdgcn_fdot2(__builtin_shufflevector(x, x, 4, 5),
+                                    __builtin_shufflevector(y, y, 4, 5), s0, false);
+        s1 = __builtin_amdgcn_fdot2(__builtin_shufflevector(x, x, 6, 7),
+                                    __builtin_shufflevector(y, y, 6, 7), s1, false);
+        return s0 + s1;
+    }
 };
 template <>
 struct Elem<HP_BF16> {
     static constexpr int kSize = 2;
     __device__ static float get(const u32x4 &w, int e) {
         return bf16_bits_to_float((w[e >> 1] >> (16 * (e & 1))) & 0xffffu);
+    }
+    __device__ static float dot(const u32x4 &a, const u32x4 &b) {
+        const sbf16x8 x = __builtin_bit_cast(sbf16x8, a), y = __builtin_bit_cast(sbf16x8, b);
+        float s0 = __builtin_amdgcn_fdot2_f32_bf16(__builtin_shufflevector(x, x, 0, 1),
+                                                   __builtin_shufflevector(y, y, 0, 1), 0.f,
+                                                   false);
+        float s1 = __builtin_amdgcn_fdot2_f32_bf16(__builtin_shufflevector(x, x, 2, 3),
+                                                   __builtin_shufflevector(y, y, 2, 3), 0.f,
+                                                   false);
+        s0 = __builtin_amdgcn_fdot2_f32_bf16(__builtin_shufflevector(x, x, 4, 5),
+                                             __builtin_shufflevector(y, y, 4, 5), s0, false);
+        s1 = __builtin_amdgcn_fdot2_f32_bf16(__builtin_shufflevector(x, x, 6, 7),
+                                             __builtin_shufflevector(y, y, 6, 7), s1, false);
+        return s0 + s1;
     }
 };
 
@@ -101,15 +144,8 @@ __global__ __launch_bounds__(64 * NWS) void suffix_kernel(SuffixArgs a) {
     const int li = lane % kLpt;  // lane within the token's group
     const int d0 = li * kEpl;
 
-    // The G query rows of this KV head, in fp32.
-    float qf[G][kEpl];
-#pragma unroll
-    for (int j = 0; j < G; ++j) {
-        const u32x4 w = *(const u32x4 *)((const char *)a.q +
-                                         (((int64_t)b * a.Hq + g * G + j) * D + d0) * E::kSize);
-#pragma unroll
-        for (int e = 0; e < kEpl; ++e) qf[j][e] = E::get(w, e);
-    }
+    // The G query rows of this KV head, this lane's 16-byte slice of each.
+    u32x4 qraw[G];
 
     int len = 0;
     bool bad = false;
@@ -141,9 +177,10 @@ __global__ __launch_bounds__(64 * NWS) void suffix_kernel(SuffixArgs a) {
     // latency hides behind the suffix stream and the epilogue reads them
     // from LDS.  Part p holds G rows of D floats and G LSEs; rows whose
     // parts do not fit the stage are read from memory in the epilogue.
-    constexpr int kStageO = G == 1 ? 2048 : 8192;  // floats; a multiple of 4 * kWave
-    constexpr int kCpp = G * D / 4;                 // 16-byte chunks per part
-    __shared__ __attribute__((aligned(16))) float sm_po[kMode == kTree ? 4 : kStageO];
+    // The stage is the launch's dynamic LDS (a.stage_floats floats, sized by
+    // the host for the rows with the most partials; 0 when they do not fit).
+    constexpr int kCpp = G * D / 4;  // 16-byte chunks per part
+    extern __shared__ __attribute__((aligned(16))) float sm_po[];
     __shared__ float sm_pl[kWave];
     int nparts = 0;
     if constexpr (kMode != kTree) {
@@ -151,43 +188,47 @@ __global__ __launch_bounds__(64 * NWS) void suffix_kernel(SuffixArgs a) {
         for (int si = 0; si < a.nsrc; ++si)
             if (b >= a.src[si].b0 && b < a.src[si].b1) nparts += a.src[si].nsplit;
     }
-    const bool staged = kMode != kTree && nparts > 0 && nparts * kCpp * 4 <= kStageO && nparts * G <= kWave;
-    if constexpr (kMode != kTree) {
-        if (staged) {
-            // Locate part p of this row: pointers to its first O float and LSE.
-            auto part = [&](int p, const float *&po, const float *&pl) {
-                po = a.src[0].o;  // replaced below: p < nparts always matches one source
-                pl = a.src[0].lse;
-                int pb = 0;
+    const bool staged = kMode != kTree && nparts > 0 && nparts * G <= kWave &&
+                        (nparts * kCpp + kWave - 1) / kWave * kWave * 4 <= a.stage_floats;
+    // Copies the row's partials into LDS.  The global-to-LDS loads are the
+    // compiler-tracked form, so its waits for later register loads stay exact.
+    auto stage = [&]() {
+        if constexpr (kMode != kTree) {
+            if (!staged) return;
+            // Lane p < nparts holds the base pointers of part p (uniform walk
+            // over the sources); each transfer picks its part's base by shuffle.
+            const float *pbo = a.src[0].o, *pbl = a.src[0].lse;
+            int pb = 0;
 #pragma unroll 1
-                for (int si = 0; si < a.nsrc; ++si) {
-                    const MergeSrc &sr = a.src[si];
-                    if (b < sr.b0 || b >= sr.b1) continue;
-                    const int i = p - pb;
-                    if (i >= 0 && i < sr.nsplit) {
-                        const int64_t ri = (b - sr.b0) * a.Hq + (int64_t)g * G;
-                        po = sr.o + (int64_t)i * sr.o_split + ri * D;
-                        pl = sr.lse + (int64_t)i * sr.lse_split + ri;
-                    }
-                    pb += sr.nsplit;
+            for (int si = 0; si < a.nsrc; ++si) {
+                const MergeSrc &sr = a.src[si];
+                if (b < sr.b0 || b >= sr.b1) continue;
+                const int i = lane - pb;
+                if (i >= 0 && i < sr.nsplit) {
+                    const int64_t ri = (b - sr.b0) * a.Hq + (int64_t)g * G;
+                    pbo = sr.o + (int64_t)i * sr.o_split + ri * D;
+                    pbl = sr.lse + (int64_t)i * sr.lse_split + ri;
                 }
-            };
+                pb += sr.nsplit;
+            }
             const int chunks = nparts * kCpp;
 #pragma unroll 1
             for (int c0 = wave * kWave; c0 < chunks; c0 += NWS * kWave) {
                 const int c = min(c0 + lane, chunks - 1);  // lanes past the end re-read the last chunk
-                const float *po, *pl;
-                part(c / kCpp, po, pl);
-                lds_dma<16>(po + (c % kCpp) * 4, &sm_po[c0 * 4]);
+                const float *po = (const float *)__shfl((long long)(intptr_t)pbo, c / kCpp, kWave);
+                __builtin_amdgcn_global_load_lds(
+                    (const __attribute__((address_space(1))) void *)(po + (c % kCpp) * 4),
+                    (__attribute__((address_space(3))) void *)&sm_po[c0 * 4], 16, 0, 0);
             }
             if (wave == 0) {
                 const int e = min(lane, nparts * G - 1);
-                const float *po, *pl;
-                part(e / G, po, pl);
-                lds_dma<4>(pl + e % G, sm_pl);
+                const float *pl = (const float *)__shfl((long long)(intptr_t)pbl, e / G, kWave);
+                __builtin_amdgcn_global_load_lds(
+                    (const __attribute__((address_space(1))) void *)(pl + e % G),
+                    (__attribute__((address_space(3))) void *)sm_pl, 4, 0, 0);
             }
         }
-    }
+    };
 
     float m[G], l[G], acc[G][kEpl];
 #pragma unroll
@@ -262,16 +303,10 @@ __global__ __launch_bounds__(64 * NWS) void suffix_kernel(SuffixArgs a) {
         float x[kPasses][G];
 #pragma unroll
         for (int p = 0; p < kPasses; ++p) {
-            float kf[kEpl];
-#pragma unroll
-            for (int e = 0; e < kEpl; ++e) kf[e] = E::get(kr[p], e);
             const bool ok = p * kTpp + tg < valid;
 #pragma unroll
             for (int j = 0; j < G; ++j) {
-                float dot = 0.f;
-#pragma unroll
-                for (int e = 0; e < kEpl; ++e) dot = fmaf(qf[j][e], kf[e], dot);
-                dot = group_sum<kLpt>(dot);
+                const float dot = group_sum<kLpt>(E::dot(kr[p], qraw[j]));
                 x[p][j] = ok ? dot * a.scale_log2 : -INFINITY;
             }
         }
@@ -304,7 +339,12 @@ __global__ __launch_bounds__(64 * NWS) void suffix_kernel(SuffixArgs a) {
         int n0 = 0, n1 = 0;
         int blk = wave;
         Ref id0 = table_id(blk), id1 = table_id(blk + NWS);
+#pragma unroll
+        for (int j = 0; j < G; ++j)
+            qraw[j] = *(const u32x4 *)((const char *)a.q +
+                                       (((int64_t)b * a.Hq + g * G + j) * D + d0) * E::kSize);
         if (blk < nblk) fetch(blk, id0, k0, v0, n0);
+        stage();
 #pragma unroll 1
         for (; blk < nblk; blk += 2 * NWS) {
             const int b1 = blk + NWS, b2 = blk + 2 * NWS, b3 = blk + 3 * NWS;
@@ -335,7 +375,6 @@ __global__ __launch_bounds__(64 * NWS) void suffix_kernel(SuffixArgs a) {
     // of the wave marks it.
     const bool wave_bad = __any(bad);
     if (lane == 0) sm_bad[wave] = wave_bad ? 1 : 0;
-    if (staged) wait_vmcnt<0>();  // this wave's partial DMAs have landed (the barrier publishes them)
     __syncthreads();
 
     // Final merge: this row's suffix (the waves' states) and every prefix
@@ -464,11 +503,12 @@ __global__ __launch_bounds__(64 * NWS) void suffix_kernel(SuffixArgs a) {
 template <int kDt, int D, int NWS, int kMode>
 static void launch_g(const SuffixArgs &a, int G, dim3 grid, hipStream_t s) {
     constexpr int T = 64 * NWS;
+    const size_t lds = (size_t)a.stage_floats * sizeof(float);
     switch (G) {
-    case 1: suffix_kernel<kDt, D, 1, NWS, kMode><<<grid, T, 0, s>>>(a); break;
-    case 2: suffix_kernel<kDt, D, 2, NWS, kMode><<<grid, T, 0, s>>>(a); break;
-    case 4: suffix_kernel<kDt, D, 4, NWS, kMode><<<grid, T, 0, s>>>(a); break;
-    default: suffix_kernel<kDt, D, 8, NWS, kMode><<<grid, T, 0, s>>>(a); break;
+    case 1: suffix_kernel<kDt, D, 1, NWS, kMode><<<grid, T, lds, s>>>(a); break;
+    case 2: suffix_kernel<kDt, D, 2, NWS, kMode><<<grid, T, lds, s>>>(a); break;
+    case 4: suffix_kernel<kDt, D, 4, NWS, kMode><<<grid, T, lds, s>>>(a); break;
+    default: suffix_kernel<kDt, D, 8, NWS, kMode><<<grid, T, lds, s>>>(a); break;
     }
 }
 
