@@ -34,9 +34,10 @@ constexpr int kTileKeys = 64;           // keys per prefix tile (matches the ker
 constexpr int kCUs = 256;               // MI355X compute units
 constexpr int kWavesPerCU = 8;          // two waves per SIMD at the prefix kernels' register use
 // Cost of one byte of split partials (written once, read once by the merge),
-// in units of one tile of prefix work per resident workgroup (~1 us at
-// ~5 TB/s effective): used to trade scheduling rounds against partial traffic.
-constexpr double kPartialByteCost = 2e-7;
+// in units of one 64-key tile of prefix work per resident workgroup (about
+// 2.5 us on MI355X; a byte at ~5 TB/s effective is 2e-13 s): used to trade
+// scheduling rounds against partial traffic.
+constexpr double kPartialByteCost = 8e-8;
 constexpr size_t kWsAlign = 256;
 
 inline size_t round_up(size_t x, size_t a) { return (x + a - 1) / a * a; }

@@ -362,16 +362,17 @@ __device__ __forceinline__ void mfma16_body(const PrefixArgs &args, const WgTask
     const float c = args.scale_log2;
 
     // Q as the B operand of S^T = K Q^T: lane holds 8 consecutive dims per k-step.
+    // Loaded once the first tiles' transfers are issued (below), then waited for
+    // together with them: the compiler does not count the transfers, so a wait
+    // for Q inside the tile loop would drain every transfer in flight.
     u32x4 qf[kDSteps];
-    {
-        const uint16_t *qp = (const uint16_t *)args.q + ((int64_t)b * args.Hq + h) * D + hi * 8;
+    const uint16_t *qp = (const uint16_t *)args.q + ((int64_t)b * args.Hq + h) * D + hi * 8;
+    auto load_q = [&]() {
 #pragma unroll
         for (int kk = 0; kk < kDSteps; ++kk)
             qf[kk] = row_ok ? *(const u32x4 *)(qp + kk * 16) : u32x4{0, 0, 0, 0};
-    }
-    // Q must be in registers before the first transfer: the compiler does not
-    // count the transfers, and would otherwise wait for all of them to retire.
-    wait_vmcnt<0>();
+        wait_vmcnt<0>();
+    };
 
     f32x16 oacc[kDBlocks];
 #pragma unroll
@@ -497,6 +498,7 @@ __device__ __forceinline__ void mfma16_body(const PrefixArgs &args, const WgTask
 #pragma unroll
         for (int k = 0; k < kStages - 1; ++k)
             if (tb + k < te) issue(tb + k);
+        load_q();  // also lands the prologue tiles
         const int younger = min(kStages - 2, te - tb - 1);
         if constexpr (kStages >= 4) {
             if (younger >= 2) wait_vmcnt<2 * kPerTile>();
@@ -590,16 +592,10 @@ __device__ __forceinline__ void pp_body(const PrefixArgs &args, const WgTask &ta
     const int h = task.g * G + (row_ok ? row % G : 0);
     const float c = args.scale_log2;
 
+    // Q (B operand of the score product), loaded after the first two tiles'
+    // transfers are issued and waited for with them (see the 32-row body).
     u32x4 qf[kDSteps];
-    {
-        const uint16_t *qp = (const uint16_t *)args.q + ((int64_t)b * args.Hq + h) * D + hi * 8;
-#pragma unroll
-        for (int kk = 0; kk < kDSteps; ++kk)
-            qf[kk] = row_ok ? *(const u32x4 *)(qp + kk * 16) : u32x4{0, 0, 0, 0};
-    }
-    // Q must be in registers before the first transfer: the compiler does not
-    // count the transfers, and would otherwise wait for all of them to retire.
-    wait_vmcnt<0>();
+    const uint16_t *qp = (const uint16_t *)args.q + ((int64_t)b * args.Hq + h) * D + hi * 8;
     f32x16 oacc[kDBlocks];
 #pragma unroll
     for (int db = 0; db < kDBlocks; ++db) oacc[db] = f32x16{};
@@ -729,6 +725,10 @@ __device__ __forceinline__ void pp_body(const PrefixArgs &args, const WgTask &ta
     if (T > 0) {
         issue(tb);
         if (T > 1) issue(tb + 1);
+#pragma unroll
+        for (int kk = 0; kk < kDSteps; ++kk)
+            qf[kk] = row_ok ? *(const u32x4 *)(qp + kk * 16) : u32x4{0, 0, 0, 0};
+        wait_vmcnt<0>();  // Q and the first two tiles
 #pragma unroll 1
         for (int u = 0; u <= T; ++u) {
             // this wave's part of tile u has landed (tile u+1 may be in flight)
