@@ -5,6 +5,8 @@ max-abs 1e-2, mean-abs 1e-3, LSE max-abs 1e-3.  Block-table indexing is checked
 bit-exactly with needles (one key scores 0, every other key scores about -1450,
 so softmax puts weight exactly 1 on it and O must equal that key's value row).
 """
+import ctypes
+
 import numpy as np
 import pytest
 import torch
@@ -362,3 +364,72 @@ def test_cascade_full_size_sampled(cfg):
     ref_o, ref_l = oracle.step_attention(step, "all", rows=rows)
     compare(out, lse, ref_o, ref_l, cfg.dtype, cfg.name, rows=rows)
     assert torch.isfinite(out).all() and torch.isfinite(lse).all()
+
+
+# ------------------------------------------------------------------ graph capture, timed entry
+
+def test_cascade_graph_replay_matches_eager():
+    """The whole step captured into a HIP graph: every replay, with eager work and
+    synchronisations between replays and changed suffix lengths before one of them,
+    equals the eager call on the same inputs."""
+    cfg = REDUCED[4]
+    step = workloads.generate(cfg, seed=11)
+    ds = dev_step(step)
+    call = hp.CascadeCall(ds["q"], ds["levels"], ds["k_pool"], ds["v_pool"], ds["block_table"],
+                          ds["seq_lens"], step.scale)
+    s = torch.cuda.Stream()
+    with torch.cuda.stream(s):
+        call(stream=s)
+        torch.cuda.synchronize()
+        eager_o, eager_l = call.out.clone(), call.lse.clone()
+        g = torch.cuda.CUDAGraph()
+        g.capture_begin()
+        call(stream=s)
+        g.capture_end()
+    for rep in range(4):
+        call.out.fill_(3.0)
+        call.lse.fill_(3.0)
+        torch.cuda.synchronize()
+        g.replay()
+        torch.cuda.synchronize()
+        assert torch.equal(call.out, eager_o) and torch.equal(call.lse, eager_l), f"replay {rep}"
+    # lengths live in device memory: shortening them changes the replayed step
+    new_lens = (step.seq_lens // 2).to(torch.int32)
+    ds["seq_lens"].copy_(new_lens.to(DEV))
+    torch.cuda.synchronize()
+    g.replay()
+    torch.cuda.synchronize()
+    segs = []
+    for b in range(cfg.B):
+        k, v = step.suffix(b)
+        n = int(new_lens[b])
+        segs.append([(nd.k, nd.v) for nd in step.nodes_of(b)] + [(k[:n], v[:n])])
+    ref_o, ref_l = oracle.attention(step.q, segs, cfg.Hkv, step.scale)
+    compare(call.out, call.lse, ref_o, ref_l, cfg.dtype, "replay with new lengths")
+
+
+def test_cascade_timed_records_events_and_matches():
+    cfg = REDUCED[2]
+    step = workloads.generate(cfg, seed=12)
+    ds = dev_step(step)
+    call = hp.CascadeCall(ds["q"], ds["levels"], ds["k_pool"], ds["v_pool"], ds["block_table"],
+                          ds["seq_lens"], step.scale)
+    o1, l1 = [t.clone() for t in call()]
+    torch.cuda.synchronize()
+    rt = ctypes.CDLL("libamdhip64.so")
+    raw = []
+    for _ in range(4):
+        h = ctypes.c_void_p()
+        assert rt.hipEventCreate(ctypes.byref(h)) == 0
+        raw.append(h.value)
+    o2, l2 = call.timed(raw)
+    torch.cuda.synchronize()
+    assert torch.equal(o1, o2) and torch.equal(l1, l2)
+    ms = []
+    for a, b in zip(raw[:-1], raw[1:]):
+        t = ctypes.c_float()
+        assert rt.hipEventElapsedTime(ctypes.byref(t), ctypes.c_void_p(a), ctypes.c_void_p(b)) == 0
+        ms.append(t.value)
+    assert all(m >= 0 for m in ms) and ms[0] > 0, ms
+    for h in raw:
+        rt.hipEventDestroy(ctypes.c_void_p(h))
