@@ -285,7 +285,7 @@ SuffixArgs suffix_args(const hp_query &q, const hp_paged_kv &kv, RowDest dest) {
 // Plan of a whole cascade step (shared by the size query and the run).
 struct CascadePlan {
     int total_nodes = 0;
-    int num_levels = 0;
+    int num_levels = 0;  // launch groups: tree levels, or one group holding every node
     LevelPlan levels[HP_MAX_LEVELS];
     bool has_suffix = false;
     size_t node_off[HP_MAX_NODES];
@@ -304,11 +304,29 @@ hp_status plan_cascade(const hp_query *q, const hp_prefix_tree *tree, const hp_p
     }
     size_t off = 0;
     int idx = 0;
-    cp.num_levels = tree ? tree->num_levels : 0;
+    const int levels = tree ? tree->num_levels : 0;
+    // The levels' prefix passes are independent (only the merge needs them
+    // all): launch every node together when their stacked row counts call
+    // for row blocks within a factor of two of each other, so one launch
+    // fills the GPU instead of one per level (each with its own pipeline
+    // fill and partial write-out); otherwise one launch per level.
+    bool joint = levels > 1 && cp.total_nodes <= kMaxLaunchNodes;
+    if (joint) {
+        const int G = q->Hq / q->Hkv;
+        int nw_max = 1, nw_min = 8;
+        for (int i = 0; i < cp.total_nodes; ++i) {
+            const hp_prefix_node &n = tree->nodes[i];
+            const int nw = choose_nw((int64_t)(n.seq_end - n.seq_begin) * G);
+            nw_max = std::max(nw_max, nw);
+            nw_min = std::min(nw_min, nw);
+        }
+        joint = nw_min * 2 >= nw_max;
+    }
+    cp.num_levels = joint ? 1 : levels;  // launch groups
     for (int l = 0; l < cp.num_levels; ++l) {
         LevelPlan &lp = cp.levels[l];
         lp.first = idx;
-        plan_level(*q, tree->nodes + idx, tree->nodes_per_level[l], lp);
+        plan_level(*q, tree->nodes + idx, joint ? cp.total_nodes : tree->nodes_per_level[l], lp);
         for (int i = 0; i < lp.count; ++i) {
             cp.node_off[idx + i] = off;
             off += node_ws_bytes(lp.nodes[i], q->d);
