@@ -160,6 +160,17 @@ __device__ __forceinline__ ChunkTiles load_pieces(const PrefixArgs &args, int pi
     return src;
 }
 
+// Max of x over this lane and the lane 32 apart (the other half-wave), with
+// gfx950's v_permlane32_swap: the exchange stays in the vector ALU instead of
+// queueing on the LDS crossbar (as ds_bpermute would) behind the operand
+// reads of the other waves.  The two results hold x of lane l and of lane
+// l ^ 32 in some order, so their max is the same on both halves.
+__device__ __forceinline__ float max_across_halves(float x) {
+    const unsigned u = __builtin_bit_cast(unsigned, x);
+    const auto r = __builtin_amdgcn_permlane32_swap(u, u, false, false);
+    return fmaxf(__builtin_bit_cast(float, (unsigned)r[0]), __builtin_bit_cast(float, (unsigned)r[1]));
+}
+
 // Online-softmax update for one 64-key tile held as two 32x32 score blocks.
 // x0/x1 hold scores already scaled to the exp2 domain (masked keys = -inf).
 // Returns alpha (the rescale factor of the old state) and leaves p in x.
@@ -167,7 +178,7 @@ __device__ __forceinline__ float softmax_tile(float (&x)[32], float &m_run, floa
     float mt = x[0];
 #pragma unroll
     for (int i = 1; i < 32; ++i) mt = fmaxf(mt, x[i]);
-    mt = fmaxf(mt, __shfl_xor(mt, 32, kWave));  // the other half-wave holds the other keys of this query
+    mt = max_across_halves(mt);  // the other half-wave holds the other keys of this query
     const float m_new = fmaxf(m_run, mt);
     const float alpha = fast_exp2(m_run - m_new);  // 0 on the first tile (m_run = -inf)
     float sum = 0.f;
@@ -266,7 +277,7 @@ __device__ __forceinline__ bool softmax_max(const f32x16 &s0, const f32x16 &s1, 
                                                   __builtin_elementwise_maximum(s0[i], s1[i]));
     float mt = __builtin_elementwise_maximum(__builtin_elementwise_maximum(mq[0], mq[1]),
                                              __builtin_elementwise_maximum(mq[2], mq[3]));
-    mt = fmaxf(mt, __shfl_xor(mt, 32, kWave));  // the other half-wave: the other keys of this query
+    mt = max_across_halves(mt);  // the other half-wave: the other keys of this query
     const float mts = mt * c;  // c > 0: the max commutes with the scaling
     const bool rescale = __any(mts > m_run + kLazy);
     alpha = 1.f;
@@ -696,12 +707,68 @@ __device__ __forceinline__ void pp_body(const PrefixArgs &args, const WgTask &ta
         __builtin_amdgcn_sched_group_barrier(0x100, 2 * kDBlocks, 0);  // reads of step 3
         __builtin_amdgcn_sched_group_barrier(0x008, 2 * kDBlocks, 0);  // products of steps 2, 3
     };
-    const int T = te - tb;
-    // Matrix phase of step u: S(u) and O += V(u-1) P(u-1).
-    auto mphase = [&](int u) {
-        if (u < T) qk(u % kStages);
-        if (u >= 1) pv((u - 1) % kStages);
+    // K operands of this wave's next matrix phase: the first kPre k-steps are
+    // read during its vector phase (LDS reads take no vector-ALU issue slots,
+    // so their latency hides behind the softmax and the score products start
+    // with operands in hand), the rest at the start of the matrix phase,
+    // behind the first products.  Prefetching all of them would not fit in
+    // the registers beside the softmax.
+    constexpr int kPre = kDSteps / 4;
+    u32x4 kpre[kDSteps][2];
+    auto load_k_steps = [&](int st, int k0, int k1) {
+        const uint16_t *kb = &lds[st][0][n * D];
+#pragma unroll
+        for (int kk = k0; kk < k1; ++kk) {
+            const int col = ((2 * kk + hi) ^ k_swz) * 8;
+            kpre[kk][0] = *(const u32x4 *)&kb[col];
+            kpre[kk][1] = *(const u32x4 *)&kb[32 * D + col];
+        }
     };
+    auto load_k = [&](int st) { load_k_steps(st, 0, kPre); };
+    int kst = 0;  // stage of the tile whose K is (partly) prefetched
+    auto qk_pre = [&]() {
+        load_k_steps(kst, kPre, kDSteps);
+        s0 = f32x16{};
+        s1 = f32x16{};
+#pragma unroll
+        for (int kk = 0; kk < kDSteps; ++kk) {
+            s0 = mfma32x32x16<kBf16>(kpre[kk][0], qf[kk], s0);
+            s1 = mfma32x32x16<kBf16>(kpre[kk][1], qf[kk], s1);
+        }
+    };
+    // Both products of one matrix phase: the V operands (transposing reads,
+    // slower than 16-byte ones) are read while the score products run, a
+    // quarter after each pair of them, into the registers the consumed K
+    // operands free; the value product then starts with its operands in hand.
+    auto qkpv_pre = [&](int stv) {
+        const uint16_t *vb = &lds[stv][1][0];
+        u32x4 va[4][kDBlocks];
+#pragma unroll
+        for (int u = 0; u < 4; ++u)
+#pragma unroll
+            for (int db = 0; db < kDBlocks; ++db) {
+                const uint16_t *vr = vb + 16 * u * D + v_col[db];
+                const u32x2 lo = lds_read_tr16(vr);
+                const u32x2 up = lds_read_tr16(vr + 8 * D);
+                va[u][db] = u32x4{lo.x, lo.y, up.x, up.y};
+            }
+        qk_pre();
+#pragma unroll
+        for (int u = 0; u < 4; ++u) {
+            const u32x4 bop = {pk[4 * u], pk[4 * u + 1], pk[4 * u + 2], pk[4 * u + 3]};
+#pragma unroll
+            for (int db = 0; db < kDBlocks; ++db) oacc[db] = mfma32x32x16<kBf16>(va[u][db], bop, oacc[db]);
+        }
+        constexpr int kVReadsPerPair = 8 * kDBlocks / kDSteps;
+        static_assert(kVReadsPerPair * kDSteps == 8 * kDBlocks, "V reads spread over the pairs");
+#pragma unroll
+        for (int kk = 0; kk < kDSteps; ++kk) {
+            __builtin_amdgcn_sched_group_barrier(0x008, 2, 0);               // two score products
+            __builtin_amdgcn_sched_group_barrier(0x100, kVReadsPerPair, 0);  // a share of V
+        }
+        __builtin_amdgcn_sched_group_barrier(0x008, 4 * kDBlocks, 0);  // the value products
+    };
+    const int T = te - tb;
     // Vector phase: online softmax of tile u (scores in s0/s1) into pk.  O
     // already holds every earlier tile, so a rescale applies to all of it.
     auto vphase = [&](int u) {
@@ -729,22 +796,42 @@ __device__ __forceinline__ void pp_body(const PrefixArgs &args, const WgTask &ta
         for (int kk = 0; kk < kDSteps; ++kk)
             qf[kk] = row_ok ? *(const u32x4 *)(qp + kk * 16) : u32x4{0, 0, 0, 0};
         wait_vmcnt<0>();  // Q and the first two tiles
-#pragma unroll 1
-        for (int u = 0; u <= T; ++u) {
-            // this wave's part of tile u has landed (tile u+1 may be in flight)
-            if (u + 1 < T) wait_vmcnt<kPerTile>();
-            else wait_vmcnt<0>();
-            block_sync();
+        block_sync();
+        if (grp == 0) load_k(0);  // kst = 0
+        // Vector phase of tile x with the K prefetch of tile x + 1.
+        auto vp = [&](int x) {
+            if (x + 1 < T) {
+                kst = (x + 1) % kStages;
+                load_k(kst);
+            }
+            if (x >= 0 && x < T) vphase(x);
+        };
+        // Step u: group 0 takes the matrix phase of u (S(u), O += V(u-1)
+        // P(u-1)) then the vector phase of u; group 1 the vector phase of u-1
+        // then the matrix phase of u.  Tile u+1 is waited for at the middle
+        // barrier, since its K operands are read in the second half.  Tile
+        // u+2 goes into the stage of tile u-2, whose last reads (K prefetches
+        // in the step before last, the value products in the last step) are
+        // behind the step's first barrier.  The first and last steps (a lone
+        // score or value product) are peeled off so that the loop body holds
+        // only the fused phase.
+        auto step = [&](int u, auto &&mphase) {
+            if (u > 0) block_sync();
             if (u + 2 < T) issue(tb + u + 2);
             if (grp == 0) mphase(u);
-            else if (u >= 1) vphase(u - 1);
-            block_sync();
-            if (grp == 0) {
-                if (u < T) vphase(u);
-            } else {
-                mphase(u);
+            else vp(u - 1);
+            if (u + 1 < T) {
+                if (u + 2 < T) wait_vmcnt<kPerTile>();
+                else wait_vmcnt<0>();
             }
-        }
+            block_sync();
+            if (grp == 0) vp(u);
+            else mphase(u);
+        };
+        step(0, [&](int) { qk_pre(); });
+#pragma unroll 1
+        for (int u = 1; u < T; ++u) step(u, [&](int w) { qkpv_pre((w - 1) % kStages); });
+        step(T, [&](int w) { pv((w - 1) % kStages); });
     }
 
     if (row_ok) {
