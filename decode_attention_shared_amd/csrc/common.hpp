@@ -267,6 +267,20 @@ __device__ __forceinline__ void lds_dma(const void *g, void *lds_base) {
 }
 __device__ __forceinline__ void dma16(const void *g, void *lds_base) { lds_dma<16>(g, lds_base); }
 
+// The same 16-byte transfer with every wave-uniform part in scalar
+// registers: the global base, and the LDS destination as an LDS byte address
+// (M0); only the per-lane unsigned 32-bit byte offset is a vector register.
+// No vector instruction is needed to issue it.
+__device__ __forceinline__ void dma16_s(const void *base, uint32_t byte_off, uint32_t lds_addr) {
+    uint32_t saved;
+    asm volatile(
+        "s_mov_b32 %0, m0\n\ts_mov_b32 m0, %3\n\tglobal_load_lds_dwordx4 %1, %2\n\t"
+        "s_mov_b32 m0, %0"
+        : "=&s"(saved)
+        : "v"(byte_off), "s"(base), "s"(lds_addr)
+        : "memory");
+}
+
 // s_waitcnt with only vmcnt = n (expcnt and lgkmcnt left unconstrained).
 template <int n>
 __device__ __forceinline__ void wait_vmcnt() {

@@ -622,35 +622,51 @@ __device__ __forceinline__ void pp_body(const PrefixArgs &args, const WgTask &ta
     // (the launch picks this kernel only when kTile * stride_tok + d fits in
     // int32); per tile only a wave-uniform tile offset is added.
     int dma_row[kDmas];
-    uint32_t koff[kDmas], voff[kDmas];
+    uint32_t koff[kDmas], voff[kDmas];  // bytes
 #pragma unroll
     for (int j = 0; j < kDmas; ++j) {
         const int r = (wave * kDmas + j) * kRowsPerDma + lane / kRowChunks;
         const int pos = lane % kRowChunks;
         dma_row[j] = r;
-        koff[j] = (uint32_t)(r * stride_tok) + (pos ^ (r % kRowChunks)) * 8;
-        voff[j] = (uint32_t)(r * stride_tok) + (pos ^ v_swizzle<D>(r)) * 8;
+        koff[j] = 2u * ((uint32_t)(r * stride_tok) + (pos ^ (r % kRowChunks)) * 8);
+        voff[j] = 2u * ((uint32_t)(r * stride_tok) + (pos ^ v_swizzle<D>(r)) * 8);
     }
+    // The transfers are issued with scalar instructions only: the wave index
+    // and the LDS destinations live in scalar registers (the vector ALU is
+    // held by the other group's matrix products while this runs).
+    const int wave_s = __builtin_amdgcn_readfirstlane(wave);
+    const uint32_t lds0 =
+        (uint32_t)(uintptr_t)(__attribute__((address_space(3))) uint16_t *)&lds[0][0][0];
     auto issue = [&](int tile) {
         const int st = (tile - tb) % kStages;
-        const int key0 = src.key0(tile);
-        const int valid = src.valid(tile);
+        const int key0 = __builtin_amdgcn_readfirstlane(src.key0(tile));
+        const int valid = __builtin_amdgcn_readfirstlane(src.valid(tile));  // a scalar branch
         const int64_t tile_off = (int64_t)key0 * stride_tok;
         const uint16_t *kt = kbase + tile_off;
         const uint16_t *vt = vbase + tile_off;
-        const bool full = valid >= kTile;
+        const uint32_t kdst = lds0 + 2u * (uint32_t)(st * 2 * kTileElems +
+                                                     wave_s * kDmas * kRowsPerDma * D);
+        const uint32_t vdst = kdst + 2u * kTileElems;
+        // element offsets below kTile * stride_tok + d < 2^31: the byte offsets fit
+        if (valid >= kTile) {
 #pragma unroll
-        for (int j = 0; j < kDmas; ++j) {
-            uint16_t *dst = &lds[st][0][(wave * kDmas + j) * kRowsPerDma * D];
-            uint32_t ko = koff[j], vo = voff[j];
-            if (!full && dma_row[j] >= valid) {
-                // keys past the tile's end re-read its last key (masked to -inf)
-                const uint32_t back = (uint32_t)((dma_row[j] - (valid - 1)) * stride_tok);
-                ko -= back;
-                vo -= back;
+            for (int j = 0; j < kDmas; ++j) {
+                dma16_s(kt, koff[j], kdst + 2u * j * kRowsPerDma * D);
+                dma16_s(vt, voff[j], vdst + 2u * j * kRowsPerDma * D);
             }
-            dma16(kt + ko, dst);
-            dma16(vt + vo, dst + kTileElems);
+        } else {
+#pragma unroll
+            for (int j = 0; j < kDmas; ++j) {
+                uint32_t ko = koff[j], vo = voff[j];
+                if (dma_row[j] >= valid) {
+                    // keys past the tile's end re-read its last key (masked to -inf)
+                    const uint32_t back = 2u * (uint32_t)((dma_row[j] - (valid - 1)) * stride_tok);
+                    ko -= back;
+                    vo -= back;
+                }
+                dma16_s(kt, ko, kdst + 2u * j * kRowsPerDma * D);
+                dma16_s(vt, vo, vdst + 2u * j * kRowsPerDma * D);
+            }
         }
     };
     const int k_swz = n % kRowChunks;
