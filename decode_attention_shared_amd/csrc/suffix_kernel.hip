@@ -150,10 +150,12 @@ __global__ __launch_bounds__(64 * NWS) void suffix_kernel(SuffixArgs a) {
     int len = 0;
     bool bad = false;
     const int *trow;
+    int row_cap = a.max_blocks;  // entries of this sequence's table row
     if constexpr (kMode == kTree) {
         const int tok0 = a.tree[a.seq_tok_off + b];
         const int cap = a.tree[a.seq_tok_off + b + 1] - tok0;
         trow = a.tree + a.tok_rows_off + tok0;
+        row_cap = cap;
         len = cap;
         if (a.lens != nullptr) {
             len = a.lens[b] - a.tree[a.shared_off + b];
@@ -246,7 +248,10 @@ __global__ __launch_bounds__(64 * NWS) void suffix_kernel(SuffixArgs a) {
     // Where a block's keys are: its block id (block table), or in chunk-tree
     // mode the pool row of each token this lane loads.  Read one block-step
     // ahead of the K/V loads, so the lookup's latency never sits in front of
-    // a block's loads.
+    // a block's loads.  The lookup is bounded by the row's capacity, not by
+    // the sequence length, so the first ones go out together with the length
+    // read instead of after it; entries past the length are never used (only
+    // blocks below nblk are fetched, and their ids are checked there).
     struct Ref {
         int v[kRows ? kPasses : 1];
     };
@@ -256,10 +261,10 @@ __global__ __launch_bounds__(64 * NWS) void suffix_kernel(SuffixArgs a) {
 #pragma unroll
             for (int p = 0; p < kPasses; ++p) {
                 const int t = blk * kBlock + p * kTpp + tg;
-                r.v[p] = blk < nblk && t < len ? trow[t] : 0;  // nblk = 0 when len is bad
+                r.v[p] = t < row_cap ? trow[t] : 0;
             }
         } else {
-            r.v[0] = blk < nblk ? trow[blk] : 0;
+            r.v[0] = blk < row_cap ? trow[blk] : 0;
         }
         return r;
     };
