@@ -42,6 +42,8 @@ PREFIX_CASES = [
     ("bf16", 128, 32, 4, 4, 64, 0, 32),       # exactly one tile of keys
     ("f16", 128, 100, 1, 1, 3000, 0, 100),    # 100 rows, one head
     ("bf16", 128, 130, 8, 1, 700, 0, 130),    # MQA-like group of 8: 1040 rows, 5 row blocks
+    ("f16", 64, 150, 2, 1, 900, 0, 150),      # d=64 in the 256-row kernel: 300 rows, ragged tile
+    ("bf16", 64, 140, 1, 1, 1111, 3, 140),    # d=64, 137 rows from sequence 3 on, ragged tile
     ("f32", 64, 4, 1, 1, 512, 0, 4),          # the tiny fp32 shape
     ("f32", 128, 9, 4, 2, 777, 0, 9),         # fp32, d=128, GQA
     ("f32", 64, 70, 2, 1, 300, 5, 70),        # fp32, 130 rows
