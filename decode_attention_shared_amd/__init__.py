@@ -47,6 +47,7 @@ EXPORTS = ["hp_prefix_attn_workspace_size", "hp_prefix_attn", "hp_suffix_decode_
            "hp_tree_plan_build", "hp_share_decision", "hp_tree_step", "hp_kv_append",
            "hp_pakv_create", "hp_pakv_destroy", "hp_pakv_insert", "hp_pakv_append",
            "hp_pakv_remove", "hp_pakv_context", "hp_pakv_seq_rows", "hp_pakv_get_stats",
+           "hp_set_concurrency", "hp_cascade_concurrent",
            "hp_status_string", "hp_last_hip_error", "hp_version"]
 
 _DTYPE = {torch.float32: HP_F32, torch.float16: HP_F16, torch.bfloat16: HP_BF16}
@@ -163,6 +164,12 @@ def lib():
                                                     ctypes.POINTER(PrefixTree),
                                                     ctypes.POINTER(PagedKV),
                                                     ctypes.POINTER(ctypes.c_size_t)]
+            L.hp_set_concurrency.restype = st
+            L.hp_set_concurrency.argtypes = [ctypes.c_int32]
+            L.hp_cascade_concurrent.restype = st
+            L.hp_cascade_concurrent.argtypes = [ctypes.POINTER(Query), ctypes.POINTER(PrefixTree),
+                                                ctypes.POINTER(PagedKV),
+                                                ctypes.POINTER(ctypes.c_int32)]
             L.hp_cascade_step.restype = st
             L.hp_cascade_step.argtypes = [ctypes.POINTER(Query), ctypes.POINTER(PrefixTree),
                                           ctypes.POINTER(PagedKV), p, p, p, ctypes.c_size_t, p]
@@ -381,6 +388,10 @@ class CascadeCall:
                                            ctypes.byref(nbytes)), "hp_cascade_workspace_size")
         self.workspace_bytes = nbytes.value
         self.ws = _workspace(nbytes.value, q.device)
+        flag = ctypes.c_int32(0)
+        _check(L.hp_cascade_concurrent(ctypes.byref(self.query), self._tree_p, self._kv_p,
+                                       ctypes.byref(flag)), "hp_cascade_concurrent")
+        self.concurrent = bool(flag.value)  # suffix pass beside the prefix pass
         self._refs = (levels, k_pool, v_pool, block_table, seq_lens)
 
     def __call__(self, stream=None):
@@ -502,6 +513,14 @@ def tree_plan_build(B: int, Hq: int, Hkv: int, d: int, dtype: torch.dtype, descs
                                 pool_rows, blob.data_ptr(), blob.numel(), ctypes.byref(plan)),
            "hp_tree_plan_build")
     return plan, blob
+
+
+def set_concurrency(mode: int) -> None:
+    """Policy for running a cascade step's suffix pass beside its prefix pass
+    (hp_set_concurrency): 0 never, 1 when the plan expects a gain (the default),
+    2 whenever there is a suffix.  Build CascadeCall objects after changing it (the
+    workspace size depends on it)."""
+    _check(lib().hp_set_concurrency(int(mode)), "hp_set_concurrency")
 
 
 def share_decision(Hq: int, Hkv: int, tokens: int, nseq: int, d: int = 128,

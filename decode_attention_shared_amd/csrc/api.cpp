@@ -6,6 +6,8 @@
 #include <hip/hip_runtime.h>
 
 #include <algorithm>
+#include <atomic>
+#include <mutex>
 #include <cmath>
 #include <utility>
 #include <cstdint>
@@ -26,9 +28,9 @@ hp_status fail_hip(hipError_t e) {
 }
 
 void plan_splits(const SplitItem *items, int count, int Hkv, int d, int nw, int64_t max_T,
-                 SplitPlan *out) {
+                 SplitPlan *out, int cus) {
     const int64_t rows_per_wg = 32 * nw;
-    const int64_t slots = (int64_t)kCUs * kWavesPerCU / nw;
+    const int64_t slots = (int64_t)cus * kWavesPerCU / nw;
     int64_t max_tiles = 0;
     for (int i = 0; i < count; ++i) {
         max_tiles = std::max<int64_t>(max_tiles, items[i].tiles);
@@ -152,7 +154,8 @@ struct LevelPlan {
 };
 
 // Splits of every node of one level (one launch): plan_splits over the nodes.
-void plan_level(const hp_query &q, const hp_prefix_node *nodes, int count, LevelPlan &lp) {
+void plan_level(const hp_query &q, const hp_prefix_node *nodes, int count, LevelPlan &lp,
+                int cus = kCUs) {
     const int G = q.Hq / q.Hkv;
     SplitItem items[HP_MAX_NODES];
     SplitPlan sp[HP_MAX_NODES];
@@ -163,7 +166,7 @@ void plan_level(const hp_query &q, const hp_prefix_node *nodes, int count, Level
         maxM = std::max<int64_t>(maxM, nseq * G);
     }
     lp.nw = choose_nw(maxM);
-    plan_splits(items, count, q.Hkv, q.d, lp.nw, INT64_MAX, sp);
+    plan_splits(items, count, q.Hkv, q.d, lp.nw, INT64_MAX, sp, cus);
     for (int i = 0; i < count; ++i) {
         NodePlan &np = lp.nodes[i];
         np.nsplit = sp[i].nsplit;
@@ -288,20 +291,19 @@ struct CascadePlan {
     int num_levels = 0;  // launch groups: tree levels, or one group holding every node
     LevelPlan levels[HP_MAX_LEVELS];
     bool has_suffix = false;
+    bool conc = false;   // suffix pass beside the prefix pass, then one merge
     size_t node_off[HP_MAX_NODES];
+    size_t suf_off = 0;  // concurrent plan: the suffix pass's (O, LSE) rows
     size_t bytes = 0;
 };
 
-hp_status plan_cascade(const hp_query *q, const hp_prefix_tree *tree, const hp_paged_kv *kv,
-                       CascadePlan &cp) {
-    hp_status st = check_query(q);
-    if (st != HP_OK) return st;
-    st = check_tree(q, tree, &cp.total_nodes);
-    if (st != HP_OK) return st;
-    if (kv) {
-        st = check_kv(q, kv);
-        if (st != HP_OK) return st;
-    }
+// 0: never run the passes concurrently, 1: when the plan says it pays, 2:
+// whenever there is a suffix.
+std::atomic<int> g_concurrency{1};
+
+// Lay out the prefix launches of the tree for `cus` compute units; returns
+// the workspace bytes of their partials.
+size_t plan_prefix(const hp_query *q, const hp_prefix_tree *tree, CascadePlan &cp, int cus) {
     size_t off = 0;
     int idx = 0;
     const int levels = tree ? tree->num_levels : 0;
@@ -326,15 +328,49 @@ hp_status plan_cascade(const hp_query *q, const hp_prefix_tree *tree, const hp_p
     for (int l = 0; l < cp.num_levels; ++l) {
         LevelPlan &lp = cp.levels[l];
         lp.first = idx;
-        plan_level(*q, tree->nodes + idx, joint ? cp.total_nodes : tree->nodes_per_level[l], lp);
+        plan_level(*q, tree->nodes + idx, joint ? cp.total_nodes : tree->nodes_per_level[l], lp,
+                   cus);
         for (int i = 0; i < lp.count; ++i) {
             cp.node_off[idx + i] = off;
             off += node_ws_bytes(lp.nodes[i], q->d);
         }
         idx += lp.count;
     }
+    return off;
+}
+
+// Plan of a whole cascade step (shared by the size query and the run).
+hp_status plan_cascade(const hp_query *q, const hp_prefix_tree *tree, const hp_paged_kv *kv,
+                       CascadePlan &cp) {
+    hp_status st = check_query(q);
+    if (st != HP_OK) return st;
+    st = check_tree(q, tree, &cp.total_nodes);
+    if (st != HP_OK) return st;
+    if (kv) {
+        st = check_kv(q, kv);
+        if (st != HP_OK) return st;
+    }
     cp.has_suffix = kv != nullptr;
-    cp.bytes = off;
+    cp.bytes = plan_prefix(q, tree, cp, kCUs);
+    // The suffix pass beside the prefix pass: the prefix is planned for
+    // kConcCUs compute units, the suffix writes its own (O, LSE) rows and one
+    // merge combines them with the prefix partials.
+    const int mode = g_concurrency.load(std::memory_order_relaxed);
+    if (cp.has_suffix && cp.total_nodes > 0 && q->B > 0 && mode != 0) {
+        CascadePlan alt = cp;
+        const size_t pbytes = plan_prefix(q, tree, alt, kConcCUs);
+        bool pays = (int64_t)q->B * q->Hkv >= kConcMinUnits;
+        for (int l = 0; l < alt.num_levels && pays; ++l)
+            for (int i = 0; i < alt.levels[l].count; ++i)
+                pays = pays && alt.levels[l].nodes[i].tiles_per_split >= kConcMinTiles;
+        if (mode == 2 || pays) {
+            cp = alt;
+            cp.conc = true;
+            cp.suf_off = pbytes;
+            cp.bytes = pbytes + round_up((size_t)q->B * q->Hq * q->d * sizeof(float), kWsAlign) +
+                       round_up((size_t)q->B * q->Hq * sizeof(float), kWsAlign);
+        }
+    }
     return HP_OK;
 }
 
@@ -479,6 +515,22 @@ hp_status hp_lse_merge(int32_t n, const float *const *o_in, const float *const *
 
 // ------------------------------- cascade ----------------------------------
 
+hp_status hp_set_concurrency(int32_t mode) {
+    if (mode < 0 || mode > 2) return HP_ERR_INVALID_ARG;
+    g_concurrency.store(mode, std::memory_order_relaxed);
+    return HP_OK;
+}
+
+hp_status hp_cascade_concurrent(const hp_query *q, const hp_prefix_tree *tree,
+                                const hp_paged_kv *kv, int32_t *concurrent) {
+    if (!concurrent) return HP_ERR_NULL;
+    CascadePlan cp;
+    hp_status st = plan_cascade(q, tree, kv, cp);
+    if (st != HP_OK) return st;
+    *concurrent = cp.conc ? 1 : 0;
+    return HP_OK;
+}
+
 hp_status hp_cascade_workspace_size(const hp_query *q, const hp_prefix_tree *tree,
                                     const hp_paged_kv *kv, size_t *bytes) {
     if (!bytes) return HP_ERR_NULL;
@@ -497,6 +549,86 @@ hp_status record(void *const *events, int i, hipStream_t s) {
     if (!events || !events[i]) return HP_OK;
     hipError_t e = hipEventRecord((hipEvent_t)events[i], s);
     return e == hipSuccess ? HP_OK : fail_hip(e);
+}
+
+// A second stream per device for the suffix pass when it runs beside the
+// prefix pass, with its fork and join events: created on first use (default
+// priority, not synchronising with the null stream) and kept until the
+// process ends.  The fork/launch/join sequence is enqueued under a mutex, so
+// calls from several host threads do not interleave their uses of the events.
+struct SideStream {
+    hipStream_t s = nullptr;
+    hipEvent_t fork = nullptr, join = nullptr;
+    bool tried = false;
+};
+constexpr int kMaxDevices = 64;
+SideStream g_side[kMaxDevices];
+std::mutex g_side_mu;
+
+// The current device's side stream (g_side_mu held), or null when it could
+// not be created; the step then runs the same plan on the caller's stream.
+SideStream *side_stream_locked() {
+    int dev = 0;
+    if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= kMaxDevices) return nullptr;
+    SideStream &sd = g_side[dev];
+    if (!sd.tried) {
+        sd.tried = true;
+        bool ok = hipStreamCreateWithFlags(&sd.s, hipStreamNonBlocking) == hipSuccess;
+        ok = ok && hipEventCreateWithFlags(&sd.fork, hipEventDisableTiming) == hipSuccess;
+        ok = ok && hipEventCreateWithFlags(&sd.join, hipEventDisableTiming) == hipSuccess;
+        if (!ok) {
+            if (sd.join) (void)hipEventDestroy(sd.join);
+            if (sd.fork) (void)hipEventDestroy(sd.fork);
+            if (sd.s) (void)hipStreamDestroy(sd.s);
+            sd.s = nullptr;
+            sd.fork = sd.join = nullptr;
+            (void)hipGetLastError();  // do not leave the failure for the caller's next check
+        }
+    }
+    return sd.s ? &sd : nullptr;
+}
+
+hp_status run_prefix_levels(const hp_query *q, const hp_prefix_tree *tree, const CascadePlan &cp,
+                            char *base, MergeArgs &m, hipStream_t s);
+
+// Suffix pass beside the prefix pass: fork the side stream from s, prefix
+// launches on s, the suffix pass (its own (O, LSE) rows, no merge) on the side
+// stream, join, then one merge of every prefix partial with the suffix rows.
+hp_status cascade_concurrent(const hp_query *q, const hp_prefix_tree *tree,
+                             const hp_paged_kv *kv, const CascadePlan &cp, float *o, float *lse,
+                             char *base, hipStream_t s, void *const *events) {
+    float *so = (float *)(base + cp.suf_off);
+    float *sl = (float *)((char *)so +
+                          round_up((size_t)q->B * q->Hq * q->d * sizeof(float), kWsAlign));
+    std::lock_guard<std::mutex> lock(g_side_mu);
+    SideStream *side = side_stream_locked();
+    hipStream_t ss = side ? side->s : s;
+    hipError_t e;
+    if (side) {
+        if ((e = hipEventRecord(side->fork, s)) != hipSuccess) return fail_hip(e);
+        if ((e = hipStreamWaitEvent(ss, side->fork, 0)) != hipSuccess) return fail_hip(e);
+    }
+    MergeArgs m;
+    std::memset(&m, 0, sizeof m);
+    hp_status st = run_prefix_levels(q, tree, cp, base, m, s);
+    if (st != HP_OK) return st;
+    if ((st = record(events, 1, s)) != HP_OK) return st;
+    SuffixArgs a = suffix_args(*q, *kv, RowDest{so, sl, 0, 0, 0});
+    e = launch_suffix(a, q->dtype, q->d, q->Hq / q->Hkv, suffix_waves(*q, *kv), ss);
+    if (e != hipSuccess) return fail_hip(e);
+    if ((st = record(events, 2, ss)) != HP_OK) return st;
+    if (side) {
+        if ((e = hipEventRecord(side->join, ss)) != hipSuccess) return fail_hip(e);
+        if ((e = hipStreamWaitEvent(s, side->join, 0)) != hipSuccess) return fail_hip(e);
+    }
+    m.src[m.nsrc++] = MergeSrc{so, sl, 0, 0, 1, 0, 0, q->B};
+    m.Hq = q->Hq;
+    m.row_b0 = 0;
+    m.row_b1 = q->B;
+    m.o = o;
+    m.lse = lse;
+    if ((e = launch_merge(m, q->d, s)) != hipSuccess) return fail_hip(e);
+    return record(events, 3, s);
 }
 
 // Prefix pass of every tree level (root first), results into the cascade
@@ -535,6 +667,7 @@ hp_status cascade_impl(const hp_query *q, const hp_prefix_tree *tree, const hp_p
     hipStream_t s = (hipStream_t)stream;
     char *base = (char *)ws;
     if ((st = record(events, 0, s)) != HP_OK) return st;
+    if (cp.conc) return cascade_concurrent(q, tree, kv, cp, o, lse, base, s, events);
 
     MergeArgs m;
     std::memset(&m, 0, sizeof m);

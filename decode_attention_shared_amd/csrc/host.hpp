@@ -80,8 +80,19 @@ struct SplitPlan {
 // where rounds(T) is how many times the launch fills the GPU's workgroup slots
 // (a partly filled last round costs a full round) and partial_bytes(T) the
 // split results written and read back by the merge.
+// `cus` is the number of compute units the launch may fill.
 void plan_splits(const SplitItem *items, int count, int Hkv, int d, int nw, int64_t max_T,
-                 SplitPlan *out);
+                 SplitPlan *out, int cus = kCUs);
+
+// Running the suffix pass beside the prefix pass (see the cascade step): the
+// prefix is then planned for kConcCUs compute units, which it fills at about
+// the same speed as all of them (the chip's power budget, not its CU count,
+// bounds the matrix-core pass), leaving the rest to the memory-bound suffix.
+// Used when every prefix split keeps at least kConcMinTiles tiles under that
+// plan and the suffix has at least kConcMinUnits (sequence, KV head) units.
+constexpr int kConcCUs = 160;
+constexpr int kConcMinTiles = 48;
+constexpr int64_t kConcMinUnits = 1024;
 
 }  // namespace host
 }  // namespace hp

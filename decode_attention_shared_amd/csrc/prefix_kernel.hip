@@ -671,27 +671,6 @@ __device__ __forceinline__ void pp_body(const PrefixArgs &args, const WgTask &ta
     };
     const int k_swz = n % kRowChunks;
     f32x16 s0, s1;  // scores of the latest tile (keys 0-31, 32-63)
-    // All K operands of the tile are read before the first product, so the
-    // matrix core is not left waiting on one LDS round trip per k-step.
-    auto qk = [&](int st) {
-        const uint16_t *kb = &lds[st][0][n * D];
-        u32x4 ka[kDSteps][2];
-#pragma unroll
-        for (int kk = 0; kk < kDSteps; ++kk) {
-            const int col = ((2 * kk + hi) ^ k_swz) * 8;
-            ka[kk][0] = *(const u32x4 *)&kb[col];
-            ka[kk][1] = *(const u32x4 *)&kb[32 * D + col];
-        }
-        s0 = f32x16{};
-        s1 = f32x16{};
-#pragma unroll
-        for (int kk = 0; kk < kDSteps; ++kk) {
-            s0 = mfma32x32x16<kBf16>(ka[kk][0], qf[kk], s0);
-            s1 = mfma32x32x16<kBf16>(ka[kk][1], qf[kk], s1);
-        }
-        __builtin_amdgcn_sched_group_barrier(0x100, 2 * kDSteps, 0);  // the LDS reads
-        __builtin_amdgcn_sched_group_barrier(0x008, 2 * kDSteps, 0);  // then the products
-    };
     const int gi = lane >> 4, li = lane & 15;
     const int v_key = 4 * hi + (li >> 2);
     const int v_swz = v_swizzle<D>(v_key);

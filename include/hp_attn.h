@@ -175,10 +175,22 @@ hp_status hp_lse_merge(int32_t n, const float *const *o_in, const float *const *
 /*
  * One whole decode step: every row (b, h) attends the keys of every tree node
  * covering b (root level first) followed by its paged suffix.  Runs the prefix
- * pass for every node, the suffix pass, and one n-way merge, in that order on
- * `stream` (Hydragen page, "Hierarchical Sharing": decomposition at every
- * tree vertex, recombined with the stored LSE of each level).  tree may be
- * NULL (suffix only); kv may be NULL (prefix only).  lse may be NULL.
+ * pass for every node, the suffix pass, and one n-way merge (Hydragen page,
+ * "Hierarchical Sharing": decomposition at every tree vertex, recombined with
+ * the stored LSE of each level).  tree may be NULL (suffix only); kv may be
+ * NULL (prefix only).  lse may be NULL.
+ *
+ * The prefix and suffix passes depend on nothing but the inputs (the merge
+ * needs both; Hydragen page, "Attention Decomposition Across Subsequences",
+ * Eq. 5), so the step may run them side by side: the prefix pass on `stream`,
+ * the suffix pass on a second stream that the library creates for the
+ * current device on first use (default priority, kept until the process
+ * ends), forked from and joined back to `stream` with events, then the merge
+ * on `stream`.  Everything enqueued on `stream` before the call is ordered
+ * before both passes and everything after it after the merge, eagerly and
+ * under graph capture alike.  Otherwise every launch is on `stream`, the
+ * suffix pass with the merge fused into it.  hp_set_concurrency selects the
+ * policy; hp_cascade_concurrent reports the choice for given arguments.
  */
 hp_status hp_cascade_workspace_size(const hp_query *query, const hp_prefix_tree *tree,
                                     const hp_paged_kv *kv, size_t *bytes);
@@ -187,9 +199,30 @@ hp_status hp_cascade_step(const hp_query *query, const hp_prefix_tree *tree,
                           size_t workspace_bytes, void *stream);
 
 /*
+ * Policy for running the passes side by side (see hp_cascade_step).  mode 0:
+ * never; 1 (the default): when the plan expects a gain, that is when, with
+ * the prefix pass planned for 160 of the 256 compute units, every prefix split
+ * still covers at least 48 tiles of 64 keys, and the suffix has at least 1024
+ * (sequence, KV head) units; 2: whenever the step has both a prefix and a
+ * suffix.  Process-wide.  The workspace size depends on the choice: query
+ * hp_cascade_workspace_size after changing the mode.  HP_ERR_INVALID_ARG for
+ * any other mode.
+ */
+hp_status hp_set_concurrency(int32_t mode);
+
+/*
+ * *concurrent = 1 when hp_cascade_step with these arguments would run the
+ * suffix pass beside the prefix pass under the current policy, else 0.
+ * Validates the arguments like hp_cascade_workspace_size.
+ */
+hp_status hp_cascade_concurrent(const hp_query *query, const hp_prefix_tree *tree,
+                                const hp_paged_kv *kv, int32_t *concurrent);
+
+/*
  * hp_cascade_step plus per-pass timing: records events[0] on `stream` before
  * the first launch, events[1] after the prefix pass (all levels), events[2]
- * after the suffix pass and events[3] after the merge.  events is a host
+ * after the suffix pass (on the library's second stream when the passes run
+ * side by side) and events[3] after the merge.  events is a host
  * array of n_events (0 or 4) hipEvent_t handles created by the caller; NULL
  * entries are skipped.  Otherwise identical to hp_cascade_step.  For
  * measurement harnesses; the computation is the one described above.

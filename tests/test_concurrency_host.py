@@ -1,0 +1,94 @@
+"""Policy for running a cascade step's suffix pass beside its prefix pass, on the CPU:
+hp_cascade_concurrent reports the plan's choice (planning reads no device memory, so
+host tensors stand in for the device buffers), hp_set_concurrency switches the policy,
+and the workspace grows by exactly the suffix pass's (O, LSE) rows when it is on."""
+import ctypes
+
+import pytest
+
+import decode_attention_shared_amd as hp
+
+
+@pytest.fixture(scope="module")
+def L():
+    import os
+    if not os.path.exists(hp.LIB_PATH):
+        import __graft_entry__
+        __graft_entry__.build()
+    return hp.lib()
+
+
+@pytest.fixture(autouse=True)
+def _restore(L):
+    yield
+    assert L.hp_set_concurrency(1) == 0
+
+
+FAKE = 1 << 40  # an aligned address: planning checks pointers, never reads them
+
+
+def _args(B, Hq, Hkv, d, P, max_blocks, prefix=True, suffix=True):
+    query = hp.Query(FAKE, B, Hq, Hkv, d, hp.HP_F16, 1.0)
+    tree = kv = None
+    keep = []
+    if prefix:
+        nodes = (hp.PrefixNode * 1)(hp.PrefixNode(FAKE, FAKE, Hkv * d, d, P, 0, B))
+        tree = hp.PrefixTree()
+        tree.num_levels = 1
+        tree.nodes_per_level[0] = 1
+        tree.nodes = ctypes.cast(nodes, ctypes.POINTER(hp.PrefixNode))
+        keep.append(nodes)
+    if suffix:
+        kv = hp.PagedKV(FAKE, FAKE, FAKE, FAKE, max_blocks, 16, B * max_blocks)
+    return query, tree, kv, keep
+
+
+def _plan(L, args):
+    query, tree, kv, _ = args
+    flag = ctypes.c_int32(-1)
+    nbytes = ctypes.c_size_t(0)
+    tp = ctypes.byref(tree) if tree is not None else None
+    kp = ctypes.byref(kv) if kv is not None else None
+    assert L.hp_cascade_concurrent(ctypes.byref(query), tp, kp, ctypes.byref(flag)) == 0
+    assert L.hp_cascade_workspace_size(ctypes.byref(query), tp, kp, ctypes.byref(nbytes)) == 0
+    return flag.value, nbytes.value
+
+
+@pytest.mark.parametrize("shape,want", [
+    ((256, 40, 40, 128, 16384, 8), 1),    # the 16K MHA step: 64 tiles per split at 160 CUs
+    ((256, 32, 32, 128, 16384, 32), 1),   # a 16K document, long suffixes
+    ((256, 40, 40, 128, 4096, 8), 0),     # 4K prefix: 16 tiles per split, no gain measured
+    ((64, 32, 8, 128, 4096, 16), 0),      # GQA, 512 suffix units
+    ((16, 8, 8, 64, 16384, 4), 0),        # too few suffix units
+])
+def test_auto_policy(L, shape, want):
+    assert _plan(L, _args(*shape))[0] == want
+
+
+def test_modes_and_workspace(L):
+    B, Hq, Hkv, d = 8, 4, 2, 64
+    args = _args(B, Hq, Hkv, d, 300, 4)
+    assert L.hp_set_concurrency(0) == 0
+    off, ws_off = _plan(L, args)
+    assert off == 0
+    assert L.hp_set_concurrency(2) == 0
+    on, ws_on = _plan(L, args)
+    assert on == 1
+
+    def up(x):
+        return (x + 255) // 256 * 256
+    # the prefix partials for 160 compute units plus the suffix rows (O and LSE)
+    assert ws_on >= up(B * Hq * d * 4) + up(B * Hq * 4)
+    # prefix only or suffix only: nothing to run side by side
+    assert _plan(L, _args(B, Hq, Hkv, d, 300, 4, suffix=False))[0] == 0
+    assert _plan(L, _args(B, Hq, Hkv, d, 300, 4, prefix=False))[0] == 0
+    assert L.hp_set_concurrency(1) == 0
+    assert _plan(L, args)[0] == 0
+
+
+def test_mode_validation(L):
+    assert L.hp_set_concurrency(3) == 2
+    assert L.hp_set_concurrency(-1) == 2
+    query, tree, kv, _ = _args(4, 2, 2, 64, 100, 2)
+    assert L.hp_cascade_concurrent(ctypes.byref(query), ctypes.byref(tree), ctypes.byref(kv),
+                                   None) == 1

@@ -1,0 +1,143 @@
+"""GPU parity of the cascade step when its suffix pass runs beside its prefix pass (on
+the library's second stream, forked from and joined to the caller's stream), forced on
+for shapes the automatic policy would run serially: results against the fp64 oracle
+(tolerances in gpu_util.TOL), NaN rows for bad metadata, ordering with work the caller
+enqueues just before and after the step, graph capture, and the timed entry point.
+The full-size MHA and document steps, which the automatic policy runs this way, are
+covered by test_cascade_full_size_sampled."""
+import ctypes
+
+import numpy as np
+import pytest
+import torch
+
+import decode_attention_shared_amd as hp
+import oracle
+import workloads
+from gpu_util import DEV, compare, dev_step, say
+from test_gpu_parity import REDUCED
+
+pytestmark = pytest.mark.gpu
+
+
+@pytest.fixture(scope="module", autouse=True)
+def _forced():
+    if not torch.cuda.is_available():
+        pytest.fail("GPU tests need an MI355X (no GPU visible)")
+    hp.set_concurrency(2)
+    yield
+    hp.set_concurrency(1)
+
+
+def _call(ds, scale):
+    call = hp.CascadeCall(ds["q"], ds["levels"], ds["k_pool"], ds["v_pool"], ds["block_table"],
+                          ds["seq_lens"], scale)
+    assert call.concurrent, "forced mode must run the passes side by side"
+    return call
+
+
+@pytest.mark.parametrize("cfg", REDUCED, ids=lambda c: c.name)
+def test_concurrent_matches_oracle(cfg):
+    say(f"concurrent cascade {cfg.name}")
+    step = workloads.generate(cfg, seed=3)
+    ds = dev_step(step)
+    out, lse = _call(ds, step.scale)()
+    torch.cuda.synchronize()
+    ref_o, ref_l = oracle.step_attention(step, "all")
+    compare(out, lse, ref_o, ref_l, cfg.dtype, f"concurrent {cfg.name}")
+
+
+def test_concurrent_bad_metadata_gives_nan_rows_only():
+    cfg = REDUCED[1]
+    step = workloads.generate(cfg, seed=8)
+    ds = dev_step(step)
+    ds["block_table"][3, 0] = step.num_blocks
+    ds["block_table"][5, 0] = -1
+    ds["seq_lens"][9] = cfg.max_blocks * 16 + 1
+    out, lse = _call(ds, step.scale)()
+    torch.cuda.synchronize()
+    bad = [3, 5, 9]
+    assert torch.isnan(out[bad]).all() and torch.isnan(lse[bad]).all()
+    good = [b for b in range(cfg.B) if b not in bad]
+    rows = np.array([b * cfg.Hq + h for b in good for h in range(cfg.Hq)])
+    ref_o, ref_l = oracle.step_attention(step, "all", rows=rows)
+    compare(out, lse, ref_o, ref_l, cfg.dtype, "concurrent good rows", rows=rows)
+
+
+def test_concurrent_orders_with_caller_stream():
+    """Work enqueued on the caller's stream right before the step (a change of q) is seen
+    by both passes, and a read enqueued right after it sees the merged result."""
+    cfg = REDUCED[2]
+    step = workloads.generate(cfg, seed=13)
+    ds = dev_step(step)
+    call = _call(ds, step.scale)
+    s = torch.cuda.Stream()
+    with torch.cuda.stream(s):
+        for rep in range(3):
+            ds["q"].copy_((step.q * (1.0 + 0.5 * rep)).to(DEV), non_blocking=True)
+            call(stream=s)
+            got_o, got_l = call.out.clone(), call.lse.clone()  # ordered after the merge on s
+            call.out.fill_(5.0)                                 # and before the next step
+            s.synchronize()
+            q_rep = (step.q.float() * (1.0 + 0.5 * rep)).to(step.q.dtype)
+            segs = [[(nd.k, nd.v) for nd in step.nodes_of(b)] + [step.suffix(b)]
+                    for b in range(cfg.B)]
+            ref_o, ref_l = oracle.attention(q_rep, segs, cfg.Hkv, step.scale)
+            compare(got_o, got_l, ref_o, ref_l, cfg.dtype, f"ordered step {rep}")
+
+
+def test_concurrent_graph_replay_matches_eager():
+    cfg = REDUCED[4]
+    step = workloads.generate(cfg, seed=11)
+    ds = dev_step(step)
+    call = _call(ds, step.scale)
+    s = torch.cuda.Stream()
+    with torch.cuda.stream(s):
+        call(stream=s)
+        torch.cuda.synchronize()
+        eager_o, eager_l = call.out.clone(), call.lse.clone()
+        g = torch.cuda.CUDAGraph()
+        g.capture_begin()
+        call(stream=s)
+        g.capture_end()
+    for rep in range(4):
+        call.out.fill_(3.0)
+        call.lse.fill_(3.0)
+        torch.cuda.synchronize()
+        g.replay()
+        torch.cuda.synchronize()
+        assert torch.equal(call.out, eager_o) and torch.equal(call.lse, eager_l), f"replay {rep}"
+        call()  # eager work between replays
+        torch.cuda.synchronize()
+        assert torch.equal(call.out, eager_o), f"eager after replay {rep}"
+
+
+def test_concurrent_timed_records_events():
+    """events[2] is recorded on the library's second stream: every event is after
+    events[0] and no later than events[3], and the result equals the untimed call."""
+    cfg = REDUCED[2]
+    step = workloads.generate(cfg, seed=12)
+    ds = dev_step(step)
+    call = _call(ds, step.scale)
+    o1, l1 = [t.clone() for t in call()]
+    torch.cuda.synchronize()
+    rt = ctypes.CDLL("libamdhip64.so")
+    raw = []
+    for _ in range(4):
+        h = ctypes.c_void_p()
+        assert rt.hipEventCreate(ctypes.byref(h)) == 0
+        raw.append(h.value)
+    o2, l2 = call.timed(raw)
+    torch.cuda.synchronize()
+    assert torch.equal(o1, o2) and torch.equal(l1, l2)
+
+    def ms(a, b):
+        t = ctypes.c_float()
+        assert rt.hipEventElapsedTime(ctypes.byref(t), ctypes.c_void_p(a), ctypes.c_void_p(b)) == 0
+        return t.value
+    total = ms(raw[0], raw[3])
+    assert 0 < ms(raw[0], raw[1]) <= total and 0 < ms(raw[0], raw[2]) <= total
+    for h in raw:
+        rt.hipEventDestroy(ctypes.c_void_p(h))
+    ref_o, ref_l = oracle.step_attention(step, "all")
+    compare(o2, l2, ref_o, ref_l, cfg.dtype, "concurrent timed")
