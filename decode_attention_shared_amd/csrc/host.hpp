@@ -91,7 +91,7 @@ void plan_splits(const SplitItem *items, int count, int Hkv, int d, int nw, int6
 // Used when every prefix split keeps at least kConcMinTiles tiles under that
 // plan and the suffix has at least kConcMinUnits (sequence, KV head) units.
 constexpr int kConcCUs = 160;
-constexpr int kConcMinTiles = 48;
+constexpr int kConcMinTiles = 32;
 constexpr int64_t kConcMinUnits = 1024;
 
 }  // namespace host

@@ -57,7 +57,8 @@ def _plan(L, args):
 @pytest.mark.parametrize("shape,want", [
     ((256, 40, 40, 128, 16384, 8), 1),    # the 16K MHA step: 64 tiles per split at 160 CUs
     ((256, 32, 32, 128, 16384, 32), 1),   # a 16K document, long suffixes
-    ((256, 40, 40, 128, 4096, 8), 0),     # 4K prefix: 16 tiles per split, no gain measured
+    ((256, 40, 40, 128, 8192, 8), 1),     # 8K: 32 tiles per split
+    ((256, 40, 40, 128, 4096, 8), 0),     # 4K prefix: 16 tiles per split, slower side by side
     ((64, 32, 8, 128, 4096, 16), 0),      # GQA, 512 suffix units
     ((16, 8, 8, 64, 16384, 4), 0),        # too few suffix units
 ])
