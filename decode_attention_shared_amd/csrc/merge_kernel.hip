@@ -43,8 +43,14 @@ __global__ __launch_bounds__(256) void merge_kernel(MergeArgs a) {
     const int64_t b = a.row_b0 + r / a.Hq;
     const int h = (int)(r % a.Hq);
 
+    // One pass with a running max: each partial's LSE and O are loaded together
+    // (no second round trip for the O rows after a max over the LSEs), and the
+    // sum so far is rescaled when a larger LSE arrives.  The result is the same
+    // weighted mean up to rounding order.
     bool bad = false;
     float mx = -INFINITY;
+    f32x4 acc = {0.f, 0.f, 0.f, 0.f};
+    float wsum = 0.f;
 #pragma unroll 1
     for (int si = 0; si < a.nsrc; ++si) {
         const MergeSrc &s = a.src[si];
@@ -53,26 +59,18 @@ __global__ __launch_bounds__(256) void merge_kernel(MergeArgs a) {
 #pragma unroll 4
         for (int i = 0; i < n; ++i) {
             const float L = s.lse[(int64_t)i * s.lse_split + ri];
+            const f32x4 v = *(const f32x4 *)(s.o + (int64_t)i * s.o_split + ri * D + c4);
             bad |= (L != L);
-            mx = fmaxf(mx, L);
-        }
-    }
-    f32x4 acc = {0.f, 0.f, 0.f, 0.f};
-    float wsum = 0.f;
-    if (mx > -INFINITY && !bad) {
-#pragma unroll 1
-        for (int si = 0; si < a.nsrc; ++si) {
-            const MergeSrc &s = a.src[si];
-            const int n = src_count(s, b, a, bad);
-            const int64_t ri = (b - s.b0) * a.Hq + h;
-#pragma unroll 4
-            for (int i = 0; i < n; ++i) {
-                const float L = s.lse[(int64_t)i * s.lse_split + ri];
-                const float w = fast_exp2((L - mx) * kLog2e);
-                const f32x4 v = *(const f32x4 *)(s.o + (int64_t)i * s.o_split + ri * D + c4);
-                acc += w * v;
-                wsum += w;
+            if (!(L > -INFINITY)) continue;  // an empty part (or NaN, flagged above)
+            if (L > mx) {
+                const float rs = fast_exp2((mx - L) * kLog2e);  // 0 while mx = -inf
+                acc *= rs;
+                wsum *= rs;
+                mx = L;
             }
+            const float w = fast_exp2((L - mx) * kLog2e);
+            acc += w * v;
+            wsum += w;
         }
     }
     f32x4 out;
