@@ -119,7 +119,7 @@ def time_steps(call, ev: HipEvents, steps: int, warmup: int):
     for _ in range(warmup):
         call()
     timed_at = set(range(0, steps, EVENT_EVERY))
-    evs = {k: ev.create(4) for k in sorted(timed_at)}
+    evs = {k: ev.create(5) for k in sorted(timed_at)}
     torch.cuda.synchronize()
     t0 = time.perf_counter()
     for k in range(steps):
@@ -130,15 +130,14 @@ def time_steps(call, ev: HipEvents, steps: int, warmup: int):
     torch.cuda.synchronize()
     wall = time.perf_counter() - t0
     passes = {"prefix": [], "suffix": [], "merge": [], "step": []}
-    # When the library runs the suffix pass beside the prefix pass, events[2] is
-    # recorded on its second stream: both passes start at events[0], and the merge
-    # starts when the later of them ends.
-    conc = bool(getattr(call, "concurrent", False))
+    # events[4] is recorded right before the suffix launch on its own stream (the
+    # library's second stream when the passes run side by side), so the suffix
+    # pass is timed from its start; the merge starts when the later pass ends.
     for e in evs.values():
         t1, t2, t3 = ev.ms(e[0], e[1]), ev.ms(e[0], e[2]), ev.ms(e[0], e[3])
         passes["prefix"].append(t1)
-        passes["suffix"].append(t2 if conc else t2 - t1)
-        passes["merge"].append(t3 - max(t1, t2) if conc else t3 - t2)
+        passes["suffix"].append(ev.ms(e[4], e[2]))
+        passes["merge"].append(t3 - max(t1, t2))
         passes["step"].append(t3)
     ev.close()
     return wall, passes

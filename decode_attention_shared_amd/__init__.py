@@ -401,13 +401,15 @@ class CascadeCall:
         return self.out, self.lse
 
     def timed(self, events, stream=None):
-        """Run the step and record 4 caller-created hipEvent_t handles: before the
-        prefix pass, after it, after the suffix pass and after the merge."""
-        arr = (ctypes.c_void_p * 4)(*events)
+        """Run the step and record 4 or 5 caller-created hipEvent_t handles: before the
+        prefix pass, after it, after the suffix pass, after the merge and (optional)
+        right before the suffix pass on its stream."""
+        n = len(events)
+        arr = (ctypes.c_void_p * n)(*events)
         _check(self._L.hp_cascade_step_timed(ctypes.byref(self.query), self._tree_p, self._kv_p,
                                              self.out.data_ptr(), _ptr(self.lse), _ptr(self.ws),
                                              self.workspace_bytes, _stream(stream),
-                                             ctypes.addressof(arr), 4), "hp_cascade_step_timed")
+                                             ctypes.addressof(arr), n), "hp_cascade_step_timed")
         return self.out, self.lse
 
 

@@ -608,12 +608,14 @@ hp_status cascade_concurrent(const hp_query *q, const hp_prefix_tree *tree,
         if ((e = hipEventRecord(side->fork, s)) != hipSuccess) return fail_hip(e);
         if ((e = hipStreamWaitEvent(ss, side->fork, 0)) != hipSuccess) return fail_hip(e);
     }
+    hp_status st = record(events, 0, s);  // right before the first prefix launch
+    if (st != HP_OK) return st;
     MergeArgs m;
     std::memset(&m, 0, sizeof m);
-    hp_status st = run_prefix_levels(q, tree, cp, base, m, s);
-    if (st != HP_OK) return st;
+    if ((st = run_prefix_levels(q, tree, cp, base, m, s)) != HP_OK) return st;
     if ((st = record(events, 1, s)) != HP_OK) return st;
     SuffixArgs a = suffix_args(*q, *kv, RowDest{so, sl, 0, 0, 0});
+    if ((st = record(events, 4, ss)) != HP_OK) return st;
     e = launch_suffix(a, q->dtype, q->d, q->Hq / q->Hkv, suffix_waves(*q, *kv), ss);
     if (e != hipSuccess) return fail_hip(e);
     if ((st = record(events, 2, ss)) != HP_OK) return st;
@@ -666,8 +668,8 @@ hp_status cascade_impl(const hp_query *q, const hp_prefix_tree *tree, const hp_p
     if (cp.bytes > 0 && (!ws || ws_bytes < cp.bytes || !aligned16(ws))) return HP_ERR_WORKSPACE;
     hipStream_t s = (hipStream_t)stream;
     char *base = (char *)ws;
-    if ((st = record(events, 0, s)) != HP_OK) return st;
     if (cp.conc) return cascade_concurrent(q, tree, kv, cp, o, lse, base, s, events);
+    if ((st = record(events, 0, s)) != HP_OK) return st;
 
     MergeArgs m;
     std::memset(&m, 0, sizeof m);
@@ -679,6 +681,7 @@ hp_status cascade_impl(const hp_query *q, const hp_prefix_tree *tree, const hp_p
         a.nsrc = m.nsrc;
         for (int i = 0; i < m.nsrc; ++i) a.src[i] = m.src[i];
         a.stage_floats = stage_floats(m.src, m.nsrc, q->Hq / q->Hkv, q->d);
+        if ((st = record(events, 4, s)) != HP_OK) return st;
         hipError_t e = launch_suffix(a, q->dtype, q->d, q->Hq / q->Hkv, suffix_waves(*q, *kv), s);
         if (e != hipSuccess) return fail_hip(e);
         if ((st = record(events, 2, s)) != HP_OK) return st;
@@ -812,8 +815,10 @@ hp_status hp_cascade_step_timed(const hp_query *q, const hp_prefix_tree *tree,
                                 const hp_paged_kv *kv, float *o, float *lse, void *ws,
                                 size_t ws_bytes, void *stream, void *const *events,
                                 int32_t n_events) {
-    if (n_events != 0 && n_events != 4) return HP_ERR_INVALID_ARG;
-    return cascade_impl(q, tree, kv, o, lse, ws, ws_bytes, stream, n_events ? events : nullptr);
+    if (n_events != 0 && n_events != 4 && n_events != 5) return HP_ERR_INVALID_ARG;
+    if (n_events == 0) return cascade_impl(q, tree, kv, o, lse, ws, ws_bytes, stream, nullptr);
+    void *ev[5] = {events[0], events[1], events[2], events[3], n_events == 5 ? events[4] : nullptr};
+    return cascade_impl(q, tree, kv, o, lse, ws, ws_bytes, stream, ev);
 }
 
 }  // extern "C"

@@ -219,12 +219,15 @@ hp_status hp_cascade_concurrent(const hp_query *query, const hp_prefix_tree *tre
                                 const hp_paged_kv *kv, int32_t *concurrent);
 
 /*
- * hp_cascade_step plus per-pass timing: records events[0] on `stream` before
- * the first launch, events[1] after the prefix pass (all levels), events[2]
+ * hp_cascade_step plus per-pass timing: records events[0] on `stream` right
+ * before the first prefix launch (after the fork when the passes run side by
+ * side), events[1] after the prefix pass (all levels), events[2]
  * after the suffix pass (on the library's second stream when the passes run
- * side by side) and events[3] after the merge.  events is a host
- * array of n_events (0 or 4) hipEvent_t handles created by the caller; NULL
- * entries are skipped.  Otherwise identical to hp_cascade_step.  For
+ * side by side) and events[3] after the merge; with n_events = 5, events[4]
+ * on the suffix pass's stream right before its launch (so that the suffix
+ * pass can be timed from its own start when it does not follow the prefix
+ * pass).  events is a host array of n_events (0, 4 or 5) hipEvent_t handles
+ * created by the caller; NULL entries are skipped.  Otherwise identical to hp_cascade_step.  For
  * measurement harnesses; the computation is the one described above.
  */
 hp_status hp_cascade_step_timed(const hp_query *query, const hp_prefix_tree *tree,

@@ -93,3 +93,11 @@ def test_mode_validation(L):
     query, tree, kv, _ = _args(4, 2, 2, 64, 100, 2)
     assert L.hp_cascade_concurrent(ctypes.byref(query), ctypes.byref(tree), ctypes.byref(kv),
                                    None) == 1
+
+
+def test_timed_event_count_validation(L):
+    query, tree, kv, _ = _args(4, 2, 2, 64, 100, 2)
+    ev = (ctypes.c_void_p * 6)()
+    for n in (1, 3, 6, -1):
+        assert L.hp_cascade_step_timed(ctypes.byref(query), ctypes.byref(tree), ctypes.byref(kv),
+                                       FAKE, FAKE, None, 0, None, ctypes.addressof(ev), n) == 2

@@ -113,8 +113,9 @@ def test_concurrent_graph_replay_matches_eager():
 
 
 def test_concurrent_timed_records_events():
-    """events[2] is recorded on the library's second stream: every event is after
-    events[0] and no later than events[3], and the result equals the untimed call."""
+    """events[2] and events[4] are recorded on the library's second stream: the passes
+    end between events[0] and events[3], the suffix pass lies between events[4] and
+    events[2], and the result equals the untimed call."""
     cfg = REDUCED[2]
     step = workloads.generate(cfg, seed=12)
     ds = dev_step(step)
@@ -123,7 +124,7 @@ def test_concurrent_timed_records_events():
     torch.cuda.synchronize()
     rt = ctypes.CDLL("libamdhip64.so")
     raw = []
-    for _ in range(4):
+    for _ in range(5):
         h = ctypes.c_void_p()
         assert rt.hipEventCreate(ctypes.byref(h)) == 0
         raw.append(h.value)
@@ -137,6 +138,9 @@ def test_concurrent_timed_records_events():
         return t.value
     total = ms(raw[0], raw[3])
     assert 0 < ms(raw[0], raw[1]) <= total and 0 < ms(raw[0], raw[2]) <= total
+    # events[4]: on the second stream, right before the suffix pass (events[0] is
+    # right before the prefix pass, so the two may come in either order)
+    assert 0 < ms(raw[4], raw[2]) < ms(raw[4], raw[3])
     for h in raw:
         rt.hipEventDestroy(ctypes.c_void_p(h))
     ref_o, ref_l = oracle.step_attention(step, "all")
