@@ -188,9 +188,13 @@ hp_status hp_lse_merge(int32_t n, const float *const *o_in, const float *const *
  * ends), forked from and joined back to `stream` with events, then the merge
  * on `stream`.  Everything enqueued on `stream` before the call is ordered
  * before both passes and everything after it after the merge, eagerly and
- * under graph capture alike.  Otherwise every launch is on `stream`, the
- * suffix pass with the merge fused into it.  hp_set_concurrency selects the
- * policy; hp_cascade_concurrent reports the choice for given arguments.
+ * under graph capture alike.  The second stream is shared by every such call
+ * on the device (calls from several host threads are ordered on it, each with
+ * its own fork and join); while one thread captures such a step into a graph,
+ * another must not run one on the same device (the second stream then belongs
+ * to the capture).  Otherwise every launch is on `stream`, the suffix pass
+ * with the merge fused into it.  hp_set_concurrency selects the policy;
+ * hp_cascade_concurrent reports the choice for given arguments.
  */
 hp_status hp_cascade_workspace_size(const hp_query *query, const hp_prefix_tree *tree,
                                     const hp_paged_kv *kv, size_t *bytes);

@@ -145,3 +145,43 @@ def test_concurrent_timed_records_events():
         rt.hipEventDestroy(ctypes.c_void_p(h))
     ref_o, ref_l = oracle.step_attention(step, "all")
     compare(o2, l2, ref_o, ref_l, cfg.dtype, "concurrent timed")
+
+
+def test_concurrent_from_two_host_threads():
+    """Two host threads, each with its own stream, inputs and workspace, step side by side
+    many times: the library's shared second stream and events keep every step's fork and
+    join its own, so each thread's results equal its single-threaded ones."""
+    import threading
+    cfgs = [REDUCED[2], REDUCED[3]]
+    setups = []
+    for i, cfg in enumerate(cfgs):
+        step = workloads.generate(cfg, seed=20 + i)
+        ds = dev_step(step)
+        call = _call(ds, step.scale)
+        o, l = [t.clone() for t in call()]
+        torch.cuda.synchronize()
+        setups.append((call, o, l))
+    errors = []
+
+    def run(i):
+        call, o_ref, l_ref = setups[i]
+        s = torch.cuda.Stream()
+        try:
+            with torch.cuda.stream(s):
+                for rep in range(20):
+                    call.out.fill_(9.0)
+                    call(stream=s)
+                    got_o, got_l = call.out.clone(), call.lse.clone()
+                    s.synchronize()
+                    if not (torch.equal(got_o, o_ref) and torch.equal(got_l, l_ref)):
+                        errors.append((i, rep))
+        except Exception as e:  # noqa: BLE001 - reported below
+            errors.append((i, repr(e)))
+
+    threads = [threading.Thread(target=run, args=(i,)) for i in range(2)]
+    for t in threads:
+        t.start()
+    for t in threads:
+        t.join(timeout=120)
+    assert not any(t.is_alive() for t in threads), "a thread did not finish"
+    assert not errors, errors
