@@ -38,7 +38,10 @@
  *              16 bytes; d elements of one (token, head) are contiguous.
  * Streams.     `stream` is a hipStream_t (NULL = the null stream).  Work is
  *              enqueued asynchronously; calls are graph-capture safe (no
- *              allocation, host sync, memset or host-to-device copy).
+ *              allocation, host sync, memset or host-to-device copy).  The
+ *              cascade step may also use one stream of the library's own per
+ *              device, created with two events on its first use there and kept
+ *              until the process ends (see hp_cascade_step).
  * Errors.      Every argument is validated on the host before anything is
  *              enqueued; on an error nothing is enqueued and nothing is written.
  *              A failed launch returns HP_ERR_HIP (hp_last_hip_error() has the
