@@ -565,17 +565,28 @@ constexpr int kMaxDevices = 64;
 SideStream g_side[kMaxDevices];
 std::mutex g_side_mu;
 
-// The current device's side stream (g_side_mu held), or null when it could
-// not be created; the step then runs the same plan on the caller's stream.
-SideStream *side_stream_locked() {
-    int dev = 0;
-    if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= kMaxDevices) return nullptr;
+// The side stream of the device that owns stream s (the current device for
+// the null stream), g_side_mu held; null when it could not be created, and the
+// step then runs the same plan on s.  The stream and its events are created
+// with that device current, so a caller whose current device differs from its
+// stream's still gets both passes on one GPU.
+SideStream *side_stream_locked(hipStream_t s) {
+    int cur = 0, dev = 0;
+    if (hipGetDevice(&cur) != hipSuccess) return nullptr;
+    dev = cur;
+    if (s != nullptr && hipStreamGetDevice(s, &dev) != hipSuccess) {
+        (void)hipGetLastError();
+        return nullptr;
+    }
+    if (dev < 0 || dev >= kMaxDevices) return nullptr;
     SideStream &sd = g_side[dev];
     if (!sd.tried) {
         sd.tried = true;
-        bool ok = hipStreamCreateWithFlags(&sd.s, hipStreamNonBlocking) == hipSuccess;
+        bool ok = dev == cur || hipSetDevice(dev) == hipSuccess;
+        ok = ok && hipStreamCreateWithFlags(&sd.s, hipStreamNonBlocking) == hipSuccess;
         ok = ok && hipEventCreateWithFlags(&sd.fork, hipEventDisableTiming) == hipSuccess;
         ok = ok && hipEventCreateWithFlags(&sd.join, hipEventDisableTiming) == hipSuccess;
+        if (dev != cur) (void)hipSetDevice(cur);
         if (!ok) {
             if (sd.join) (void)hipEventDestroy(sd.join);
             if (sd.fork) (void)hipEventDestroy(sd.fork);
@@ -601,7 +612,7 @@ hp_status cascade_concurrent(const hp_query *q, const hp_prefix_tree *tree,
     float *sl = (float *)((char *)so +
                           round_up((size_t)q->B * q->Hq * q->d * sizeof(float), kWsAlign));
     std::lock_guard<std::mutex> lock(g_side_mu);
-    SideStream *side = side_stream_locked();
+    SideStream *side = side_stream_locked(s);
     hipStream_t ss = side ? side->s : s;
     hipError_t e;
     if (side) {

@@ -187,8 +187,8 @@ hp_status hp_lse_merge(int32_t n, const float *const *o_in, const float *const *
  * needs both; Hydragen page, "Attention Decomposition Across Subsequences",
  * Eq. 5), so the step may run them side by side: the prefix pass on `stream`,
  * the suffix pass on a second stream that the library creates for the
- * current device on first use (default priority, kept until the process
- * ends), forked from and joined back to `stream` with events, then the merge
+ * device that owns `stream` (the current device for the null stream) on first
+ * use (default priority, kept until the process ends), forked from and joined back to `stream` with events, then the merge
  * on `stream`.  Everything enqueued on `stream` before the call is ordered
  * before both passes and everything after it after the merge, eagerly and
  * under graph capture alike.  The second stream is shared by every such call
