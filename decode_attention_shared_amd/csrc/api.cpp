@@ -282,6 +282,10 @@ SuffixArgs suffix_args(const hp_query &q, const hp_paged_kv &kv, RowDest dest) {
     a.has_suffix = 1;
     a.scale_log2 = (float)((double)q.scale * 1.4426950408889634);
     a.dest = dest;
+    // K/V footprint: the pool, or what the block tables can reach if less.
+    const int64_t blocks = std::min<int64_t>(kv.num_blocks, (int64_t)q.B * kv.max_blocks);
+    const int64_t kv_bytes = blocks * kBlock * q.Hkv * q.d * esize(q.dtype) * 2;
+    a.stream_kv = kv_bytes > kLlcBytes ? 1 : 0;
     return a;
 }
 

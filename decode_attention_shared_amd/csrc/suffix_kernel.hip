@@ -121,7 +121,7 @@ __device__ __forceinline__ float group_sum(float x) {
 //            kernel; its document is merged in as a by-value source).
 constexpr int kBlocks = 0, kTree = 1, kTokens = 2;
 
-template <int kDt, int D, int G, int NWS, int kMode>
+template <int kDt, int D, int G, int NWS, int kMode, bool kNT>
 __global__ __launch_bounds__(64 * NWS) void suffix_kernel(SuffixArgs a) {
     constexpr bool kRows = kMode != kBlocks;  // one pool row per token
     using E = Elem<kDt>;
@@ -268,6 +268,12 @@ __global__ __launch_bounds__(64 * NWS) void suffix_kernel(SuffixArgs a) {
         }
         return r;
     };
+    // 16 bytes of one K or V row; kNT marks the load non-temporal (the data is
+    // read once per step and would not survive in the cache until the next).
+    auto load16 = [](const char *p) -> u32x4 {
+        if constexpr (kNT) return __builtin_nontemporal_load((const u32x4 *)p);
+        else return *(const u32x4 *)p;
+    };
     // Issue the loads of one block (keys past the sequence's end and blocks
     // with an out-of-range id are never read).
     auto fetch = [&](int blk, const Ref &ref, u32x4 (&kr)[kPasses], u32x4 (&vr)[kPasses],
@@ -283,8 +289,8 @@ __global__ __launch_bounds__(64 * NWS) void suffix_kernel(SuffixArgs a) {
                 const bool ok = t < valid && row_ok;
                 const int64_t off = ((int64_t)(ok ? row : 0) * a.Hkv + g) * D * E::kSize +
                                     d0 * E::kSize;
-                kr[p] = ok ? *(const u32x4 *)(kp + off) : u32x4{0, 0, 0, 0};
-                vr[p] = ok ? *(const u32x4 *)(vp + off) : u32x4{0, 0, 0, 0};
+                kr[p] = ok ? load16(kp + off) : u32x4{0, 0, 0, 0};
+                vr[p] = ok ? load16(vp + off) : u32x4{0, 0, 0, 0};
             }
         } else {
             const int id = ref.v[0];
@@ -298,8 +304,8 @@ __global__ __launch_bounds__(64 * NWS) void suffix_kernel(SuffixArgs a) {
                 const int t = p * kTpp + tg;
                 const bool ok = t < valid;
                 const int64_t off = base + t * tok_stride;
-                kr[p] = ok ? *(const u32x4 *)(kp + off) : u32x4{0, 0, 0, 0};
-                vr[p] = ok ? *(const u32x4 *)(vp + off) : u32x4{0, 0, 0, 0};
+                kr[p] = ok ? load16(kp + off) : u32x4{0, 0, 0, 0};
+                vr[p] = ok ? load16(vp + off) : u32x4{0, 0, 0, 0};
             }
         }
     };
@@ -505,45 +511,46 @@ __global__ __launch_bounds__(64 * NWS) void suffix_kernel(SuffixArgs a) {
     }
 }
 
-template <int kDt, int D, int NWS, int kMode>
+template <int kDt, int D, int NWS, int kMode, bool kNT>
 static void launch_g(const SuffixArgs &a, int G, dim3 grid, hipStream_t s) {
     constexpr int T = 64 * NWS;
     const size_t lds = (size_t)a.stage_floats * sizeof(float);
     switch (G) {
-    case 1: suffix_kernel<kDt, D, 1, NWS, kMode><<<grid, T, lds, s>>>(a); break;
-    case 2: suffix_kernel<kDt, D, 2, NWS, kMode><<<grid, T, lds, s>>>(a); break;
-    case 4: suffix_kernel<kDt, D, 4, NWS, kMode><<<grid, T, lds, s>>>(a); break;
-    default: suffix_kernel<kDt, D, 8, NWS, kMode><<<grid, T, lds, s>>>(a); break;
+    case 1: suffix_kernel<kDt, D, 1, NWS, kMode, kNT><<<grid, T, lds, s>>>(a); break;
+    case 2: suffix_kernel<kDt, D, 2, NWS, kMode, kNT><<<grid, T, lds, s>>>(a); break;
+    case 4: suffix_kernel<kDt, D, 4, NWS, kMode, kNT><<<grid, T, lds, s>>>(a); break;
+    default: suffix_kernel<kDt, D, 8, NWS, kMode, kNT><<<grid, T, lds, s>>>(a); break;
     }
 }
 
-template <int kDt, int NWS, int kMode>
+template <int kDt, int NWS, int kMode, bool kNT>
 static void launch_d(const SuffixArgs &a, int d, int G, dim3 grid, hipStream_t s) {
-    if (d == 128) launch_g<kDt, 128, NWS, kMode>(a, G, grid, s);
-    else launch_g<kDt, 64, NWS, kMode>(a, G, grid, s);
+    if (d == 128) launch_g<kDt, 128, NWS, kMode, kNT>(a, G, grid, s);
+    else launch_g<kDt, 64, NWS, kMode, kNT>(a, G, grid, s);
 }
 
-template <int kDt, int kMode>
+template <int kDt, int kMode, bool kNT>
 static void launch_dt(const SuffixArgs &a, int d, int G, int nws, dim3 grid, hipStream_t s) {
     switch (nws) {
-    case 1: launch_d<kDt, 1, kMode>(a, d, G, grid, s); break;
-    case 2: launch_d<kDt, 2, kMode>(a, d, G, grid, s); break;
-    default: launch_d<kDt, 4, kMode>(a, d, G, grid, s); break;
+    case 1: launch_d<kDt, 1, kMode, kNT>(a, d, G, grid, s); break;
+    case 2: launch_d<kDt, 2, kMode, kNT>(a, d, G, grid, s); break;
+    default: launch_d<kDt, 4, kMode, kNT>(a, d, G, grid, s); break;
     }
 }
 
-template <int kMode>
+template <int kMode, bool kNT = false>
 static hipError_t launch_mode(const SuffixArgs &a, int dtype, int d, int G, int nws,
                               hipStream_t s) {
     const dim3 grid((unsigned)((int64_t)a.B * a.Hkv));
-    if (dtype == HP_BF16) launch_dt<HP_BF16, kMode>(a, d, G, nws, grid, s);
-    else if (dtype == HP_F16) launch_dt<HP_F16, kMode>(a, d, G, nws, grid, s);
-    else launch_dt<HP_F32, kMode>(a, d, G, nws, grid, s);
+    if (dtype == HP_BF16) launch_dt<HP_BF16, kMode, kNT>(a, d, G, nws, grid, s);
+    else if (dtype == HP_F16) launch_dt<HP_F16, kMode, kNT>(a, d, G, nws, grid, s);
+    else launch_dt<HP_F32, kMode, kNT>(a, d, G, nws, grid, s);
     return hipGetLastError();
 }
 
 hipError_t launch_suffix(const SuffixArgs &a, int dtype, int d, int G, int nws, hipStream_t s) {
-    return launch_mode<kBlocks>(a, dtype, d, G, nws, s);
+    return a.stream_kv ? launch_mode<kBlocks, true>(a, dtype, d, G, nws, s)
+                       : launch_mode<kBlocks, false>(a, dtype, d, G, nws, s);
 }
 
 // Sequence-first pass of a chunk-tree step (a.tree set).
