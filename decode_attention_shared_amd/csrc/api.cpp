@@ -254,12 +254,15 @@ hp_status run_level(const hp_query &q, const hp_prefix_node *nodes, const LevelP
     for (int c0 = 0; c0 < lp.count; c0 += kMaxLaunchNodes) {
         PrefixArgs a = base_prefix_args(q);
         int wg = 0;
+        int64_t kv_bytes = 0;  // the launch's K/V (each node's keys and values once)
         const int c1 = std::min(lp.count, c0 + kMaxLaunchNodes);
         for (int i = c0; i < c1; ++i) {
             a.nodes[a.num_nodes++] = node_arg(nodes[i], lp.nodes[i], wg, dests[i]);
             wg += lp.nodes[i].wgs;
+            kv_bytes += (int64_t)nodes[i].len * q.Hkv * q.d * esize(q.dtype) * 2;
         }
         if (wg == 0) continue;
+        a.stream_kv = kv_bytes >= kLlcBytes ? 1 : 0;
         hipError_t e = launch_prefix(a, q.dtype, q.d, lp.nw, wg, s);
         if (e != hipSuccess) return fail_hip(e);
     }
@@ -285,7 +288,7 @@ SuffixArgs suffix_args(const hp_query &q, const hp_paged_kv &kv, RowDest dest) {
     // K/V footprint: the pool, or what the block tables can reach if less.
     const int64_t blocks = std::min<int64_t>(kv.num_blocks, (int64_t)q.B * kv.max_blocks);
     const int64_t kv_bytes = blocks * kBlock * q.Hkv * q.d * esize(q.dtype) * 2;
-    a.stream_kv = kv_bytes > kLlcBytes ? 1 : 0;
+    a.stream_kv = kv_bytes >= kLlcBytes ? 1 : 0;
     return a;
 }
 

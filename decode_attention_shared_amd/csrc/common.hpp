@@ -116,6 +116,8 @@ struct PrefixArgs {
     int64_t row_stride;       // elements between pool rows (Hkv * d)
     int32_t d;
     float *part_o, *part_lse; // partial results, [part_rows][Hq][d] and [part_rows][Hq]
+    int32_t stream_kv;        // node launches: K/V transfers marked non-temporal (the launch's
+                              // K/V exceed the last-level cache)
 };
 
 constexpr int kMaxMergeSrc = HP_MAX_NODES + 1;
@@ -273,14 +275,26 @@ __device__ __forceinline__ void dma16(const void *g, void *lds_base) { lds_dma<1
 // registers: the global base, and the LDS destination as an LDS byte address
 // (M0); only the per-lane unsigned 32-bit byte offset is a vector register.
 // No vector instruction is needed to issue it.
+// kNT marks the load non-temporal (data read once per step that would not
+// survive in the last-level cache until the next).
+template <bool kNT = false>
 __device__ __forceinline__ void dma16_s(const void *base, uint32_t byte_off, uint32_t lds_addr) {
     uint32_t saved;
-    asm volatile(
-        "s_mov_b32 %0, m0\n\ts_mov_b32 m0, %3\n\tglobal_load_lds_dwordx4 %1, %2\n\t"
-        "s_mov_b32 m0, %0"
-        : "=&s"(saved)
-        : "v"(byte_off), "s"(base), "s"(lds_addr)
-        : "memory");
+    if constexpr (kNT) {
+        asm volatile(
+            "s_mov_b32 %0, m0\n\ts_mov_b32 m0, %3\n\tglobal_load_lds_dwordx4 %1, %2 nt\n\t"
+            "s_mov_b32 m0, %0"
+            : "=&s"(saved)
+            : "v"(byte_off), "s"(base), "s"(lds_addr)
+            : "memory");
+    } else {
+        asm volatile(
+            "s_mov_b32 %0, m0\n\ts_mov_b32 m0, %3\n\tglobal_load_lds_dwordx4 %1, %2\n\t"
+            "s_mov_b32 m0, %0"
+            : "=&s"(saved)
+            : "v"(byte_off), "s"(base), "s"(lds_addr)
+            : "memory");
+    }
 }
 
 // s_waitcnt with only vmcnt = n (expcnt and lgkmcnt left unconstrained).

@@ -39,9 +39,10 @@ constexpr int kWavesPerCU = 8;          // two waves per SIMD at the prefix kern
 // scheduling rounds against partial traffic.
 constexpr double kPartialByteCost = 8e-8;
 constexpr size_t kWsAlign = 256;
-// MI355X's last-level (Infinity) cache.  A paged suffix whose K/V footprint is
-// larger cannot be found there on the next step, so its loads are marked
-// non-temporal; a smaller one is left to stay cached.
+// MI355X's last-level (Infinity) cache.  K/V that a prefix launch or a paged
+// suffix reads and that are at least this large cannot be found there on the
+// next step, so their loads are marked non-temporal; smaller ones are left to
+// stay cached.
 constexpr int64_t kLlcBytes = int64_t(256) << 20;
 
 inline size_t round_up(size_t x, size_t a) { return (x + a - 1) / a * a; }

@@ -570,7 +570,7 @@ __global__ __launch_bounds__(64 * NW) void tree_mfma16_kernel(PrefixArgs args) {
 // matrix core and the vector ALUs of a SIMD can work at the same time.
 // ---------------------------------------------------------------------------
 
-template <bool kBf16, int D, class Tiles>
+template <bool kBf16, int D, bool kNT, class Tiles>
 __device__ __forceinline__ void pp_body(const PrefixArgs &args, const WgTask &task,
                                         const PrefixNodeArg &nd, const Tiles &src, int tb,
                                         int te) {
@@ -651,8 +651,8 @@ __device__ __forceinline__ void pp_body(const PrefixArgs &args, const WgTask &ta
         if (valid >= kTile) {
 #pragma unroll
             for (int j = 0; j < kDmas; ++j) {
-                dma16_s(kt, koff[j], kdst + 2u * j * kRowsPerDma * D);
-                dma16_s(vt, voff[j], vdst + 2u * j * kRowsPerDma * D);
+                dma16_s<kNT>(kt, koff[j], kdst + 2u * j * kRowsPerDma * D);
+                dma16_s<kNT>(vt, voff[j], vdst + 2u * j * kRowsPerDma * D);
             }
         } else {
 #pragma unroll
@@ -664,8 +664,8 @@ __device__ __forceinline__ void pp_body(const PrefixArgs &args, const WgTask &ta
                     ko -= back;
                     vo -= back;
                 }
-                dma16_s(kt, ko, kdst + 2u * j * kRowsPerDma * D);
-                dma16_s(vt, vo, vdst + 2u * j * kRowsPerDma * D);
+                dma16_s<kNT>(kt, ko, kdst + 2u * j * kRowsPerDma * D);
+                dma16_s<kNT>(vt, vo, vdst + 2u * j * kRowsPerDma * D);
             }
         }
     };
@@ -835,7 +835,7 @@ __device__ __forceinline__ void pp_body(const PrefixArgs &args, const WgTask &ta
     }
 }
 
-template <bool kBf16, int D>
+template <bool kBf16, int D, bool kNT>
 __global__ __launch_bounds__(512) void prefix_mfma16_pp_kernel(PrefixArgs args) {
     const WgTask task = decode_wg(args);
     if (!task.valid) return;
@@ -843,7 +843,7 @@ __global__ __launch_bounds__(512) void prefix_mfma16_pp_kernel(PrefixArgs args) 
     const int ntiles = (nd.len + kTile - 1) / kTile;
     const int tb = task.split * nd.tiles_per_split;
     const int te = min(tb + nd.tiles_per_split, ntiles);
-    pp_body<kBf16, D>(args, task, nd, ContigTiles{nd.len}, tb, te);
+    pp_body<kBf16, D, kNT>(args, task, nd, ContigTiles{nd.len}, tb, te);
 }
 
 template <bool kBf16, int D>
@@ -855,7 +855,7 @@ __global__ __launch_bounds__(512) void tree_mfma16_pp_kernel(PrefixArgs args) {
     const int ntiles = nd.len / kTile;
     const int tb = task.split * nd.tiles_per_split;
     const int te = min(tb + nd.tiles_per_split, ntiles);
-    pp_body<kBf16, D>(args, task, nd, load_pieces(args, piece_begin, tb, te), tb, te);
+    pp_body<kBf16, D, false>(args, task, nd, load_pieces(args, piece_begin, tb, te), tb, te);
 }
 
 // ---------------------------------------------------------------------------
@@ -1009,12 +1009,22 @@ hipError_t launch_prefix(const PrefixArgs &a, int dtype, int d, int nw, int wgs,
         fits32 = fits32 && (int64_t)kTile * a.nodes[i].stride_tok + d <= (int64_t)INT32_MAX;
     if (kPingPongEnabled && fits32 && nw == 8 && dtype != HP_F32) {
         const dim3 grid(wgs), block(512);
-        if (dtype == HP_BF16) {
-            if (d == 128) prefix_mfma16_pp_kernel<true, 128><<<grid, block, 0, s>>>(a);
-            else prefix_mfma16_pp_kernel<true, 64><<<grid, block, 0, s>>>(a);
+        if (a.stream_kv) {
+            if (dtype == HP_BF16) {
+                if (d == 128) prefix_mfma16_pp_kernel<true, 128, true><<<grid, block, 0, s>>>(a);
+                else prefix_mfma16_pp_kernel<true, 64, true><<<grid, block, 0, s>>>(a);
+            } else {
+                if (d == 128) prefix_mfma16_pp_kernel<false, 128, true><<<grid, block, 0, s>>>(a);
+                else prefix_mfma16_pp_kernel<false, 64, true><<<grid, block, 0, s>>>(a);
+            }
         } else {
-            if (d == 128) prefix_mfma16_pp_kernel<false, 128><<<grid, block, 0, s>>>(a);
-            else prefix_mfma16_pp_kernel<false, 64><<<grid, block, 0, s>>>(a);
+            if (dtype == HP_BF16) {
+                if (d == 128) prefix_mfma16_pp_kernel<true, 128, false><<<grid, block, 0, s>>>(a);
+                else prefix_mfma16_pp_kernel<true, 64, false><<<grid, block, 0, s>>>(a);
+            } else {
+                if (d == 128) prefix_mfma16_pp_kernel<false, 128, false><<<grid, block, 0, s>>>(a);
+                else prefix_mfma16_pp_kernel<false, 64, false><<<grid, block, 0, s>>>(a);
+            }
         }
         return hipGetLastError();
     }
