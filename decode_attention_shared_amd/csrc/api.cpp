@@ -815,6 +815,9 @@ hp_status hp_stream_decode(const hp_query *q, const hp_prefix_tree *doc,
     a.scale_log2 = (float)((double)q->scale * 1.4426950408889634);
     a.dest = RowDest{o, lse, 0, 0, 0};
     a.pool_rows = rows->pool_rows;
+    // K/V footprint: the pool rows, or what the token tables can reach if less.
+    const int64_t kv_rows = std::min<int64_t>(rows->pool_rows, (int64_t)q->B * rows->row_cap);
+    a.stream_kv = kv_rows * q->Hkv * q->d * esize(q->dtype) * 2 >= kLlcBytes ? 1 : 0;
     a.nsrc = m.nsrc;
     for (int i = 0; i < m.nsrc; ++i) a.src[i] = m.src[i];
     a.stage_floats = stage_floats(m.src, m.nsrc, q->Hq / q->Hkv, q->d);

@@ -157,8 +157,9 @@ struct SuffixArgs {
     int64_t pool_rows;
     const float *part_o, *part_lse;
     int32_t stage_floats;     // dynamic LDS for staged partials (0: read them from memory)
-    int32_t stream_kv;        // paged mode: K/V loads marked non-temporal (footprint beyond the
-                              // last-level cache, so nothing of it would be found there next step)
+    int32_t stream_kv;        // paged and token-table modes: K/V loads marked non-temporal
+                              // (footprint beyond the last-level cache, so nothing of it would be
+                              // found there next step)
 };
 
 // Stream selection of a shared-context step: query b (request q_req[b],

@@ -562,7 +562,8 @@ hipError_t launch_tree_suffix(const SuffixArgs &a, int dtype, int d, int G, int 
 // Per-stream token tables of a shared-context request (a.table [B][cap]).
 hipError_t launch_token_suffix(const SuffixArgs &a, int dtype, int d, int G, int nws,
                                hipStream_t s) {
-    return launch_mode<kTokens>(a, dtype, d, G, nws, s);
+    return a.stream_kv ? launch_mode<kTokens, true>(a, dtype, d, G, nws, s)
+                       : launch_mode<kTokens, false>(a, dtype, d, G, nws, s);
 }
 
 }  // namespace hp
