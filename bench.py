@@ -109,6 +109,12 @@ def prepare(cfg, seed: int):
 EVENT_EVERY = 10  # steps between event-instrumented steps inside the timed region
 
 
+# Untimed steps before each sweep point and other shape: as many as before the
+# headline run, so that every line is timed after the same ramp of clocks and
+# queues.
+SWEEP_WARMUP = 20
+
+
 def time_steps(call, ev: HipEvents, steps: int, warmup: int):
     """Returns wall seconds for `steps` back-to-back steps and per-pass event times (ms).
 
@@ -259,7 +265,7 @@ def other_configs(ev, seed: int, steps: int):
                 workloads.two_level_gqa()):
         print(f"[bench] config {cfg.name}", file=sys.stderr, flush=True)
         st, cl = prepare(cfg, seed)
-        w, ps = time_steps(cl, ev, steps, 5)
+        w, ps = time_steps(cl, ev, steps, SWEEP_WARMUP)
         b = workloads.algorithmic_bytes(cfg, st.seq_lens.tolist())["total"]
         wms = w / steps * 1e3
         out.append({"workload": cfg.name, "path": "cascade", "steps_per_s": round(steps / w, 1),
@@ -279,7 +285,7 @@ def other_configs(ev, seed: int, steps: int):
     call = hp.StreamCall(st.q.to(dev), levels, st.k_pool.to(dev), st.v_pool.to(dev),
                          st.row_slots.to(dev), st.row_sid.to(dev), st.row_len.to(dev),
                          st.q_req.to(dev), st.q_sid.to(dev), st.scale)
-    for _ in range(5):
+    for _ in range(SWEEP_WARMUP):
         call()
     torch.cuda.synchronize()
     t0 = time.perf_counter()
@@ -324,7 +330,7 @@ def main():
     ap.add_argument("--no-sweep", action="store_true")
     ap.add_argument("--no-configs", action="store_true",
                     help="skip the other workload shapes and the stream-decode workload")
-    ap.add_argument("--sweep-steps", type=int, default=50)
+    ap.add_argument("--sweep-steps", type=int, default=200)
     ap.add_argument("--profile-only", action="store_true",
                     help="only run warmup + timed steps (for rocprofv3); no sweep or CPU leg")
     ap.add_argument("--share-sweep", action="store_true",
@@ -436,7 +442,7 @@ def main():
             c = workloads.codellama13b_mha(P)
             print(f"[bench] sweep prefix {P}", file=sys.stderr, flush=True)
             st, cl = prepare(c, args.seed)
-            w, ps = time_steps(cl, ev, args.sweep_steps, 5)
+            w, ps = time_steps(cl, ev, args.sweep_steps, SWEEP_WARMUP)
             sm = mean(ps["step"])
             b = workloads.algorithmic_bytes(c, st.seq_lens.tolist())["total"]
             wms = w / args.sweep_steps * 1e3
