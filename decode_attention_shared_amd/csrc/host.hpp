@@ -94,10 +94,13 @@ void plan_splits(const SplitItem *items, int count, int Hkv, int d, int nw, int6
 // the same speed as all of them (the chip's power budget, not its CU count,
 // bounds the matrix-core pass), leaving the rest to the memory-bound suffix.
 // Used when every prefix split keeps at least kConcMinTiles tiles under that
-// plan and the suffix has at least kConcMinUnits (sequence, KV head) units.
+// plan and the suffix has at least kConcMinUnits (sequence, KV head) units
+// (measured on MI355X: MHA steps with 2K-16K prefixes and 10 240 units gain
+// 2-10 %, a 1K prefix (4 tiles per split) loses 1 %, a two-level GQA step with
+// 2 048 units loses 10 %).
 constexpr int kConcCUs = 160;
-constexpr int kConcMinTiles = 32;
-constexpr int64_t kConcMinUnits = 1024;
+constexpr int kConcMinTiles = 8;
+constexpr int64_t kConcMinUnits = 4096;
 
 }  // namespace host
 }  // namespace hp

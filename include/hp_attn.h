@@ -209,7 +209,7 @@ hp_status hp_cascade_step(const hp_query *query, const hp_prefix_tree *tree,
  * Policy for running the passes side by side (see hp_cascade_step).  mode 0:
  * never; 1 (the default): when the plan expects a gain, that is when, with
  * the prefix pass planned for 160 of the 256 compute units, every prefix split
- * still covers at least 32 tiles of 64 keys, and the suffix has at least 1024
+ * still covers at least 8 tiles of 64 keys, and the suffix has at least 4096
  * (sequence, KV head) units; 2: whenever the step has both a prefix and a
  * suffix.  Process-wide.  The workspace size depends on the choice: query
  * hp_cascade_workspace_size after changing the mode.  HP_ERR_INVALID_ARG for
