@@ -36,6 +36,9 @@
  *              scratch space comes from the caller's workspace.  Q, K, V and O
  *              pointers must be 16-byte aligned and every stride a multiple of
  *              16 bytes; d elements of one (token, head) are contiguous.
+ *              K/V that a prefix launch, a paged suffix or a token-table pass
+ *              reads and that reach 256 MiB (MI355X's last-level cache) are
+ *              loaded non-temporal; results do not depend on it.
  * Streams.     `stream` is a hipStream_t (NULL = the null stream).  Work is
  *              enqueued asynchronously; calls are graph-capture safe (no
  *              allocation, host sync, memset or host-to-device copy).  The
