@@ -10,7 +10,14 @@ and raises AssertionError when that build disagrees with:
   * the split/merge identity of the Hydragen page ("Attention Decomposition
     Across Subsequences", Eq. 5), at the size and magnitude the "Shared Prefix
     KV Caching, in depth" page reports for its own float64 check (golden
-    fixture ``golden/split_merge_fp64.json``).
+    fixture ``golden/split_merge_fp64.json``);
+  * which keys a sequence of a generated step attends, rebuilt from the
+    config's node ranges alone (a node (len, i, j) serves sequences i .. j-1:
+    the ChunkAttention page's (C, i, j) descriptor, section "Context
+    Generation and GPU-CPU Coordination"; every node on the sequence's path,
+    root first: the Hydragen page, section "Hierarchical Sharing") and
+    evaluated by a dense numpy softmax;
+  * a subset of rows computed alone equals those rows of the full result.
 Run against the real build by test_oracle_pins.py, and against builds with
 planted mistakes by test_oracle_mutants.py.
 """
@@ -263,5 +270,75 @@ def pin_workload_step(lib):
     _close(l, bl, 1e-14, "tree brute LSE")
 
 
+def _dense_rows(q, keys_per_seq, Hkv, scale):
+    """Softmax attention of every (b, h) row by whole-array numpy fp64 operations
+    (scores as one matrix-vector product, logsumexp by numpy), a second
+    implementation of the definition independent of oracle.c."""
+    B, Hq, d = q.shape
+    G = Hq // Hkv
+    o = np.zeros((B * Hq, d))
+    l = np.full(B * Hq, -math.inf)
+    sc = float(np.float32(scale))
+    for b in range(B):
+        if not keys_per_seq[b]:
+            continue
+        K = np.concatenate([k.double().numpy() for (k, _) in keys_per_seq[b]], axis=0)
+        V = np.concatenate([v.double().numpy() for (_, v) in keys_per_seq[b]], axis=0)
+        for h in range(Hq):
+            s = sc * (K[:, h // G, :] @ q[b, h].double().numpy())
+            w = np.exp(s - s.max())
+            o[b * Hq + h] = (w @ V[:, h // G, :]) / w.sum()
+            l[b * Hq + h] = np.logaddexp.reduce(s)
+    return o, l
+
+
+def pin_workload_keys(lib):
+    """The keys a generated step's sequence attends, rebuilt from the config alone:
+    node (len, i, j) of a level serves sequences i .. j-1 (half-open, the (C, i, j)
+    descriptor of the ChunkAttention page), root level first, then the sequence's
+    own suffix.  The tree has sequences at both ends of a group's range and one
+    sequence under no group node, so a node range read one past either end, or a
+    level skipped, changes some row."""
+    cfg = workloads.custom("pin_keys", B=7, Hq=4, Hkv=2, d=16, dtype="f32",
+                           levels=(((30, 0, 7),), ((11, 0, 2), (9, 3, 5), (14, 5, 7))),
+                           suffix_lo=1, suffix_hi=12)
+    step = workloads.generate(cfg, seed=5)
+    keys = [[] for _ in range(cfg.B)]
+    for li, level in enumerate(cfg.levels):
+        for ni, (ln, i, j) in enumerate(level):
+            node = step.levels[li][ni]
+            assert node.k.shape[0] == ln, "generated node length differs from the config"
+            for b in range(i, j):
+                keys[b].append((node.k, node.v))
+    for b in range(cfg.B):
+        keys[b].append(step.suffix(b))
+    assert sum(1 for b in range(cfg.B) if len(keys[b]) == 2) == 1, "one sequence under no group"
+    want_o, want_l = _dense_rows(step.q, keys, cfg.Hkv, step.scale)
+    o, l = oracle.step_attention(step, "all", lib=lib)
+    _close(o, want_o, 1e-12, "step keys O")
+    _close(l, want_l, 1e-12, "step keys LSE")
+    # the prefix-only view attends the same nodes and nothing else
+    pre = [ks[:-1] for ks in keys]
+    want_o, want_l = _dense_rows(step.q, pre, cfg.Hkv, step.scale)
+    o, l = oracle.step_attention(step, "prefix", lib=lib)
+    _close(o, want_o, 1e-12, "prefix keys O")
+    _close(l, want_l, 1e-12, "prefix keys LSE")
+
+
+def pin_rows_subset(lib):
+    """Rows computed on their own (the rows= path, in any order, repeats allowed)
+    are bit-identical to the same rows of the full result."""
+    gen = torch.Generator().manual_seed(17)
+    q, segs = _tiny_problem(torch.bfloat16, gen, d=8, Hq=4, Hkv=2, B=5, plen=9)
+    scale = workloads.scale_for(8)
+    o, l = oracle.attention(q, segs, 2, scale, lib=lib)
+    rows = [17, 3, 3, 0, 11, 19, 8]
+    os_, ls_ = oracle.attention(q, segs, 2, scale, rows=rows, lib=lib)
+    assert os_.shape == (len(rows), 8) and ls_.shape == (len(rows),), "subset shapes"
+    for i, r in enumerate(rows):
+        assert np.array_equal(os_[i], o[r]) and ls_[i] == l[r], f"subset row {i} (row {r})"
+
+
 ALL_PINS = [pin_brute_force, pin_brute_force_extreme_values, pin_closed_forms, pin_invariances,
-            pin_split_merge_identity, pin_merge_edges, pin_workload_step]
+            pin_split_merge_identity, pin_merge_edges, pin_workload_step, pin_workload_keys,
+            pin_rows_subset]
