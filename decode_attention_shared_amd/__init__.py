@@ -40,14 +40,14 @@ HP_BLOCK_SIZE = 16
 HP_CHUNK = 64
 HP_TREE_MAX_LAUNCHES = 4
 STATUS = {0: "HP_OK", 1: "HP_ERR_NULL", 2: "HP_ERR_INVALID_ARG", 3: "HP_ERR_UNSUPPORTED",
-          4: "HP_ERR_WORKSPACE", 5: "HP_ERR_HIP", 6: "HP_ERR_CAPACITY"}
+          4: "HP_ERR_WORKSPACE", 5: "HP_ERR_HIP", 6: "HP_ERR_CAPACITY", 7: "HP_ERR_HOST"}
 EXPORTS = ["hp_prefix_attn_workspace_size", "hp_prefix_attn", "hp_suffix_decode_workspace_size",
            "hp_suffix_decode", "hp_lse_merge", "hp_cascade_workspace_size", "hp_cascade_step",
            "hp_cascade_step_timed", "hp_stream_decode_workspace_size", "hp_stream_decode",
            "hp_tree_plan_build", "hp_share_decision", "hp_tree_step", "hp_kv_append",
            "hp_pakv_create", "hp_pakv_destroy", "hp_pakv_insert", "hp_pakv_append",
            "hp_pakv_remove", "hp_pakv_context", "hp_pakv_seq_rows", "hp_pakv_get_stats",
-           "hp_set_concurrency", "hp_cascade_concurrent",
+           "hp_cascade_step_overlap", "hp_cascade_overlap_plan",
            "hp_status_string", "hp_last_hip_error", "hp_version"]
 
 _DTYPE = {torch.float32: HP_F32, torch.float16: HP_F16, torch.bfloat16: HP_BF16}
@@ -95,6 +95,11 @@ class StreamRows(ctypes.Structure):
                 ("row_len", ctypes.c_void_p), ("q_req", ctypes.c_void_p),
                 ("q_sid", ctypes.c_void_p), ("num_requests", ctypes.c_int32),
                 ("row_cap", ctypes.c_int32), ("pool_rows", ctypes.c_int64)]
+
+
+class Overlap(ctypes.Structure):
+    _fields_ = [("side_stream", ctypes.c_void_p), ("fork_event", ctypes.c_void_p),
+                ("join_event", ctypes.c_void_p), ("mode", ctypes.c_int32)]
 
 
 class ChunkDesc(ctypes.Structure):
@@ -164,19 +169,22 @@ def lib():
                                                     ctypes.POINTER(PrefixTree),
                                                     ctypes.POINTER(PagedKV),
                                                     ctypes.POINTER(ctypes.c_size_t)]
-            L.hp_set_concurrency.restype = st
-            L.hp_set_concurrency.argtypes = [ctypes.c_int32]
-            L.hp_cascade_concurrent.restype = st
-            L.hp_cascade_concurrent.argtypes = [ctypes.POINTER(Query), ctypes.POINTER(PrefixTree),
-                                                ctypes.POINTER(PagedKV),
-                                                ctypes.POINTER(ctypes.c_int32)]
+            L.hp_cascade_overlap_plan.restype = st
+            L.hp_cascade_overlap_plan.argtypes = [ctypes.POINTER(Query), ctypes.POINTER(PrefixTree),
+                                                  ctypes.POINTER(PagedKV), ctypes.c_int32,
+                                                  ctypes.POINTER(ctypes.c_int32)]
+            L.hp_cascade_step_overlap.restype = st
+            L.hp_cascade_step_overlap.argtypes = [ctypes.POINTER(Query), ctypes.POINTER(PrefixTree),
+                                                  ctypes.POINTER(PagedKV), p, p, p,
+                                                  ctypes.c_size_t, p, ctypes.POINTER(Overlap)]
             L.hp_cascade_step.restype = st
             L.hp_cascade_step.argtypes = [ctypes.POINTER(Query), ctypes.POINTER(PrefixTree),
                                           ctypes.POINTER(PagedKV), p, p, p, ctypes.c_size_t, p]
             L.hp_cascade_step_timed.restype = st
             L.hp_cascade_step_timed.argtypes = [ctypes.POINTER(Query), ctypes.POINTER(PrefixTree),
                                                 ctypes.POINTER(PagedKV), p, p, p,
-                                                ctypes.c_size_t, p, p, ctypes.c_int32]
+                                                ctypes.c_size_t, p, ctypes.POINTER(Overlap), p,
+                                                ctypes.c_int32]
             i32, i64 = ctypes.c_int32, ctypes.c_int64
             L.hp_stream_decode_workspace_size.restype = st
             L.hp_stream_decode_workspace_size.argtypes = [ctypes.POINTER(Query),
@@ -218,6 +226,54 @@ def lib():
     return _lib
 
 
+_hiprt = None
+
+
+def _hip():
+    """The HIP runtime (for the events a side-by-side step records); the binding owns
+    every handle it creates."""
+    global _hiprt
+    if _hiprt is None:
+        rt = ctypes.CDLL("libamdhip64.so")
+        rt.hipEventCreateWithFlags.argtypes = [ctypes.POINTER(ctypes.c_void_p), ctypes.c_uint]
+        rt.hipEventCreateWithFlags.restype = ctypes.c_int
+        rt.hipEventDestroy.argtypes = [ctypes.c_void_p]
+        rt.hipEventDestroy.restype = ctypes.c_int
+        _hiprt = rt
+    return _hiprt
+
+
+class SideStreams:
+    """A second stream and the fork/join events for hp_cascade_step_overlap, owned here:
+    a torch stream on ``device`` (default priority) and two hipEvent_t handles created
+    with hipEventDisableTiming, destroyed with this object."""
+
+    def __init__(self, device, mode: int = 1):
+        self.stream = torch.cuda.Stream(device=device)
+        rt = _hip()
+        self._events = []
+        for _ in range(2):
+            h = ctypes.c_void_p()
+            with torch.cuda.device(device):
+                if rt.hipEventCreateWithFlags(ctypes.byref(h), 2) != 0:  # hipEventDisableTiming
+                    raise RuntimeError("hipEventCreateWithFlags failed")
+            self._events.append(h.value)
+        self.desc = Overlap(self.stream.cuda_stream, self._events[0], self._events[1], mode)
+
+    def close(self):
+        # destroying an event that is still pending is allowed: HIP releases it once
+        # the work it marks has completed
+        for h in self._events:
+            _hip().hipEventDestroy(h)
+        self._events = []
+
+    def __del__(self):
+        try:
+            self.close()
+        except Exception:
+            pass
+
+
 def _check(status: int, where: str) -> None:
     if status != 0:
         raise HpError(status, where, lib())
@@ -233,6 +289,37 @@ def _stream(stream) -> Optional[int]:
     if isinstance(stream, int):
         return stream
     return stream.cuda_stream
+
+
+def _torch_stream(stream, device):
+    """The torch stream object for ``stream`` (None: the current stream; an int: a raw
+    hipStream_t handle, wrapped without taking ownership)."""
+    if stream is None:
+        return torch.cuda.current_stream(device)
+    if isinstance(stream, int):
+        return torch.cuda.ExternalStream(stream, device=device)
+    return stream
+
+
+def _on(stream, device):
+    """Context in which temporaries are allocated from ``stream``'s pool of the caching
+    allocator, so that freeing them after the call is ordered after the kernels that the
+    call enqueued on that stream (not on whichever stream happens to be current)."""
+    return torch.cuda.stream(_torch_stream(stream, device))
+
+
+def _record(stream, tensors) -> None:
+    """Mark long-lived buffers as in use by ``stream`` when it is not the stream they
+    were allocated on, so the caching allocator does not reuse them early when freed."""
+    if stream is None:
+        return
+    ts = None
+    for t in tensors:
+        if t is None:
+            continue
+        if ts is None:
+            ts = _torch_stream(stream, t.device)
+        t.record_stream(ts)
 
 
 def _require_cuda(t: torch.Tensor, name: str) -> None:
@@ -313,13 +400,14 @@ def prefix_attn(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, seq_begin: in
     Hkv = k.shape[1]
     qs = make_query(q, Hkv, scale)
     node = make_node(k, v, seq_begin, q.shape[0] if seq_end is None else seq_end)
-    out, lse = _out(q, out, lse, zero=True)
     nbytes = ctypes.c_size_t(0)
     _check(L.hp_prefix_attn_workspace_size(ctypes.byref(qs), ctypes.byref(node),
                                            ctypes.byref(nbytes)), "hp_prefix_attn_workspace_size")
-    ws = _workspace(nbytes.value, q.device)
-    _check(L.hp_prefix_attn(ctypes.byref(qs), ctypes.byref(node), out.data_ptr(), _ptr(lse),
-                            _ptr(ws), nbytes.value, _stream(stream)), "hp_prefix_attn")
+    with _on(stream, q.device):
+        out, lse = _out(q, out, lse, zero=True)
+        ws = _workspace(nbytes.value, q.device)
+        _check(L.hp_prefix_attn(ctypes.byref(qs), ctypes.byref(node), out.data_ptr(), _ptr(lse),
+                                _ptr(ws), nbytes.value, _stream(stream)), "hp_prefix_attn")
     return out, lse
 
 
@@ -329,14 +417,15 @@ def suffix_decode(q: torch.Tensor, k_pool: torch.Tensor, v_pool: torch.Tensor,
     L = lib()
     qs = make_query(q, k_pool.shape[2], scale)
     kv = make_paged(k_pool, v_pool, block_table, seq_lens)
-    out, lse = _out(q, out, lse, zero=False)
     nbytes = ctypes.c_size_t(0)
     _check(L.hp_suffix_decode_workspace_size(ctypes.byref(qs), ctypes.byref(kv),
                                              ctypes.byref(nbytes)),
            "hp_suffix_decode_workspace_size")
-    ws = _workspace(nbytes.value, q.device)
-    _check(L.hp_suffix_decode(ctypes.byref(qs), ctypes.byref(kv), out.data_ptr(), _ptr(lse),
-                              _ptr(ws), nbytes.value, _stream(stream)), "hp_suffix_decode")
+    with _on(stream, q.device):
+        out, lse = _out(q, out, lse, zero=False)
+        ws = _workspace(nbytes.value, q.device)
+        _check(L.hp_suffix_decode(ctypes.byref(qs), ctypes.byref(kv), out.data_ptr(), _ptr(lse),
+                                  _ptr(ws), nbytes.value, _stream(stream)), "hp_suffix_decode")
     return out, lse
 
 
@@ -356,23 +445,31 @@ def lse_merge(o_list: Sequence[torch.Tensor], lse_list: Sequence[torch.Tensor], 
         if o.dtype != torch.float32 or l.dtype != torch.float32 or not o.is_contiguous() or \
                 not l.is_contiguous() or o.numel() != rows * d or l.numel() != rows:
             raise ValueError("partials must be contiguous fp32 with matching shapes")
-    if out is None:
-        out = torch.empty_like(o0)
-    if lse is None:
-        lse = torch.empty_like(lse_list[0])
-    po = (ctypes.c_void_p * n)(*[o.data_ptr() for o in o_list])
-    pl = (ctypes.c_void_p * n)(*[l.data_ptr() for l in lse_list])
-    _check(L.hp_lse_merge(n, ctypes.addressof(po), ctypes.addressof(pl), out.data_ptr(),
-                          _ptr(lse), rows, d, _stream(stream)), "hp_lse_merge")
+    with _on(stream, o0.device):
+        if out is None:
+            out = torch.empty_like(o0)
+        if lse is None:
+            lse = torch.empty_like(lse_list[0])
+        po = (ctypes.c_void_p * n)(*[o.data_ptr() for o in o_list])
+        pl = (ctypes.c_void_p * n)(*[l.data_ptr() for l in lse_list])
+        _check(L.hp_lse_merge(n, ctypes.addressof(po), ctypes.addressof(pl), out.data_ptr(),
+                              _ptr(lse), rows, d, _stream(stream)), "hp_lse_merge")
     return out, lse
 
 
 class CascadeCall:
-    """A prepared hp_cascade_step: structs, workspace and outputs built once, so a
-    step costs one ctypes call (used for timing and graph capture)."""
+    """A prepared cascade step: structs, workspace and outputs built once, so a step
+    costs one ctypes call (used for timing and graph capture).
+
+    overlap: 0 runs the passes one after the other on the caller's stream
+    (hp_cascade_step); 1 (the default) or 2 passes the library a second stream and two
+    events owned by this object (hp_cascade_step_overlap, mode 1: when the plan expects a
+    gain, 2: whenever there is a prefix and a suffix).  ``concurrent`` says whether the
+    passes run side by side."""
 
     def __init__(self, q: torch.Tensor, levels, k_pool=None, v_pool=None, block_table=None,
-                 seq_lens=None, scale: Optional[float] = None, out=None, lse=None):
+                 seq_lens=None, scale: Optional[float] = None, out=None, lse=None,
+                 overlap: int = 1):
         L = lib()
         self._L = L
         Hkv = (levels[0][0][0].shape[1] if levels and levels[0] else k_pool.shape[2])
@@ -389,15 +486,27 @@ class CascadeCall:
         self.workspace_bytes = nbytes.value
         self.ws = _workspace(nbytes.value, q.device)
         flag = ctypes.c_int32(0)
-        _check(L.hp_cascade_concurrent(ctypes.byref(self.query), self._tree_p, self._kv_p,
-                                       ctypes.byref(flag)), "hp_cascade_concurrent")
+        _check(L.hp_cascade_overlap_plan(ctypes.byref(self.query), self._tree_p, self._kv_p,
+                                         int(overlap), ctypes.byref(flag)),
+               "hp_cascade_overlap_plan")
         self.concurrent = bool(flag.value)  # suffix pass beside the prefix pass
+        self.side = SideStreams(q.device, int(overlap)) if self.concurrent else None
+        self._ov_p = ctypes.byref(self.side.desc) if self.side is not None else None
         self._refs = (levels, k_pool, v_pool, block_table, seq_lens)
 
     def __call__(self, stream=None):
-        _check(self._L.hp_cascade_step(ctypes.byref(self.query), self._tree_p, self._kv_p,
-                                       self.out.data_ptr(), _ptr(self.lse), _ptr(self.ws),
-                                       self.workspace_bytes, _stream(stream)), "hp_cascade_step")
+        _record(stream, (self.ws, self.out, self.lse))
+        if self._ov_p is not None:
+            st = self._L.hp_cascade_step_overlap(ctypes.byref(self.query), self._tree_p, self._kv_p,
+                                                 self.out.data_ptr(), _ptr(self.lse),
+                                                 _ptr(self.ws), self.workspace_bytes,
+                                                 _stream(stream), self._ov_p)
+            _check(st, "hp_cascade_step_overlap")
+        else:
+            _check(self._L.hp_cascade_step(ctypes.byref(self.query), self._tree_p, self._kv_p,
+                                           self.out.data_ptr(), _ptr(self.lse), _ptr(self.ws),
+                                           self.workspace_bytes, _stream(stream)),
+                   "hp_cascade_step")
         return self.out, self.lse
 
     def timed(self, events, stream=None):
@@ -406,18 +515,23 @@ class CascadeCall:
         right before the suffix pass on its stream."""
         n = len(events)
         arr = (ctypes.c_void_p * n)(*events)
+        _record(stream, (self.ws, self.out, self.lse))
         _check(self._L.hp_cascade_step_timed(ctypes.byref(self.query), self._tree_p, self._kv_p,
                                              self.out.data_ptr(), _ptr(self.lse), _ptr(self.ws),
-                                             self.workspace_bytes, _stream(stream),
+                                             self.workspace_bytes, _stream(stream), self._ov_p,
                                              ctypes.addressof(arr), n), "hp_cascade_step_timed")
         return self.out, self.lse
 
 
 def cascade_step(q: torch.Tensor, levels, k_pool=None, v_pool=None, block_table=None,
-                 seq_lens=None, scale: Optional[float] = None, out=None, lse=None, stream=None):
+                 seq_lens=None, scale: Optional[float] = None, out=None, lse=None, stream=None,
+                 overlap: int = 1):
     """levels: root first, each a list of (k, v, seq_begin, seq_end) device tensors/ints;
     the pools, table and lengths describe the paged suffixes (or None for prefix only)."""
-    return CascadeCall(q, levels, k_pool, v_pool, block_table, seq_lens, scale, out, lse)(stream)
+    with _on(stream, q.device):
+        call = CascadeCall(q, levels, k_pool, v_pool, block_table, seq_lens, scale, out, lse,
+                           overlap)
+        return call(stream)
 
 
 # ------------------------------------------------------------------------------
@@ -476,6 +590,7 @@ class StreamCall:
         self._refs = (q, doc_levels, k_pool, v_pool, row_slots, slot_sid, row_len, q_req, q_sid)
 
     def __call__(self, stream=None):
+        _record(stream, (self.ws, self.out, self.lse))
         _check(self._L.hp_stream_decode(ctypes.byref(self.query), self._tree_p,
                                         ctypes.byref(self.rows), self.out.data_ptr(),
                                         _ptr(self.lse), _ptr(self.ws), self.workspace_bytes,
@@ -485,8 +600,9 @@ class StreamCall:
 
 def stream_decode(q: torch.Tensor, doc_levels, k_pool, v_pool, row_slots, slot_sid, row_len,
                   q_req, q_sid, scale: Optional[float] = None, out=None, lse=None, stream=None):
-    return StreamCall(q, doc_levels, k_pool, v_pool, row_slots, slot_sid, row_len, q_req,
-                      q_sid, scale, out, lse)(stream)
+    with _on(stream, q.device):
+        return StreamCall(q, doc_levels, k_pool, v_pool, row_slots, slot_sid, row_len, q_req,
+                          q_sid, scale, out, lse)(stream)
 
 
 def _descs_array(descs) -> Tuple[ctypes.Array, int]:
@@ -515,14 +631,6 @@ def tree_plan_build(B: int, Hq: int, Hkv: int, d: int, dtype: torch.dtype, descs
                                 pool_rows, blob.data_ptr(), blob.numel(), ctypes.byref(plan)),
            "hp_tree_plan_build")
     return plan, blob
-
-
-def set_concurrency(mode: int) -> None:
-    """Policy for running a cascade step's suffix pass beside its prefix pass
-    (hp_set_concurrency): 0 never, 1 when the plan expects a gain (the default),
-    2 whenever there is a suffix.  Build CascadeCall objects after changing it (the
-    workspace size depends on it)."""
-    _check(lib().hp_set_concurrency(int(mode)), "hp_set_concurrency")
 
 
 def share_decision(Hq: int, Hkv: int, tokens: int, nseq: int, d: int = 128,
@@ -567,7 +675,9 @@ class TreeStep:
             _require_cuda(seq_lens, "seq_lens")
             if seq_lens.dtype != torch.int32 or seq_lens.numel() != q.shape[0]:
                 raise ValueError("seq_lens must be int32 [B]")
-        out, lse = _out(q, out, lse, zero=False)
+        _record(stream, (self.ws, self.blob))
+        with _on(stream, q.device):
+            out, lse = _out(q, out, lse, zero=False)
         _check(L.hp_tree_step(ctypes.byref(qs), ctypes.byref(self.plan), self.blob.data_ptr(),
                               k_pool.data_ptr(), v_pool.data_ptr(), _ptr(seq_lens),
                               out.data_ptr(), _ptr(lse), _ptr(self.ws), self.plan.workspace_bytes,

@@ -21,6 +21,7 @@ BUILD_DIR = os.path.join(ROOT, "_build")
 LIB_PATH = os.path.join(HERE, "libhp_attn.so")
 SOURCES = ["api.cpp", "tree.cpp", "pakv.cpp", "prefix_kernel.hip", "suffix_kernel.hip",
            "merge_kernel.hip", "append_kernel.hip", "stream_kernel.hip"]
+SOURCE_FLAGS = {}  # per-source extra flags
 ARCH = "gfx950"
 
 COMMON_FLAGS = [
@@ -40,7 +41,8 @@ def _hipcc() -> str:
 
 def _compile(src: str, extra) -> str:
     obj = os.path.join(BUILD_DIR, os.path.splitext(src)[0] + ".o")
-    cmd = [_hipcc(), "-x", "hip", *COMMON_FLAGS, *extra, "-c", os.path.join(CSRC, src), "-o", obj]
+    cmd = [_hipcc(), "-x", "hip", *COMMON_FLAGS, *SOURCE_FLAGS.get(src, []), *extra, "-c",
+           os.path.join(CSRC, src), "-o", obj]
     r = subprocess.run(cmd, capture_output=True, text=True)
     # the host pass always warns about the packed-fp32 feature; show anything else
     noise = "'-packed-fp32-ops' is not a recognized feature"

@@ -6,13 +6,12 @@
 #include <hip/hip_runtime.h>
 
 #include <algorithm>
-#include <atomic>
-#include <mutex>
 #include <cmath>
 #include <utility>
 #include <cstdint>
 #include <cstring>
 
+#include "guard.hpp"
 #include "host.hpp"
 
 namespace {
@@ -304,10 +303,6 @@ struct CascadePlan {
     size_t bytes = 0;
 };
 
-// 0: never run the passes concurrently, 1: when the plan says it pays, 2:
-// whenever there is a suffix.
-std::atomic<int> g_concurrency{1};
-
 // Lay out the prefix launches of the tree for `cus` compute units; returns
 // the workspace bytes of their partials.
 size_t plan_prefix(const hp_query *q, const hp_prefix_tree *tree, CascadePlan &cp, int cus) {
@@ -347,8 +342,12 @@ size_t plan_prefix(const hp_query *q, const hp_prefix_tree *tree, CascadePlan &c
 }
 
 // Plan of a whole cascade step (shared by the size query and the run).
+// mode: 0 the passes one after the other on one stream; 1 side by side when
+// the plan expects a gain; 2 side by side whenever there is a prefix and a
+// suffix.
 hp_status plan_cascade(const hp_query *q, const hp_prefix_tree *tree, const hp_paged_kv *kv,
-                       CascadePlan &cp) {
+                       int mode, CascadePlan &cp) {
+    if (mode < 0 || mode > 2) return HP_ERR_INVALID_ARG;
     hp_status st = check_query(q);
     if (st != HP_OK) return st;
     st = check_tree(q, tree, &cp.total_nodes);
@@ -362,7 +361,6 @@ hp_status plan_cascade(const hp_query *q, const hp_prefix_tree *tree, const hp_p
     // The suffix pass beside the prefix pass: the prefix is planned for
     // kConcCUs compute units, the suffix writes its own (O, LSE) rows and one
     // merge combines them with the prefix partials.
-    const int mode = g_concurrency.load(std::memory_order_relaxed);
     if (cp.has_suffix && cp.total_nodes > 0 && q->B > 0 && mode != 0) {
         CascadePlan alt = cp;
         const size_t pbytes = plan_prefix(q, tree, alt, kConcCUs);
@@ -381,6 +379,19 @@ hp_status plan_cascade(const hp_query *q, const hp_prefix_tree *tree, const hp_p
     return HP_OK;
 }
 
+// Workspace that serves every mode: the larger of the serial plan and the
+// always-side-by-side plan.
+hp_status cascade_ws_bytes(const hp_query *q, const hp_prefix_tree *tree, const hp_paged_kv *kv,
+                           size_t *bytes) {
+    CascadePlan serial, conc;
+    hp_status st = plan_cascade(q, tree, kv, 0, serial);
+    if (st != HP_OK) return st;
+    st = plan_cascade(q, tree, kv, 2, conc);
+    if (st != HP_OK) return st;
+    *bytes = std::max(serial.bytes, conc.bytes);
+    return HP_OK;
+}
+
 }  // namespace
 
 extern "C" {
@@ -394,6 +405,7 @@ const char *hp_status_string(hp_status s) {
     case HP_ERR_WORKSPACE: return "workspace missing or too small";
     case HP_ERR_HIP: return "HIP launch failed";
     case HP_ERR_CAPACITY: return "capacity exceeded (pool, plan buffer or output array too small)";
+    case HP_ERR_HOST: return "host-side failure (out of host memory)";
     default: return "unknown status";
     }
 }
@@ -406,146 +418,151 @@ const char *hp_version(void) { return "hp_attn 0.1 gfx950"; }
 
 hp_status hp_prefix_attn_workspace_size(const hp_query *q, const hp_prefix_node *node,
                                         size_t *bytes) {
-    if (!bytes) return HP_ERR_NULL;
-    hp_status st = check_query(q);
-    if (st != HP_OK) return st;
-    st = check_node(q, node);
-    if (st != HP_OK) return st;
-    LevelPlan lp;
-    plan_level(*q, node, 1, lp);
-    *bytes = lp.nodes[0].nsplit > 1 ? node_ws_bytes(lp.nodes[0], q->d) : 0;
-    return HP_OK;
+    return hp::guarded([&]() -> hp_status {
+        if (!bytes) return HP_ERR_NULL;
+        hp_status st = check_query(q);
+        if (st != HP_OK) return st;
+        st = check_node(q, node);
+        if (st != HP_OK) return st;
+        LevelPlan lp;
+        plan_level(*q, node, 1, lp);
+        *bytes = lp.nodes[0].nsplit > 1 ? node_ws_bytes(lp.nodes[0], q->d) : 0;
+        return HP_OK;
+    });
 }
 
 hp_status hp_prefix_attn(const hp_query *q, const hp_prefix_node *node, float *o, float *lse,
                          void *ws, size_t ws_bytes, void *stream) {
-    hp_status st = check_query(q);
-    if (st != HP_OK) return st;
-    st = check_node(q, node);
-    if (st != HP_OK) return st;
-    st = check_out(o, lse);
-    if (st != HP_OK) return st;
-    LevelPlan lp;
-    plan_level(*q, node, 1, lp);
-    const NodePlan &np = lp.nodes[0];
-    hipStream_t s = (hipStream_t)stream;
-    if (np.nsplit == 1) {
-        const RowDest dest{o, lse, 0, 0, 0};
-        return run_level(*q, node, lp, &dest, s);
-    }
-    const size_t need = node_ws_bytes(np, q->d);
-    if (!ws || ws_bytes < need || !aligned16(ws)) return HP_ERR_WORKSPACE;
-    float *wo = (float *)ws;
-    float *wl = (float *)((char *)ws + round_up((size_t)np.nsplit * np.rows * q->d * 4, kWsAlign));
-    const RowDest dest{wo, wl, np.rows * q->d, np.rows, node->seq_begin};
-    st = run_level(*q, node, lp, &dest, s);
-    if (st != HP_OK) return st;
-    MergeArgs m;
-    std::memset(&m, 0, sizeof m);
-    m.src[0] = MergeSrc{wo, wl, np.rows * q->d, np.rows, np.nsplit, 0, node->seq_begin,
-                        node->seq_end};
-    m.nsrc = 1;
-    m.Hq = q->Hq;
-    m.row_b0 = node->seq_begin;
-    m.row_b1 = node->seq_end;
-    m.o = o;
-    m.lse = lse;
-    hipError_t e = launch_merge(m, q->d, s);
-    return e == hipSuccess ? HP_OK : fail_hip(e);
+    return hp::guarded([&]() -> hp_status {
+        hp_status st = check_query(q);
+        if (st != HP_OK) return st;
+        st = check_node(q, node);
+        if (st != HP_OK) return st;
+        st = check_out(o, lse);
+        if (st != HP_OK) return st;
+        LevelPlan lp;
+        plan_level(*q, node, 1, lp);
+        const NodePlan &np = lp.nodes[0];
+        hipStream_t s = (hipStream_t)stream;
+        if (np.nsplit == 1) {
+            const RowDest dest{o, lse, 0, 0, 0};
+            return run_level(*q, node, lp, &dest, s);
+        }
+        const size_t need = node_ws_bytes(np, q->d);
+        if (!ws || ws_bytes < need || !aligned16(ws)) return HP_ERR_WORKSPACE;
+        float *wo = (float *)ws;
+        float *wl =
+            (float *)((char *)ws + round_up((size_t)np.nsplit * np.rows * q->d * 4, kWsAlign));
+        const RowDest dest{wo, wl, np.rows * q->d, np.rows, node->seq_begin};
+        st = run_level(*q, node, lp, &dest, s);
+        if (st != HP_OK) return st;
+        MergeArgs m;
+        std::memset(&m, 0, sizeof m);
+        m.src[0] = MergeSrc{wo, wl, np.rows * q->d, np.rows, np.nsplit, 0, node->seq_begin,
+                            node->seq_end};
+        m.nsrc = 1;
+        m.Hq = q->Hq;
+        m.row_b0 = node->seq_begin;
+        m.row_b1 = node->seq_end;
+        m.o = o;
+        m.lse = lse;
+        hipError_t e = launch_merge(m, q->d, s);
+        return e == hipSuccess ? HP_OK : fail_hip(e);
+    });
 }
 
 // ------------------------------- suffix -----------------------------------
 
 hp_status hp_suffix_decode_workspace_size(const hp_query *q, const hp_paged_kv *kv,
                                           size_t *bytes) {
-    if (!bytes) return HP_ERR_NULL;
-    hp_status st = check_query(q);
-    if (st != HP_OK) return st;
-    st = check_kv(q, kv);
-    if (st != HP_OK) return st;
-    *bytes = 0;  // the waves of one (sequence, KV head) combine in LDS
-    return HP_OK;
+    return hp::guarded([&]() -> hp_status {
+        if (!bytes) return HP_ERR_NULL;
+        hp_status st = check_query(q);
+        if (st != HP_OK) return st;
+        st = check_kv(q, kv);
+        if (st != HP_OK) return st;
+        *bytes = 0;  // the waves of one (sequence, KV head) combine in LDS
+        return HP_OK;
+    });
 }
 
 hp_status hp_suffix_decode(const hp_query *q, const hp_paged_kv *kv, float *o, float *lse,
                            void *ws, size_t ws_bytes, void *stream) {
-    (void)ws;
-    (void)ws_bytes;
-    hp_status st = check_query(q);
-    if (st != HP_OK) return st;
-    st = check_kv(q, kv);
-    if (st != HP_OK) return st;
-    st = check_out(o, lse);
-    if (st != HP_OK) return st;
-    if (q->B == 0) return HP_OK;
-    const SuffixArgs a = suffix_args(*q, *kv, RowDest{o, lse, 0, 0, 0});
-    hipError_t e = launch_suffix(a, q->dtype, q->d, q->Hq / q->Hkv, suffix_waves(*q, *kv),
-                                 (hipStream_t)stream);
-    return e == hipSuccess ? HP_OK : fail_hip(e);
+    return hp::guarded([&]() -> hp_status {
+        (void)ws;
+        (void)ws_bytes;
+        hp_status st = check_query(q);
+        if (st != HP_OK) return st;
+        st = check_kv(q, kv);
+        if (st != HP_OK) return st;
+        st = check_out(o, lse);
+        if (st != HP_OK) return st;
+        if (q->B == 0) return HP_OK;
+        const SuffixArgs a = suffix_args(*q, *kv, RowDest{o, lse, 0, 0, 0});
+        hipError_t e = launch_suffix(a, q->dtype, q->d, q->Hq / q->Hkv, suffix_waves(*q, *kv),
+                                     (hipStream_t)stream);
+        return e == hipSuccess ? HP_OK : fail_hip(e);
+    });
 }
 
 // -------------------------------- merge -----------------------------------
 
 hp_status hp_lse_merge(int32_t n, const float *const *o_in, const float *const *lse_in, float *o,
                        float *lse, int64_t rows, int32_t d, void *stream) {
-    if (!o_in || !lse_in || !o) return HP_ERR_NULL;
-    if (n < 1 || n > HP_MAX_MERGE || rows < 0) return HP_ERR_INVALID_ARG;
-    if (d != 64 && d != 128) return HP_ERR_UNSUPPORTED;
-    if (!aligned16(o) || ((uintptr_t)lse & 3u)) return HP_ERR_INVALID_ARG;
-    const uintptr_t olo = (uintptr_t)o, ohi = olo + (uintptr_t)rows * d * sizeof(float);
-    const uintptr_t llo = (uintptr_t)lse, lhi = llo + (uintptr_t)rows * sizeof(float);
-    for (int i = 0; i < n; ++i) {
-        if (!o_in[i] || !lse_in[i]) return HP_ERR_NULL;
-        if (!aligned16(o_in[i]) || ((uintptr_t)lse_in[i] & 3u)) return HP_ERR_INVALID_ARG;
-        const uintptr_t a0 = (uintptr_t)o_in[i], a1 = a0 + (uintptr_t)rows * d * sizeof(float);
-        const uintptr_t b0 = (uintptr_t)lse_in[i], b1 = b0 + (uintptr_t)rows * sizeof(float);
-        auto overlap = [](uintptr_t x0, uintptr_t x1, uintptr_t y0, uintptr_t y1) {
-            return x0 < y1 && y0 < x1;
-        };
-        if (rows > 0 && (overlap(olo, ohi, a0, a1) || overlap(olo, ohi, b0, b1) ||
-                         (lse && (overlap(llo, lhi, a0, a1) || overlap(llo, lhi, b0, b1)))))
-            return HP_ERR_INVALID_ARG;
-    }
-    if (rows == 0) return HP_OK;
-    MergeArgs m;
-    std::memset(&m, 0, sizeof m);
-    for (int i = 0; i < n; ++i) m.src[i] = MergeSrc{o_in[i], lse_in[i], 0, 0, 1, 0, 0, rows};
-    m.nsrc = n;
-    m.Hq = 1;
-    m.row_b0 = 0;
-    m.row_b1 = rows;
-    m.o = o;
-    m.lse = lse;
-    hipError_t e = launch_merge(m, d, (hipStream_t)stream);
-    return e == hipSuccess ? HP_OK : fail_hip(e);
+    return hp::guarded([&]() -> hp_status {
+        if (!o_in || !lse_in || !o) return HP_ERR_NULL;
+        if (n < 1 || n > HP_MAX_MERGE || rows < 0) return HP_ERR_INVALID_ARG;
+        if (d != 64 && d != 128) return HP_ERR_UNSUPPORTED;
+        if (!aligned16(o) || ((uintptr_t)lse & 3u)) return HP_ERR_INVALID_ARG;
+        const uintptr_t olo = (uintptr_t)o, ohi = olo + (uintptr_t)rows * d * sizeof(float);
+        const uintptr_t llo = (uintptr_t)lse, lhi = llo + (uintptr_t)rows * sizeof(float);
+        for (int i = 0; i < n; ++i) {
+            if (!o_in[i] || !lse_in[i]) return HP_ERR_NULL;
+            if (!aligned16(o_in[i]) || ((uintptr_t)lse_in[i] & 3u)) return HP_ERR_INVALID_ARG;
+            const uintptr_t a0 = (uintptr_t)o_in[i], a1 = a0 + (uintptr_t)rows * d * sizeof(float);
+            const uintptr_t b0 = (uintptr_t)lse_in[i], b1 = b0 + (uintptr_t)rows * sizeof(float);
+            auto overlap = [](uintptr_t x0, uintptr_t x1, uintptr_t y0, uintptr_t y1) {
+                return x0 < y1 && y0 < x1;
+            };
+            if (rows > 0 && (overlap(olo, ohi, a0, a1) || overlap(olo, ohi, b0, b1) ||
+                             (lse && (overlap(llo, lhi, a0, a1) || overlap(llo, lhi, b0, b1)))))
+                return HP_ERR_INVALID_ARG;
+        }
+        if (rows == 0) return HP_OK;
+        MergeArgs m;
+        std::memset(&m, 0, sizeof m);
+        for (int i = 0; i < n; ++i) m.src[i] = MergeSrc{o_in[i], lse_in[i], 0, 0, 1, 0, 0, rows};
+        m.nsrc = n;
+        m.Hq = 1;
+        m.row_b0 = 0;
+        m.row_b1 = rows;
+        m.o = o;
+        m.lse = lse;
+        hipError_t e = launch_merge(m, d, (hipStream_t)stream);
+        return e == hipSuccess ? HP_OK : fail_hip(e);
+    });
 }
 
 // ------------------------------- cascade ----------------------------------
 
-hp_status hp_set_concurrency(int32_t mode) {
-    if (mode < 0 || mode > 2) return HP_ERR_INVALID_ARG;
-    g_concurrency.store(mode, std::memory_order_relaxed);
-    return HP_OK;
-}
-
-hp_status hp_cascade_concurrent(const hp_query *q, const hp_prefix_tree *tree,
-                                const hp_paged_kv *kv, int32_t *concurrent) {
-    if (!concurrent) return HP_ERR_NULL;
-    CascadePlan cp;
-    hp_status st = plan_cascade(q, tree, kv, cp);
-    if (st != HP_OK) return st;
-    *concurrent = cp.conc ? 1 : 0;
-    return HP_OK;
+hp_status hp_cascade_overlap_plan(const hp_query *q, const hp_prefix_tree *tree,
+                                  const hp_paged_kv *kv, int32_t mode, int32_t *overlapped) {
+    return hp::guarded([&]() -> hp_status {
+        if (!overlapped) return HP_ERR_NULL;
+        CascadePlan cp;
+        hp_status st = plan_cascade(q, tree, kv, mode, cp);
+        if (st != HP_OK) return st;
+        *overlapped = cp.conc ? 1 : 0;
+        return HP_OK;
+    });
 }
 
 hp_status hp_cascade_workspace_size(const hp_query *q, const hp_prefix_tree *tree,
                                     const hp_paged_kv *kv, size_t *bytes) {
-    if (!bytes) return HP_ERR_NULL;
-    CascadePlan cp;
-    hp_status st = plan_cascade(q, tree, kv, cp);
-    if (st != HP_OK) return st;
-    *bytes = cp.bytes;
-    return HP_OK;
+    return hp::guarded([&]() -> hp_status {
+        if (!bytes) return HP_ERR_NULL;
+        return cascade_ws_bytes(q, tree, kv, bytes);
+    });
 }
 
 }  // extern "C"
@@ -558,74 +575,24 @@ hp_status record(void *const *events, int i, hipStream_t s) {
     return e == hipSuccess ? HP_OK : fail_hip(e);
 }
 
-// A second stream per device for the suffix pass when it runs beside the
-// prefix pass, with its fork and join events: created on first use (default
-// priority, not synchronising with the null stream) and kept until the
-// process ends.  The fork/launch/join sequence is enqueued under a mutex, so
-// calls from several host threads do not interleave their uses of the events.
-struct SideStream {
-    hipStream_t s = nullptr;
-    hipEvent_t fork = nullptr, join = nullptr;
-    bool tried = false;
-};
-constexpr int kMaxDevices = 64;
-SideStream g_side[kMaxDevices];
-std::mutex g_side_mu;
-
-// The side stream of the device that owns stream s (the current device for
-// the null stream), g_side_mu held; null when it could not be created, and the
-// step then runs the same plan on s.  The stream and its events are created
-// with that device current, so a caller whose current device differs from its
-// stream's still gets both passes on one GPU.
-SideStream *side_stream_locked(hipStream_t s) {
-    int cur = 0, dev = 0;
-    if (hipGetDevice(&cur) != hipSuccess) return nullptr;
-    dev = cur;
-    if (s != nullptr && hipStreamGetDevice(s, &dev) != hipSuccess) {
-        (void)hipGetLastError();
-        return nullptr;
-    }
-    if (dev < 0 || dev >= kMaxDevices) return nullptr;
-    SideStream &sd = g_side[dev];
-    if (!sd.tried) {
-        sd.tried = true;
-        bool ok = dev == cur || hipSetDevice(dev) == hipSuccess;
-        ok = ok && hipStreamCreateWithFlags(&sd.s, hipStreamNonBlocking) == hipSuccess;
-        ok = ok && hipEventCreateWithFlags(&sd.fork, hipEventDisableTiming) == hipSuccess;
-        ok = ok && hipEventCreateWithFlags(&sd.join, hipEventDisableTiming) == hipSuccess;
-        if (dev != cur) (void)hipSetDevice(cur);
-        if (!ok) {
-            if (sd.join) (void)hipEventDestroy(sd.join);
-            if (sd.fork) (void)hipEventDestroy(sd.fork);
-            if (sd.s) (void)hipStreamDestroy(sd.s);
-            sd.s = nullptr;
-            sd.fork = sd.join = nullptr;
-            (void)hipGetLastError();  // do not leave the failure for the caller's next check
-        }
-    }
-    return sd.s ? &sd : nullptr;
-}
-
 hp_status run_prefix_levels(const hp_query *q, const hp_prefix_tree *tree, const CascadePlan &cp,
                             char *base, MergeArgs &m, hipStream_t s);
 
-// Suffix pass beside the prefix pass: fork the side stream from s, prefix
-// launches on s, the suffix pass (its own (O, LSE) rows, no merge) on the side
-// stream, join, then one merge of every prefix partial with the suffix rows.
+// Suffix pass beside the prefix pass: fork the caller's side stream from s,
+// prefix launches on s, the suffix pass (its own (O, LSE) rows, no merge) on
+// the side stream, join, then one merge of every prefix partial with the
+// suffix rows on s.
 hp_status cascade_concurrent(const hp_query *q, const hp_prefix_tree *tree,
                              const hp_paged_kv *kv, const CascadePlan &cp, float *o, float *lse,
-                             char *base, hipStream_t s, void *const *events) {
+                             char *base, hipStream_t s, const hp_overlap &ov, void *const *events) {
     float *so = (float *)(base + cp.suf_off);
     float *sl = (float *)((char *)so +
                           round_up((size_t)q->B * q->Hq * q->d * sizeof(float), kWsAlign));
-    std::lock_guard<std::mutex> lock(g_side_mu);
-    SideStream *side = side_stream_locked(s);
-    hipStream_t ss = side ? side->s : s;
+    const hipStream_t ss = (hipStream_t)ov.side_stream;
+    const hipEvent_t fork = (hipEvent_t)ov.fork_event, join = (hipEvent_t)ov.join_event;
     hipError_t e;
-    if (side) {
-        if ((e = hipEventRecord(side->fork, s)) != hipSuccess) return fail_hip(e);
-        if ((e = hipStreamWaitEvent(ss, side->fork, 0)) != hipSuccess) return fail_hip(e);
-    }
+    if ((e = hipEventRecord(fork, s)) != hipSuccess) return fail_hip(e);
+    if ((e = hipStreamWaitEvent(ss, fork, 0)) != hipSuccess) return fail_hip(e);
     hp_status st = record(events, 0, s);  // right before the first prefix launch
     if (st != HP_OK) return st;
     MergeArgs m;
@@ -637,10 +604,8 @@ hp_status cascade_concurrent(const hp_query *q, const hp_prefix_tree *tree,
     e = launch_suffix(a, q->dtype, q->d, q->Hq / q->Hkv, suffix_waves(*q, *kv), ss);
     if (e != hipSuccess) return fail_hip(e);
     if ((st = record(events, 2, ss)) != HP_OK) return st;
-    if (side) {
-        if ((e = hipEventRecord(side->join, ss)) != hipSuccess) return fail_hip(e);
-        if ((e = hipStreamWaitEvent(s, side->join, 0)) != hipSuccess) return fail_hip(e);
-    }
+    if ((e = hipEventRecord(join, ss)) != hipSuccess) return fail_hip(e);
+    if ((e = hipStreamWaitEvent(s, join, 0)) != hipSuccess) return fail_hip(e);
     m.src[m.nsrc++] = MergeSrc{so, sl, 0, 0, 1, 0, 0, q->B};
     m.Hq = q->Hq;
     m.row_b0 = 0;
@@ -676,17 +641,21 @@ hp_status run_prefix_levels(const hp_query *q, const hp_prefix_tree *tree, const
 
 hp_status cascade_impl(const hp_query *q, const hp_prefix_tree *tree, const hp_paged_kv *kv,
                        float *o, float *lse, void *ws, size_t ws_bytes, void *stream,
-                       void *const *events) {
+                       const hp_overlap *ov, void *const *events) {
     CascadePlan cp;
-    hp_status st = plan_cascade(q, tree, kv, cp);
+    hp_status st = plan_cascade(q, tree, kv, ov ? ov->mode : 0, cp);
     if (st != HP_OK) return st;
     st = check_out(o, lse);
     if (st != HP_OK) return st;
+    if (cp.conc) {
+        if (!ov->side_stream || !ov->fork_event || !ov->join_event) return HP_ERR_NULL;
+        if (ov->side_stream == stream) return HP_ERR_INVALID_ARG;
+    }
     if (q->B == 0) return HP_OK;
     if (cp.bytes > 0 && (!ws || ws_bytes < cp.bytes || !aligned16(ws))) return HP_ERR_WORKSPACE;
     hipStream_t s = (hipStream_t)stream;
     char *base = (char *)ws;
-    if (cp.conc) return cascade_concurrent(q, tree, kv, cp, o, lse, base, s, events);
+    if (cp.conc) return cascade_concurrent(q, tree, kv, cp, o, lse, base, s, *ov, events);
     if ((st = record(events, 0, s)) != HP_OK) return st;
 
     MergeArgs m;
@@ -744,7 +713,7 @@ struct StreamPlan {
 
 hp_status plan_stream(const hp_query *q, const hp_prefix_tree *doc, const hp_stream_rows *r,
                       StreamPlan &sp) {
-    hp_status st = plan_cascade(q, doc, nullptr, sp.cp);
+    hp_status st = plan_cascade(q, doc, nullptr, 0, sp.cp);
     if (st != HP_OK) return st;
     if ((st = check_stream_rows(q, r)) != HP_OK) return st;
     sp.len_off = round_up(sp.cp.bytes, kWsAlign);
@@ -759,87 +728,107 @@ extern "C" {
 
 hp_status hp_stream_decode_workspace_size(const hp_query *q, const hp_prefix_tree *doc,
                                           const hp_stream_rows *rows, size_t *bytes) {
-    if (!bytes) return HP_ERR_NULL;
-    StreamPlan sp;
-    hp_status st = plan_stream(q, doc, rows, sp);
-    if (st != HP_OK) return st;
-    *bytes = sp.bytes;
-    return HP_OK;
+    return hp::guarded([&]() -> hp_status {
+        if (!bytes) return HP_ERR_NULL;
+        StreamPlan sp;
+        hp_status st = plan_stream(q, doc, rows, sp);
+        if (st != HP_OK) return st;
+        *bytes = sp.bytes;
+        return HP_OK;
+    });
 }
 
 hp_status hp_stream_decode(const hp_query *q, const hp_prefix_tree *doc,
                            const hp_stream_rows *rows, float *o, float *lse, void *ws,
                            size_t ws_bytes, void *stream) {
-    StreamPlan sp;
-    hp_status st = plan_stream(q, doc, rows, sp);
-    if (st != HP_OK) return st;
-    if ((st = check_out(o, lse)) != HP_OK) return st;
-    if (q->B == 0) return HP_OK;
-    if (!ws || ws_bytes < sp.bytes || !aligned16(ws)) return HP_ERR_WORKSPACE;
-    hipStream_t s = (hipStream_t)stream;
-    char *base = (char *)ws;
-    int32_t *tok_len = (int32_t *)(base + sp.len_off);
-    int32_t *tok_table = (int32_t *)(base + sp.table_off);
+    return hp::guarded([&]() -> hp_status {
+        StreamPlan sp;
+        hp_status st = plan_stream(q, doc, rows, sp);
+        if (st != HP_OK) return st;
+        if ((st = check_out(o, lse)) != HP_OK) return st;
+        if (q->B == 0) return HP_OK;
+        if (!ws || ws_bytes < sp.bytes || !aligned16(ws)) return HP_ERR_WORKSPACE;
+        hipStream_t s = (hipStream_t)stream;
+        char *base = (char *)ws;
+        int32_t *tok_len = (int32_t *)(base + sp.len_off);
+        int32_t *tok_table = (int32_t *)(base + sp.table_off);
 
-    MergeArgs m;
-    std::memset(&m, 0, sizeof m);
-    if ((st = run_prefix_levels(q, doc, sp.cp, base, m, s)) != HP_OK) return st;
+        MergeArgs m;
+        std::memset(&m, 0, sizeof m);
+        if ((st = run_prefix_levels(q, doc, sp.cp, base, m, s)) != HP_OK) return st;
 
-    StreamSelectArgs sel;
-    std::memset(&sel, 0, sizeof sel);
-    sel.row_slots = rows->row_slots;
-    sel.slot_sid = rows->slot_sid;
-    sel.row_len = rows->row_len;
-    sel.q_req = rows->q_req;
-    sel.q_sid = rows->q_sid;
-    sel.B = q->B;
-    sel.R = rows->num_requests;
-    sel.row_cap = rows->row_cap;
-    sel.tok_table = tok_table;
-    sel.tok_len = tok_len;
-    hipError_t e = launch_stream_select(sel, s);
-    if (e != hipSuccess) return fail_hip(e);
+        StreamSelectArgs sel;
+        std::memset(&sel, 0, sizeof sel);
+        sel.row_slots = rows->row_slots;
+        sel.slot_sid = rows->slot_sid;
+        sel.row_len = rows->row_len;
+        sel.q_req = rows->q_req;
+        sel.q_sid = rows->q_sid;
+        sel.B = q->B;
+        sel.R = rows->num_requests;
+        sel.row_cap = rows->row_cap;
+        sel.tok_table = tok_table;
+        sel.tok_len = tok_len;
+        hipError_t e = launch_stream_select(sel, s);
+        if (e != hipSuccess) return fail_hip(e);
 
-    SuffixArgs a;
-    std::memset(&a, 0, sizeof a);
-    a.q = q->q;
-    a.k_pool = rows->k_pool;
-    a.v_pool = rows->v_pool;
-    a.table = tok_table;
-    a.lens = tok_len;
-    a.B = q->B;
-    a.Hq = q->Hq;
-    a.Hkv = q->Hkv;
-    a.max_blocks = rows->row_cap;  // capacity of each query's table
-    a.has_suffix = 1;
-    a.scale_log2 = (float)((double)q->scale * 1.4426950408889634);
-    a.dest = RowDest{o, lse, 0, 0, 0};
-    a.pool_rows = rows->pool_rows;
-    // K/V footprint: the pool rows, or what the token tables can reach if less.
-    const int64_t kv_rows = std::min<int64_t>(rows->pool_rows, (int64_t)q->B * rows->row_cap);
-    a.stream_kv = kv_rows * q->Hkv * q->d * esize(q->dtype) * 2 >= kLlcBytes ? 1 : 0;
-    a.nsrc = m.nsrc;
-    for (int i = 0; i < m.nsrc; ++i) a.src[i] = m.src[i];
-    a.stage_floats = stage_floats(m.src, m.nsrc, q->Hq / q->Hkv, q->d);
-    const int blocks = (int)cdiv(rows->row_cap, HP_BLOCK_SIZE);
-    const int nws = blocks <= 2 ? 1 : blocks <= 16 ? 2 : 4;
-    e = launch_token_suffix(a, q->dtype, q->d, q->Hq / q->Hkv, nws, s);
-    return e == hipSuccess ? HP_OK : fail_hip(e);
+        SuffixArgs a;
+        std::memset(&a, 0, sizeof a);
+        a.q = q->q;
+        a.k_pool = rows->k_pool;
+        a.v_pool = rows->v_pool;
+        a.table = tok_table;
+        a.lens = tok_len;
+        a.B = q->B;
+        a.Hq = q->Hq;
+        a.Hkv = q->Hkv;
+        a.max_blocks = rows->row_cap;  // capacity of each query's table
+        a.has_suffix = 1;
+        a.scale_log2 = (float)((double)q->scale * 1.4426950408889634);
+        a.dest = RowDest{o, lse, 0, 0, 0};
+        a.pool_rows = rows->pool_rows;
+        // K/V footprint: the pool rows, or what the token tables can reach if less.
+        const int64_t kv_rows = std::min<int64_t>(rows->pool_rows, (int64_t)q->B * rows->row_cap);
+        a.stream_kv = kv_rows * q->Hkv * q->d * esize(q->dtype) * 2 >= kLlcBytes ? 1 : 0;
+        a.nsrc = m.nsrc;
+        for (int i = 0; i < m.nsrc; ++i) a.src[i] = m.src[i];
+        a.stage_floats = stage_floats(m.src, m.nsrc, q->Hq / q->Hkv, q->d);
+        const int blocks = (int)cdiv(rows->row_cap, HP_BLOCK_SIZE);
+        const int nws = blocks <= 2 ? 1 : blocks <= 16 ? 2 : 4;
+        e = launch_token_suffix(a, q->dtype, q->d, q->Hq / q->Hkv, nws, s);
+        return e == hipSuccess ? HP_OK : fail_hip(e);
+    });
 }
 
 hp_status hp_cascade_step(const hp_query *q, const hp_prefix_tree *tree, const hp_paged_kv *kv,
                           float *o, float *lse, void *ws, size_t ws_bytes, void *stream) {
-    return cascade_impl(q, tree, kv, o, lse, ws, ws_bytes, stream, nullptr);
+    return hp::guarded([&]() -> hp_status {
+        return cascade_impl(q, tree, kv, o, lse, ws, ws_bytes, stream, nullptr, nullptr);
+    });
+}
+
+hp_status hp_cascade_step_overlap(const hp_query *q, const hp_prefix_tree *tree,
+                                  const hp_paged_kv *kv, float *o, float *lse, void *ws,
+                                  size_t ws_bytes, void *stream, const hp_overlap *overlap) {
+    return hp::guarded([&]() -> hp_status {
+        if (!overlap) return HP_ERR_NULL;
+        return cascade_impl(q, tree, kv, o, lse, ws, ws_bytes, stream, overlap, nullptr);
+    });
 }
 
 hp_status hp_cascade_step_timed(const hp_query *q, const hp_prefix_tree *tree,
                                 const hp_paged_kv *kv, float *o, float *lse, void *ws,
-                                size_t ws_bytes, void *stream, void *const *events,
-                                int32_t n_events) {
-    if (n_events != 0 && n_events != 4 && n_events != 5) return HP_ERR_INVALID_ARG;
-    if (n_events == 0) return cascade_impl(q, tree, kv, o, lse, ws, ws_bytes, stream, nullptr);
-    void *ev[5] = {events[0], events[1], events[2], events[3], n_events == 5 ? events[4] : nullptr};
-    return cascade_impl(q, tree, kv, o, lse, ws, ws_bytes, stream, ev);
+                                size_t ws_bytes, void *stream, const hp_overlap *overlap,
+                                void *const *events, int32_t n_events) {
+    return hp::guarded([&]() -> hp_status {
+        if (n_events != 0 && n_events != 4 && n_events != 5) return HP_ERR_INVALID_ARG;
+        if (n_events == 0)
+            return cascade_impl(q, tree, kv, o, lse, ws, ws_bytes, stream, overlap, nullptr);
+        if (!events) return HP_ERR_NULL;
+        void *ev[5] = {events[0], events[1], events[2], events[3],
+                       n_events == 5 ? events[4] : nullptr};
+        return cascade_impl(q, tree, kv, o, lse, ws, ws_bytes, stream, overlap, ev);
+    });
 }
 
 }  // extern "C"

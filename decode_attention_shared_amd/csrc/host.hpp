@@ -58,7 +58,10 @@ inline hp_status check_geometry(const hp_query *q, bool need_q) {
     if (!q) return HP_ERR_NULL;
     if (q->B < 0 || q->Hq <= 0 || q->Hkv <= 0 || q->Hq % q->Hkv != 0) return HP_ERR_INVALID_ARG;
     if (q->dtype < HP_F32 || q->dtype > HP_BF16) return HP_ERR_INVALID_ARG;
-    if (need_q && !std::isfinite(q->scale)) return HP_ERR_INVALID_ARG;
+    // scale >= 0: the 16-bit prefix kernels take the row max of the raw dot
+    // products and scale it afterwards, which is the max of the scaled scores
+    // only when the scale is not negative.
+    if (need_q && !(std::isfinite(q->scale) && q->scale >= 0.f)) return HP_ERR_INVALID_ARG;
     if (q->d != 64 && q->d != 128) return HP_ERR_UNSUPPORTED;
     const int G = q->Hq / q->Hkv;
     if (G > 8 || (G & (G - 1)) != 0) return HP_ERR_UNSUPPORTED;

@@ -15,9 +15,11 @@
 #include <algorithm>
 #include <cstdint>
 #include <cstring>
+#include <memory>
 #include <unordered_map>
 #include <vector>
 
+#include "guard.hpp"
 #include "hp_attn.h"
 
 namespace {
@@ -143,184 +145,203 @@ struct hp_pakv {
 extern "C" {
 
 hp_status hp_pakv_create(int32_t num_chunks, hp_pakv **out) {
-    if (!out) return HP_ERR_NULL;
-    *out = nullptr;
-    if (num_chunks < 0 || (int64_t)num_chunks * HP_CHUNK > INT32_MAX) return HP_ERR_INVALID_ARG;
-    hp_pakv *p = new hp_pakv;
-    p->num_chunks = num_chunks;
-    p->chunk_nodes.assign(num_chunks, 0);
-    p->chunk_used.assign(num_chunks, 0);
-    *out = p;
-    return HP_OK;
+    return hp::guarded([&]() -> hp_status {
+        if (!out) return HP_ERR_NULL;
+        *out = nullptr;
+        if (num_chunks < 0 || (int64_t)num_chunks * HP_CHUNK > INT32_MAX) return HP_ERR_INVALID_ARG;
+        std::unique_ptr<hp_pakv> p(new hp_pakv);
+        p->num_chunks = num_chunks;
+        p->chunk_nodes.assign(num_chunks, 0);
+        p->chunk_used.assign(num_chunks, 0);
+        *out = p.release();
+        return HP_OK;
+    });
 }
 
-void hp_pakv_destroy(hp_pakv *p) { delete p; }
+void hp_pakv_destroy(hp_pakv *p) {
+    try {
+        delete p;
+    } catch (...) {
+    }
+}
 
 hp_status hp_pakv_insert(hp_pakv *p, int64_t seq_id, const int32_t *tokens, int32_t n,
                          int32_t *rows, int32_t *matched) {
-    if (!p) return HP_ERR_NULL;
-    if (n < 0) return HP_ERR_INVALID_ARG;
-    if (n > 0 && !tokens) return HP_ERR_NULL;
-    if (p->seqs.count(seq_id)) return HP_ERR_INVALID_ARG;
-    hp_pakv::Match m = p->best_match(&p->root, tokens, n, 0);
-    const int64_t rest = n - m.total;
-    if ((rest + HP_CHUNK - 1) / HP_CHUNK > p->available()) return HP_ERR_CAPACITY;
+    return hp::guarded([&]() -> hp_status {
+        if (!p) return HP_ERR_NULL;
+        if (n < 0) return HP_ERR_INVALID_ARG;
+        if (n > 0 && !tokens) return HP_ERR_NULL;
+        if (p->seqs.count(seq_id)) return HP_ERR_INVALID_ARG;
+        hp_pakv::Match m = p->best_match(&p->root, tokens, n, 0);
+        const int64_t rest = n - m.total;
+        if ((rest + HP_CHUNK - 1) / HP_CHUNK > p->available()) return HP_ERR_CAPACITY;
 
-    Node *end = m.node;
-    if (end != &p->root && m.k < (int32_t)end->tokens.size()) p->split(end, m.k);
-    for (Node *x = end; x; x = x->parent) x->refs++;
-    Node *leaf = end;
-    for (int64_t t = m.total; t < n;) {
-        const int32_t c = p->alloc_chunk();
-        Node *nn = p->new_node(leaf, c, 0);
-        const int64_t take = std::min<int64_t>(HP_CHUNK, n - t);
-        nn->tokens.assign(tokens + t, tokens + t + take);
-        p->chunk_used[c] = (int32_t)take;
-        nn->refs = 1;
-        leaf = nn;
-        t += take;
-    }
-    leaf->ending.push_back(seq_id);
-    Seq s{leaf, n};
-    p->seqs[seq_id] = s;
-    if (rows) p->rows_of(s, rows);
-    if (matched) *matched = (int32_t)m.total;
-    return HP_OK;
+        Node *end = m.node;
+        if (end != &p->root && m.k < (int32_t)end->tokens.size()) p->split(end, m.k);
+        for (Node *x = end; x; x = x->parent) x->refs++;
+        Node *leaf = end;
+        for (int64_t t = m.total; t < n;) {
+            const int32_t c = p->alloc_chunk();
+            Node *nn = p->new_node(leaf, c, 0);
+            const int64_t take = std::min<int64_t>(HP_CHUNK, n - t);
+            nn->tokens.assign(tokens + t, tokens + t + take);
+            p->chunk_used[c] = (int32_t)take;
+            nn->refs = 1;
+            leaf = nn;
+            t += take;
+        }
+        leaf->ending.push_back(seq_id);
+        Seq s{leaf, n};
+        p->seqs[seq_id] = s;
+        if (rows) p->rows_of(s, rows);
+        if (matched) *matched = (int32_t)m.total;
+        return HP_OK;
+    });
 }
 
 hp_status hp_pakv_append(hp_pakv *p, int64_t seq_id, int32_t token, int32_t *row,
                          int32_t *changed) {
-    if (!p) return HP_ERR_NULL;
-    auto it = p->seqs.find(seq_id);
-    if (it == p->seqs.end()) return HP_ERR_INVALID_ARG;
-    Seq &s = it->second;
-    Node *L = s.leaf;
-    const int32_t end = L->slot0 + (int32_t)L->tokens.size();
-    const bool grow = L != &p->root && L->refs == 1 && L->children.empty() && end < HP_CHUNK &&
-                      hp_pakv::owns_tail(*p, L);
-    int32_t r;
-    if (grow) {
-        r = L->chunk * HP_CHUNK + end;
-        L->tokens.push_back(token);
-        p->chunk_used[L->chunk]++;
-    } else {
-        if (p->available() < 1) return HP_ERR_CAPACITY;
-        const int32_t c = p->alloc_chunk();
-        Node *nn = p->new_node(L, c, 0);
-        nn->tokens.push_back(token);
-        nn->refs = 1;
-        p->chunk_used[c] = 1;
-        L->ending.erase(std::find(L->ending.begin(), L->ending.end(), seq_id));
-        nn->ending.push_back(seq_id);
-        s.leaf = nn;
-        r = c * HP_CHUNK;
-    }
-    s.len++;
-    if (row) *row = r;
-    if (changed) *changed = grow ? 0 : 1;
-    return HP_OK;
+    return hp::guarded([&]() -> hp_status {
+        if (!p) return HP_ERR_NULL;
+        auto it = p->seqs.find(seq_id);
+        if (it == p->seqs.end()) return HP_ERR_INVALID_ARG;
+        Seq &s = it->second;
+        Node *L = s.leaf;
+        const int32_t end = L->slot0 + (int32_t)L->tokens.size();
+        const bool grow = L != &p->root && L->refs == 1 && L->children.empty() && end < HP_CHUNK &&
+                          hp_pakv::owns_tail(*p, L);
+        int32_t r;
+        if (grow) {
+            r = L->chunk * HP_CHUNK + end;
+            L->tokens.push_back(token);
+            p->chunk_used[L->chunk]++;
+        } else {
+            if (p->available() < 1) return HP_ERR_CAPACITY;
+            const int32_t c = p->alloc_chunk();
+            Node *nn = p->new_node(L, c, 0);
+            nn->tokens.push_back(token);
+            nn->refs = 1;
+            p->chunk_used[c] = 1;
+            L->ending.erase(std::find(L->ending.begin(), L->ending.end(), seq_id));
+            nn->ending.push_back(seq_id);
+            s.leaf = nn;
+            r = c * HP_CHUNK;
+        }
+        s.len++;
+        if (row) *row = r;
+        if (changed) *changed = grow ? 0 : 1;
+        return HP_OK;
+    });
 }
 
 hp_status hp_pakv_remove(hp_pakv *p, int64_t seq_id) {
-    if (!p) return HP_ERR_NULL;
-    auto it = p->seqs.find(seq_id);
-    if (it == p->seqs.end()) return HP_ERR_INVALID_ARG;
-    Node *n = it->second.leaf;
-    n->ending.erase(std::find(n->ending.begin(), n->ending.end(), seq_id));
-    while (n != &p->root) {
-        Node *parent = n->parent;
-        if (--n->refs == 0) {  // no live sequence passes here: nor below
-            auto &sib = parent->children;
-            sib.erase(std::find(sib.begin(), sib.end(), n));
-            p->release_chunk(n->chunk);
-            delete n;
-            --p->nodes;
+    return hp::guarded([&]() -> hp_status {
+        if (!p) return HP_ERR_NULL;
+        auto it = p->seqs.find(seq_id);
+        if (it == p->seqs.end()) return HP_ERR_INVALID_ARG;
+        Node *n = it->second.leaf;
+        n->ending.erase(std::find(n->ending.begin(), n->ending.end(), seq_id));
+        while (n != &p->root) {
+            Node *parent = n->parent;
+            if (--n->refs == 0) {  // no live sequence passes here: nor below
+                auto &sib = parent->children;
+                sib.erase(std::find(sib.begin(), sib.end(), n));
+                p->release_chunk(n->chunk);
+                delete n;
+                --p->nodes;
+            }
+            n = parent;
         }
-        n = parent;
-    }
-    p->root.refs--;
-    p->seqs.erase(it);
-    return HP_OK;
+        p->root.refs--;
+        p->seqs.erase(it);
+        return HP_OK;
+    });
 }
 
 hp_status hp_pakv_context(hp_pakv *p, int64_t *seq_order, int32_t *seq_lens,
                           int32_t seq_capacity, hp_chunk_desc *descs, int32_t desc_capacity,
                           int32_t *num_seqs, int32_t *num_descs) {
-    if (!p || !num_seqs || !num_descs) return HP_ERR_NULL;
-    const int32_t ns = (int32_t)p->seqs.size(), nd = p->nodes;
-    *num_seqs = ns;
-    *num_descs = nd;
-    if (seq_capacity < ns || desc_capacity < nd) return HP_ERR_CAPACITY;
-    if ((ns > 0 && (!seq_order || !seq_lens)) || (nd > 0 && !descs)) return HP_ERR_NULL;
-    int32_t b = 0, k = 0;
-    // Pre-order: a node's own sequences first, then its children's, so the
-    // sequences under every node are the contiguous batch rows [i, j).
-    struct Frame {
-        Node *n;
-        size_t next;
-        int32_t desc;
-    };
-    std::vector<Frame> stack;
-    auto enter = [&](Node *n) {
-        int32_t di = -1;
-        if (n != &p->root) {
-            di = k++;
-            const bool grow = n->refs == 1 && n->children.empty() && hp_pakv::owns_tail(*p, n);
-            descs[di].row = n->chunk * HP_CHUNK + n->slot0;
-            descs[di].count = grow ? HP_CHUNK - n->slot0 : (int32_t)n->tokens.size();
-            descs[di].seq_begin = b;
+    return hp::guarded([&]() -> hp_status {
+        if (!p || !num_seqs || !num_descs) return HP_ERR_NULL;
+        const int32_t ns = (int32_t)p->seqs.size(), nd = p->nodes;
+        *num_seqs = ns;
+        *num_descs = nd;
+        if (seq_capacity < ns || desc_capacity < nd) return HP_ERR_CAPACITY;
+        if ((ns > 0 && (!seq_order || !seq_lens)) || (nd > 0 && !descs)) return HP_ERR_NULL;
+        int32_t b = 0, k = 0;
+        // Pre-order: a node's own sequences first, then its children's, so the
+        // sequences under every node are the contiguous batch rows [i, j).
+        struct Frame {
+            Node *n;
+            size_t next;
+            int32_t desc;
+        };
+        std::vector<Frame> stack;
+        auto enter = [&](Node *n) {
+            int32_t di = -1;
+            if (n != &p->root) {
+                di = k++;
+                const bool grow = n->refs == 1 && n->children.empty() && hp_pakv::owns_tail(*p, n);
+                descs[di].row = n->chunk * HP_CHUNK + n->slot0;
+                descs[di].count = grow ? HP_CHUNK - n->slot0 : (int32_t)n->tokens.size();
+                descs[di].seq_begin = b;
+            }
+            for (int64_t id : n->ending) {
+                seq_order[b] = id;
+                seq_lens[b] = (int32_t)p->seqs[id].len;
+                ++b;
+            }
+            stack.push_back(Frame{n, 0, di});
+        };
+        enter(&p->root);
+        while (!stack.empty()) {
+            Frame &f = stack.back();
+            if (f.next < f.n->children.size()) {
+                Node *c = f.n->children[f.next++];
+                enter(c);
+            } else {
+                if (f.desc >= 0) descs[f.desc].seq_end = b;
+                stack.pop_back();
+            }
         }
-        for (int64_t id : n->ending) {
-            seq_order[b] = id;
-            seq_lens[b] = (int32_t)p->seqs[id].len;
-            ++b;
-        }
-        stack.push_back(Frame{n, 0, di});
-    };
-    enter(&p->root);
-    while (!stack.empty()) {
-        Frame &f = stack.back();
-        if (f.next < f.n->children.size()) {
-            Node *c = f.n->children[f.next++];
-            enter(c);
-        } else {
-            if (f.desc >= 0) descs[f.desc].seq_end = b;
-            stack.pop_back();
-        }
-    }
-    return HP_OK;
+        return HP_OK;
+    });
 }
 
 hp_status hp_pakv_seq_rows(hp_pakv *p, int64_t seq_id, int32_t *rows, int32_t capacity,
                            int32_t *n) {
-    if (!p || !n) return HP_ERR_NULL;
-    auto it = p->seqs.find(seq_id);
-    if (it == p->seqs.end()) return HP_ERR_INVALID_ARG;
-    *n = (int32_t)it->second.len;
-    if (capacity < it->second.len) return HP_ERR_CAPACITY;
-    if (it->second.len > 0 && !rows) return HP_ERR_NULL;
-    p->rows_of(it->second, rows);
-    return HP_OK;
+    return hp::guarded([&]() -> hp_status {
+        if (!p || !n) return HP_ERR_NULL;
+        auto it = p->seqs.find(seq_id);
+        if (it == p->seqs.end()) return HP_ERR_INVALID_ARG;
+        *n = (int32_t)it->second.len;
+        if (capacity < it->second.len) return HP_ERR_CAPACITY;
+        if (it->second.len > 0 && !rows) return HP_ERR_NULL;
+        p->rows_of(it->second, rows);
+        return HP_OK;
+    });
 }
 
 hp_status hp_pakv_get_stats(hp_pakv *p, hp_pakv_stats *st) {
-    if (!p || !st) return HP_ERR_NULL;
-    std::memset(st, 0, sizeof *st);
-    st->num_chunks = p->num_chunks;
-    for (int32_t c = 0; c < p->fresh; ++c) st->chunks_used += p->chunk_nodes[c] > 0;
-    st->chunks_free = (int32_t)p->free_list.size();
-    st->chunks_fresh = p->num_chunks - p->fresh;
-    st->nodes = p->nodes;
-    st->seqs = (int32_t)p->seqs.size();
-    std::vector<Node *> todo{&p->root};
-    while (!todo.empty()) {
-        Node *n = todo.back();
-        todo.pop_back();
-        st->tokens_stored += (int64_t)n->tokens.size();
-        for (Node *c : n->children) todo.push_back(c);
-    }
-    for (auto &kv : p->seqs) st->tokens_logical += kv.second.len;
-    return HP_OK;
+    return hp::guarded([&]() -> hp_status {
+        if (!p || !st) return HP_ERR_NULL;
+        std::memset(st, 0, sizeof *st);
+        st->num_chunks = p->num_chunks;
+        for (int32_t c = 0; c < p->fresh; ++c) st->chunks_used += p->chunk_nodes[c] > 0;
+        st->chunks_free = (int32_t)p->free_list.size();
+        st->chunks_fresh = p->num_chunks - p->fresh;
+        st->nodes = p->nodes;
+        st->seqs = (int32_t)p->seqs.size();
+        std::vector<Node *> todo{&p->root};
+        while (!todo.empty()) {
+            Node *n = todo.back();
+            todo.pop_back();
+            st->tokens_stored += (int64_t)n->tokens.size();
+            for (Node *c : n->children) todo.push_back(c);
+        }
+        for (auto &kv : p->seqs) st->tokens_logical += kv.second.len;
+        return HP_OK;
+    });
 }
 
 }  // extern "C"

@@ -19,6 +19,7 @@
 #include <cstring>
 #include <vector>
 
+#include "guard.hpp"
 #include "host.hpp"
 
 using namespace hp;
@@ -277,142 +278,150 @@ extern "C" {
 hp_status hp_tree_plan_build(const hp_query *geom, const hp_chunk_desc *descs, int32_t n,
                              int32_t share_min, int64_t pool_rows, void *blob,
                              size_t blob_capacity, hp_tree_plan *plan) {
-    if (!plan) return HP_ERR_NULL;
-    hp_status st = check_geometry(geom, false);
-    if (st != HP_OK) return st;
-    if (share_min != 0 && share_min < 2) return HP_ERR_INVALID_ARG;
-    st = check_descs(*geom, descs, n, pool_rows);
-    if (st != HP_OK) return st;
-    hp_tree_plan p;
-    Image img;
-    st = build(*geom, descs, n, share_min, pool_rows, p, img);
-    if (st != HP_OK) return st;
-    if (blob) {
-        if (blob_capacity < p.blob_bytes) return HP_ERR_CAPACITY;
-        write_image(p, img, blob);
-    }
-    *plan = p;
-    return HP_OK;
+    return hp::guarded([&]() -> hp_status {
+        if (!plan) return HP_ERR_NULL;
+        hp_status st = check_geometry(geom, false);
+        if (st != HP_OK) return st;
+        if (share_min != 0 && share_min < 2) return HP_ERR_INVALID_ARG;
+        st = check_descs(*geom, descs, n, pool_rows);
+        if (st != HP_OK) return st;
+        hp_tree_plan p;
+        Image img;
+        st = build(*geom, descs, n, share_min, pool_rows, p, img);
+        if (st != HP_OK) return st;
+        if (blob) {
+            if (blob_capacity < p.blob_bytes) return HP_ERR_CAPACITY;
+            write_image(p, img, blob);
+        }
+        *plan = p;
+        return HP_OK;
+    });
 }
 
 hp_status hp_share_decision(const hp_query *geom, int64_t tokens, int32_t nseq,
                             int32_t *batch) {
-    if (!batch) return HP_ERR_NULL;
-    hp_status st = check_geometry(geom, false);
-    if (st != HP_OK) return st;
-    if (tokens < 0 || nseq < 0 || nseq > geom->B) return HP_ERR_INVALID_ARG;
-    *batch = share_decision(geom->Hq / geom->Hkv, tokens, nseq) ? 1 : 0;
-    return HP_OK;
+    return hp::guarded([&]() -> hp_status {
+        if (!batch) return HP_ERR_NULL;
+        hp_status st = check_geometry(geom, false);
+        if (st != HP_OK) return st;
+        if (tokens < 0 || nseq < 0 || nseq > geom->B) return HP_ERR_INVALID_ARG;
+        *batch = share_decision(geom->Hq / geom->Hkv, tokens, nseq) ? 1 : 0;
+        return HP_OK;
+    });
 }
 
 hp_status hp_tree_step(const hp_query *q, const hp_tree_plan *plan, const void *blob_dev,
                        const void *k_pool, const void *v_pool, const int32_t *seq_lens,
                        float *o, float *lse, void *ws, size_t ws_bytes, void *stream) {
-    hp_status st = check_geometry(q, true);
-    if (st != HP_OK) return st;
-    if (!plan || !o) return HP_ERR_NULL;
-    if (plan->B != q->B || plan->Hq != q->Hq || plan->Hkv != q->Hkv || plan->d != q->d ||
-        plan->dtype != q->dtype)
-        return HP_ERR_INVALID_ARG;
-    if (plan->num_launches < 0 || plan->num_launches > HP_TREE_MAX_LAUNCHES)
-        return HP_ERR_INVALID_ARG;
-    if (!aligned16(o) || ((uintptr_t)lse & 3u) || ((uintptr_t)seq_lens & 3u))
-        return HP_ERR_INVALID_ARG;
-    if (q->B == 0) return HP_OK;
-    if (!blob_dev) return HP_ERR_NULL;
-    if (!aligned16(blob_dev)) return HP_ERR_INVALID_ARG;
-    const bool reads_pool = plan->num_pieces > 0 || plan->num_tok_rows > 0;
-    if (reads_pool && (!k_pool || !v_pool)) return HP_ERR_NULL;
-    if (reads_pool && (!aligned16(k_pool) || !aligned16(v_pool))) return HP_ERR_INVALID_ARG;
-    const int64_t row_stride = (int64_t)q->Hkv * q->d;
-    if ((int64_t)kTileKeys * row_stride + q->d > (int64_t)INT32_MAX) return HP_ERR_UNSUPPORTED;
-    if (plan->workspace_bytes > 0 && (!ws || ws_bytes < plan->workspace_bytes || !aligned16(ws)))
-        return HP_ERR_WORKSPACE;
+    return hp::guarded([&]() -> hp_status {
+        hp_status st = check_geometry(q, true);
+        if (st != HP_OK) return st;
+        if (!plan || !o) return HP_ERR_NULL;
+        if (plan->B != q->B || plan->Hq != q->Hq || plan->Hkv != q->Hkv || plan->d != q->d ||
+            plan->dtype != q->dtype)
+            return HP_ERR_INVALID_ARG;
+        if (plan->num_launches < 0 || plan->num_launches > HP_TREE_MAX_LAUNCHES)
+            return HP_ERR_INVALID_ARG;
+        if (!aligned16(o) || ((uintptr_t)lse & 3u) || ((uintptr_t)seq_lens & 3u))
+            return HP_ERR_INVALID_ARG;
+        if (q->B == 0) return HP_OK;
+        if (!blob_dev) return HP_ERR_NULL;
+        if (!aligned16(blob_dev)) return HP_ERR_INVALID_ARG;
+        const bool reads_pool = plan->num_pieces > 0 || plan->num_tok_rows > 0;
+        if (reads_pool && (!k_pool || !v_pool)) return HP_ERR_NULL;
+        if (reads_pool && (!aligned16(k_pool) || !aligned16(v_pool))) return HP_ERR_INVALID_ARG;
+        const int64_t row_stride = (int64_t)q->Hkv * q->d;
+        if ((int64_t)kTileKeys * row_stride + q->d > (int64_t)INT32_MAX) return HP_ERR_UNSUPPORTED;
+        if (plan->workspace_bytes > 0 && (!ws || ws_bytes < plan->workspace_bytes || !aligned16(ws)))
+            return HP_ERR_WORKSPACE;
 
-    const TreeLayout L = tree_layout(plan->num_segs, plan->num_pieces, total_wgs(*plan), q->B,
-                                     plan->num_tok_rows, plan->num_srcs);
-    float *part_o = (float *)ws;
-    float *part_lse = plan->part_rows == 0
-                          ? nullptr
-                          : (float *)((char *)ws + round_up((size_t)plan->part_rows * q->Hq *
-                                                                q->d * sizeof(float),
-                                                            kWsAlign));
-    hipStream_t s = (hipStream_t)stream;
-    const float scale_log2 = (float)((double)q->scale * 1.4426950408889634);
+        const TreeLayout L = tree_layout(plan->num_segs, plan->num_pieces, total_wgs(*plan), q->B,
+                                         plan->num_tok_rows, plan->num_srcs);
+        float *part_o = (float *)ws;
+        float *part_lse = plan->part_rows == 0
+                              ? nullptr
+                              : (float *)((char *)ws + round_up((size_t)plan->part_rows * q->Hq *
+                                                                    q->d * sizeof(float),
+                                                                kWsAlign));
+        hipStream_t s = (hipStream_t)stream;
+        const float scale_log2 = (float)((double)q->scale * 1.4426950408889634);
 
-    // Chunk-first phase: every segment, one launch per row-block width.
-    for (int li = 0; li < plan->num_launches; ++li) {
-        if (plan->launch_wgs[li] <= 0) continue;
-        PrefixArgs a;
+        // Chunk-first phase: every segment, one launch per row-block width.
+        for (int li = 0; li < plan->num_launches; ++li) {
+            if (plan->launch_wgs[li] <= 0) continue;
+            PrefixArgs a;
+            std::memset(&a, 0, sizeof a);
+            a.q = q->q;
+            a.B = q->B;
+            a.Hq = q->Hq;
+            a.Hkv = q->Hkv;
+            a.G = q->Hq / q->Hkv;
+            a.scale_log2 = scale_log2;
+            a.tree = (const int32_t *)blob_dev;
+            a.seg_off = L.segs;
+            a.piece_off = L.pieces;
+            a.wgseg_off = L.wgseg;
+            a.wg0 = plan->launch_wg0[li];
+            a.k_pool = k_pool;
+            a.v_pool = v_pool;
+            a.row_stride = row_stride;
+            a.d = q->d;
+            a.part_o = part_o;
+            a.part_lse = part_lse;
+            hipError_t e = launch_tree_prefix(a, q->dtype, q->d, plan->launch_nw[li],
+                                              plan->launch_wgs[li], s);
+            if (e != hipSuccess) return fail_hip(e);
+        }
+
+        // Sequence-first phase: private rows plus the merge of the partials.
+        SuffixArgs a;
         std::memset(&a, 0, sizeof a);
         a.q = q->q;
+        a.k_pool = k_pool;
+        a.v_pool = v_pool;
+        a.lens = seq_lens;
         a.B = q->B;
         a.Hq = q->Hq;
         a.Hkv = q->Hkv;
-        a.G = q->Hq / q->Hkv;
+        a.has_suffix = 1;
         a.scale_log2 = scale_log2;
+        a.dest = RowDest{o, lse, 0, 0, 0};
         a.tree = (const int32_t *)blob_dev;
-        a.seg_off = L.segs;
-        a.piece_off = L.pieces;
-        a.wgseg_off = L.wgseg;
-        a.wg0 = plan->launch_wg0[li];
-        a.k_pool = k_pool;
-        a.v_pool = v_pool;
-        a.row_stride = row_stride;
-        a.d = q->d;
+        a.seq_tok_off = L.seq_tok;
+        a.tok_rows_off = L.tok_rows;
+        a.seq_src_off = L.seq_src;
+        a.srcs_off = L.srcs;
+        a.shared_off = L.shared;
+        a.pool_rows = plan->pool_rows;
         a.part_o = part_o;
         a.part_lse = part_lse;
-        hipError_t e = launch_tree_prefix(a, q->dtype, q->d, plan->launch_nw[li],
-                                          plan->launch_wgs[li], s);
-        if (e != hipSuccess) return fail_hip(e);
-    }
-
-    // Sequence-first phase: private rows plus the merge of the partials.
-    SuffixArgs a;
-    std::memset(&a, 0, sizeof a);
-    a.q = q->q;
-    a.k_pool = k_pool;
-    a.v_pool = v_pool;
-    a.lens = seq_lens;
-    a.B = q->B;
-    a.Hq = q->Hq;
-    a.Hkv = q->Hkv;
-    a.has_suffix = 1;
-    a.scale_log2 = scale_log2;
-    a.dest = RowDest{o, lse, 0, 0, 0};
-    a.tree = (const int32_t *)blob_dev;
-    a.seq_tok_off = L.seq_tok;
-    a.tok_rows_off = L.tok_rows;
-    a.seq_src_off = L.seq_src;
-    a.srcs_off = L.srcs;
-    a.shared_off = L.shared;
-    a.pool_rows = plan->pool_rows;
-    a.part_o = part_o;
-    a.part_lse = part_lse;
-    const int64_t mb = cdiv(plan->max_private, HP_BLOCK_SIZE);
-    const int nws = mb <= 2 ? 1 : mb <= 16 ? 2 : 4;
-    hipError_t e = launch_tree_suffix(a, q->dtype, q->d, q->Hq / q->Hkv, nws, s);
-    return e == hipSuccess ? HP_OK : fail_hip(e);
+        const int64_t mb = cdiv(plan->max_private, HP_BLOCK_SIZE);
+        const int nws = mb <= 2 ? 1 : mb <= 16 ? 2 : 4;
+        hipError_t e = launch_tree_suffix(a, q->dtype, q->d, q->Hq / q->Hkv, nws, s);
+        return e == hipSuccess ? HP_OK : fail_hip(e);
+    });
 }
 
 hp_status hp_kv_append(const void *k_new, const void *v_new, const int32_t *rows, int32_t n,
                        int32_t Hkv, int32_t d, int32_t dtype, void *k_pool, void *v_pool,
                        int64_t pool_rows, int32_t *seq_lens, const int32_t *seq_idx,
                        int32_t num_seqs, void *stream) {
-    if (n < 0 || Hkv <= 0 || d <= 0 || pool_rows < 0 || num_seqs < 0) return HP_ERR_INVALID_ARG;
-    if (dtype < HP_F32 || dtype > HP_BF16) return HP_ERR_INVALID_ARG;
-    if ((seq_lens == nullptr) != (seq_idx == nullptr)) return HP_ERR_INVALID_ARG;
-    const int64_t row_bytes = (int64_t)Hkv * d * esize(dtype);
-    if (row_bytes % 16) return HP_ERR_INVALID_ARG;
-    if (n == 0) return HP_OK;
-    if (!k_new || !v_new || !rows || !k_pool || !v_pool) return HP_ERR_NULL;
-    if (!aligned16(k_new) || !aligned16(v_new) || !aligned16(k_pool) || !aligned16(v_pool) ||
-        ((uintptr_t)rows & 3u) || ((uintptr_t)seq_lens & 3u) || ((uintptr_t)seq_idx & 3u))
-        return HP_ERR_INVALID_ARG;
-    if (cdiv(row_bytes / 16, 256) > 65535) return HP_ERR_UNSUPPORTED;
-    hipError_t e = launch_kv_append(k_new, v_new, rows, n, row_bytes, k_pool, v_pool, pool_rows,
-                                    seq_lens, seq_idx, num_seqs, (hipStream_t)stream);
-    return e == hipSuccess ? HP_OK : fail_hip(e);
+    return hp::guarded([&]() -> hp_status {
+        if (n < 0 || Hkv <= 0 || d <= 0 || pool_rows < 0 || num_seqs < 0) return HP_ERR_INVALID_ARG;
+        if (dtype < HP_F32 || dtype > HP_BF16) return HP_ERR_INVALID_ARG;
+        if ((seq_lens == nullptr) != (seq_idx == nullptr)) return HP_ERR_INVALID_ARG;
+        const int64_t row_bytes = (int64_t)Hkv * d * esize(dtype);
+        if (row_bytes % 16) return HP_ERR_INVALID_ARG;
+        if (n == 0) return HP_OK;
+        if (!k_new || !v_new || !rows || !k_pool || !v_pool) return HP_ERR_NULL;
+        if (!aligned16(k_new) || !aligned16(v_new) || !aligned16(k_pool) || !aligned16(v_pool) ||
+            ((uintptr_t)rows & 3u) || ((uintptr_t)seq_lens & 3u) || ((uintptr_t)seq_idx & 3u))
+            return HP_ERR_INVALID_ARG;
+        if (cdiv(row_bytes / 16, 256) > 65535) return HP_ERR_UNSUPPORTED;
+        hipError_t e = launch_kv_append(k_new, v_new, rows, n, row_bytes, k_pool, v_pool, pool_rows,
+                                        seq_lens, seq_idx, num_seqs, (hipStream_t)stream);
+        return e == hipSuccess ? HP_OK : fail_hip(e);
+    });
 }
 
 }  // extern "C"

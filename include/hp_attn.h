@@ -42,9 +42,9 @@
  * Streams.     `stream` is a hipStream_t (NULL = the null stream).  Work is
  *              enqueued asynchronously; calls are graph-capture safe (no
  *              allocation, host sync, memset or host-to-device copy).  The
- *              cascade step may also use one stream of the library's own per
- *              device, created with two events on its first use there and kept
- *              until the process ends (see hp_cascade_step).
+ *              library holds no state of its own: no streams, events, buffers
+ *              or settings; a second stream, when a step uses one, is the
+ *              caller's (hp_cascade_step_overlap).
  * Errors.      Every argument is validated on the host before anything is
  *              enqueued; on an error nothing is enqueued and nothing is written.
  *              A failed launch returns HP_ERR_HIP (hp_last_hip_error() has the
@@ -53,8 +53,12 @@
  *              makes that row's O and LSE NaN and is never dereferenced.
  * Empty sets.  A row with no keys gets O = 0 and LSE = -inf.  Merging with an
  *              empty part returns the other part.
- * Determinism. No atomics: the same inputs on the same GPU and build give the
- *              same bits.
+ * Determinism. The attention kernels use no atomics and no order-dependent
+ *              reduction: the same inputs on the same GPU and build give the same
+ *              bits.  (hp_kv_append's optional length advance uses integer atomic
+ *              adds, whose result does not depend on their order.)
+ * Exceptions.  None crosses the boundary: a host-side failure inside an entry
+ *              point (out of host memory) returns HP_ERR_HOST.
  * Domain (v1). d in {64, 128}; block_size 16; 1 <= Hq/Hkv <= 8 and a power of
  *              two; at most HP_MAX_LEVELS tree levels and HP_MAX_NODES nodes.
  *              Anything else returns HP_ERR_UNSUPPORTED.
@@ -84,7 +88,8 @@ typedef enum hp_status {
     HP_ERR_UNSUPPORTED = 3, /* valid, but outside the implemented domain */
     HP_ERR_WORKSPACE = 4,   /* workspace NULL or smaller than the size query's answer */
     HP_ERR_HIP = 5,         /* a HIP launch failed; see hp_last_hip_error() */
-    HP_ERR_CAPACITY = 6     /* a pool, plan buffer or output array is too small */
+    HP_ERR_CAPACITY = 6,    /* a pool, plan buffer or output array is too small */
+    HP_ERR_HOST = 7         /* host-side failure (out of host memory); nothing was enqueued */
 } hp_status;
 
 /* The query side of one decode step. */
@@ -94,7 +99,8 @@ typedef struct hp_query {
     int32_t Hq, Hkv;    /* query and KV heads; Hq % Hkv == 0 */
     int32_t d;          /* head dimension */
     int32_t dtype;      /* hp_dtype of q, k and v */
-    float scale;        /* score = scale * q.k (normally 1/sqrt(d)) */
+    float scale;        /* score = scale * q.k (normally 1/sqrt(d)); finite and >= 0,
+                           else HP_ERR_INVALID_ARG */
 } hp_query;
 
 /*
@@ -181,26 +187,12 @@ hp_status hp_lse_merge(int32_t n, const float *const *o_in, const float *const *
 /*
  * One whole decode step: every row (b, h) attends the keys of every tree node
  * covering b (root level first) followed by its paged suffix.  Runs the prefix
- * pass for every node, the suffix pass, and one n-way merge (Hydragen page,
- * "Hierarchical Sharing": decomposition at every tree vertex, recombined with
- * the stored LSE of each level).  tree may be NULL (suffix only); kv may be
- * NULL (prefix only).  lse may be NULL.
- *
- * The prefix and suffix passes depend on nothing but the inputs (the merge
- * needs both; Hydragen page, "Attention Decomposition Across Subsequences",
- * Eq. 5), so the step may run them side by side: the prefix pass on `stream`,
- * the suffix pass on a second stream that the library creates for the
- * device that owns `stream` (the current device for the null stream) on first
- * use (default priority, kept until the process ends), forked from and joined back to `stream` with events, then the merge
- * on `stream`.  Everything enqueued on `stream` before the call is ordered
- * before both passes and everything after it after the merge, eagerly and
- * under graph capture alike.  The second stream is shared by every such call
- * on the device (calls from several host threads are ordered on it, each with
- * its own fork and join); while one thread captures such a step into a graph,
- * another must not run one on the same device (the second stream then belongs
- * to the capture).  Otherwise every launch is on `stream`, the suffix pass
- * with the merge fused into it.  hp_set_concurrency selects the policy;
- * hp_cascade_concurrent reports the choice for given arguments.
+ * pass for every node, then the suffix pass with one n-way merge fused into
+ * its epilogue (Hydragen page, "Hierarchical Sharing": decomposition at every
+ * tree vertex, recombined with the stored LSE of each level), all on
+ * `stream`.  tree may be NULL (suffix only); kv may be NULL (prefix only).
+ * lse may be NULL.  Workspace: hp_cascade_workspace_size(), which covers
+ * hp_cascade_step_overlap() too.
  */
 hp_status hp_cascade_workspace_size(const hp_query *query, const hp_prefix_tree *tree,
                                     const hp_paged_kv *kv, size_t *bytes);
@@ -209,41 +201,71 @@ hp_status hp_cascade_step(const hp_query *query, const hp_prefix_tree *tree,
                           size_t workspace_bytes, void *stream);
 
 /*
- * Policy for running the passes side by side (see hp_cascade_step).  mode 0:
- * never; 1 (the default): when the plan expects a gain, that is when, with
- * the prefix pass planned for 160 of the 256 compute units, every prefix split
- * still covers at least 8 tiles of 64 keys, and the suffix has at least 4096
- * (sequence, KV head) units; 2: whenever the step has both a prefix and a
- * suffix.  Process-wide.  The workspace size depends on the choice: query
- * hp_cascade_workspace_size after changing the mode.  HP_ERR_INVALID_ARG for
- * any other mode.
+ * Running the prefix and suffix passes side by side.  They depend on nothing
+ * but the inputs (only the merge needs both; Hydragen page, "Attention
+ * Decomposition Across Subsequences", Eq. 5), so a step may launch the
+ * suffix pass on a second stream while the prefix pass, planned for fewer
+ * compute units, runs on `stream`; one merge on `stream` then combines every
+ * partial.  The caller owns the second stream and both events (the library
+ * creates, keeps and synchronises nothing):
+ *   side_stream  a hipStream_t of the same device as `stream`, not `stream`
+ *                itself (a stream that does not synchronise with the null
+ *                stream, at default priority, is what this path is made for);
+ *   fork_event, join_event  hipEvent_t handles created by the caller
+ *                (hipEventDisableTiming suffices), recorded and waited on by
+ *                the step: fork on `stream` before any launch and waited on by
+ *                side_stream, join on side_stream after the suffix pass and
+ *                waited on by `stream` before the merge;
+ *   mode         0: never (exactly hp_cascade_step); 1: when the plan expects
+ *                a gain, that is when, with the prefix pass planned for 160 of
+ *                the 256 compute units, every prefix split still covers at
+ *                least 8 tiles of 64 keys and the suffix has at least 4096
+ *                (sequence, KV head) units; 2: whenever the step has both a
+ *                prefix and a suffix.
+ * Everything enqueued on `stream` before the call is ordered before both
+ * passes and everything after it after the merge, eagerly and under graph
+ * capture alike (the events become the graph's fork and join).  Calls that
+ * share the same events or side stream must not run concurrently from
+ * several host threads.  HP_ERR_NULL when the plan runs side by side and a
+ * handle is NULL; HP_ERR_INVALID_ARG for side_stream == stream or another
+ * mode.
  */
-hp_status hp_set_concurrency(int32_t mode);
+typedef struct hp_overlap {
+    void *side_stream;
+    void *fork_event;
+    void *join_event;
+    int32_t mode;
+} hp_overlap;
+
+hp_status hp_cascade_step_overlap(const hp_query *query, const hp_prefix_tree *tree,
+                                  const hp_paged_kv *kv, float *o, float *lse, void *workspace,
+                                  size_t workspace_bytes, void *stream, const hp_overlap *overlap);
 
 /*
- * *concurrent = 1 when hp_cascade_step with these arguments would run the
- * suffix pass beside the prefix pass under the current policy, else 0.
- * Validates the arguments like hp_cascade_workspace_size.
+ * *overlapped = 1 when hp_cascade_step_overlap with these arguments and this
+ * mode would run the passes side by side, else 0.  Validates the arguments
+ * like hp_cascade_workspace_size.
  */
-hp_status hp_cascade_concurrent(const hp_query *query, const hp_prefix_tree *tree,
-                                const hp_paged_kv *kv, int32_t *concurrent);
+hp_status hp_cascade_overlap_plan(const hp_query *query, const hp_prefix_tree *tree,
+                                  const hp_paged_kv *kv, int32_t mode, int32_t *overlapped);
 
 /*
- * hp_cascade_step plus per-pass timing: records events[0] on `stream` right
- * before the first prefix launch (after the fork when the passes run side by
- * side), events[1] after the prefix pass (all levels), events[2]
- * after the suffix pass (on the library's second stream when the passes run
- * side by side) and events[3] after the merge; with n_events = 5, events[4]
- * on the suffix pass's stream right before its launch (so that the suffix
- * pass can be timed from its own start when it does not follow the prefix
- * pass).  events is a host array of n_events (0, 4 or 5) hipEvent_t handles
- * created by the caller; NULL entries are skipped.  Otherwise identical to hp_cascade_step.  For
- * measurement harnesses; the computation is the one described above.
+ * hp_cascade_step (overlap NULL) or hp_cascade_step_overlap plus per-pass
+ * timing: records events[0] on `stream` right before the first prefix launch
+ * (after the fork when the passes run side by side), events[1] after the
+ * prefix pass (all levels), events[2] after the suffix pass (on the side
+ * stream when the passes run side by side) and events[3] after the merge;
+ * with n_events = 5, events[4] on the suffix pass's stream right before its
+ * launch (so that the suffix pass can be timed from its own start when it
+ * does not follow the prefix pass).  events is a host array of n_events (0, 4
+ * or 5) hipEvent_t handles created by the caller; NULL entries are skipped; a
+ * NULL array with n_events > 0 is HP_ERR_NULL.  For measurement harnesses;
+ * the computation is the one described above.
  */
 hp_status hp_cascade_step_timed(const hp_query *query, const hp_prefix_tree *tree,
                                 const hp_paged_kv *kv, float *o, float *lse, void *workspace,
-                                size_t workspace_bytes, void *stream, void *const *events,
-                                int32_t n_events);
+                                size_t workspace_bytes, void *stream, const hp_overlap *overlap,
+                                void *const *events, int32_t n_events);
 
 /* ------------------------------------------------------------------------
  * Shared-context requests: stream-id masked decode
@@ -441,6 +463,8 @@ hp_status hp_kv_append(const void *k_new, const void *v_new, const int32_t *rows
  *           reported with its remaining room, so the plan stays valid while
  *           tokens are appended into it.
  * Sequence ids are caller-chosen int64 values.  A handle is not thread-safe.
+ * After HP_ERR_HOST (host memory exhausted part-way) a handle may be left
+ * inconsistent and must only be destroyed.
  */
 typedef struct hp_pakv hp_pakv;
 typedef struct hp_pakv_stats {

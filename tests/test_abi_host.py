@@ -42,7 +42,7 @@ def test_exports_every_declared_symbol(L):
 
 
 def test_status_strings_and_version(L):
-    for code in range(6):
+    for code in range(8):
         assert L.hp_status_string(code)
     assert L.hp_status_string(99) == b"unknown status"
     assert b"gfx950" in L.hp_version()
@@ -72,6 +72,8 @@ def prefix_status(L, q, n, o=FAKE, lse=FAKE, ws=None, wsb=0):
     (dict(Hkv=0), INVALID),
     (dict(dtype=7), INVALID),
     (dict(scale=float("nan")), INVALID),
+    (dict(scale=-0.088), INVALID),          # negative scale: the max of the raw scores is not
+    (dict(scale=float("-inf")), INVALID),   # the max of the scaled ones
     (dict(d=96), UNSUPPORTED),
     (dict(Hq=48, Hkv=3), UNSUPPORTED),      # group of 16
     (dict(Hq=6, Hkv=2), UNSUPPORTED),       # group of 3
@@ -230,3 +232,34 @@ def test_missing_library_fails_loudly(monkeypatch, tmp_path):
     monkeypatch.setattr(hp, "LIB_PATH", str(tmp_path / "absent.so"))
     with pytest.raises(RuntimeError, match="not built"):
         hp.lib()
+
+
+def test_timed_step_events_checked(L):
+    """hp_cascade_step_timed: a NULL event array with a nonzero count is rejected before
+    anything is enqueued, and counts other than 0, 4 and 5 are invalid."""
+    q = q_()
+    kv = kv_()
+    step = L.hp_cascade_step_timed
+    assert step(ctypes.byref(q), None, ctypes.byref(kv), FAKE, FAKE, FAKE, 1 << 30, None, None,
+                None, 4) == NULL
+    assert step(ctypes.byref(q), None, ctypes.byref(kv), FAKE, FAKE, FAKE, 1 << 30, None, None,
+                None, 5) == NULL
+    ev = (ctypes.c_void_p * 3)()
+    assert step(ctypes.byref(q), None, ctypes.byref(kv), FAKE, FAKE, FAKE, 1 << 30, None, None,
+                ctypes.addressof(ev), 3) == INVALID
+
+
+def test_negative_scale_rejected_by_every_step(L):
+    """Every entry point that reads a query rejects a negative scale before any launch."""
+    q = q_(scale=-1.0)
+    n = node_()
+    assert prefix_status(L, q, n) == INVALID
+    kv = kv_()
+    assert L.hp_suffix_decode(ctypes.byref(q), ctypes.byref(kv), FAKE, FAKE, None, 0,
+                              None) == INVALID
+    assert L.hp_cascade_step(ctypes.byref(q), None, ctypes.byref(kv), FAKE, FAKE, FAKE, 1 << 30,
+                             None) == INVALID
+    q0 = q_(scale=0.0)  # zero is allowed: every score is 0
+    sz = ctypes.c_size_t(0)
+    assert L.hp_cascade_workspace_size(ctypes.byref(q0), None, ctypes.byref(kv),
+                                       ctypes.byref(sz)) == OK

@@ -1,7 +1,8 @@
 """Policy for running a cascade step's suffix pass beside its prefix pass, on the CPU:
-hp_cascade_concurrent reports the plan's choice (planning reads no device memory, so
-host tensors stand in for the device buffers), hp_set_concurrency switches the policy,
-and the workspace grows by exactly the suffix pass's (O, LSE) rows when it is on."""
+hp_cascade_overlap_plan reports the plan's choice for a mode (planning reads no device
+memory, so fake addresses stand in for the device buffers), the workspace size covers
+every mode, and hp_cascade_step_overlap validates the caller's streams and events
+before anything is enqueued."""
 import ctypes
 
 import pytest
@@ -16,12 +17,6 @@ def L():
         import __graft_entry__
         __graft_entry__.build()
     return hp.lib()
-
-
-@pytest.fixture(autouse=True)
-def _restore(L):
-    yield
-    assert L.hp_set_concurrency(1) == 0
 
 
 FAKE = 1 << 40  # an aligned address: planning checks pointers, never reads them
@@ -43,13 +38,13 @@ def _args(B, Hq, Hkv, d, P, max_blocks, prefix=True, suffix=True):
     return query, tree, kv, keep
 
 
-def _plan(L, args):
+def _plan(L, args, mode=1):
     query, tree, kv, _ = args
     flag = ctypes.c_int32(-1)
     nbytes = ctypes.c_size_t(0)
     tp = ctypes.byref(tree) if tree is not None else None
     kp = ctypes.byref(kv) if kv is not None else None
-    assert L.hp_cascade_concurrent(ctypes.byref(query), tp, kp, ctypes.byref(flag)) == 0
+    assert L.hp_cascade_overlap_plan(ctypes.byref(query), tp, kp, mode, ctypes.byref(flag)) == 0
     assert L.hp_cascade_workspace_size(ctypes.byref(query), tp, kp, ctypes.byref(nbytes)) == 0
     return flag.value, nbytes.value
 
@@ -89,30 +84,45 @@ def test_auto_policy_two_level_gqa_stays_serial(L):
 def test_modes_and_workspace(L):
     B, Hq, Hkv, d = 8, 4, 2, 64
     args = _args(B, Hq, Hkv, d, 300, 4)
-    assert L.hp_set_concurrency(0) == 0
-    off, ws_off = _plan(L, args)
+    off, ws = _plan(L, args, mode=0)
     assert off == 0
-    assert L.hp_set_concurrency(2) == 0
-    on, ws_on = _plan(L, args)
+    on, ws_on = _plan(L, args, mode=2)
     assert on == 1
+    assert ws_on == ws, "one workspace size serves every mode"
 
     def up(x):
         return (x + 255) // 256 * 256
     # the prefix partials for 160 compute units plus the suffix rows (O and LSE)
-    assert ws_on >= up(B * Hq * d * 4) + up(B * Hq * 4)
+    assert ws >= up(B * Hq * d * 4) + up(B * Hq * 4)
     # prefix only or suffix only: nothing to run side by side
-    assert _plan(L, _args(B, Hq, Hkv, d, 300, 4, suffix=False))[0] == 0
-    assert _plan(L, _args(B, Hq, Hkv, d, 300, 4, prefix=False))[0] == 0
-    assert L.hp_set_concurrency(1) == 0
-    assert _plan(L, args)[0] == 0
+    assert _plan(L, _args(B, Hq, Hkv, d, 300, 4, suffix=False), mode=2)[0] == 0
+    assert _plan(L, _args(B, Hq, Hkv, d, 300, 4, prefix=False), mode=2)[0] == 0
+    assert _plan(L, args, mode=1)[0] == 0
 
 
 def test_mode_validation(L):
-    assert L.hp_set_concurrency(3) == 2
-    assert L.hp_set_concurrency(-1) == 2
     query, tree, kv, _ = _args(4, 2, 2, 64, 100, 2)
-    assert L.hp_cascade_concurrent(ctypes.byref(query), ctypes.byref(tree), ctypes.byref(kv),
-                                   None) == 1
+    flag = ctypes.c_int32(0)
+    for bad in (3, -1):
+        assert L.hp_cascade_overlap_plan(ctypes.byref(query), ctypes.byref(tree),
+                                         ctypes.byref(kv), bad, ctypes.byref(flag)) == 2
+    assert L.hp_cascade_overlap_plan(ctypes.byref(query), ctypes.byref(tree), ctypes.byref(kv),
+                                     1, None) == 1
+
+
+def test_overlap_handles_validated(L):
+    """A side-by-side plan needs the caller's side stream and both events, and the side
+    stream must differ from the step's stream; each is checked before any launch."""
+    query, tree, kv, _ = _args(8, 4, 2, 64, 300, 4)
+    step = L.hp_cascade_step_overlap
+    args = (ctypes.byref(query), ctypes.byref(tree), ctypes.byref(kv), FAKE, FAKE, FAKE, 1 << 30)
+    assert step(*args, None, None) == 1
+    S, E1, E2 = 0x1000, 0x2000, 0x3000  # never dereferenced: validation fails first
+    assert step(*args, None, ctypes.byref(hp.Overlap(None, E1, E2, 2))) == 1
+    assert step(*args, None, ctypes.byref(hp.Overlap(S, None, E2, 2))) == 1
+    assert step(*args, None, ctypes.byref(hp.Overlap(S, E1, None, 2))) == 1
+    assert step(*args, S, ctypes.byref(hp.Overlap(S, E1, E2, 2))) == 2
+    assert step(*args, None, ctypes.byref(hp.Overlap(S, E1, E2, 7))) == 2
 
 
 def test_timed_event_count_validation(L):
@@ -120,4 +130,5 @@ def test_timed_event_count_validation(L):
     ev = (ctypes.c_void_p * 6)()
     for n in (1, 3, 6, -1):
         assert L.hp_cascade_step_timed(ctypes.byref(query), ctypes.byref(tree), ctypes.byref(kv),
-                                       FAKE, FAKE, None, 0, None, ctypes.addressof(ev), n) == 2
+                                       FAKE, FAKE, None, 0, None, None, ctypes.addressof(ev),
+                                       n) == 2

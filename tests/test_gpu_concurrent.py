@@ -1,10 +1,11 @@
-"""GPU parity of the cascade step when its suffix pass runs beside its prefix pass (on
-the library's second stream, forked from and joined to the caller's stream), forced on
-for shapes the automatic policy would run serially: results against the fp64 oracle
-(tolerances in gpu_util.TOL), NaN rows for bad metadata, ordering with work the caller
-enqueues just before and after the step, graph capture, and the timed entry point.
-The full-size MHA and document steps, which the automatic policy runs this way, are
-covered by test_cascade_full_size_sampled."""
+"""GPU parity of the cascade step when its suffix pass runs beside its prefix pass
+(hp_cascade_step_overlap: on a second stream that the caller owns, forked from and
+joined to the caller's stream with the caller's events), forced on (mode 2) for shapes
+the automatic policy would run serially: results against the fp64 oracle (tolerances
+in gpu_util.TOL), NaN rows for bad metadata, ordering with work the caller enqueues just
+before and after the step, graph capture (also of a step's very first call), and the
+timed entry point.  The full-size MHA and document steps, which the automatic policy
+runs this way, are covered by test_cascade_full_size_every_row."""
 import ctypes
 
 import numpy as np
@@ -21,17 +22,14 @@ pytestmark = pytest.mark.gpu
 
 
 @pytest.fixture(scope="module", autouse=True)
-def _forced():
+def _gpu():
     if not torch.cuda.is_available():
         pytest.fail("GPU tests need an MI355X (no GPU visible)")
-    hp.set_concurrency(2)
-    yield
-    hp.set_concurrency(1)
 
 
 def _call(ds, scale):
     call = hp.CascadeCall(ds["q"], ds["levels"], ds["k_pool"], ds["v_pool"], ds["block_table"],
-                          ds["seq_lens"], scale)
+                          ds["seq_lens"], scale, overlap=2)
     assert call.concurrent, "forced mode must run the passes side by side"
     return call
 
@@ -112,8 +110,38 @@ def test_concurrent_graph_replay_matches_eager():
         assert torch.equal(call.out, eager_o), f"eager after replay {rep}"
 
 
+def test_concurrent_first_call_captured():
+    """The very first call of a side-by-side step may be the one captured into a graph:
+    nothing is created on first use (the second stream and the events exist before the
+    call), and every replay equals a separate eager step on the same inputs."""
+    cfg = REDUCED[3]
+    step = workloads.generate(cfg, seed=17)
+    ds = dev_step(step)
+    ref_call = _call(ds, step.scale)
+    eager_o, eager_l = [t.clone() for t in ref_call()]
+    torch.cuda.synchronize()
+    call = _call(ds, step.scale)
+    s = torch.cuda.Stream()
+    with torch.cuda.stream(s):
+        g = torch.cuda.CUDAGraph()
+        g.capture_begin()
+        call(stream=s)
+        g.capture_end()
+    for rep in range(4):
+        call.out.fill_(3.0)
+        call.lse.fill_(3.0)
+        torch.cuda.synchronize()
+        g.replay()
+        torch.cuda.synchronize()
+        assert torch.equal(call.out, eager_o) and torch.equal(call.lse, eager_l), f"replay {rep}"
+        ref_call()  # eager work between replays
+        torch.cuda.synchronize()
+    ref_o, ref_l = oracle.step_attention(step, "all")
+    compare(call.out, call.lse, ref_o, ref_l, cfg.dtype, "first call captured")
+
+
 def test_concurrent_timed_records_events():
-    """events[2] and events[4] are recorded on the library's second stream: the passes
+    """events[2] and events[4] are recorded on the second stream: the passes
     end between events[0] and events[3], the suffix pass lies between events[4] and
     events[2], and the result equals the untimed call."""
     cfg = REDUCED[2]
@@ -148,9 +176,9 @@ def test_concurrent_timed_records_events():
 
 
 def test_concurrent_from_two_host_threads():
-    """Two host threads, each with its own stream, inputs and workspace, step side by side
-    many times: the library's shared second stream and events keep every step's fork and
-    join its own, so each thread's results equal its single-threaded ones."""
+    """Two host threads, each with its own stream, inputs, workspace, second stream and
+    events, step side by side many times: each thread's results equal its
+    single-threaded ones (the library shares nothing between the calls)."""
     import threading
     cfgs = [REDUCED[2], REDUCED[3]]
     setups = []
