@@ -92,7 +92,7 @@ def workload(name: str):
     raise SystemExit(f"unknown workload {name}")
 
 
-def prepare(cfg, seed: int):
+def prepare(cfg, seed: int, overlap: int = 1):
     import torch
     import workloads
     import decode_attention_shared_amd as hp
@@ -101,7 +101,8 @@ def prepare(cfg, seed: int):
     levels = [[(n.k.to(dev), n.v.to(dev), n.seq_begin, n.seq_end) for n in lvl]
               for lvl in step.levels]
     call = hp.CascadeCall(step.q.to(dev), levels, step.k_pool.to(dev), step.v_pool.to(dev),
-                          step.block_table.to(dev), step.seq_lens.to(dev), step.scale)
+                          step.block_table.to(dev), step.seq_lens.to(dev), step.scale,
+                          overlap=overlap)
     torch.cuda.synchronize()
     return step, call
 

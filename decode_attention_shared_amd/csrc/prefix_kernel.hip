@@ -195,8 +195,9 @@ __device__ __forceinline__ float softmax_tile(float (&x)[32], float &m_run, floa
 template <int D>
 __device__ __forceinline__ void write_row(const RowDest &dest, int split, int64_t row_index,
                                           const f32x16 (&oacc)[D / 32], int hi, float m_run,
-                                          float l_run) {
+                                          float l_run, float l_lse) {
     const float l_tot = l_run + __shfl_xor(l_run, 32, kWave);
+    const float l_lse_tot = l_lse + __shfl_xor(l_lse, 32, kWave);
     const bool empty = !(l_tot > 0.f);
     const float inv = empty ? 0.f : 1.f / l_tot;
     float *op = dest.o + (int64_t)split * dest.o_split + row_index * D;
@@ -214,7 +215,7 @@ __device__ __forceinline__ void write_row(const RowDest &dest, int split, int64_
     }
     if (hi == 0 && dest.lse != nullptr)
         dest.lse[(int64_t)split * dest.lse_split + row_index] =
-            empty ? -INFINITY : (m_run + fast_log2(l_tot)) * kLn2;
+            empty ? -INFINITY : (m_run + fast_log2(l_lse_tot)) * kLn2;
 }
 
 // ---------------------------------------------------------------------------
@@ -254,17 +255,33 @@ __device__ __forceinline__ float add_packed(uint32_t pk, float sum) {
     }
 }
 
+// Running softmax denominators of one row (this lane's keys).  `o` sums the
+// probabilities after rounding to the 16-bit P operand, so that the weights
+// O is divided by are the ones the value product used.  The log-sum-exp needs
+// the sum before rounding: rounding each term moves the log of the sum by at
+// most the type's unit roundoff, 2^-11 (4.9e-4) for fp16 but 2^-8 (3.9e-3) for
+// bf16, so bf16 keeps the unrounded sum as well.
+template <bool kBf16>
+struct RowSum {
+    float o = 0.f;
+    float x = 0.f;  // bf16 only: the probabilities before rounding
+    __device__ __forceinline__ void scale(float a) {
+        o *= a;
+        if constexpr (kBf16) x *= a;
+    }
+    __device__ __forceinline__ float lse() const { return kBf16 ? x : o; }
+};
+
 // Online softmax for one 64-key tile of raw scores q.k (masked keys are
 // -inf), in two halves.  softmax_max: the tile's row max (both half-waves hold
 // keys of the same query) and, when it exceeds the running max by more than
 // kLazy, the new max and the factor alpha by which the running state must be
 // rescaled (the return value, wave-uniform).  softmax_exp: the probabilities
 // 2^(s*c - m) with c = scale * log2(e), packed into 16 pairs of the 16-bit
-// type (the B operand of the value product), and the row sum of exactly those
-// rounded values, so numerator and denominator use the same weights.
+// type (the B operand of the value product), and the row sums.
 template <bool kBf16>
 __device__ __forceinline__ bool softmax_max(const f32x16 &s0, const f32x16 &s1, float c,
-                                            float &m_run, float &l_run, float &alpha) {
+                                            float &m_run, RowSum<kBf16> &l, float &alpha) {
     // maximum (not fmaxf): no NaN canonicalisation of every input, and
     // v_maximum3 takes two new scores per instruction.
     // four independent chains, then a short tree (latency, not op count)
@@ -284,7 +301,7 @@ __device__ __forceinline__ bool softmax_max(const f32x16 &s0, const f32x16 &s1, 
     if (rescale) {
         const float m_new = fmaxf(m_run, mts);
         alpha = fast_exp2(m_run - m_new);  // 0 on the first tile (m_run = -inf)
-        l_run *= alpha;
+        l.scale(alpha);
         m_run = m_new;
     }
     return rescale;
@@ -292,22 +309,22 @@ __device__ __forceinline__ bool softmax_max(const f32x16 &s0, const f32x16 &s1, 
 
 template <bool kBf16>
 __device__ __forceinline__ void softmax_exp(const f32x16 &s0, const f32x16 &s1, float c,
-                                            float m_run, float &l_run, uint32_t (&pk)[16]) {
+                                            float m_run, RowSum<kBf16> &l, uint32_t (&pk)[16]) {
     const float neg_m = -m_run;
     float sq[4] = {0.f, 0.f, 0.f, 0.f};  // independent accumulation chains
+    float sx[4] = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-    for (int i = 0; i < 8; ++i) {
-        pk[i] = pack_p<kBf16>(fast_exp2(fmaf(s0[2 * i], c, neg_m)),
-                              fast_exp2(fmaf(s0[2 * i + 1], c, neg_m)));
+    for (int i = 0; i < 16; ++i) {
+        const f32x16 &s = i < 8 ? s0 : s1;
+        const int j = 2 * (i % 8);
+        const float a = fast_exp2(fmaf(s[j], c, neg_m));
+        const float b = fast_exp2(fmaf(s[j + 1], c, neg_m));
+        pk[i] = pack_p<kBf16>(a, b);
         sq[i % 4] = add_packed<kBf16>(pk[i], sq[i % 4]);
+        if constexpr (kBf16) sx[i % 4] += a + b;
     }
-#pragma unroll
-    for (int i = 0; i < 8; ++i) {
-        pk[8 + i] = pack_p<kBf16>(fast_exp2(fmaf(s1[2 * i], c, neg_m)),
-                                  fast_exp2(fmaf(s1[2 * i + 1], c, neg_m)));
-        sq[i % 4] = add_packed<kBf16>(pk[8 + i], sq[i % 4]);
-    }
-    l_run += (sq[0] + sq[1]) + (sq[2] + sq[3]);
+    l.o += (sq[0] + sq[1]) + (sq[2] + sq[3]);
+    if constexpr (kBf16) l.x += (sx[0] + sx[1]) + (sx[2] + sx[3]);
 }
 
 // Position of a V row's 16-byte chunks in LDS: chunk c of row r sits at
@@ -388,7 +405,8 @@ __device__ __forceinline__ void mfma16_body(const PrefixArgs &args, const WgTask
     f32x16 oacc[kDBlocks];
 #pragma unroll
     for (int db = 0; db < kDBlocks; ++db) oacc[db] = f32x16{};
-    float m_run = -INFINITY, l_run = 0.f;
+    float m_run = -INFINITY;
+    RowSum<kBf16> l;
 
     const uint16_t *kbase = (const uint16_t *)nd.k + (int64_t)task.g * nd.stride_head;
     const uint16_t *vbase = (const uint16_t *)nd.v + (int64_t)task.g * nd.stride_head;
@@ -489,13 +507,13 @@ __device__ __forceinline__ void mfma16_body(const PrefixArgs &args, const WgTask
             }
         }
         float alpha;
-        if (softmax_max<kBf16>(sc0, sc1, c, m_run, l_run, alpha)) {
+        if (softmax_max<kBf16>(sc0, sc1, c, m_run, l, alpha)) {
 #pragma unroll
             for (int db = 0; db < kDBlocks; ++db) oacc[db] *= alpha;
         }
         qk((tile + 1 - tb) % kStages, sn0, sn1);
         uint32_t pk[16];
-        softmax_exp<kBf16>(sc0, sc1, c, m_run, l_run, pk);
+        softmax_exp<kBf16>(sc0, sc1, c, m_run, l, pk);
         pv(pk, (tile - tb) % kStages);
 #pragma unroll
         for (int k = 0; k < 2 * kDSteps + 4 * kDBlocks; ++k) {
@@ -533,7 +551,7 @@ __device__ __forceinline__ void mfma16_body(const PrefixArgs &args, const WgTask
 
     if (row_ok) {
         const int64_t ri = ((int64_t)(b - nd.dest.row_base)) * args.Hq + h;
-        write_row<D>(nd.dest, task.split, ri, oacc, hi, m_run, l_run);
+        write_row<D>(nd.dest, task.split, ri, oacc, hi, m_run, l.o, l.lse());
     }
 }
 
@@ -610,7 +628,8 @@ __device__ __forceinline__ void pp_body(const PrefixArgs &args, const WgTask &ta
     f32x16 oacc[kDBlocks];
 #pragma unroll
     for (int db = 0; db < kDBlocks; ++db) oacc[db] = f32x16{};
-    float m_run = -INFINITY, l_run = 0.f;
+    float m_run = -INFINITY;
+    RowSum<kBf16> l;
 
     // Node fields the loop needs, read once (the compiler would otherwise
     // reload them from the argument segment, a scalar-memory round trip, at
@@ -777,11 +796,11 @@ __device__ __forceinline__ void pp_body(const PrefixArgs &args, const WgTask &ta
             }
         }
         float alpha;
-        if (softmax_max<kBf16>(s0, s1, c, m_run, l_run, alpha)) {
+        if (softmax_max<kBf16>(s0, s1, c, m_run, l, alpha)) {
 #pragma unroll
             for (int db = 0; db < kDBlocks; ++db) oacc[db] *= alpha;
         }
-        softmax_exp<kBf16>(s0, s1, c, m_run, l_run, pk);
+        softmax_exp<kBf16>(s0, s1, c, m_run, l, pk);
     };
 
     if (T > 0) {
@@ -831,7 +850,7 @@ __device__ __forceinline__ void pp_body(const PrefixArgs &args, const WgTask &ta
 
     if (row_ok) {
         const int64_t ri = ((int64_t)(b - nd.dest.row_base)) * args.Hq + h;
-        write_row<D>(nd.dest, task.split, ri, oacc, hi, m_run, l_run);
+        write_row<D>(nd.dest, task.split, ri, oacc, hi, m_run, l.o, l.lse());
     }
 }
 
@@ -958,7 +977,7 @@ __device__ __forceinline__ void mfma32_body(const PrefixArgs &args, const WgTask
 
     if (row_ok) {
         const int64_t ri = ((int64_t)(b - nd.dest.row_base)) * args.Hq + h;
-        write_row<D>(nd.dest, task.split, ri, oacc, hi, m_run, l_run);
+        write_row<D>(nd.dest, task.split, ri, oacc, hi, m_run, l_run, l_run);
     }
 }
 

@@ -18,6 +18,12 @@ TOL = {"f32": dict(max_abs=1e-5, mean_abs=1e-5, lse=1e-5),
        "bf16": dict(max_abs=1e-2, mean_abs=1e-3, lse=1e-3)}
 
 
+# Every compare() appends (what, dtype, max-abs, mean-abs, LSE max-abs, rel-L2); the
+# test session prints them at its end (conftest.py), so the margins against the
+# tolerances stay in the output of a quiet run.
+MARGINS = []
+
+
 def say(msg: str) -> None:
     print(msg, flush=True)
     sys.stdout.flush()
@@ -58,6 +64,8 @@ def compare(got_o, got_l, ref_o, ref_l, dtype: str, what: str, rows=None):
     rel_l2 = float(np.linalg.norm(go - ref_o) / max(1e-300, np.linalg.norm(ref_o)))
     say(f"  {what}: max-abs {err.max():.3e} mean-abs {err.mean():.3e} "
         f"lse-max {lerr.max():.3e} rel-l2 {rel_l2:.3e}")
+    MARGINS.append((what, dtype, float(err.max()), float(err.mean()), float(lerr.max()), rel_l2,
+                    go.shape[0]))
     assert err.max() <= tol["max_abs"], f"{what}: max-abs {err.max():.3e} > {tol['max_abs']}"
     assert err.mean() <= tol["mean_abs"], f"{what}: mean-abs {err.mean():.3e} > {tol['mean_abs']}"
     assert lerr.max() <= tol["lse"], f"{what}: LSE max-abs {lerr.max():.3e} > {tol['lse']}"

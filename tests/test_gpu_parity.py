@@ -205,6 +205,84 @@ def test_cascade_peaky_scores():
     compare(out, lse, ref_o, ref_l, cfg.dtype, "peaky")
 
 
+def _prefix_splits(q, k, b0, b1):
+    """Key-range splits the library plans for one node (from its workspace size)."""
+    L = hp.lib()
+    qs = hp.make_query(q, k.shape[1])
+    node = hp.make_node(k, k, b0, b1)
+    nbytes = ctypes.c_size_t(0)
+    assert L.hp_prefix_attn_workspace_size(ctypes.byref(qs), ctypes.byref(node),
+                                           ctypes.byref(nbytes)) == 0
+    rows, d = (b1 - b0) * q.shape[1], q.shape[2]
+    up = lambda x: (x + 255) // 256 * 256  # noqa: E731
+    for n in range(1, 257):
+        if (n == 1 and nbytes.value == 0) or nbytes.value == up(n * rows * d * 4) + up(n * rows * 4):
+            return n
+    raise AssertionError(f"unexpected workspace size {nbytes.value}")
+
+
+def _late_rescales(step, node, nsplit):
+    """(row, tile) pairs, over all splits of the node, where a tile that is not the first
+    of its split has a row max more than 8 log2 units above the row's max over the
+    split's earlier tiles: the kernel's running max (which moves lazily, so it is never
+    above that max) must then move, and the accumulated O is rescaled by a factor
+    strictly between 0 and 1."""
+    c = float(np.float32(step.scale)) / np.log(2.0)
+    K = node.k.double()
+    G = step.cfg.Hq // step.cfg.Hkv
+    P = K.shape[0]
+    tiles = -(-P // 64)
+    tps = -(-tiles // nsplit)
+    count = 0
+    for h in range(step.cfg.Hq):
+        S = (step.q[node.seq_begin:node.seq_end, h, :].double() @ K[:, h // G, :].T) * c
+        for t0 in range(0, tiles, tps):
+            run = S[:, t0 * 64:(t0 + 1) * 64].max(dim=1).values
+            for t in range(t0 + 1, min(t0 + tps, tiles)):
+                tm = S[:, t * 64:min((t + 1) * 64, P)].max(dim=1).values
+                count += int((tm > run + 8.0).sum())
+                run = torch.maximum(run, tm)
+    return count
+
+
+@pytest.mark.parametrize("dtype", ["f16", "bf16"])
+@pytest.mark.parametrize("P", [4000, 16384], ids=["p4000", "p16384_nontemporal"])
+def test_prefix_256row_rescale_mid_split(dtype, P):
+    """The 256-row (ping-pong) prefix kernel with peaky scores: Q scaled by 8 and one key
+    in the middle of the prefix scaled by 6, so that tiles inside a split raise the row
+    max by more than the lazy threshold (checked on the inputs) and O is rescaled by a
+    factor strictly between 0 and 1 mid-split.  160 rows per KV head (more than 128
+    selects the 256-row kernel).  At P = 16384 the launch's K/V reach 256 MiB, so the
+    non-temporal variant of the kernel runs."""
+    B, Hq, Hkv, d = 160, 32, 32, 128
+    cfg = workloads.custom(f"peaky256_{dtype}_{P}", B=B, Hq=Hq, Hkv=Hkv, d=d, dtype=dtype,
+                           levels=(((P, 0, B),),), suffix_lo=1, suffix_hi=20)
+    step = workloads.generate(cfg, seed=21, q_mult=8.0)
+    node = step.levels[0][0]
+    node.k[P // 2 + 37] *= 6.0
+    if P * Hkv * d * 2 * 2 >= 256 << 20:
+        say("  K/V of the launch reach 256 MiB: non-temporal transfers")
+    q = step.q.to(DEV)
+    kd, vd = node.k.to(DEV), node.v.to(DEV)
+    nsplit = _prefix_splits(q, kd, 0, B)
+    late = _late_rescales(step, node, nsplit)
+    say(f"peaky 256-row prefix {dtype} P={P}: {nsplit} splits, {late} mid-split rescales")
+    assert late >= 100, "the inputs must force rescales inside splits"
+    out = torch.zeros(B, Hq, d, device=DEV)
+    lse = torch.zeros(B, Hq, device=DEV)
+    hp.prefix_attn(q, kd, vd, 0, B, step.scale, out=out, lse=lse)
+    torch.cuda.synchronize()
+    rows = None if P <= 4000 else sample_rows(B, Hq, 320, seed=3)
+    ref_o, ref_l = oracle.step_attention(step, "prefix", rows=rows)
+    compare(out, lse, ref_o, ref_l, dtype, f"peaky prefix {dtype} P={P}", rows=rows)
+    # and through the whole step (prefix, suffix and merge)
+    ds = dev_step(step)
+    out2, lse2 = cascade(ds, step.scale)
+    torch.cuda.synchronize()
+    ref_o, ref_l = oracle.step_attention(step, "all", rows=rows)
+    compare(out2, lse2, ref_o, ref_l, dtype, f"peaky step {dtype} P={P}", rows=rows)
+
+
 def test_cascade_prefix_only_and_suffix_only():
     cfg = REDUCED[4]
     step = workloads.generate(cfg, seed=6)
@@ -355,16 +433,21 @@ FULL = [workloads.tiny_f32(), workloads.llama3_8b_gqa(), workloads.codellama13b_
 
 
 @pytest.mark.parametrize("cfg", FULL, ids=lambda c: c.name)
-def test_cascade_full_size_sampled(cfg):
+def test_cascade_full_size_every_row(cfg):
+    """Each benchmark shape at full size, in the launch configuration bench.py times
+    (CascadeCall, passes side by side where the policy picks it): every row against the
+    oracle."""
     say(f"full {cfg.name}: generating")
     step = workloads.generate(cfg, seed=0)
     ds = dev_step(step)
     say(f"full {cfg.name}: running")
-    out, lse = cascade(ds, step.scale)
+    call = hp.CascadeCall(ds["q"], ds["levels"], ds["k_pool"], ds["v_pool"], ds["block_table"],
+                          ds["seq_lens"], step.scale)
+    out, lse = call()
     torch.cuda.synchronize()
-    rows = sample_rows(cfg.B, cfg.Hq, 48)
-    ref_o, ref_l = oracle.step_attention(step, "all", rows=rows)
-    compare(out, lse, ref_o, ref_l, cfg.dtype, cfg.name, rows=rows)
+    say(f"full {cfg.name}: oracle over {cfg.B * cfg.Hq} rows (side by side: {call.concurrent})")
+    ref_o, ref_l = oracle.step_attention(step, "all")
+    compare(out, lse, ref_o, ref_l, cfg.dtype, f"{cfg.name} (all rows)")
     assert torch.isfinite(out).all() and torch.isfinite(lse).all()
 
 
