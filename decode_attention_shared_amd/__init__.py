@@ -39,6 +39,7 @@ HP_MAX_MERGE = 16
 HP_BLOCK_SIZE = 16
 HP_CHUNK = 64
 HP_TREE_MAX_LAUNCHES = 4
+HP_NOALLOC_SCRATCH_BYTES = 64 * 1024 * 1024
 STATUS = {0: "HP_OK", 1: "HP_ERR_NULL", 2: "HP_ERR_INVALID_ARG", 3: "HP_ERR_UNSUPPORTED",
           4: "HP_ERR_WORKSPACE", 5: "HP_ERR_HIP", 6: "HP_ERR_CAPACITY", 7: "HP_ERR_HOST"}
 EXPORTS = ["hp_prefix_attn_workspace_size", "hp_prefix_attn", "hp_suffix_decode_workspace_size",
@@ -47,7 +48,7 @@ EXPORTS = ["hp_prefix_attn_workspace_size", "hp_prefix_attn", "hp_suffix_decode_
            "hp_tree_plan_build", "hp_share_decision", "hp_tree_step", "hp_kv_append",
            "hp_pakv_create", "hp_pakv_destroy", "hp_pakv_insert", "hp_pakv_append",
            "hp_pakv_remove", "hp_pakv_context", "hp_pakv_seq_rows", "hp_pakv_get_stats",
-           "hp_cascade_step_overlap", "hp_cascade_overlap_plan",
+           "hp_cascade_step_overlap", "hp_cascade_overlap_plan", "hp_cascade_step_noalloc",
            "hp_status_string", "hp_last_hip_error", "hp_version"]
 
 _DTYPE = {torch.float32: HP_F32, torch.float16: HP_F16, torch.bfloat16: HP_BF16}
@@ -177,6 +178,9 @@ def lib():
             L.hp_cascade_step_overlap.argtypes = [ctypes.POINTER(Query), ctypes.POINTER(PrefixTree),
                                                   ctypes.POINTER(PagedKV), p, p, p,
                                                   ctypes.c_size_t, p, ctypes.POINTER(Overlap)]
+            L.hp_cascade_step_noalloc.restype = st
+            L.hp_cascade_step_noalloc.argtypes = [ctypes.POINTER(Query), ctypes.POINTER(PrefixTree),
+                                                  ctypes.POINTER(PagedKV), p, p, p]
             L.hp_cascade_step.restype = st
             L.hp_cascade_step.argtypes = [ctypes.POINTER(Query), ctypes.POINTER(PrefixTree),
                                           ctypes.POINTER(PagedKV), p, p, p, ctypes.c_size_t, p]
@@ -532,6 +536,29 @@ def cascade_step(q: torch.Tensor, levels, k_pool=None, v_pool=None, block_table=
         call = CascadeCall(q, levels, k_pool, v_pool, block_table, seq_lens, scale, out, lse,
                            overlap)
         return call(stream)
+
+
+def cascade_step_noalloc(q: torch.Tensor, levels, k_pool=None, v_pool=None, block_table=None,
+                         seq_lens=None, scale: Optional[float] = None, out=None, lse=None,
+                         stream=None):
+    """hp_cascade_step_noalloc: cascade_step on one stream with the workspace taken from
+    the library's fixed per-GPU scratch array (at most HP_NOALLOC_SCRATCH_BYTES).  The
+    library allocates nothing; pass ``out`` (and ``lse``) to allocate nothing here either.
+    Calls on one GPU share that array: the caller orders calls that could overlap."""
+    L = lib()
+    Hkv = (levels[0][0][0].shape[1] if levels and levels[0] else k_pool.shape[2])
+    query = make_query(q, Hkv, scale)
+    tree, keep = make_tree(levels) if levels else (None, None)
+    kv = make_paged(k_pool, v_pool, block_table, seq_lens) if k_pool is not None else None
+    with _on(stream, q.device):
+        out, lse = _out(q, out, lse, zero=False)
+    _check(L.hp_cascade_step_noalloc(ctypes.byref(query),
+                                     ctypes.byref(tree) if tree is not None else None,
+                                     ctypes.byref(kv) if kv is not None else None,
+                                     out.data_ptr(), _ptr(lse), _stream(stream)),
+           "hp_cascade_step_noalloc")
+    del keep
+    return out, lse
 
 
 # ------------------------------------------------------------------------------

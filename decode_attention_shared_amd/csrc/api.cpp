@@ -404,7 +404,8 @@ const char *hp_status_string(hp_status s) {
     case HP_ERR_UNSUPPORTED: return "unsupported (outside the implemented domain)";
     case HP_ERR_WORKSPACE: return "workspace missing or too small";
     case HP_ERR_HIP: return "HIP launch failed";
-    case HP_ERR_CAPACITY: return "capacity exceeded (pool, plan buffer or output array too small)";
+    case HP_ERR_CAPACITY:
+        return "capacity exceeded (pool, plan buffer, output array or fixed scratch too small)";
     case HP_ERR_HOST: return "host-side failure (out of host memory)";
     default: return "unknown status";
     }
@@ -723,6 +724,28 @@ hp_status plan_stream(const hp_query *q, const hp_prefix_tree *doc, const hp_str
 }
 
 }  // namespace
+
+namespace hp {
+namespace host {
+
+hp_status cascade_serial_plan(const hp_query *q, const hp_prefix_tree *tree,
+                              const hp_paged_kv *kv, const float *o, const float *lse,
+                              size_t *bytes) {
+    CascadePlan cp;
+    hp_status st = plan_cascade(q, tree, kv, 0, cp);
+    if (st != HP_OK) return st;
+    if ((st = check_out(o, lse)) != HP_OK) return st;
+    *bytes = cp.bytes;
+    return HP_OK;
+}
+
+hp_status cascade_serial(const hp_query *q, const hp_prefix_tree *tree, const hp_paged_kv *kv,
+                         float *o, float *lse, void *ws, size_t ws_bytes, void *stream) {
+    return cascade_impl(q, tree, kv, o, lse, ws, ws_bytes, stream, nullptr, nullptr);
+}
+
+}  // namespace host
+}  // namespace hp
 
 extern "C" {
 

@@ -105,5 +105,14 @@ constexpr int kConcCUs = 160;
 constexpr int kConcMinTiles = 8;
 constexpr int64_t kConcMinUnits = 4096;
 
+// The cascade step on one stream (hp_cascade_step), for entry points that
+// supply the workspace themselves: cascade_serial_plan validates every
+// argument of the step (outputs included) and gives the workspace bytes.
+hp_status cascade_serial_plan(const hp_query *q, const hp_prefix_tree *tree,
+                              const hp_paged_kv *kv, const float *o, const float *lse,
+                              size_t *bytes);
+hp_status cascade_serial(const hp_query *q, const hp_prefix_tree *tree, const hp_paged_kv *kv,
+                         float *o, float *lse, void *ws, size_t ws_bytes, void *stream);
+
 }  // namespace host
 }  // namespace hp

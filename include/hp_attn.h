@@ -33,7 +33,9 @@
  * GQA.         Query head h reads KV head h / (Hq / Hkv).
  * Memory.      Every tensor pointer is a device pointer the caller owns.  The
  *              library allocates nothing, frees nothing and never synchronises;
- *              scratch space comes from the caller's workspace.  Q, K, V and O
+ *              scratch space comes from the caller's workspace (for
+ *              hp_cascade_step_noalloc, from a fixed array in the library's
+ *              device image).  Q, K, V and O
  *              pointers must be 16-byte aligned and every stride a multiple of
  *              16 bytes; d elements of one (token, head) are contiguous.
  *              K/V that a prefix launch, a paged suffix or a token-table pass
@@ -44,7 +46,8 @@
  *              allocation, host sync, memset or host-to-device copy).  The
  *              library holds no state of its own: no streams, events, buffers
  *              or settings; a second stream, when a step uses one, is the
- *              caller's (hp_cascade_step_overlap).
+ *              caller's (hp_cascade_step_overlap).  The one exception is the
+ *              per-GPU scratch array of hp_cascade_step_noalloc.
  * Errors.      Every argument is validated on the host before anything is
  *              enqueued; on an error nothing is enqueued and nothing is written.
  *              A failed launch returns HP_ERR_HIP (hp_last_hip_error() has the
@@ -88,7 +91,8 @@ typedef enum hp_status {
     HP_ERR_UNSUPPORTED = 3, /* valid, but outside the implemented domain */
     HP_ERR_WORKSPACE = 4,   /* workspace NULL or smaller than the size query's answer */
     HP_ERR_HIP = 5,         /* a HIP launch failed; see hp_last_hip_error() */
-    HP_ERR_CAPACITY = 6,    /* a pool, plan buffer or output array is too small */
+    HP_ERR_CAPACITY = 6,    /* a pool, plan buffer, output array or fixed scratch array
+                               is too small */
     HP_ERR_HOST = 7         /* host-side failure (out of host memory); nothing was enqueued */
 } hp_status;
 
@@ -266,6 +270,33 @@ hp_status hp_cascade_step_timed(const hp_query *query, const hp_prefix_tree *tre
                                 const hp_paged_kv *kv, float *o, float *lse, void *workspace,
                                 size_t workspace_bytes, void *stream, const hp_overlap *overlap,
                                 void *const *events, int32_t n_events);
+
+/*
+ * For callers that cannot allocate device memory (code under HIP graph
+ * capture, serving loops that must not call hipMalloc, harnesses that forbid
+ * it): hp_cascade_step with its workspace taken from a fixed array of
+ * HP_NOALLOC_SCRATCH_BYTES in the library's device image instead of a
+ * caller-allocated one.  The caller still passes every input and the outputs;
+ * the step allocates and frees nothing (host or device) and computes exactly
+ * what hp_cascade_step computes, on `stream` alone.
+ *   The array exists once per GPU, from when the library's code object is
+ * loaded on that GPU until the process ends.  Its device address is looked up
+ * on the first call for a GPU (the GPU `stream` belongs to; the current device
+ * for the null stream), with that device made current for the lookup and the
+ * caller's current device restored.  Every call on a GPU uses that GPU's one
+ * array: calls that may overlap on one GPU (several streams, several host
+ * threads, a graph replayed beside an eager call) race on it and must be
+ * ordered by the caller.  The array keeps what the last call left in it;
+ * no call depends on those contents.
+ *   Returns HP_ERR_CAPACITY, enqueuing nothing, when the step's workspace
+ * (hp_cascade_workspace_size reports at least that much) exceeds
+ * HP_NOALLOC_SCRATCH_BYTES; HP_ERR_UNSUPPORTED for a device ordinal of 64 or
+ * more; otherwise the errors of hp_cascade_step.
+ */
+#define HP_NOALLOC_SCRATCH_BYTES (64u * 1024u * 1024u)
+
+hp_status hp_cascade_step_noalloc(const hp_query *query, const hp_prefix_tree *tree,
+                                  const hp_paged_kv *kv, float *o, float *lse, void *stream);
 
 /* ------------------------------------------------------------------------
  * Shared-context requests: stream-id masked decode
