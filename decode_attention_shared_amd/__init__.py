@@ -30,7 +30,8 @@ from typing import List, Optional, Sequence, Tuple
 import torch
 
 _HERE = os.path.dirname(os.path.abspath(__file__))
-LIB_PATH = os.path.join(_HERE, "libhp_attn.so")
+# HP_ATTN_LIB selects another build of the same library (the host-sanitizer build)
+LIB_PATH = os.environ.get("HP_ATTN_LIB") or os.path.join(_HERE, "libhp_attn.so")
 
 HP_F32, HP_F16, HP_BF16 = 0, 1, 2
 HP_MAX_LEVELS = 4

@@ -39,8 +39,8 @@ def _hipcc() -> str:
     return "hipcc"
 
 
-def _compile(src: str, extra) -> str:
-    obj = os.path.join(BUILD_DIR, os.path.splitext(src)[0] + ".o")
+def _compile(src: str, extra, out_dir: str = BUILD_DIR) -> str:
+    obj = os.path.join(out_dir, os.path.splitext(src)[0] + ".o")
     cmd = [_hipcc(), "-x", "hip", *COMMON_FLAGS, *SOURCE_FLAGS.get(src, []), *extra, "-c",
            os.path.join(CSRC, src), "-o", obj]
     r = subprocess.run(cmd, capture_output=True, text=True)
@@ -54,19 +54,46 @@ def _compile(src: str, extra) -> str:
     return obj
 
 
-def build(extra_flags=(), jobs: int = 4) -> str:
-    """Compile every source and link libhp_attn.so.  Always recompiles."""
-    os.makedirs(BUILD_DIR, exist_ok=True)
+# Host-side sanitizer build (AddressSanitizer + UndefinedBehaviorSanitizer on the
+# host code of the C ABI: validation, planning, the prefix-tree manager).  Each
+# -fsanitize applies to the host pass only (-Xarch_host); the kernels are built
+# as usual.  The result is a separate library, loaded by setting HP_ATTN_LIB;
+# Python itself is not instrumented, so the runtime has to be preloaded:
+#   python -m decode_attention_shared_amd.build --sanitize
+#   HP_ATTN_LIB=$PWD/_build_san/libhp_attn_san.so \
+#   LD_PRELOAD=$(/opt/rocm/llvm/bin/clang -print-file-name=libclang_rt.asan-x86_64.so) \
+#   ASAN_OPTIONS=detect_leaks=0:halt_on_error=1 UBSAN_OPTIONS=halt_on_error=1:print_stacktrace=1 \
+#   python -m pytest tests -m "not gpu"
+SAN_BUILD_DIR = os.path.join(ROOT, "_build_san")
+SAN_LIB_PATH = os.path.join(SAN_BUILD_DIR, "libhp_attn_san.so")
+SAN_SOURCES = ("api.cpp", "tree.cpp", "pakv.cpp", "noalloc.hip")
+SAN_FLAGS = ["-Xarch_host", "-fsanitize=address", "-Xarch_host", "-fsanitize=undefined",
+             "-Xarch_host", "-fno-omit-frame-pointer", "-Xarch_host", "-fno-sanitize-recover=all",
+             "-g"]
+
+
+def build(extra_flags=(), jobs: int = 4, sanitize: bool = False) -> str:
+    """Compile every source and link libhp_attn.so (with sanitize=True, the host-side
+    sanitizer build instead).  Always recompiles."""
+    out_dir = SAN_BUILD_DIR if sanitize else BUILD_DIR
+    out_lib = SAN_LIB_PATH if sanitize else LIB_PATH
+    os.makedirs(out_dir, exist_ok=True)
+
+    def one(src):
+        flags = list(extra_flags) + (SAN_FLAGS if sanitize and src in SAN_SOURCES else [])
+        return _compile(src, flags, out_dir)
+
     with ThreadPoolExecutor(max_workers=jobs) as ex:
-        objs = list(ex.map(lambda s: _compile(s, list(extra_flags)), SOURCES))
-    tmp = LIB_PATH + f".tmp{os.getpid()}"
+        objs = list(ex.map(one, SOURCES))
+    tmp = out_lib + f".tmp{os.getpid()}"
+    # the sanitizer runtime is not linked in: it is preloaded into the process
     cmd = [_hipcc(), f"--offload-arch={ARCH}", "-shared", "-fPIC", "-o", tmp, *objs]
     r = subprocess.run(cmd, capture_output=True, text=True)
     if r.returncode != 0:
         raise RuntimeError("link failed:\n" + r.stdout + r.stderr)
-    os.replace(tmp, LIB_PATH)
-    return LIB_PATH
+    os.replace(tmp, out_lib)
+    return out_lib
 
 
 if __name__ == "__main__":
-    print(build())
+    print(build(sanitize="--sanitize" in sys.argv[1:]))

@@ -396,8 +396,14 @@ hp_status cascade_ws_bytes(const hp_query *q, const hp_prefix_tree *tree, const 
 
 extern "C" {
 
+static_assert(sizeof(hp_status) == sizeof(int32_t), "hp_status is a 32-bit int at the ABI");
+
 const char *hp_status_string(hp_status s) {
-    switch (s) {
+    // A C caller may pass any int; read it as one (a C++ load of an enum value
+    // outside its enumerators' range is undefined).
+    int32_t v;
+    std::memcpy(&v, &s, sizeof v);
+    switch (v) {
     case HP_OK: return "ok";
     case HP_ERR_NULL: return "a required pointer is NULL";
     case HP_ERR_INVALID_ARG: return "invalid argument (size, range, stride or alignment)";
