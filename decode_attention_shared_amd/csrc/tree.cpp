@@ -56,18 +56,33 @@ hp_status check_descs(const hp_query &g, const hp_chunk_desc *descs, int32_t n,
 // cost more than the shared read saves ("Shared Prefix KV Caching, in depth",
 // section "Trade-offs"; the boundary conditions listed in "Hydragen:
 // High-Throughput LLM Inference with Shared Prefixes", section "How Hydragen
-// Positions Itself": long shared prefixes and large batches).  The thresholds are the smallest run lengths at which the
-// batched step measured faster than the private one on MI355X (bf16, d = 128,
-// 32 query heads with 32 or 8 KV heads, 2..256 sequences, 64 private rows per
-// sequence; the run length doubled from 64 to 16384).  With one query head
-// per KV head the private pass keeps up longer, as each (sequence, KV head)
-// workgroup then streams its keys for a single query.
-bool share_decision(int G, int64_t tokens, int64_t nseq) {
+// Positions Itself": long shared prefixes and large batches).
+//
+// The thresholds are fitted to timings of both ways on MI355X: bf16 and fp16
+// (one table: they measure alike), and fp32, each at d = 128 and d = 64; 32
+// query heads with 32 KV heads (the column for one query head per KV head)
+// or 8 (every larger group); 2, 4, ..., 256 sequences, each with 64 private
+// rows; run lengths 64, 128, ..., 4096 and 16384.  Per (type, d, group) the
+// thresholds are the smallest that classify every measured point where one
+// way beat the other by at least 5 % and that never rise with the number of
+// sequences.  A sequence count between two measured ones takes the lower
+// one's threshold.  With one query head per KV head the private pass keeps
+// up longer (each (sequence, KV head) workgroup streams its keys for a
+// single query); fp32 keys favour it longer still (the batched pass then
+// runs on the fp32 matrix path).
+bool share_decision(int dtype, int d, int G, int64_t tokens, int64_t nseq) {
     if (nseq < 2 || tokens <= 0) return false;
-    int64_t t;
-    if (G == 1) t = nseq <= 8 ? 1024 : nseq <= 32 ? 512 : nseq <= 128 ? 256 : 128;
-    else t = nseq <= 64 ? 512 : nseq <= 128 ? 256 : 128;
-    return tokens >= t;
+    // [16-bit d128, 16-bit d64, fp32 d128, fp32 d64][G == 1, G > 1][2, 4, ..., 256 sequences]
+    static constexpr int32_t kThreshold[4][2][8] = {
+        {{2048, 1024, 512, 512, 256, 256, 128, 128}, {512, 512, 512, 512, 512, 512, 256, 128}},
+        {{1024, 1024, 1024, 512, 512, 256, 256, 128}, {1024, 1024, 1024, 1024, 1024, 1024, 256, 128}},
+        {{2048, 2048, 2048, 1024, 512, 256, 128, 128}, {1024, 1024, 1024, 1024, 1024, 1024, 512, 256}},
+        {{2048, 2048, 2048, 2048, 1024, 512, 256, 256}, {1024, 1024, 1024, 1024, 1024, 1024, 512, 256}},
+    };
+    const int kind = (dtype == HP_F32 ? 2 : 0) + (d == 64 ? 1 : 0);
+    int bucket = 0;  // largest measured count (2 << bucket) not above nseq
+    while (bucket < 7 && (int64_t(2) << (bucket + 1)) <= nseq) ++bucket;
+    return tokens >= kThreshold[kind][G > 1 ? 1 : 0][bucket];
 }
 
 // Everything of the plan but the image bytes; fills `plan` and `img`.
@@ -100,7 +115,7 @@ hp_status build(const hp_query &g, const hp_chunk_desc *descs, int32_t n, int32_
         if (share_min == 0) {
             int64_t tokens = 0;
             for (int32_t j = k; j < e; ++j) tokens += descs[j].count;
-            batch = share_decision(G, tokens, nseq);
+            batch = share_decision(g.dtype, g.d, G, tokens, nseq);
         } else {
             batch = nseq >= share_min;
         }
@@ -305,7 +320,7 @@ hp_status hp_share_decision(const hp_query *geom, int64_t tokens, int32_t nseq,
         hp_status st = check_geometry(geom, false);
         if (st != HP_OK) return st;
         if (tokens < 0 || nseq < 0 || nseq > geom->B) return HP_ERR_INVALID_ARG;
-        *batch = share_decision(geom->Hq / geom->Hkv, tokens, nseq) ? 1 : 0;
+        *batch = share_decision(geom->dtype, geom->d, geom->Hq / geom->Hkv, tokens, nseq) ? 1 : 0;
         return HP_OK;
     });
 }

@@ -424,8 +424,8 @@ hp_status hp_tree_plan_build(const hp_query *geom, const hp_chunk_desc *descs, i
  * sequences the extra launch and merge cost more than they save; Hydragen
  * page, section "How Hydragen Positions Itself", on its boundary conditions).  The rule is
  * a threshold on `tokens` that falls as `nseq` grows, fitted to timings of
- * both passes on MI355X; it depends on geom's Hq / Hkv (geom->q and
- * geom->scale are not used).  nseq in [0, geom->B], tokens >= 0.
+ * both passes on MI355X; it depends on geom's dtype, d and Hq / Hkv (geom->q
+ * and geom->scale are not used).  nseq in [0, geom->B], tokens >= 0.
  */
 hp_status hp_share_decision(const hp_query *geom, int64_t tokens, int32_t nseq, int32_t *batch);
 

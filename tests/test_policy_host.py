@@ -1,7 +1,7 @@
 """The batching policy (hp_share_decision) on the CPU: it picks the faster path at every
-decisive point of the measured crossover grid (profiles/share_sweep_bf16_d128.json, MI355X
-timings of both paths), it is monotone, and the chunk-tree planner's automatic mode
-(share_min = 0) batches exactly the runs it chooses."""
+decisive point of the measured crossover grids (profiles/share_sweep_<dtype>_d<d>.json, MI355X
+timings of both paths for bf16, fp16 and fp32 at d = 128 and 64), it is monotone, and the
+chunk-tree planner's automatic mode (share_min = 0) batches exactly the runs it chooses."""
 import ctypes
 import json
 import os
@@ -13,7 +13,8 @@ import decode_attention_shared_amd as hp
 from decode_attention_shared_amd import HP_BF16, Query
 
 ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
-SWEEP = os.path.join(ROOT, "profiles", "share_sweep_bf16_d128.json")
+SWEEPS = [("bf16", 128), ("f16", 128), ("bf16", 64), ("f16", 64), ("f32", 128), ("f32", 64)]
+TORCH = {"bf16": torch.bfloat16, "f16": torch.float16, "f32": torch.float32}
 
 
 @pytest.fixture(scope="module")
@@ -24,31 +25,37 @@ def L():
     return hp.lib()
 
 
-def test_policy_picks_the_measured_winner(L):
-    rows = json.load(open(SWEEP))["share_sweep"]
+@pytest.mark.parametrize("dtype,d", SWEEPS)
+def test_policy_picks_the_measured_winner(L, dtype, d):
+    data = json.load(open(os.path.join(ROOT, "profiles", f"share_sweep_{dtype}_d{d}.json")))
+    assert (data["dtype"], data["d"]) == (dtype, d)
     decisive = 0
-    for r in rows:
+    for r in data["share_sweep"]:
         ratio = r["private_us"] / r["batched_us"]
         if abs(ratio - 1.0) < 0.05:       # a tie within timing noise: either path is fine
             continue
         decisive += 1
-        got = hp.share_decision(r["Hq"], r["Hkv"], r["tokens"], r["nseq"])
+        got = hp.share_decision(r["Hq"], r["Hkv"], r["tokens"], r["nseq"], d=d, dtype=TORCH[dtype])
         assert got == (ratio > 1.0), r
-    assert decisive >= 100
+    assert decisive >= 90
 
 
+@pytest.mark.parametrize("dtype,d", SWEEPS)
 @pytest.mark.parametrize("Hq,Hkv", [(32, 32), (32, 8), (16, 8), (8, 1)])
-def test_policy_monotone(L, Hq, Hkv):
-    toks = [0, 1, 63, 64, 128, 255, 256, 511, 512, 1023, 1024, 4096, 1 << 20]
-    seqs = [0, 1, 2, 3, 8, 9, 32, 33, 64, 65, 128, 129, 256, 1000]
+def test_policy_monotone(L, Hq, Hkv, dtype, d):
+    toks = [0, 1, 63, 64, 128, 255, 256, 511, 512, 1023, 1024, 2047, 2048, 4096, 1 << 20]
+    seqs = [0, 1, 2, 3, 4, 7, 8, 9, 16, 31, 32, 33, 64, 65, 128, 129, 255, 256, 1000]
+
+    def dec(t, n):
+        return hp.share_decision(Hq, Hkv, t, n, d=d, dtype=TORCH[dtype])
     for n in seqs:
-        row = [hp.share_decision(Hq, Hkv, t, n) for t in toks]
+        row = [dec(t, n) for t in toks]
         assert row == sorted(row), (n, row)          # more shared tokens never un-batches
     for t in toks:
-        col = [hp.share_decision(Hq, Hkv, t, n) for n in seqs]
+        col = [dec(t, n) for n in seqs]
         assert col == sorted(col), (t, col)          # more sharers never un-batches
-    assert not any(hp.share_decision(Hq, Hkv, t, n) for t in toks for n in (0, 1))
-    assert all(hp.share_decision(Hq, Hkv, 1024, n) for n in seqs if n >= 2)
+    assert not any(dec(t, n) for t in toks for n in (0, 1))
+    assert all(dec(2048, n) for n in seqs if n >= 2)
 
 
 def test_policy_validation(L):

@@ -101,6 +101,16 @@ def codellama13b_mha(prefix: int = 16384) -> Config:
 CODELLAMA13B_SWEEP = (1024, 2048, 4096, 8192, 16384)
 
 
+def codellama13b_mha_share(ways: int = 8, prefix: int = 16384) -> Config:
+    """One GPU's share of the CodeLlama-13B shape when its 40 heads are split over
+    `ways` GPUs by KV head (40 / ways heads each, no exchange between them)."""
+    h = 40 // ways
+    return Config(f"codellama13b_mha_p{prefix}_share{ways}", B=256, Hq=h, Hkv=h, d=128,
+                  dtype="f16", levels=(((prefix, 0, 256),),), suffix_lo=1, suffix_hi=128,
+                  description=f"one {ways}-way head share of CodeLlama-13B: MHA {h}, fp16, "
+                              f"prefix {prefix}, B=256, suffix U[1,128]")
+
+
 def docqa_codellama7b() -> Config:
     return Config("docqa_codellama7b", B=256, Hq=32, Hkv=32, d=128, dtype="bf16",
                   levels=(((16384, 0, 256),),), suffix_lo=64, suffix_hi=512,
