@@ -81,7 +81,8 @@ class PrefixNode(ctypes.Structure):
 class PrefixTree(ctypes.Structure):
     _fields_ = [("num_levels", ctypes.c_int32),
                 ("nodes_per_level", ctypes.c_int32 * HP_MAX_LEVELS),
-                ("nodes", ctypes.POINTER(PrefixNode))]
+                ("nodes", ctypes.POINTER(PrefixNode)),
+                ("share_min", ctypes.c_int32)]
 
 
 class PagedKV(ctypes.Structure):
@@ -354,15 +355,20 @@ def make_node(k: torch.Tensor, v: torch.Tensor, seq_begin: int, seq_end: int) ->
                       seq_begin, seq_end)
 
 
-def make_tree(levels: Sequence[Sequence[Tuple[torch.Tensor, torch.Tensor, int, int]]]):
-    """levels: root first; each a list of (k, v, seq_begin, seq_end).  Returns (tree, keepalive)."""
+def make_tree(levels: Sequence[Sequence[Tuple[torch.Tensor, torch.Tensor, int, int]]],
+              share_min: int = 0):
+    """levels: root first; each a list of (k, v, seq_begin, seq_end).  share_min: which nodes
+    a cascade step batches (0: the batching policy per node; k >= 1: nodes over at least k
+    sequences; the others are read by each of their sequences in the suffix pass).
+    Returns (tree, keepalive)."""
     if len(levels) > HP_MAX_LEVELS:
         raise ValueError(f"at most {HP_MAX_LEVELS} levels")
     flat = [make_node(k, v, b0, b1) for level in levels for (k, v, b0, b1) in level]
     arr = (PrefixNode * max(1, len(flat)))(*flat)
     counts = (ctypes.c_int32 * HP_MAX_LEVELS)(*([len(l) for l in levels] +
                                                 [0] * (HP_MAX_LEVELS - len(levels))))
-    tree = PrefixTree(len(levels), counts, ctypes.cast(arr, ctypes.POINTER(PrefixNode)))
+    tree = PrefixTree(len(levels), counts, ctypes.cast(arr, ctypes.POINTER(PrefixNode)),
+                      int(share_min))
     return tree, arr
 
 
@@ -470,17 +476,18 @@ class CascadeCall:
     (hp_cascade_step); 1 (the default) or 2 passes the library a second stream and two
     events owned by this object (hp_cascade_step_overlap, mode 1: when the plan expects a
     gain, 2: whenever there is a prefix and a suffix).  ``concurrent`` says whether the
-    passes run side by side."""
+    passes run side by side.  share_min: which tree nodes the prefix pass batches (see
+    make_tree; 0, the default, is the library's batching policy)."""
 
     def __init__(self, q: torch.Tensor, levels, k_pool=None, v_pool=None, block_table=None,
                  seq_lens=None, scale: Optional[float] = None, out=None, lse=None,
-                 overlap: int = 1):
+                 overlap: int = 1, share_min: int = 0):
         L = lib()
         self._L = L
         Hkv = (levels[0][0][0].shape[1] if levels and levels[0] else k_pool.shape[2])
         self.q = q
         self.query = make_query(q, Hkv, scale)
-        self.tree, self._keep = make_tree(levels) if levels else (None, None)
+        self.tree, self._keep = make_tree(levels, share_min) if levels else (None, None)
         self.kv = make_paged(k_pool, v_pool, block_table, seq_lens) if k_pool is not None else None
         self.out, self.lse = _out(q, out, lse, zero=False)
         self._tree_p = ctypes.byref(self.tree) if self.tree is not None else None
@@ -530,18 +537,19 @@ class CascadeCall:
 
 def cascade_step(q: torch.Tensor, levels, k_pool=None, v_pool=None, block_table=None,
                  seq_lens=None, scale: Optional[float] = None, out=None, lse=None, stream=None,
-                 overlap: int = 1):
+                 overlap: int = 1, share_min: int = 0):
     """levels: root first, each a list of (k, v, seq_begin, seq_end) device tensors/ints;
-    the pools, table and lengths describe the paged suffixes (or None for prefix only)."""
+    the pools, table and lengths describe the paged suffixes (or None for prefix only).
+    share_min: see make_tree."""
     with _on(stream, q.device):
         call = CascadeCall(q, levels, k_pool, v_pool, block_table, seq_lens, scale, out, lse,
-                           overlap)
+                           overlap, share_min)
         return call(stream)
 
 
 def cascade_step_noalloc(q: torch.Tensor, levels, k_pool=None, v_pool=None, block_table=None,
                          seq_lens=None, scale: Optional[float] = None, out=None, lse=None,
-                         stream=None):
+                         stream=None, share_min: int = 0):
     """hp_cascade_step_noalloc: cascade_step on one stream with the workspace taken from
     the library's fixed per-GPU scratch array (at most HP_NOALLOC_SCRATCH_BYTES).  The
     library allocates nothing; pass ``out`` (and ``lse``) to allocate nothing here either.
@@ -549,7 +557,7 @@ def cascade_step_noalloc(q: torch.Tensor, levels, k_pool=None, v_pool=None, bloc
     L = lib()
     Hkv = (levels[0][0][0].shape[1] if levels and levels[0] else k_pool.shape[2])
     query = make_query(q, Hkv, scale)
-    tree, keep = make_tree(levels) if levels else (None, None)
+    tree, keep = make_tree(levels, share_min) if levels else (None, None)
     kv = make_paged(k_pool, v_pool, block_table, seq_lens) if k_pool is not None else None
     with _on(stream, q.device):
         out, lse = _out(q, out, lse, zero=False)

@@ -206,13 +206,13 @@ int32_t stage_floats(const MergeSrc *src, int nsrc, int G, int d) {
 // Waves per (sequence, KV head) workgroup of the suffix pass.  More waves
 // shorten each sequence's walk but leave more of them idle on short
 // sequences; two waves measured best for suffixes of up to 16 blocks.
-int suffix_waves(const hp_query &q, const hp_paged_kv &kv) {
+int suffix_waves(const hp_query &q, int64_t max_blocks) {
     const int64_t units = (int64_t)q.B * q.Hkv;
-    if (kv.max_blocks <= 2) return 1;
+    if (max_blocks <= 2) return 1;
     // Few (sequence, KV head) units: more waves per unit keep enough blocks in
     // flight (measured: 512 units of up to 16 blocks run 30% faster on four).
-    if (units <= 1024 && kv.max_blocks > 4) return 4;
-    return kv.max_blocks <= 16 ? 2 : 4;
+    if (units <= 1024 && max_blocks > 4) return 4;
+    return max_blocks <= 16 ? 2 : 4;
 }
 
 PrefixArgs base_prefix_args(const hp_query &q) {
@@ -268,24 +268,26 @@ hp_status run_level(const hp_query &q, const hp_prefix_node *nodes, const LevelP
     return HP_OK;
 }
 
-SuffixArgs suffix_args(const hp_query &q, const hp_paged_kv &kv, RowDest dest) {
+// kv may be NULL: no paged suffix (only private prefix nodes and partials).
+SuffixArgs suffix_args(const hp_query &q, const hp_paged_kv *kv, RowDest dest) {
     SuffixArgs a;
     std::memset(&a, 0, sizeof a);
     a.q = q.q;
-    a.k_pool = kv.k_pool;
-    a.v_pool = kv.v_pool;
-    a.table = kv.block_table;
-    a.lens = kv.seq_lens;
     a.B = q.B;
     a.Hq = q.Hq;
     a.Hkv = q.Hkv;
-    a.max_blocks = kv.max_blocks;
-    a.num_blocks = kv.num_blocks;
-    a.has_suffix = 1;
     a.scale_log2 = (float)((double)q.scale * 1.4426950408889634);
     a.dest = dest;
+    if (!kv) return a;
+    a.k_pool = kv->k_pool;
+    a.v_pool = kv->v_pool;
+    a.table = kv->block_table;
+    a.lens = kv->seq_lens;
+    a.max_blocks = kv->max_blocks;
+    a.num_blocks = kv->num_blocks;
+    a.has_suffix = 1;
     // K/V footprint: the pool, or what the block tables can reach if less.
-    const int64_t blocks = std::min<int64_t>(kv.num_blocks, (int64_t)q.B * kv.max_blocks);
+    const int64_t blocks = std::min<int64_t>(kv->num_blocks, (int64_t)q.B * kv->max_blocks);
     const int64_t kv_bytes = blocks * kBlock * q.Hkv * q.d * esize(q.dtype) * 2;
     a.stream_kv = kv_bytes >= kLlcBytes ? 1 : 0;
     return a;
@@ -293,7 +295,7 @@ SuffixArgs suffix_args(const hp_query &q, const hp_paged_kv &kv, RowDest dest) {
 
 // Plan of a whole cascade step (shared by the size query and the run).
 struct CascadePlan {
-    int total_nodes = 0;
+    int total_nodes = 0;  // nodes of the prefix pass (batched)
     int num_levels = 0;  // launch groups: tree levels, or one group holding every node
     LevelPlan levels[HP_MAX_LEVELS];
     bool has_suffix = false;
@@ -301,7 +303,39 @@ struct CascadePlan {
     size_t node_off[HP_MAX_NODES];
     size_t suf_off = 0;  // concurrent plan: the suffix pass's (O, LSE) rows
     size_t bytes = 0;
+    // The tree as the prefix pass sees it (the batched nodes, level-major) and
+    // the nodes that each of their sequences reads in its suffix pass instead.
+    int tree_levels = 0;
+    int32_t batched_per_level[HP_MAX_LEVELS] = {};
+    hp_prefix_node batched[HP_MAX_NODES];
+    int nseg = 0;
+    PrivSeg seg[HP_MAX_NODES];
+    int64_t seg_blocks = 0;  // blocks of private nodes a sequence reads, at most
+    hp_prefix_tree view() const {
+        hp_prefix_tree t;
+        std::memset(&t, 0, sizeof t);
+        t.num_levels = tree_levels;
+        for (int l = 0; l < tree_levels; ++l) t.nodes_per_level[l] = batched_per_level[l];
+        t.nodes = batched;
+        t.share_min = 1;
+        return t;
+    }
+    bool suffix_pass() const { return has_suffix || nseg > 0; }
 };
+
+// The suffix pass's arguments for the plan: the paged suffix (if any) and
+// the private prefix nodes.
+SuffixArgs plan_suffix_args(const hp_query &q, const hp_paged_kv *kv, const CascadePlan &cp,
+                            RowDest dest) {
+    SuffixArgs a = suffix_args(q, kv, dest);
+    a.nseg = cp.nseg;
+    for (int i = 0; i < cp.nseg; ++i) a.seg[i] = cp.seg[i];
+    return a;
+}
+
+int plan_suffix_waves(const hp_query &q, const hp_paged_kv *kv, const CascadePlan &cp) {
+    return suffix_waves(q, (kv ? kv->max_blocks : 0) + cp.seg_blocks);
+}
 
 // Lay out the prefix launches of the tree for `cus` compute units; returns
 // the workspace bytes of their partials.
@@ -346,24 +380,54 @@ size_t plan_prefix(const hp_query *q, const hp_prefix_tree *tree, CascadePlan &c
 // the plan expects a gain; 2 side by side whenever there is a prefix and a
 // suffix.
 hp_status plan_cascade(const hp_query *q, const hp_prefix_tree *tree, const hp_paged_kv *kv,
-                       int mode, CascadePlan &cp) {
+                       int mode, CascadePlan &cp, bool batch_all = false) {
     if (mode < 0 || mode > 2) return HP_ERR_INVALID_ARG;
     hp_status st = check_query(q);
     if (st != HP_OK) return st;
-    st = check_tree(q, tree, &cp.total_nodes);
+    int total = 0;
+    st = check_tree(q, tree, &total);
     if (st != HP_OK) return st;
+    if (tree && tree->share_min < 0) return HP_ERR_INVALID_ARG;
     if (kv) {
         st = check_kv(q, kv);
         if (st != HP_OK) return st;
     }
     cp.has_suffix = kv != nullptr;
-    cp.bytes = plan_prefix(q, tree, cp, kCUs);
+    // Which nodes the prefix pass batches (the rest are read by each of their
+    // sequences in the suffix pass): share_min 0 asks the batching policy per
+    // node, k >= 1 batches the nodes over at least k sequences.
+    if (tree) {
+        const int G = q->Hq / q->Hkv;
+        cp.tree_levels = tree->num_levels;
+        for (int l = 0, idx = 0; l < tree->num_levels; ++l) {
+            int64_t level_blocks = 0;
+            for (int i = 0; i < tree->nodes_per_level[l]; ++i, ++idx) {
+                const hp_prefix_node &n = tree->nodes[idx];
+                const int64_t nseq = (int64_t)n.seq_end - n.seq_begin;
+                const bool batch = batch_all ||
+                    (tree->share_min == 0 ? share_decision(q->dtype, q->d, G, n.len, nseq)
+                                          : nseq >= tree->share_min);
+                if (batch) {
+                    cp.batched[cp.total_nodes++] = n;
+                    ++cp.batched_per_level[l];
+                } else if (n.len > 0 && nseq > 0) {
+                    cp.seg[cp.nseg++] = PrivSeg{n.k, n.v, n.stride_tok, n.stride_head,
+                                                n.len, n.seq_begin, n.seq_end, 0};
+                    level_blocks = std::max<int64_t>(level_blocks, cdiv(n.len, kBlock));
+                }
+            }
+            cp.seg_blocks += level_blocks;
+        }
+    }
+    (void)total;
+    const hp_prefix_tree bt = cp.view();
+    cp.bytes = plan_prefix(q, tree ? &bt : nullptr, cp, kCUs);
     // The suffix pass beside the prefix pass: the prefix is planned for
     // kConcCUs compute units, the suffix writes its own (O, LSE) rows and one
     // merge combines them with the prefix partials.
     if (cp.has_suffix && cp.total_nodes > 0 && q->B > 0 && mode != 0) {
         CascadePlan alt = cp;
-        const size_t pbytes = plan_prefix(q, tree, alt, kConcCUs);
+        const size_t pbytes = plan_prefix(q, tree ? &bt : nullptr, alt, kConcCUs);
         bool pays = (int64_t)q->B * q->Hkv >= kConcMinUnits;
         for (int l = 0; l < alt.num_levels && pays; ++l)
             for (int i = 0; i < alt.levels[l].count; ++i)
@@ -505,9 +569,9 @@ hp_status hp_suffix_decode(const hp_query *q, const hp_paged_kv *kv, float *o, f
         st = check_out(o, lse);
         if (st != HP_OK) return st;
         if (q->B == 0) return HP_OK;
-        const SuffixArgs a = suffix_args(*q, *kv, RowDest{o, lse, 0, 0, 0});
-        hipError_t e = launch_suffix(a, q->dtype, q->d, q->Hq / q->Hkv, suffix_waves(*q, *kv),
-                                     (hipStream_t)stream);
+        const SuffixArgs a = suffix_args(*q, kv, RowDest{o, lse, 0, 0, 0});
+        hipError_t e = launch_suffix(a, q->dtype, q->d, q->Hq / q->Hkv,
+                                     suffix_waves(*q, kv->max_blocks), (hipStream_t)stream);
         return e == hipSuccess ? HP_OK : fail_hip(e);
     });
 }
@@ -582,8 +646,8 @@ hp_status record(void *const *events, int i, hipStream_t s) {
     return e == hipSuccess ? HP_OK : fail_hip(e);
 }
 
-hp_status run_prefix_levels(const hp_query *q, const hp_prefix_tree *tree, const CascadePlan &cp,
-                            char *base, MergeArgs &m, hipStream_t s);
+hp_status run_prefix_levels(const hp_query *q, const CascadePlan &cp, char *base, MergeArgs &m,
+                            hipStream_t s);
 
 // Suffix pass beside the prefix pass: fork the caller's side stream from s,
 // prefix launches on s, the suffix pass (its own (O, LSE) rows, no merge) on
@@ -604,11 +668,11 @@ hp_status cascade_concurrent(const hp_query *q, const hp_prefix_tree *tree,
     if (st != HP_OK) return st;
     MergeArgs m;
     std::memset(&m, 0, sizeof m);
-    if ((st = run_prefix_levels(q, tree, cp, base, m, s)) != HP_OK) return st;
+    if ((st = run_prefix_levels(q, cp, base, m, s)) != HP_OK) return st;
     if ((st = record(events, 1, s)) != HP_OK) return st;
-    SuffixArgs a = suffix_args(*q, *kv, RowDest{so, sl, 0, 0, 0});
+    SuffixArgs a = plan_suffix_args(*q, kv, cp, RowDest{so, sl, 0, 0, 0});
     if ((st = record(events, 4, ss)) != HP_OK) return st;
-    e = launch_suffix(a, q->dtype, q->d, q->Hq / q->Hkv, suffix_waves(*q, *kv), ss);
+    e = launch_suffix(a, q->dtype, q->d, q->Hq / q->Hkv, plan_suffix_waves(*q, kv, cp), ss);
     if (e != hipSuccess) return fail_hip(e);
     if ((st = record(events, 2, ss)) != HP_OK) return st;
     if ((e = hipEventRecord(join, ss)) != hipSuccess) return fail_hip(e);
@@ -625,8 +689,10 @@ hp_status cascade_concurrent(const hp_query *q, const hp_prefix_tree *tree,
 
 // Prefix pass of every tree level (root first), results into the cascade
 // plan's workspace slots; m receives one merge source per node.
-hp_status run_prefix_levels(const hp_query *q, const hp_prefix_tree *tree, const CascadePlan &cp,
-                            char *base, MergeArgs &m, hipStream_t s) {
+hp_status run_prefix_levels(const hp_query *q, const CascadePlan &cp, char *base, MergeArgs &m,
+                            hipStream_t s) {
+    const hp_prefix_tree view = cp.view();
+    const hp_prefix_tree *tree = &view;
     for (int l = 0; l < cp.num_levels; ++l) {
         const LevelPlan &lp = cp.levels[l];
         RowDest dests[HP_MAX_NODES];
@@ -667,16 +733,18 @@ hp_status cascade_impl(const hp_query *q, const hp_prefix_tree *tree, const hp_p
 
     MergeArgs m;
     std::memset(&m, 0, sizeof m);
-    if ((st = run_prefix_levels(q, tree, cp, base, m, s)) != HP_OK) return st;
+    if ((st = run_prefix_levels(q, cp, base, m, s)) != HP_OK) return st;
     if ((st = record(events, 1, s)) != HP_OK) return st;
-    if (cp.has_suffix) {
-        // Suffix pass with the merge of every level's partials fused in.
-        SuffixArgs a = suffix_args(*q, *kv, RowDest{o, lse, 0, 0, 0});
+    if (cp.suffix_pass()) {
+        // Suffix pass (paged suffix and private prefix nodes) with the merge of
+        // every level's partials fused in.
+        SuffixArgs a = plan_suffix_args(*q, kv, cp, RowDest{o, lse, 0, 0, 0});
         a.nsrc = m.nsrc;
         for (int i = 0; i < m.nsrc; ++i) a.src[i] = m.src[i];
         a.stage_floats = stage_floats(m.src, m.nsrc, q->Hq / q->Hkv, q->d);
         if ((st = record(events, 4, s)) != HP_OK) return st;
-        hipError_t e = launch_suffix(a, q->dtype, q->d, q->Hq / q->Hkv, suffix_waves(*q, *kv), s);
+        hipError_t e = launch_suffix(a, q->dtype, q->d, q->Hq / q->Hkv,
+                                     plan_suffix_waves(*q, kv, cp), s);
         if (e != hipSuccess) return fail_hip(e);
         if ((st = record(events, 2, s)) != HP_OK) return st;
     } else {
@@ -720,7 +788,7 @@ struct StreamPlan {
 
 hp_status plan_stream(const hp_query *q, const hp_prefix_tree *doc, const hp_stream_rows *r,
                       StreamPlan &sp) {
-    hp_status st = plan_cascade(q, doc, nullptr, 0, sp.cp);
+    hp_status st = plan_cascade(q, doc, nullptr, 0, sp.cp, /*batch_all=*/true);
     if (st != HP_OK) return st;
     if ((st = check_stream_rows(q, r)) != HP_OK) return st;
     sp.len_off = round_up(sp.cp.bytes, kWsAlign);
@@ -784,7 +852,7 @@ hp_status hp_stream_decode(const hp_query *q, const hp_prefix_tree *doc,
 
         MergeArgs m;
         std::memset(&m, 0, sizeof m);
-        if ((st = run_prefix_levels(q, doc, sp.cp, base, m, s)) != HP_OK) return st;
+        if ((st = run_prefix_levels(q, sp.cp, base, m, s)) != HP_OK) return st;
 
         StreamSelectArgs sel;
         std::memset(&sel, 0, sizeof sel);

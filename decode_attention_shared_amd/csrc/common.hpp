@@ -136,6 +136,16 @@ struct MergeSrc {
     int64_t b0, b1;
 };
 
+// A prefix node that each of its sequences reads in its own suffix pass (the
+// batching policy found the node too short, or shared by too few sequences,
+// for the batched pass to pay).  Key of token t, KV head g at
+// k + t*stride_tok + g*stride_head (elements); sequences [b0, b1).
+struct PrivSeg {
+    const void *k, *v;
+    int64_t stride_tok, stride_head;
+    int32_t len, b0, b1, pad;
+};
+
 // Suffix pass with the final merge fused in: every row (b, h) merges its
 // suffix attention with the partials of the sources covering sequence b.
 struct SuffixArgs {
@@ -160,6 +170,10 @@ struct SuffixArgs {
     int32_t stream_kv;        // paged and token-table modes: K/V loads marked non-temporal
                               // (footprint beyond the last-level cache, so nothing of it would be
                               // found there next step)
+    // Paged mode: prefix nodes read privately, before the paged suffix.  At
+    // most one per tree level covers a sequence (a level's ranges are disjoint).
+    int32_t nseg;
+    PrivSeg seg[HP_MAX_NODES];
 };
 
 // Stream selection of a shared-context step: query b (request q_req[b],

@@ -105,6 +105,10 @@ constexpr int kConcCUs = 160;
 constexpr int kConcMinTiles = 8;
 constexpr int64_t kConcMinUnits = 4096;
 
+// Batching policy (hp_share_decision): whether `tokens` keys shared by `nseq`
+// sequences are better read once for all of them than by each sequence.
+bool share_decision(int dtype, int d, int G, int64_t tokens, int64_t nseq);
+
 // The cascade step on one stream (hp_cascade_step), for entry points that
 // supply the workspace themselves: cascade_serial_plan validates every
 // argument of the step (outputs included) and gives the workspace bytes.

@@ -172,7 +172,35 @@ __global__ __launch_bounds__(64 * NWS) void suffix_kernel(SuffixArgs a) {
         len = a.lens[b];
         bad = len < 0 || len > a.max_blocks * kBlock;
     }
-    const int nblk = bad ? 0 : (len + kBlock - 1) / kBlock;
+    // Paged mode: the prefix nodes this sequence reads privately come first,
+    // as blocks [sb[i], sb[i + 1]) of node sid[i] (at most one per level).
+    // (Indexed by constants only, so the arrays stay in registers.)
+    int sid[HP_MAX_LEVELS], sb[HP_MAX_LEVELS + 1];
+#pragma unroll
+    for (int j = 0; j < HP_MAX_LEVELS; ++j) sid[j] = 0;
+#pragma unroll
+    for (int j = 0; j <= HP_MAX_LEVELS; ++j) sb[j] = 0;
+    int nps = 0;
+    if constexpr (kMode == kBlocks) {
+#pragma unroll 1
+        for (int si = 0; si < a.nseg; ++si) {
+            const PrivSeg &sg = a.seg[si];
+            if (b < sg.b0 || b >= sg.b1 || sg.len <= 0) continue;
+            const int nb = (sg.len + kBlock - 1) / kBlock;
+#pragma unroll
+            for (int j = 0; j < HP_MAX_LEVELS; ++j)
+                if (j == nps) {
+                    sid[j] = si;
+                    sb[j + 1] = sb[j] + nb;
+                }
+            nps = min(nps + 1, HP_MAX_LEVELS);
+        }
+    }
+    int nsb = 0;  // blocks over the private prefix nodes
+#pragma unroll
+    for (int j = 1; j <= HP_MAX_LEVELS; ++j)
+        if (j == nps) nsb = sb[j];
+    const int nblk = bad ? 0 : nsb + (len + kBlock - 1) / kBlock;
 
     // The prefix partials this row merges (splits of the by-value sources
     // covering sequence b) are copied into LDS by DMA right away, so their
@@ -264,7 +292,8 @@ __global__ __launch_bounds__(64 * NWS) void suffix_kernel(SuffixArgs a) {
                 r.v[p] = t < row_cap ? trow[t] : 0;
             }
         } else {
-            r.v[0] = blk < row_cap ? trow[blk] : 0;
+            const int pb = blk - nsb;  // block of the paged suffix
+            r.v[0] = pb >= 0 && pb < row_cap ? trow[pb] : 0;
         }
         return r;
     };
@@ -292,11 +321,36 @@ __global__ __launch_bounds__(64 * NWS) void suffix_kernel(SuffixArgs a) {
                 kr[p] = ok ? load16(kp + off) : u32x4{0, 0, 0, 0};
                 vr[p] = ok ? load16(vp + off) : u32x4{0, 0, 0, 0};
             }
+        } else if (blk < nsb) {
+            // a block of a private prefix node: contiguous rows, plain loads
+            // (the node's other sequences read the same rows in this step)
+            int si = sid[0], s0 = 0;
+#pragma unroll
+            for (int j = 1; j < HP_MAX_LEVELS; ++j)
+                if (j < nps && blk >= sb[j]) {
+                    si = sid[j];
+                    s0 = sb[j];
+                }
+            const PrivSeg &sg = a.seg[si];
+            const int t0 = (blk - s0) * kBlock;
+            valid = min(kBlock, sg.len - t0);
+            const int64_t base = ((int64_t)t0 * sg.stride_tok + (int64_t)g * sg.stride_head + d0) *
+                                 E::kSize;
+            const char *ks = (const char *)sg.k + base;
+            const char *vs = (const char *)sg.v + base;
+#pragma unroll
+            for (int p = 0; p < kPasses; ++p) {
+                const int t = p * kTpp + tg;
+                const bool ok = t < valid;
+                const int64_t off = (int64_t)t * sg.stride_tok * E::kSize;
+                kr[p] = ok ? *(const u32x4 *)(ks + off) : u32x4{0, 0, 0, 0};
+                vr[p] = ok ? *(const u32x4 *)(vs + off) : u32x4{0, 0, 0, 0};
+            }
         } else {
             const int id = ref.v[0];
             const bool id_ok = id >= 0 && id < a.num_blocks;
             bad |= !id_ok;
-            valid = id_ok ? min(kBlock, len - blk * kBlock) : 0;
+            valid = id_ok ? min(kBlock, len - (blk - nsb) * kBlock) : 0;
             const int64_t base = ((int64_t)(id_ok ? id : 0) * kBlock * a.Hkv + g) * D * E::kSize +
                                  d0 * E::kSize;
 #pragma unroll

@@ -25,29 +25,8 @@
 using namespace hp;
 using namespace hp::host;
 
-namespace {
-
-struct Image {
-    std::vector<TreeSeg> segs;
-    std::vector<TreePiece> pieces;
-    std::vector<int32_t> wgseg;
-    std::vector<int32_t> seq_tok, tok_rows, seq_src, shared;
-    std::vector<TreeSrc> srcs;
-};
-
-hp_status check_descs(const hp_query &g, const hp_chunk_desc *descs, int32_t n,
-                      int64_t pool_rows) {
-    if (n < 0 || pool_rows < 0 || pool_rows > INT32_MAX) return HP_ERR_INVALID_ARG;
-    if (n > 0 && !descs) return HP_ERR_NULL;
-    for (int32_t k = 0; k < n; ++k) {
-        const hp_chunk_desc &c = descs[k];
-        if (c.count < 1 || c.count > HP_CHUNK) return HP_ERR_INVALID_ARG;
-        if (c.row < 0 || (int64_t)c.row + c.count > pool_rows) return HP_ERR_INVALID_ARG;
-        if (c.seq_begin < 0 || c.seq_begin >= c.seq_end || c.seq_end > g.B)
-            return HP_ERR_INVALID_ARG;
-    }
-    return HP_OK;
-}
+namespace hp {
+namespace host {
 
 // Batching policy: read a run of `tokens` shared keys once for its `nseq`
 // sequences (the chunk-first phase, plus the partial merge) only when that is
@@ -83,6 +62,33 @@ bool share_decision(int dtype, int d, int G, int64_t tokens, int64_t nseq) {
     int bucket = 0;  // largest measured count (2 << bucket) not above nseq
     while (bucket < 7 && (int64_t(2) << (bucket + 1)) <= nseq) ++bucket;
     return tokens >= kThreshold[kind][G > 1 ? 1 : 0][bucket];
+}
+
+}  // namespace host
+}  // namespace hp
+
+namespace {
+
+struct Image {
+    std::vector<TreeSeg> segs;
+    std::vector<TreePiece> pieces;
+    std::vector<int32_t> wgseg;
+    std::vector<int32_t> seq_tok, tok_rows, seq_src, shared;
+    std::vector<TreeSrc> srcs;
+};
+
+hp_status check_descs(const hp_query &g, const hp_chunk_desc *descs, int32_t n,
+                      int64_t pool_rows) {
+    if (n < 0 || pool_rows < 0 || pool_rows > INT32_MAX) return HP_ERR_INVALID_ARG;
+    if (n > 0 && !descs) return HP_ERR_NULL;
+    for (int32_t k = 0; k < n; ++k) {
+        const hp_chunk_desc &c = descs[k];
+        if (c.count < 1 || c.count > HP_CHUNK) return HP_ERR_INVALID_ARG;
+        if (c.row < 0 || (int64_t)c.row + c.count > pool_rows) return HP_ERR_INVALID_ARG;
+        if (c.seq_begin < 0 || c.seq_begin >= c.seq_end || c.seq_end > g.B)
+            return HP_ERR_INVALID_ARG;
+    }
+    return HP_OK;
 }
 
 // Everything of the plan but the image bytes; fills `plan` and `img`.

@@ -126,11 +126,25 @@ typedef struct hp_prefix_node {
  * hold narrower shared ranges.  Within a level, nodes are sorted by seq_begin
  * and their ranges are disjoint; a sequence may have no node at a level.
  * `nodes` is a host array, level-major, sum(nodes_per_level) entries.
+ *
+ * share_min chooses which nodes a cascade step reads once for all their
+ * sequences (the batched prefix pass) and which each of their sequences reads
+ * in its own suffix pass, as keys before its paged suffix.  Under a few
+ * hundred shared tokens, or with few sharing sequences, the batched pass and
+ * its merge cost more than they save ("Shared Prefix KV Caching, in depth",
+ * section "Trade-offs"):
+ *   0      per node, by hp_share_decision() on its length and number of
+ *          sequences (the automatic policy);
+ *   k >= 1 batch the nodes over at least k sequences (1: every node).
+ * Negative values are HP_ERR_INVALID_ARG.  The result is the same attention
+ * either way (up to rounding); hp_stream_decode batches every node of its
+ * documents whatever the value.
  */
 typedef struct hp_prefix_tree {
     int32_t num_levels;
     int32_t nodes_per_level[HP_MAX_LEVELS];
     const hp_prefix_node *nodes;
+    int32_t share_min;
 } hp_prefix_tree;
 
 /*
@@ -191,11 +205,13 @@ hp_status hp_lse_merge(int32_t n, const float *const *o_in, const float *const *
 /*
  * One whole decode step: every row (b, h) attends the keys of every tree node
  * covering b (root level first) followed by its paged suffix.  Runs the prefix
- * pass for every node, then the suffix pass with one n-way merge fused into
- * its epilogue (Hydragen page, "Hierarchical Sharing": decomposition at every
- * tree vertex, recombined with the stored LSE of each level), all on
- * `stream`.  tree may be NULL (suffix only); kv may be NULL (prefix only).
- * lse may be NULL.  Workspace: hp_cascade_workspace_size(), which covers
+ * pass for every batched node (tree->share_min), then the suffix pass --
+ * each sequence's private nodes and paged suffix -- with one n-way merge
+ * fused into its epilogue (Hydragen page, "Hierarchical Sharing":
+ * decomposition at every tree vertex, recombined with the stored LSE of each
+ * level), all on `stream`.  tree may be NULL (suffix only); kv may be NULL
+ * (prefix only).  lse may be NULL.  Workspace: hp_cascade_workspace_size()
+ * for the same tree (its share_min included), which covers
  * hp_cascade_step_overlap() too.
  */
 hp_status hp_cascade_workspace_size(const hp_query *query, const hp_prefix_tree *tree,

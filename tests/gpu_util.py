@@ -38,12 +38,14 @@ def dev_step(step, dev=DEV):
                 seq_lens=step.seq_lens.to(dev))
 
 
-def cascade(ds, scale, levels=None, paged=True):
+def cascade(ds, scale, levels=None, paged=True, share_min=0):
+    """share_min 0: the library's batching policy picks the nodes the prefix pass reads
+    (the rest are read by each sequence in the suffix pass); 1: every node batched."""
     lv = ds["levels"] if levels is None else levels
     if paged:
         return hp.cascade_step(ds["q"], lv, ds["k_pool"], ds["v_pool"], ds["block_table"],
-                               ds["seq_lens"], scale)
-    return hp.cascade_step(ds["q"], lv, scale=scale)
+                               ds["seq_lens"], scale, share_min=share_min)
+    return hp.cascade_step(ds["q"], lv, scale=scale, share_min=share_min)
 
 
 def compare(got_o, got_l, ref_o, ref_l, dtype: str, what: str, rows=None):

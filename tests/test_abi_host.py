@@ -171,12 +171,12 @@ def test_merge_validation(L):
     assert L.hp_lse_merge(1, None, None, out, lse, 10, 128, None) == NULL
 
 
-def tree_status(L, q, levels, kv=None, o=FAKE, num_levels=None):
+def tree_status(L, q, levels, kv=None, o=FAKE, num_levels=None, share_min=1):
     flat = [n for lvl in levels for n in lvl]
     arr = (PrefixNode * max(1, len(flat)))(*flat)
     counts = (ctypes.c_int32 * 4)(*([len(l) for l in levels[:4]] + [0] * (4 - len(levels[:4]))))
     tree = PrefixTree(len(levels) if num_levels is None else num_levels, counts,
-                      ctypes.cast(arr, ctypes.POINTER(PrefixNode)))
+                      ctypes.cast(arr, ctypes.POINTER(PrefixNode)), share_min)
     sz = ctypes.c_size_t()
     st = L.hp_cascade_workspace_size(ctypes.byref(q), ctypes.byref(tree),
                                      ctypes.byref(kv) if kv else None, ctypes.byref(sz))
@@ -202,6 +202,43 @@ def test_tree_validation(L):
     assert tree_status(L, q, wide)[0] in (UNSUPPORTED, INVALID)
     bad_node = [[node_(64, 0, 9)]]
     assert tree_status(L, q, bad_node)[0] == INVALID
+
+
+def tree_ws(L, q, levels, kv=None, share_min=1):
+    """hp_cascade_workspace_size only (a step with nothing to batch would enqueue)."""
+    flat = [n for lvl in levels for n in lvl]
+    arr = (PrefixNode * max(1, len(flat)))(*flat)
+    counts = (ctypes.c_int32 * 4)(*([len(l) for l in levels] + [0] * (4 - len(levels))))
+    tree = PrefixTree(len(levels), counts, ctypes.cast(arr, ctypes.POINTER(PrefixNode)),
+                      share_min)
+    sz = ctypes.c_size_t(7)
+    st = L.hp_cascade_workspace_size(ctypes.byref(q), ctypes.byref(tree),
+                                     ctypes.byref(kv) if kv else None, ctypes.byref(sz))
+    return st, sz.value
+
+
+def test_tree_share_min(L):
+    """share_min picks the nodes the prefix pass batches; the others need no partials
+    (each of their sequences reads them in the suffix pass)."""
+    q = q_(B=64, Hq=32, Hkv=8)
+    levels = [[node_(4096, 0, 64)], [node_(300, 0, 32), node_(300, 32, 64)]]
+    sizes = {}
+    for smin in (0, 1, 2, 33, 64, 65):
+        st, sz = tree_ws(L, q, levels, kv_(), share_min=smin)
+        assert st == OK, smin
+        sizes[smin] = sz
+    # automatic: the 4096-token root over 64 sequences is batched, the 300-token
+    # group nodes (32 sequences, 4 query heads per KV head) are read privately
+    assert hp.share_decision(32, 8, 4096, 64) and not hp.share_decision(32, 8, 300, 32)
+    assert sizes[1] == sizes[2] > sizes[0] == sizes[33] == sizes[64] > 0
+    assert sizes[65] == 0                      # no node has 65 sequences: nothing batched
+    assert tree_ws(L, q, levels, kv_(), share_min=-1)[0] == INVALID
+    assert tree_ws(L, q, levels, None, share_min=65) == (OK, 0)
+    # a step with batched nodes still checks its workspace before enqueuing anything
+    for smin in (0, 1):
+        assert tree_status(L, q, levels, kv_(), share_min=smin)[1] == WORKSPACE
+    assert tree_status(L, q, levels, kv_(), share_min=-1)[1] == INVALID
+    assert tree_status(L, q, levels, kv_(), o=None, share_min=65)[1] == NULL
 
 
 def test_cascade_null_tree_and_kv(L):

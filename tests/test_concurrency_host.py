@@ -22,7 +22,7 @@ def L():
 FAKE = 1 << 40  # an aligned address: planning checks pointers, never reads them
 
 
-def _args(B, Hq, Hkv, d, P, max_blocks, prefix=True, suffix=True):
+def _args(B, Hq, Hkv, d, P, max_blocks, prefix=True, suffix=True, share_min=0):
     query = hp.Query(FAKE, B, Hq, Hkv, d, hp.HP_F16, 1.0)
     tree = kv = None
     keep = []
@@ -31,6 +31,7 @@ def _args(B, Hq, Hkv, d, P, max_blocks, prefix=True, suffix=True):
         tree = hp.PrefixTree()
         tree.num_levels = 1
         tree.nodes_per_level[0] = 1
+        tree.share_min = share_min
         tree.nodes = ctypes.cast(nodes, ctypes.POINTER(hp.PrefixNode))
         keep.append(nodes)
     if suffix:
@@ -82,8 +83,9 @@ def test_auto_policy_two_level_gqa_stays_serial(L):
 
 
 def test_modes_and_workspace(L):
+    # a node the batching policy would leave to the suffix pass, batched on request
     B, Hq, Hkv, d = 8, 4, 2, 64
-    args = _args(B, Hq, Hkv, d, 300, 4)
+    args = _args(B, Hq, Hkv, d, 300, 4, share_min=1)
     off, ws = _plan(L, args, mode=0)
     assert off == 0
     on, ws_on = _plan(L, args, mode=2)
@@ -95,9 +97,11 @@ def test_modes_and_workspace(L):
     # the prefix partials for 160 compute units plus the suffix rows (O and LSE)
     assert ws >= up(B * Hq * d * 4) + up(B * Hq * 4)
     # prefix only or suffix only: nothing to run side by side
-    assert _plan(L, _args(B, Hq, Hkv, d, 300, 4, suffix=False), mode=2)[0] == 0
+    assert _plan(L, _args(B, Hq, Hkv, d, 300, 4, suffix=False, share_min=1), mode=2)[0] == 0
     assert _plan(L, _args(B, Hq, Hkv, d, 300, 4, prefix=False), mode=2)[0] == 0
     assert _plan(L, args, mode=1)[0] == 0
+    # the automatic policy reads this node in the suffix pass: nothing to overlap
+    assert _plan(L, _args(B, Hq, Hkv, d, 300, 4), mode=2) == (0, 0)
 
 
 def test_mode_validation(L):
@@ -113,7 +117,7 @@ def test_mode_validation(L):
 def test_overlap_handles_validated(L):
     """A side-by-side plan needs the caller's side stream and both events, and the side
     stream must differ from the step's stream; each is checked before any launch."""
-    query, tree, kv, _ = _args(8, 4, 2, 64, 300, 4)
+    query, tree, kv, _ = _args(8, 4, 2, 64, 300, 4, share_min=1)
     step = L.hp_cascade_step_overlap
     args = (ctypes.byref(query), ctypes.byref(tree), ctypes.byref(kv), FAKE, FAKE, FAKE, 1 << 30)
     assert step(*args, None, None) == 1

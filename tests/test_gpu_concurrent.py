@@ -27,9 +27,9 @@ def _gpu():
         pytest.fail("GPU tests need an MI355X (no GPU visible)")
 
 
-def _call(ds, scale):
+def _call(ds, scale, share_min=1):
     call = hp.CascadeCall(ds["q"], ds["levels"], ds["k_pool"], ds["v_pool"], ds["block_table"],
-                          ds["seq_lens"], scale, overlap=2)
+                          ds["seq_lens"], scale, overlap=2, share_min=share_min)
     assert call.concurrent, "forced mode must run the passes side by side"
     return call
 
@@ -43,6 +43,23 @@ def test_concurrent_matches_oracle(cfg):
     torch.cuda.synchronize()
     ref_o, ref_l = oracle.step_attention(step, "all")
     compare(out, lse, ref_o, ref_l, cfg.dtype, f"concurrent {cfg.name}")
+
+
+def test_concurrent_with_private_nodes():
+    """The batching policy on the two-level shape: the root (700 tokens, 24 sequences) is
+    batched, the group nodes (300 tokens, 8 sequences each) are read by each sequence in
+    the suffix pass, which runs beside the prefix pass."""
+    cfg = REDUCED[4]
+    assert cfg.name == "two_level_small"
+    step = workloads.generate(cfg, seed=4)
+    ds = dev_step(step)
+    call = _call(ds, step.scale, share_min=0)
+    batched = _call(ds, step.scale, share_min=1)
+    assert call.workspace_bytes < batched.workspace_bytes, "the group nodes need no partials"
+    out, lse = call()
+    torch.cuda.synchronize()
+    ref_o, ref_l = oracle.step_attention(step, "all")
+    compare(out, lse, ref_o, ref_l, cfg.dtype, "concurrent, private group nodes")
 
 
 def test_concurrent_bad_metadata_gives_nan_rows_only():

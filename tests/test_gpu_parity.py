@@ -184,14 +184,17 @@ REDUCED = [
 
 @pytest.mark.parametrize("cfg", REDUCED, ids=lambda c: c.name)
 @pytest.mark.parametrize("seed", [0, 1])
-def test_cascade_reduced(cfg, seed):
-    say(f"cascade {cfg.name} seed {seed}")
+@pytest.mark.parametrize("share_min", [0, 1], ids=["policy", "batch_all"])
+def test_cascade_reduced(cfg, seed, share_min):
+    """Every reduced shape, with the batching policy (short or narrowly shared nodes are
+    read by each sequence in the suffix pass) and with every node batched."""
+    say(f"cascade {cfg.name} seed {seed} share_min {share_min}")
     step = workloads.generate(cfg, seed=seed)
     ds = dev_step(step)
-    out, lse = cascade(ds, step.scale)
+    out, lse = cascade(ds, step.scale, share_min=share_min)
     torch.cuda.synchronize()
     ref_o, ref_l = oracle.step_attention(step, "all")
-    compare(out, lse, ref_o, ref_l, cfg.dtype, cfg.name)
+    compare(out, lse, ref_o, ref_l, cfg.dtype, f"{cfg.name} share_min {share_min}")
 
 
 def test_cascade_peaky_scores():
@@ -283,14 +286,17 @@ def test_prefix_256row_rescale_mid_split(dtype, P):
     compare(out2, lse2, ref_o, ref_l, dtype, f"peaky step {dtype} P={P}", rows=rows)
 
 
-def test_cascade_prefix_only_and_suffix_only():
+@pytest.mark.parametrize("share_min", [0, 1, 1000], ids=["policy", "batch_all", "none_batched"])
+def test_cascade_prefix_only_and_suffix_only(share_min):
+    """No paged suffix: the tree alone, its nodes batched, left to the policy (the group
+    nodes are read privately: the suffix pass runs on them alone) or all private."""
     cfg = REDUCED[4]
     step = workloads.generate(cfg, seed=6)
     ds = dev_step(step)
-    out, lse = cascade(ds, step.scale, paged=False)
+    out, lse = cascade(ds, step.scale, paged=False, share_min=share_min)
     torch.cuda.synchronize()
     ref_o, ref_l = oracle.step_attention(step, "prefix")
-    compare(out, lse, ref_o, ref_l, cfg.dtype, "tree only")
+    compare(out, lse, ref_o, ref_l, cfg.dtype, f"tree only share_min {share_min}")
     out, lse = cascade(ds, step.scale, levels=[])
     torch.cuda.synchronize()
     ref_o, ref_l = oracle.step_attention(step, "suffix")
@@ -387,7 +393,11 @@ def test_needles_suffix_every_position():
 
 
 @pytest.mark.parametrize("level", [0, 1])
-def test_needles_prefix_nodes(level):
+@pytest.mark.parametrize("share_min", [0, 1], ids=["policy", "batch_all"])
+def test_needles_prefix_nodes(level, share_min):
+    """Every key position of the level's nodes found exactly.  Under the policy the
+    root (1000 tokens, 64 sequences) is batched and the level-1 nodes (300 and 260
+    tokens, 32 sequences each) are read by each sequence in the suffix pass."""
     cfg = workloads.custom("needle_pfx", B=64, Hq=8, Hkv=2, d=128, dtype="f16",
                            levels=(((1000, 0, 64),), ((300, 0, 32), (260, 32, 64))),
                            suffix_lo=1, suffix_hi=40)
@@ -400,7 +410,10 @@ def test_needles_prefix_nodes(level):
             k.fill_(NEG)
     ds["k_pool"].fill_(NEG)
     call = hp.CascadeCall(ds["q"], ds["levels"], ds["k_pool"], ds["v_pool"], ds["block_table"],
-                          ds["seq_lens"], step.scale)
+                          ds["seq_lens"], step.scale, share_min=share_min)
+    if share_min == 0:
+        assert hp.share_decision(cfg.Hq, cfg.Hkv, 1000, 64, d=cfg.d, dtype=torch.float16)
+        assert not hp.share_decision(cfg.Hq, cfg.Hkv, 300, 32, d=cfg.d, dtype=torch.float16)
     d, G = cfg.d, cfg.G
     nodes = ds["levels"][level]
     cpu_nodes = step.levels[level]
