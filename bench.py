@@ -101,24 +101,31 @@ def workload(name: str):
     raise SystemExit(f"unknown workload {name}")
 
 
-def prepare(cfg, seed: int, overlap: int = 1):
+# Paged suffix blocks as head-major [Hkv][16][d] (each (sequence, KV head) reads
+# 16 contiguous rows per block; measured faster than token-major [16][Hkv][d]).
+KV_LAYOUT = "HND"
+
+
+def prepare(cfg, seed: int, overlap: int = 1, kv_layout: str = KV_LAYOUT):
     """Draw the step's inputs, copy them to the GPU and prepare the cascade call."""
     import workloads
     step = workloads.generate(cfg, seed=seed)
     dev = "cuda:0"
     levels = [[(n.k.to(dev), n.v.to(dev), n.seq_begin, n.seq_end) for n in lvl]
               for lvl in step.levels]
-    inputs = (step.q.to(dev), levels, step.k_pool.to(dev), step.v_pool.to(dev),
+    inputs = (step.q.to(dev), levels, workloads.pool_in_layout(step.k_pool, kv_layout).to(dev),
+              workloads.pool_in_layout(step.v_pool, kv_layout).to(dev),
               step.block_table.to(dev), step.seq_lens.to(dev), step.scale)
-    return step, make_call(inputs, overlap)
+    return step, make_call(inputs, overlap, kv_layout)
 
 
-def make_call(inputs, overlap: int):
+def make_call(inputs, overlap: int, kv_layout: str = KV_LAYOUT):
     """A CascadeCall over device inputs (q, levels, pools, table, lengths, scale)."""
     import torch
     import decode_attention_shared_amd as hp
-    call = hp.CascadeCall(*inputs, overlap=overlap)
+    call = hp.CascadeCall(*inputs, overlap=overlap, kv_layout=kv_layout)
     call.inputs = inputs
+    call.kv_layout = kv_layout
     torch.cuda.synchronize()
     return call
 
@@ -570,7 +577,7 @@ def main():
 
     config = {"workload": cfg.name, "B": cfg.B, "Hq": cfg.Hq, "Hkv": cfg.Hkv, "d": cfg.d,
               "prefix_tokens": [n[0] for lvl in cfg.levels for n in lvl],
-              "suffix": f"U[{cfg.suffix_lo},{cfg.suffix_hi}] paged, block 16",
+              "suffix": f"U[{cfg.suffix_lo},{cfg.suffix_hi}] paged, block 16, {KV_LAYOUT} blocks",
               "seed": args.seed, "parallelism": "single GPU"}
     common = {"unit": "steps/s", "n_gpus": 1, "steps": args.steps, "warmup": args.warmup,
               "higher_is_better": True, "scaling": "weak", "vs_baseline": None,
@@ -603,7 +610,7 @@ def main():
     # each step after a cache flush like the headline's.
     print("[bench] serial plan, flushed: each pass on the whole GPU", file=sys.stderr,
           flush=True)
-    scall = make_call(call.inputs, 0) if m["concurrent"] else call
+    scall = make_call(call.inputs, 0, call.kv_layout) if m["concurrent"] else call
     sp = time_passes_flushed(scall, ev, flush, args.steps, args.warmup)
     del scall
     alone_ms = {k: mean(sp[k]) for k in ("prefix", "suffix", "merge")}

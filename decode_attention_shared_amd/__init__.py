@@ -85,11 +85,14 @@ class PrefixTree(ctypes.Structure):
                 ("share_min", ctypes.c_int32)]
 
 
+HP_KV_NHD, HP_KV_HND = 0, 1
+
+
 class PagedKV(ctypes.Structure):
     _fields_ = [("k_pool", ctypes.c_void_p), ("v_pool", ctypes.c_void_p),
                 ("block_table", ctypes.c_void_p), ("seq_lens", ctypes.c_void_p),
                 ("max_blocks", ctypes.c_int32), ("block_size", ctypes.c_int32),
-                ("num_blocks", ctypes.c_int32)]
+                ("num_blocks", ctypes.c_int32), ("layout", ctypes.c_int32)]
 
 
 class StreamRows(ctypes.Structure):
@@ -372,19 +375,34 @@ def make_tree(levels: Sequence[Sequence[Tuple[torch.Tensor, torch.Tensor, int, i
     return tree, arr
 
 
+_KV_LAYOUTS = {"NHD": HP_KV_NHD, "HND": HP_KV_HND}
+
+
+def pool_heads(k_pool: torch.Tensor, kv_layout: str = "NHD") -> int:
+    """KV heads of a paged pool: [blocks][block_size][Hkv][d] (NHD) or
+    [blocks][Hkv][block_size][d] (HND)."""
+    return int(k_pool.shape[2] if kv_layout == "NHD" else k_pool.shape[1])
+
+
 def make_paged(k_pool: torch.Tensor, v_pool: torch.Tensor, block_table: torch.Tensor,
-               seq_lens: torch.Tensor) -> PagedKV:
+               seq_lens: torch.Tensor, kv_layout: str = "NHD") -> PagedKV:
+    """kv_layout "NHD": pools [num_blocks][block_size][Hkv][d]; "HND": [num_blocks][Hkv]
+    [block_size][d] (each block's rows of one KV head contiguous)."""
     for t, nm in ((k_pool, "k_pool"), (v_pool, "v_pool"), (block_table, "block_table"),
                   (seq_lens, "seq_lens")):
         _require_cuda(t, nm)
+    if kv_layout not in _KV_LAYOUTS:
+        raise ValueError(f"kv_layout must be one of {sorted(_KV_LAYOUTS)}")
     if k_pool.dim() != 4 or k_pool.shape != v_pool.shape or not k_pool.is_contiguous() \
             or not v_pool.is_contiguous():
-        raise ValueError("pools must be contiguous [num_blocks][block_size][Hkv][d]")
+        raise ValueError("pools must be contiguous 4-d tensors of one shape")
     if block_table.dtype != torch.int32 or seq_lens.dtype != torch.int32 or \
             not block_table.is_contiguous() or block_table.dim() != 2:
         raise ValueError("block_table [B][max_blocks] and seq_lens [B] must be int32")
+    block_size = k_pool.shape[1] if kv_layout == "NHD" else k_pool.shape[2]
     return PagedKV(k_pool.data_ptr(), v_pool.data_ptr(), block_table.data_ptr(),
-                   seq_lens.data_ptr(), block_table.shape[1], k_pool.shape[1], k_pool.shape[0])
+                   seq_lens.data_ptr(), block_table.shape[1], block_size, k_pool.shape[0],
+                   _KV_LAYOUTS[kv_layout])
 
 
 def _out(q: torch.Tensor, out, lse, zero: bool):
@@ -424,10 +442,11 @@ def prefix_attn(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, seq_begin: in
 
 def suffix_decode(q: torch.Tensor, k_pool: torch.Tensor, v_pool: torch.Tensor,
                   block_table: torch.Tensor, seq_lens: torch.Tensor,
-                  scale: Optional[float] = None, out=None, lse=None, stream=None):
+                  scale: Optional[float] = None, out=None, lse=None, stream=None,
+                  kv_layout: str = "NHD"):
     L = lib()
-    qs = make_query(q, k_pool.shape[2], scale)
-    kv = make_paged(k_pool, v_pool, block_table, seq_lens)
+    qs = make_query(q, pool_heads(k_pool, kv_layout), scale)
+    kv = make_paged(k_pool, v_pool, block_table, seq_lens, kv_layout)
     nbytes = ctypes.c_size_t(0)
     _check(L.hp_suffix_decode_workspace_size(ctypes.byref(qs), ctypes.byref(kv),
                                              ctypes.byref(nbytes)),
@@ -481,14 +500,16 @@ class CascadeCall:
 
     def __init__(self, q: torch.Tensor, levels, k_pool=None, v_pool=None, block_table=None,
                  seq_lens=None, scale: Optional[float] = None, out=None, lse=None,
-                 overlap: int = 1, share_min: int = 0):
+                 overlap: int = 1, share_min: int = 0, kv_layout: str = "NHD"):
         L = lib()
         self._L = L
-        Hkv = (levels[0][0][0].shape[1] if levels and levels[0] else k_pool.shape[2])
+        Hkv = (levels[0][0][0].shape[1] if levels and levels[0] else
+               pool_heads(k_pool, kv_layout))
         self.q = q
         self.query = make_query(q, Hkv, scale)
         self.tree, self._keep = make_tree(levels, share_min) if levels else (None, None)
-        self.kv = make_paged(k_pool, v_pool, block_table, seq_lens) if k_pool is not None else None
+        self.kv = (make_paged(k_pool, v_pool, block_table, seq_lens, kv_layout)
+                   if k_pool is not None else None)
         self.out, self.lse = _out(q, out, lse, zero=False)
         self._tree_p = ctypes.byref(self.tree) if self.tree is not None else None
         self._kv_p = ctypes.byref(self.kv) if self.kv is not None else None
@@ -537,28 +558,29 @@ class CascadeCall:
 
 def cascade_step(q: torch.Tensor, levels, k_pool=None, v_pool=None, block_table=None,
                  seq_lens=None, scale: Optional[float] = None, out=None, lse=None, stream=None,
-                 overlap: int = 1, share_min: int = 0):
+                 overlap: int = 1, share_min: int = 0, kv_layout: str = "NHD"):
     """levels: root first, each a list of (k, v, seq_begin, seq_end) device tensors/ints;
     the pools, table and lengths describe the paged suffixes (or None for prefix only).
-    share_min: see make_tree."""
+    share_min: see make_tree; kv_layout: see make_paged."""
     with _on(stream, q.device):
         call = CascadeCall(q, levels, k_pool, v_pool, block_table, seq_lens, scale, out, lse,
-                           overlap, share_min)
+                           overlap, share_min, kv_layout)
         return call(stream)
 
 
 def cascade_step_noalloc(q: torch.Tensor, levels, k_pool=None, v_pool=None, block_table=None,
                          seq_lens=None, scale: Optional[float] = None, out=None, lse=None,
-                         stream=None, share_min: int = 0):
+                         stream=None, share_min: int = 0, kv_layout: str = "NHD"):
     """hp_cascade_step_noalloc: cascade_step on one stream with the workspace taken from
     the library's fixed per-GPU scratch array (at most HP_NOALLOC_SCRATCH_BYTES).  The
     library allocates nothing; pass ``out`` (and ``lse``) to allocate nothing here either.
     Calls on one GPU share that array: the caller orders calls that could overlap."""
     L = lib()
-    Hkv = (levels[0][0][0].shape[1] if levels and levels[0] else k_pool.shape[2])
+    Hkv = (levels[0][0][0].shape[1] if levels and levels[0] else pool_heads(k_pool, kv_layout))
     query = make_query(q, Hkv, scale)
     tree, keep = make_tree(levels, share_min) if levels else (None, None)
-    kv = make_paged(k_pool, v_pool, block_table, seq_lens) if k_pool is not None else None
+    kv = (make_paged(k_pool, v_pool, block_table, seq_lens, kv_layout)
+          if k_pool is not None else None)
     with _on(stream, q.device):
         out, lse = _out(q, out, lse, zero=False)
     _check(L.hp_cascade_step_noalloc(ctypes.byref(query),

@@ -121,6 +121,7 @@ hp_status check_tree(const hp_query *q, const hp_prefix_tree *t, int *total_node
 hp_status check_kv(const hp_query *q, const hp_paged_kv *kv) {
     if (!kv) return HP_ERR_NULL;
     if (kv->block_size != HP_BLOCK_SIZE) return HP_ERR_UNSUPPORTED;
+    if (kv->layout != HP_KV_NHD && kv->layout != HP_KV_HND) return HP_ERR_INVALID_ARG;
     if (kv->max_blocks < 1 || kv->num_blocks < 1) return HP_ERR_INVALID_ARG;
     if ((int64_t)kv->max_blocks * HP_BLOCK_SIZE > INT32_MAX) return HP_ERR_INVALID_ARG;
     if (!kv->k_pool || !kv->v_pool || !kv->block_table || !kv->seq_lens) return HP_ERR_NULL;
@@ -285,6 +286,7 @@ SuffixArgs suffix_args(const hp_query &q, const hp_paged_kv *kv, RowDest dest) {
     a.lens = kv->seq_lens;
     a.max_blocks = kv->max_blocks;
     a.num_blocks = kv->num_blocks;
+    a.kv_hnd = kv->layout == HP_KV_HND ? 1 : 0;
     a.has_suffix = 1;
     // K/V footprint: the pool, or what the block tables can reach if less.
     const int64_t blocks = std::min<int64_t>(kv->num_blocks, (int64_t)q.B * kv->max_blocks);

@@ -156,6 +156,7 @@ struct SuffixArgs {
     const int32_t *lens;      // chunk-tree mode: total tokens of each sequence, may be null
     int32_t B, Hq, Hkv;
     int32_t max_blocks, num_blocks;
+    int32_t kv_hnd;           // paged mode: blocks are [Hkv][16][d] (else [16][Hkv][d])
     int32_t has_suffix;       // 0: no paged suffix (only the sources are merged)
     float scale_log2;
     RowDest dest;             // final O and LSE (o_split, lse_split unused)

@@ -269,7 +269,10 @@ __global__ __launch_bounds__(64 * NWS) void suffix_kernel(SuffixArgs a) {
         for (int e = 0; e < kEpl; ++e) acc[j][e] = 0.f;
     }
 
-    const int64_t tok_stride = (int64_t)a.Hkv * D * E::kSize;  // bytes between tokens of a block
+    // Paged blocks: bytes between a block's tokens and offset of this KV head
+    // (token-major [16][Hkv][D] or head-major [Hkv][16][D] blocks).
+    const int64_t tok_stride = a.kv_hnd ? (int64_t)D * E::kSize : (int64_t)a.Hkv * D * E::kSize;
+    const int64_t head_off = (int64_t)g * D * E::kSize * (a.kv_hnd ? kBlock : 1);
     const char *kp = (const char *)a.k_pool;
     const char *vp = (const char *)a.v_pool;
 
@@ -351,8 +354,8 @@ __global__ __launch_bounds__(64 * NWS) void suffix_kernel(SuffixArgs a) {
             const bool id_ok = id >= 0 && id < a.num_blocks;
             bad |= !id_ok;
             valid = id_ok ? min(kBlock, len - (blk - nsb) * kBlock) : 0;
-            const int64_t base = ((int64_t)(id_ok ? id : 0) * kBlock * a.Hkv + g) * D * E::kSize +
-                                 d0 * E::kSize;
+            const int64_t base = (int64_t)(id_ok ? id : 0) * kBlock * a.Hkv * D * E::kSize +
+                                 head_off + d0 * E::kSize;
 #pragma unroll
             for (int p = 0; p < kPasses; ++p) {
                 const int t = p * kTpp + tg;

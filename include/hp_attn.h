@@ -153,16 +153,24 @@ typedef struct hp_prefix_tree {
  * boundary": ordinary paged decode over each sequence's own blocks).  Token t
  * of sequence b is slot t % block_size of block block_table[b*max_blocks +
  * t / block_size]; its key for KV head g is at
- * k_pool + ((blk*block_size + slot)*Hkv + g)*d.  seq_lens may change between
- * graph replays (it is read on the device).
+ *   HP_KV_NHD  k_pool + ((blk*block_size + slot)*Hkv + g)*d   (token-major)
+ *   HP_KV_HND  k_pool + ((blk*Hkv + g)*block_size + slot)*d   (head-major)
+ * and likewise in v_pool.  Head-major blocks keep the block_size rows one
+ * (sequence, KV head) reads contiguous: the suffix pass reads them measurably
+ * faster (3-9 % on the 16K-prefix shapes).  seq_lens may change between graph
+ * replays (it is read on the device).
  */
+#define HP_KV_NHD 0
+#define HP_KV_HND 1
+
 typedef struct hp_paged_kv {
-    const void *k_pool, *v_pool;   /* device [num_blocks][block_size][Hkv][d] of dtype */
+    const void *k_pool, *v_pool;   /* device, num_blocks blocks of block_size*Hkv*d of dtype */
     const int32_t *block_table;    /* device [B][max_blocks] */
     const int32_t *seq_lens;       /* device [B], each in [0, max_blocks*block_size] */
     int32_t max_blocks;            /* >= 1 */
     int32_t block_size;            /* HP_BLOCK_SIZE */
     int32_t num_blocks;            /* >= 1 */
+    int32_t layout;                /* HP_KV_NHD or HP_KV_HND, else HP_ERR_INVALID_ARG */
 } hp_paged_kv;
 
 /*

@@ -8,6 +8,7 @@ import numpy as np
 import torch
 
 import decode_attention_shared_amd as hp
+import workloads
 
 DEV = "cuda:0"
 
@@ -29,13 +30,15 @@ def say(msg: str) -> None:
     sys.stdout.flush()
 
 
-def dev_step(step, dev=DEV):
-    """Copy a workloads.Step to the GPU: q, tree levels, paged pool."""
+def dev_step(step, dev=DEV, kv_layout="NHD"):
+    """Copy a workloads.Step to the GPU: q, tree levels, paged pool (in kv_layout)."""
     levels = [[(n.k.to(dev), n.v.to(dev), n.seq_begin, n.seq_end) for n in lvl]
               for lvl in step.levels]
-    return dict(q=step.q.to(dev), levels=levels, k_pool=step.k_pool.to(dev),
-                v_pool=step.v_pool.to(dev), block_table=step.block_table.to(dev),
-                seq_lens=step.seq_lens.to(dev))
+    return dict(q=step.q.to(dev), levels=levels,
+                k_pool=workloads.pool_in_layout(step.k_pool, kv_layout).to(dev),
+                v_pool=workloads.pool_in_layout(step.v_pool, kv_layout).to(dev),
+                block_table=step.block_table.to(dev), seq_lens=step.seq_lens.to(dev),
+                kv_layout=kv_layout)
 
 
 def cascade(ds, scale, levels=None, paged=True, share_min=0):
@@ -44,7 +47,8 @@ def cascade(ds, scale, levels=None, paged=True, share_min=0):
     lv = ds["levels"] if levels is None else levels
     if paged:
         return hp.cascade_step(ds["q"], lv, ds["k_pool"], ds["v_pool"], ds["block_table"],
-                               ds["seq_lens"], scale, share_min=share_min)
+                               ds["seq_lens"], scale, share_min=share_min,
+                               kv_layout=ds["kv_layout"])
     return hp.cascade_step(ds["q"], lv, scale=scale, share_min=share_min)
 
 

@@ -57,8 +57,9 @@ def node_(len_=100, b0=0, b1=4, k=FAKE, v=FAKE, st=256, sh=128):
     return PrefixNode(k, v, st, sh, len_, b0, b1)
 
 
-def kv_(max_blocks=4, block_size=16, num_blocks=20, k=FAKE, v=FAKE, tbl=FAKE, lens=FAKE):
-    return PagedKV(k, v, tbl, lens, max_blocks, block_size, num_blocks)
+def kv_(max_blocks=4, block_size=16, num_blocks=20, k=FAKE, v=FAKE, tbl=FAKE, lens=FAKE,
+        layout=0):
+    return PagedKV(k, v, tbl, lens, max_blocks, block_size, num_blocks, layout)
 
 
 def prefix_status(L, q, n, o=FAKE, lse=FAKE, ws=None, wsb=0):
@@ -133,6 +134,8 @@ def suffix_status(L, q, kv, o=FAKE, ws=None, wsb=0):
     (dict(lens=0), NULL),
     (dict(v=FAKE + 2), INVALID),
     (dict(tbl=FAKE + 2), INVALID),
+    (dict(layout=2), INVALID),
+    (dict(layout=-1), INVALID),
 ])
 def test_paged_validation(L, kw, code):
     assert suffix_status(L, q_(), kv_(**kw)) == code

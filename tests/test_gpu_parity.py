@@ -94,27 +94,31 @@ SUFFIX_CASES = [
 
 
 @pytest.mark.parametrize("case", SUFFIX_CASES, ids=lambda c: "-".join(map(str, c)))
-@pytest.mark.parametrize("paged", [True, False])
-def test_suffix_pass(case, paged):
+@pytest.mark.parametrize("layout", ["NHD", "HND", "contiguous"])
+def test_suffix_pass(case, layout):
+    """Paged suffixes in both block layouts (token-major NHD, head-major HND), and
+    suffixes stored contiguously (an identity block table)."""
     dtype, d, B, Hq, Hkv, lo, hi = case
-    say(f"suffix {case} paged={paged}")
+    paged = layout != "contiguous"
+    say(f"suffix {case} layout={layout}")
     step = workloads.generate(_one_level("suf", dtype, d, B, Hq, Hkv, 0, 0, B, lo, hi, paged),
                               seed=2)
-    ds = dev_step(step)
+    ds = dev_step(step, kv_layout="HND" if layout == "HND" else "NHD")
     out, lse = hp.suffix_decode(ds["q"], ds["k_pool"], ds["v_pool"], ds["block_table"],
-                                ds["seq_lens"], step.scale)
+                                ds["seq_lens"], step.scale, kv_layout=ds["kv_layout"])
     torch.cuda.synchronize()
     ref_o, ref_l = oracle.step_attention(step, "suffix")
     compare(out, lse, ref_o, ref_l, dtype, "suffix")
 
 
-def test_suffix_lengths_at_block_edges():
+@pytest.mark.parametrize("layout", ["NHD", "HND"])
+def test_suffix_lengths_at_block_edges(layout):
     lens = [0, 1, 15, 16, 17, 31, 32, 33, 127, 128, 129, 255, 256, 300]
     cfg = _one_level("edges", "bf16", 128, len(lens), 8, 2, 0, 0, len(lens), 0, 300)
     step = workloads.generate(cfg, seed=3, seq_lens=lens)
-    ds = dev_step(step)
+    ds = dev_step(step, kv_layout=layout)
     out, lse = hp.suffix_decode(ds["q"], ds["k_pool"], ds["v_pool"], ds["block_table"],
-                                ds["seq_lens"], step.scale)
+                                ds["seq_lens"], step.scale, kv_layout=layout)
     torch.cuda.synchronize()
     ref_o, ref_l = oracle.step_attention(step, "suffix")
     compare(out, lse, ref_o, ref_l, "bf16", "suffix edges")
@@ -184,17 +188,19 @@ REDUCED = [
 
 @pytest.mark.parametrize("cfg", REDUCED, ids=lambda c: c.name)
 @pytest.mark.parametrize("seed", [0, 1])
-@pytest.mark.parametrize("share_min", [0, 1], ids=["policy", "batch_all"])
-def test_cascade_reduced(cfg, seed, share_min):
+@pytest.mark.parametrize("share_min,layout", [(0, "NHD"), (1, "NHD"), (0, "HND")],
+                         ids=["policy", "batch_all", "policy_hnd"])
+def test_cascade_reduced(cfg, seed, share_min, layout):
     """Every reduced shape, with the batching policy (short or narrowly shared nodes are
-    read by each sequence in the suffix pass) and with every node batched."""
-    say(f"cascade {cfg.name} seed {seed} share_min {share_min}")
+    read by each sequence in the suffix pass) and with every node batched; the paged
+    suffix in token-major and head-major blocks."""
+    say(f"cascade {cfg.name} seed {seed} share_min {share_min} {layout}")
     step = workloads.generate(cfg, seed=seed)
-    ds = dev_step(step)
+    ds = dev_step(step, kv_layout=layout)
     out, lse = cascade(ds, step.scale, share_min=share_min)
     torch.cuda.synchronize()
     ref_o, ref_l = oracle.step_attention(step, "all")
-    compare(out, lse, ref_o, ref_l, cfg.dtype, f"{cfg.name} share_min {share_min}")
+    compare(out, lse, ref_o, ref_l, cfg.dtype, f"{cfg.name} share_min {share_min} {layout}")
 
 
 def test_cascade_peaky_scores():
@@ -347,7 +353,11 @@ def _needle_q(step):
     return q
 
 
-def test_needles_suffix_every_position():
+@pytest.mark.parametrize("layout", ["NHD", "HND"])
+def test_needles_suffix_every_position(layout):
+    """Every logical suffix position found exactly, through the block table, in both
+    block layouts (the needles are placed in the token-major pool, which is copied to
+    a head-major one before each call for HND)."""
     cfg = workloads.custom("needle_suf", B=24, Hq=8, Hkv=4, d=128, dtype="bf16",
                            levels=(((200, 0, 24),),), suffix_lo=1, suffix_hi=100)
     step = workloads.generate(cfg, seed=9)
@@ -365,8 +375,13 @@ def test_needles_suffix_every_position():
         for t in range(lens[b]):
             valid[int(tbl[b, t // 16]), t % 16, :] = True
     pk[..., 0][valid.to(DEV)] = NEG
-    call = hp.CascadeCall(ds["q"], ds["levels"], pk, ds["v_pool"], ds["block_table"],
-                          ds["seq_lens"], step.scale)
+    if layout == "HND":
+        pk_call = pk.permute(0, 2, 1, 3).contiguous()
+        pv_call = ds["v_pool"].permute(0, 2, 1, 3).contiguous()
+    else:
+        pk_call, pv_call = pk, ds["v_pool"]
+    call = hp.CascadeCall(ds["q"], ds["levels"], pk_call, pv_call, ds["block_table"],
+                          ds["seq_lens"], step.scale, kv_layout=layout)
     suf_v = step.suf_v.float()
     offs = step.suf_offsets.tolist()
     G = cfg.G
@@ -382,6 +397,8 @@ def test_needles_suffix_every_position():
         idx = (torch.tensor(blks, device=DEV), torch.tensor(slots, device=DEV),
                torch.tensor(heads, device=DEV))
         pk[idx + (0,)] = 0.0
+        if layout == "HND":
+            pk_call.copy_(pk.permute(0, 2, 1, 3))
         out, lse = call()
         got = out.cpu()
         want = torch.stack(want_rows).view(cfg.B, cfg.Hkv, 1, cfg.d).expand(
@@ -440,22 +457,24 @@ def test_needles_prefix_nodes(level, share_min):
 
 # ------------------------------------------------------------------ full sizes, sampled rows
 
-FULL = [workloads.tiny_f32(), workloads.llama3_8b_gqa(), workloads.codellama13b_mha(1024),
-        workloads.codellama13b_mha(16384), workloads.docqa_codellama7b(),
-        workloads.two_level_gqa()]
+FULL = [(workloads.tiny_f32(), "HND"), (workloads.llama3_8b_gqa(), "HND"),
+        (workloads.codellama13b_mha(1024), "HND"), (workloads.codellama13b_mha(16384), "HND"),
+        (workloads.docqa_codellama7b(), "HND"), (workloads.two_level_gqa(), "HND"),
+        (workloads.codellama13b_mha_share(8), "HND"), (workloads.codellama13b_mha(16384), "NHD")]
 
 
-@pytest.mark.parametrize("cfg", FULL, ids=lambda c: c.name)
-def test_cascade_full_size_every_row(cfg):
+@pytest.mark.parametrize("cfg,layout", FULL, ids=lambda c: c.name if hasattr(c, "name") else c)
+def test_cascade_full_size_every_row(cfg, layout):
     """Each benchmark shape at full size, in the launch configuration bench.py times
-    (CascadeCall, passes side by side where the policy picks it): every row against the
-    oracle."""
-    say(f"full {cfg.name}: generating")
+    (CascadeCall with the batching policy, head-major paged blocks, passes side by side
+    where the plan picks it), and the 16K step with token-major blocks: every row against
+    the oracle."""
+    say(f"full {cfg.name} {layout}: generating")
     step = workloads.generate(cfg, seed=0)
-    ds = dev_step(step)
-    say(f"full {cfg.name}: running")
+    ds = dev_step(step, kv_layout=layout)
+    say(f"full {cfg.name} {layout}: running")
     call = hp.CascadeCall(ds["q"], ds["levels"], ds["k_pool"], ds["v_pool"], ds["block_table"],
-                          ds["seq_lens"], step.scale)
+                          ds["seq_lens"], step.scale, kv_layout=layout)
     out, lse = call()
     torch.cuda.synchronize()
     say(f"full {cfg.name}: oracle over {cfg.B * cfg.Hq} rows (side by side: {call.concurrent})")

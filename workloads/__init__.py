@@ -204,6 +204,17 @@ class Step:
         return h.hexdigest()
 
 
+def pool_in_layout(pool: torch.Tensor, kv_layout: str) -> torch.Tensor:
+    """A paged pool [blocks][16][Hkv][d] (NHD, as generated) in the given layout: NHD
+    as is, HND as [blocks][Hkv][16][d] (the same values, each block's rows of one KV
+    head contiguous)."""
+    if kv_layout == "NHD":
+        return pool
+    if kv_layout == "HND":
+        return pool.permute(0, 2, 1, 3).contiguous()
+    raise ValueError(f"unknown layout {kv_layout}")
+
+
 def scale_for(d: int) -> float:
     """The float32 value of 1/sqrt(d), as the kernels receive it."""
     return float(np.float32(1.0 / math.sqrt(d)))
