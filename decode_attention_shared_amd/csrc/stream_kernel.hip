@@ -4,9 +4,10 @@
 // holds every stream's tokens (questions, then the streams' answer tokens
 // interleaved step by step), each position tagged with the id of the stream
 // it belongs to, or -1 for tokens every stream may see.  A query of stream s
-// attends a position only when that position's id is -1 or s, so each stream
-// sees what it would see if its question were decoded alone ("Read Once,
-// Answer Many: Parallel Prompting for Shared-Context LLM Inference", section
+// attends a position only when that position's id is -1 or s: the other
+// streams' tokens never enter its softmax, so its result equals that of a
+// request holding only the shared tokens and its own ("Read Once, Answer
+// Many: Parallel Prompting for Shared-Context LLM Inference", section
 // "Parallel Prompting", Eq. 2 and Figure 2; its document is a shared prefix
 // read once for all streams by the prefix pass).
 //

@@ -1,6 +1,6 @@
 """Shared-context streams on the CPU: the stream-id mask of the oracle against the
-Parallel Prompting page's Figure 2, the generator's row layout against the page's
-claim that a stream sees what it would see alone, the masked softmax against a
+Parallel Prompting page's Figure 2, the generator's row layout against the rule that a
+stream's visible tokens are the shared ones and its own, the masked softmax against a
 dense -inf mask, and the C ABI's validation of hp_stream_decode (no GPU needed)."""
 import ctypes
 import json
