@@ -253,6 +253,18 @@ def time_passes_flushed(call, ev: HipEvents, flush: Flusher, steps: int, warmup:
     return passes
 
 
+def copy_gbps(mib: int = 1024, reps: int = 10) -> float:
+    """Bytes moved (read + written) per second by a plain device-to-device copy of `mib`
+    MiB: the streaming rate this GPU reaches in the same run, beside the 8 TB/s spec."""
+    import torch
+    src = torch.ones((mib << 20) // 4, dtype=torch.float32, device="cuda:0")
+    dst = torch.empty_like(src)
+    dst.copy_(src)
+    ms = time_hot(lambda: dst.copy_(src), reps)
+    del src, dst
+    return 2.0 * (mib << 20) / (ms * 1e-3) / 1e9
+
+
 def time_hot(fn, steps: int) -> float:
     """Mean ms of `steps` back-to-back calls of fn, between two HIP events."""
     import torch
@@ -284,7 +296,8 @@ def measure(cfg, step, call, ev, flush, steps: int, warmup: int) -> dict:
     del g
     b = workloads.algorithmic_bytes(cfg, step.seq_lens.tolist())
     med = median(times)
-    return {"cold_ms_median": med, "cold_ms_min": times[0], "cold_ms_max": times[-1],
+    return {"cold_ms_median": med, "cold_ms_mean": mean(times), "cold_ms_min": times[0],
+            "cold_ms_max": times[-1],
             "region_wall_s": wall, "hot_graph_ms": hot_graph,
             "hot_eager_ms": eager_wall / steps * 1e3, "passes": passes, "bytes": b,
             "concurrent": bool(getattr(call, "concurrent", False))}
@@ -295,7 +308,8 @@ def summary(cfg, m: dict) -> dict:
     b = m["bytes"]["total"]
     med = m["cold_ms_median"]
     return {"workload": cfg.name, "steps_per_s": round(1e3 / med, 1),
-            "ms_per_step": round(med, 4), "algorithmic_bytes": b,
+            "ms_per_step": round(med, 4), "ms_per_step_mean": round(m["cold_ms_mean"], 4),
+            "algorithmic_bytes": b,
             "effective_gbps": round(b / (med * 1e-3) / 1e9, 1),
             "hbm_roofline_frac": round(b / (med * 1e-3) / 1e9 / HBM_PEAK_GBPS, 4),
             "hot_eager_ms": round(m["hot_eager_ms"], 4),
@@ -310,6 +324,17 @@ def mean(xs):
 
 
 def cpu_model() -> str:
+    """The host CPU's model name (lscpu when present, else /proc/cpuinfo)."""
+    import shutil
+    import subprocess
+    if shutil.which("lscpu"):
+        try:
+            out = subprocess.run(["lscpu"], capture_output=True, text=True, timeout=10).stdout
+            for line in out.splitlines():
+                if line.strip().startswith("Model name"):
+                    return line.split(":", 1)[1].strip()
+        except (OSError, subprocess.SubprocessError):
+            pass
     try:
         with open("/proc/cpuinfo") as f:
             for line in f:
@@ -624,6 +649,7 @@ def main():
         "timing": (f"median of {args.steps} HIP-graph replays of the step, each after a "
                    f"{FLUSH_BYTES >> 30} GiB read that evicts the Infinity Cache; HIP events "
                    "around each replay on its stream"),
+        "cold_ms_mean": round(m["cold_ms_mean"], 4),
         "cold_ms_min": round(m["cold_ms_min"], 4),
         "cold_ms_max": round(m["cold_ms_max"], 4),
         "timed_region_wall_s": round(m["region_wall_s"], 4),
@@ -639,9 +665,13 @@ def main():
         "prefix_mfma_frac": round(prefix_tflops / mfma_peak, 4),
         "prefix_tflops": round(prefix_tflops, 1),
         "roofline": roofline(alone_ms),
+        "device_copy_gbps": None,
     }
     del call
     torch.cuda.empty_cache()
+    cg = copy_gbps()
+    result["device_copy_gbps"] = round(cg, 1)
+    result["hbm_frac_of_device_copy"] = round(eff / cg, 4)
     if not args.no_sweep and cfg.name.startswith("codellama13b"):
         sweep = []
         for P in workloads.CODELLAMA13B_SWEEP:
@@ -650,6 +680,8 @@ def main():
             st, cl = prepare(c, args.seed)
             line = summary(c, measure(c, st, cl, ev, flush, args.sweep_steps, SWEEP_WARMUP))
             line["prefix"] = P
+            # bytes relative to the 16K step: the steps/s a bandwidth-bound step would show
+            line["bytes_vs_headline"] = round(line["algorithmic_bytes"] / ab["total"], 4)
             sweep.append(line)
             del cl, st
             torch.cuda.empty_cache()
