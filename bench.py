@@ -94,7 +94,11 @@ def kernel_hash() -> str:
 def workload(name: str):
     import workloads
     if name.startswith("codellama13b_mha_p"):
-        return workloads.codellama13b_mha(int(name.rsplit("p", 1)[1]))
+        rest = name[len("codellama13b_mha_p"):]
+        if "_share" in rest:
+            prefix, ways = rest.split("_share")
+            return workloads.codellama13b_mha_share(int(ways), int(prefix))
+        return workloads.codellama13b_mha(int(rest))
     for c in workloads.all_configs():
         if c.name == name:
             return c

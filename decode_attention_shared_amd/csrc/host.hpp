@@ -97,13 +97,15 @@ void plan_splits(const SplitItem *items, int count, int Hkv, int d, int nw, int6
 // the same speed as all of them (the chip's power budget, not its CU count,
 // bounds the matrix-core pass), leaving the rest to the memory-bound suffix.
 // Used when every prefix split keeps at least kConcMinTiles tiles under that
-// plan and the suffix has at least kConcMinUnits (sequence, KV head) units
-// (measured on MI355X: MHA steps with 2K-16K prefixes and 10 240 units gain
-// 2-10 %, a 1K prefix (4 tiles per split) loses 1 %, a two-level GQA step with
-// 2 048 units loses 10 %).
+// plan and the suffix has at least kConcMinUnits (sequence, KV head) units.
+// Measured on MI355X with the caches flushed before every step (as a layer's
+// attention finds them in a model): MHA steps with 10 240 units and 1K-16K
+// prefixes (4-64 tiles per split) gain 3-8 %, a two-level GQA step with 2 048
+// units gains 5 %; with 512 (Llama-3-8B shape) or 1 280 units (one 8-way head
+// share of the 16K MHA shape) the side-by-side step loses 13-16 %.
 constexpr int kConcCUs = 160;
-constexpr int kConcMinTiles = 8;
-constexpr int64_t kConcMinUnits = 4096;
+constexpr int kConcMinTiles = 4;
+constexpr int64_t kConcMinUnits = 2048;
 
 // Batching policy (hp_share_decision): whether `tokens` keys shared by `nseq`
 // sequences are better read once for all of them than by each sequence.

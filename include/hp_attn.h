@@ -247,7 +247,7 @@ hp_status hp_cascade_step(const hp_query *query, const hp_prefix_tree *tree,
  *   mode         0: never (exactly hp_cascade_step); 1: when the plan expects
  *                a gain, that is when, with the prefix pass planned for 160 of
  *                the 256 compute units, every prefix split still covers at
- *                least 8 tiles of 64 keys and the suffix has at least 4096
+ *                least 4 tiles of 64 keys and the suffix has at least 2048
  *                (sequence, KV head) units; 2: whenever the step has both a
  *                prefix and a suffix.
  * Everything enqueued on `stream` before the call is ordered before both
