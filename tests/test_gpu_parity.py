@@ -525,6 +525,43 @@ def test_cascade_graph_replay_matches_eager():
     compare(call.out, call.lse, ref_o, ref_l, cfg.dtype, "replay with new lengths")
 
 
+def test_calls_on_a_stream_that_is_not_current():
+    """Every entry point called with stream=s while another stream is current: the
+    binding's temporaries (workspace, outputs) must stay reserved until s has run, so
+    allocations made on the current stream right after each call (filled with NaN) may
+    not land on them."""
+    cfg = REDUCED[4]
+    step = workloads.generate(cfg, seed=21)
+    ds = dev_step(step)
+    s = torch.cuda.Stream()
+    s.wait_stream(torch.cuda.current_stream())
+    spin = torch.ones(1 << 26, device=DEV)   # keeps s busy while the current stream allocates
+    junk = []
+    with torch.cuda.stream(s):
+        for _ in range(4):
+            spin.mul_(1.0)
+    out, lse = hp.cascade_step(ds["q"], ds["levels"], ds["k_pool"], ds["v_pool"],
+                               ds["block_table"], ds["seq_lens"], step.scale, stream=s)
+    junk += [torch.full((1 << 22,), float("nan"), device=DEV) for _ in range(8)]
+    k, v, b0, b1 = ds["levels"][0][0]
+    p_out, p_lse = hp.prefix_attn(ds["q"], k, v, b0, b1, step.scale, stream=s)
+    junk += [torch.full((1 << 22,), float("nan"), device=DEV) for _ in range(8)]
+    s_out, s_lse = hp.suffix_decode(ds["q"], ds["k_pool"], ds["v_pool"], ds["block_table"],
+                                    ds["seq_lens"], step.scale, stream=s)
+    junk += [torch.full((1 << 22,), float("nan"), device=DEV) for _ in range(8)]
+    s.synchronize()
+    torch.cuda.synchronize()
+    ref_o, ref_l = oracle.step_attention(step, "all")
+    compare(out, lse, ref_o, ref_l, cfg.dtype, "cascade on a non-current stream")
+    ref_o, ref_l = oracle.step_attention(step, "suffix")
+    compare(s_out, s_lse, ref_o, ref_l, cfg.dtype, "suffix on a non-current stream")
+    node = step.levels[0][0]
+    segs = [[(node.k, node.v)] if b0 <= b < b1 else [] for b in range(cfg.B)]
+    ref_o, ref_l = oracle.attention(step.q, segs, cfg.Hkv, step.scale)
+    compare(p_out, p_lse, ref_o, ref_l, cfg.dtype, "prefix on a non-current stream")
+    del junk
+
+
 def test_cascade_timed_records_events_and_matches():
     cfg = REDUCED[2]
     step = workloads.generate(cfg, seed=12)
