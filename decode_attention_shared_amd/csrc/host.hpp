@@ -93,9 +93,9 @@ void plan_splits(const SplitItem *items, int count, int Hkv, int d, int nw, int6
                  SplitPlan *out, int cus = kCUs);
 
 // Running the suffix pass beside the prefix pass (see the cascade step): the
-// prefix is then planned for kConcCUs compute units, which it fills at about
-// the same speed as all of them (the chip's power budget, not its CU count,
-// bounds the matrix-core pass), leaving the rest to the memory-bound suffix.
+// prefix is then planned for kConcCUs compute units, where alone it takes
+// 1.15-1.28x the time of its all-CU plan (less than the CU ratio), leaving
+// the rest to the memory-bound suffix.
 // Used when every prefix split keeps at least kConcMinTiles tiles under that
 // plan and the suffix has at least kConcMinUnits (sequence, KV head) units.
 // Measured on MI355X with the caches flushed before every step (as a layer's
