@@ -43,10 +43,12 @@ __global__ __launch_bounds__(256) void merge_kernel(MergeArgs a) {
     const int64_t b = a.row_b0 + r / a.Hq;
     const int h = (int)(r % a.Hq);
 
-    // One pass with a running max: each partial's LSE and O are loaded together
-    // (no second round trip for the O rows after a max over the LSEs), and the
-    // sum so far is rescaled when a larger LSE arrives.  The result is the same
-    // weighted mean up to rounding order.
+    // One pass with a running max, the sum so far rescaled when a larger LSE
+    // arrives; the result is the same weighted mean up to rounding order.  The
+    // update has no branch, so every load of a group of partials (its LSEs and
+    // its O rows) is issued before the first of them is used: one memory round
+    // trip per group instead of two per partial.  An empty part (LSE -inf)
+    // gets weight 0; its O row is the zero row every pass writes for it.
     bool bad = false;
     float mx = -INFINITY;
     f32x4 acc = {0.f, 0.f, 0.f, 0.f};
@@ -61,16 +63,14 @@ __global__ __launch_bounds__(256) void merge_kernel(MergeArgs a) {
             const float L = s.lse[(int64_t)i * s.lse_split + ri];
             const f32x4 v = *(const f32x4 *)(s.o + (int64_t)i * s.o_split + ri * D + c4);
             bad |= (L != L);
-            if (!(L > -INFINITY)) continue;  // an empty part (or NaN, flagged above)
-            if (L > mx) {
-                const float rs = fast_exp2((mx - L) * kLog2e);  // 0 while mx = -inf
-                acc *= rs;
-                wsum *= rs;
-                mx = L;
-            }
-            const float w = fast_exp2((L - mx) * kLog2e);
-            acc += w * v;
-            wsum += w;
+            const bool live = L > -INFINITY;  // false for an empty part (and NaN, flagged)
+            const float m_new = live ? fmaxf(mx, L) : mx;
+            // 0 while mx = -inf (acc and wsum are 0 then); 1 when the max stays
+            const float rs = m_new > mx ? fast_exp2((mx - m_new) * kLog2e) : 1.f;
+            const float w = live ? fast_exp2((L - m_new) * kLog2e) : 0.f;
+            acc = acc * rs + w * v;
+            wsum = wsum * rs + w;
+            mx = m_new;
         }
     }
     f32x4 out;
