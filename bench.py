@@ -269,6 +269,22 @@ def copy_gbps(mib: int = 1024, reps: int = 10) -> float:
     return 2.0 * (mib << 20) / (ms * 1e-3) / 1e9
 
 
+def stream_read_gbps(mib: int = 4096, reps: int = 5) -> float:
+    """Bytes per second that the library's streaming-read probe (one pass of 16-byte
+    non-temporal loads, nothing written but one word per workgroup) pulls from a
+    `mib` MiB buffer, sixteen times the Infinity Cache (long enough that the launch's
+    ramp does not count): the read ceiling of this GPU in the same run, beside the
+    8 TB/s spec."""
+    import torch
+    import decode_attention_shared_amd as hp
+    buf = torch.ones((mib << 20) // 4, dtype=torch.int32, device="cuda:0")
+    sink = torch.empty(hp.HP_READ_PROBE_WGS, dtype=torch.int32, device="cuda:0")
+    hp.read_probe(buf, sink)
+    ms = time_hot(lambda: hp.read_probe(buf, sink), reps)
+    del buf, sink
+    return (mib << 20) / (ms * 1e-3) / 1e9
+
+
 def time_hot(fn, steps: int) -> float:
     """Mean ms of `steps` back-to-back calls of fn, between two HIP events."""
     import torch
@@ -676,6 +692,9 @@ def main():
     cg = copy_gbps()
     result["device_copy_gbps"] = round(cg, 1)
     result["hbm_frac_of_device_copy"] = round(eff / cg, 4)
+    rg = stream_read_gbps()
+    result["device_stream_read_gbps"] = round(rg, 1)
+    result["hbm_frac_of_stream_read"] = round(eff / rg, 4)
     if not args.no_sweep and cfg.name.startswith("codellama13b"):
         sweep = []
         for P in workloads.CODELLAMA13B_SWEEP:

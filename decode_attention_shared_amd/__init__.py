@@ -41,6 +41,7 @@ HP_BLOCK_SIZE = 16
 HP_CHUNK = 64
 HP_TREE_MAX_LAUNCHES = 4
 HP_NOALLOC_SCRATCH_BYTES = 64 * 1024 * 1024
+HP_READ_PROBE_WGS = 2048
 STATUS = {0: "HP_OK", 1: "HP_ERR_NULL", 2: "HP_ERR_INVALID_ARG", 3: "HP_ERR_UNSUPPORTED",
           4: "HP_ERR_WORKSPACE", 5: "HP_ERR_HIP", 6: "HP_ERR_CAPACITY", 7: "HP_ERR_HOST"}
 EXPORTS = ["hp_prefix_attn_workspace_size", "hp_prefix_attn", "hp_suffix_decode_workspace_size",
@@ -50,7 +51,7 @@ EXPORTS = ["hp_prefix_attn_workspace_size", "hp_prefix_attn", "hp_suffix_decode_
            "hp_pakv_create", "hp_pakv_destroy", "hp_pakv_insert", "hp_pakv_append",
            "hp_pakv_remove", "hp_pakv_context", "hp_pakv_seq_rows", "hp_pakv_get_stats",
            "hp_cascade_step_overlap", "hp_cascade_overlap_plan", "hp_cascade_step_noalloc",
-           "hp_status_string", "hp_last_hip_error", "hp_version"]
+           "hp_read_probe", "hp_status_string", "hp_last_hip_error", "hp_version"]
 
 _DTYPE = {torch.float32: HP_F32, torch.float16: HP_F16, torch.bfloat16: HP_BF16}
 
@@ -183,6 +184,8 @@ def lib():
             L.hp_cascade_step_overlap.argtypes = [ctypes.POINTER(Query), ctypes.POINTER(PrefixTree),
                                                   ctypes.POINTER(PagedKV), p, p, p,
                                                   ctypes.c_size_t, p, ctypes.POINTER(Overlap)]
+            L.hp_read_probe.restype = st
+            L.hp_read_probe.argtypes = [p, ctypes.c_size_t, p, p]
             L.hp_cascade_step_noalloc.restype = st
             L.hp_cascade_step_noalloc.argtypes = [ctypes.POINTER(Query), ctypes.POINTER(PrefixTree),
                                                   ctypes.POINTER(PagedKV), p, p, p]
@@ -590,6 +593,24 @@ def cascade_step_noalloc(q: torch.Tensor, levels, k_pool=None, v_pool=None, bloc
            "hp_cascade_step_noalloc")
     del keep
     return out, lse
+
+
+def read_probe(buf: torch.Tensor, sink: Optional[torch.Tensor] = None, stream=None):
+    """hp_read_probe: one streaming read of ``buf`` (contiguous device memory, a multiple
+    of 16 bytes); returns ``sink`` (int32 [HP_READ_PROBE_WGS], the XOR partials).  For
+    measuring the device's streaming-read rate."""
+    L = lib()
+    if not buf.is_cuda or not buf.is_contiguous():
+        raise ValueError("buf must be a contiguous device tensor")
+    nbytes = buf.numel() * buf.element_size()
+    with _on(stream, buf.device):
+        if sink is None:
+            sink = torch.empty(HP_READ_PROBE_WGS, dtype=torch.int32, device=buf.device)
+    if sink.dtype != torch.int32 or sink.numel() < HP_READ_PROBE_WGS or not sink.is_cuda:
+        raise ValueError(f"sink must be a device int32 tensor of {HP_READ_PROBE_WGS} words")
+    _check(L.hp_read_probe(buf.data_ptr(), nbytes, sink.data_ptr(), _stream(stream)),
+           "hp_read_probe")
+    return sink
 
 
 # ------------------------------------------------------------------------------

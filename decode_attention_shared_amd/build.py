@@ -20,7 +20,8 @@ INCLUDE = os.path.join(ROOT, "include")
 BUILD_DIR = os.path.join(ROOT, "_build")
 LIB_PATH = os.path.join(HERE, "libhp_attn.so")
 SOURCES = ["api.cpp", "tree.cpp", "pakv.cpp", "prefix_kernel.hip", "suffix_kernel.hip",
-           "merge_kernel.hip", "append_kernel.hip", "stream_kernel.hip", "noalloc.hip"]
+           "merge_kernel.hip", "append_kernel.hip", "stream_kernel.hip", "noalloc.hip",
+           "probe_kernel.hip"]
 SOURCE_FLAGS = {}  # per-source extra flags
 ARCH = "gfx950"
 

@@ -618,6 +618,17 @@ hp_status hp_lse_merge(int32_t n, const float *const *o_in, const float *const *
 
 // ------------------------------- cascade ----------------------------------
 
+hp_status hp_read_probe(const void *buf, size_t bytes, uint32_t *sink, void *stream) {
+    return hp::guarded([&]() -> hp_status {
+        if (!sink || (!buf && bytes > 0)) return HP_ERR_NULL;
+        if (bytes % 16 || !aligned16(buf) || ((uintptr_t)sink & 3u)) return HP_ERR_INVALID_ARG;
+        if (bytes > (size_t)INT64_MAX) return HP_ERR_INVALID_ARG;
+        hipError_t e = launch_read_probe(buf, (int64_t)bytes, sink, HP_READ_PROBE_WGS,
+                                         (hipStream_t)stream);
+        return e == hipSuccess ? HP_OK : fail_hip(e);
+    });
+}
+
 hp_status hp_cascade_overlap_plan(const hp_query *q, const hp_prefix_tree *tree,
                                   const hp_paged_kv *kv, int32_t mode, int32_t *overlapped) {
     return hp::guarded([&]() -> hp_status {

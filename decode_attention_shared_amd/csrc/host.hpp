@@ -23,6 +23,8 @@ hipError_t launch_merge(const MergeArgs &a, int d, hipStream_t s);
 hipError_t launch_token_suffix(const SuffixArgs &a, int dtype, int d, int G, int nws,
                                hipStream_t s);
 hipError_t launch_stream_select(const StreamSelectArgs &a, hipStream_t s);
+hipError_t launch_read_probe(const void *buf, int64_t bytes, uint32_t *sink, int wgs,
+                             hipStream_t s);
 hipError_t launch_kv_append(const void *k_new, const void *v_new, const int32_t *rows, int32_t n,
                             int64_t row_bytes, void *k_pool, void *v_pool, int64_t pool_rows,
                             int32_t *seq_lens, const int32_t *seq_idx, int32_t num_seqs,

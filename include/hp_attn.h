@@ -493,6 +493,20 @@ hp_status hp_kv_append(const void *k_new, const void *v_new, const int32_t *rows
                        int32_t num_seqs, void *stream);
 
 /*
+ * Measurement aid (no part of the attention): reads `bytes` of device memory
+ * at `buf` once, front to back, with 16-byte non-temporal loads, and writes
+ * the XOR of all its 32-bit words, one partial per workgroup, to
+ * sink[0 .. HP_READ_PROBE_WGS) (device memory; the XOR of the sink words is
+ * the XOR of the buffer's words, so the loads cannot be elided).  A caller
+ * times it to learn the device's streaming-read rate, reported beside the 8
+ * TB/s specification.  buf 16-byte aligned, bytes a multiple of 16 (0 is
+ * allowed: every sink word is then 0); HP_ERR_NULL for a NULL buf (bytes > 0)
+ * or sink, HP_ERR_INVALID_ARG for misalignment.  Enqueued on `stream`.
+ */
+#define HP_READ_PROBE_WGS 2048
+hp_status hp_read_probe(const void *buf, size_t bytes, uint32_t *sink, void *stream);
+
+/*
  * Prefix-aware KV cache manager (host only; ChunkAttention page, section
  * "Prefix-Aware KV Cache (PAKV): The Prefix Tree Structure", its Insert,
  * Append and Delete operations and its memory allocator; section "Design

@@ -303,3 +303,12 @@ def test_negative_scale_rejected_by_every_step(L):
     sz = ctypes.c_size_t(0)
     assert L.hp_cascade_workspace_size(ctypes.byref(q0), None, ctypes.byref(kv),
                                        ctypes.byref(sz)) == OK
+
+
+def test_read_probe_validation(L):
+    """hp_read_probe: pointer, size and alignment checks (before anything is enqueued)."""
+    assert L.hp_read_probe(None, 16, FAKE, None) == NULL
+    assert L.hp_read_probe(FAKE, 16, None, None) == NULL
+    assert L.hp_read_probe(FAKE, 15, FAKE, None) == INVALID
+    assert L.hp_read_probe(FAKE + 8, 16, FAKE, None) == INVALID
+    assert L.hp_read_probe(FAKE, 16, FAKE + 2, None) == INVALID
