@@ -41,7 +41,7 @@ HP_BLOCK_SIZE = 16
 HP_CHUNK = 64
 HP_TREE_MAX_LAUNCHES = 4
 HP_NOALLOC_SCRATCH_BYTES = 64 * 1024 * 1024
-HP_READ_PROBE_WGS = 2048
+HP_READ_PROBE_WGS = 512
 STATUS = {0: "HP_OK", 1: "HP_ERR_NULL", 2: "HP_ERR_INVALID_ARG", 3: "HP_ERR_UNSUPPORTED",
           4: "HP_ERR_WORKSPACE", 5: "HP_ERR_HIP", 6: "HP_ERR_CAPACITY", 7: "HP_ERR_HOST"}
 EXPORTS = ["hp_prefix_attn_workspace_size", "hp_prefix_attn", "hp_suffix_decode_workspace_size",

@@ -503,7 +503,7 @@ hp_status hp_kv_append(const void *k_new, const void *v_new, const int32_t *rows
  * allowed: every sink word is then 0); HP_ERR_NULL for a NULL buf (bytes > 0)
  * or sink, HP_ERR_INVALID_ARG for misalignment.  Enqueued on `stream`.
  */
-#define HP_READ_PROBE_WGS 2048
+#define HP_READ_PROBE_WGS 512
 hp_status hp_read_probe(const void *buf, size_t bytes, uint32_t *sink, void *stream);
 
 /*
