@@ -255,10 +255,16 @@ def _hip():
     return _hiprt
 
 
+# hipEventDisableTiming | hipEventDisableSystemFence: an eager side-by-side step then
+# skips two system-scope cache write-backs (document-shaped steps 307 -> 256 us hot).
+_SIDE_EVENT_FLAGS = 0x2 | 0x20000000
+
+
 class SideStreams:
     """A second stream and the fork/join events for hp_cascade_step_overlap, owned here:
     a torch stream on ``device`` (default priority) and two hipEvent_t handles created
-    with hipEventDisableTiming, destroyed with this object."""
+    with hipEventDisableTiming and hipEventDisableSystemFence (they only order two
+    streams of one device), destroyed with this object."""
 
     def __init__(self, device, mode: int = 1):
         self.stream = torch.cuda.Stream(device=device)
@@ -267,7 +273,7 @@ class SideStreams:
         for _ in range(2):
             h = ctypes.c_void_p()
             with torch.cuda.device(device):
-                if rt.hipEventCreateWithFlags(ctypes.byref(h), 2) != 0:  # hipEventDisableTiming
+                if rt.hipEventCreateWithFlags(ctypes.byref(h), _SIDE_EVENT_FLAGS) != 0:
                     raise RuntimeError("hipEventCreateWithFlags failed")
             self._events.append(h.value)
         self.desc = Overlap(self.stream.cuda_stream, self._events[0], self._events[1], mode)

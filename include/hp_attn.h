@@ -243,7 +243,12 @@ hp_status hp_cascade_step(const hp_query *query, const hp_prefix_tree *tree,
  *                (hipEventDisableTiming suffices), recorded and waited on by
  *                the step: fork on `stream` before any launch and waited on by
  *                side_stream, join on side_stream after the suffix pass and
- *                waited on by `stream` before the merge;
+ *                waited on by `stream` before the merge.  They only order
+ *                two streams of one device, so events created with
+ *                hipEventDisableSystemFence as well serve (the kernels' own
+ *                device-scope release and acquire carry the data), and spare
+ *                each eager step two system-scope cache write-backs; under
+ *                graph capture the events become graph edges either way;
  *   mode         0: never (exactly hp_cascade_step); 1: when the plan expects
  *                a gain, that is when, with the prefix pass planned for 160 of
  *                the 256 compute units, every prefix split still covers at
