@@ -255,8 +255,8 @@ def _hip():
     return _hiprt
 
 
-# hipEventDisableTiming | hipEventDisableSystemFence: an eager side-by-side step then
-# skips two system-scope cache write-backs (document-shaped steps 307 -> 256 us hot).
+# hipEventDisableTiming | hipEventDisableSystemFence: the fork and join only order two
+# streams of one device, which needs no system-scope fence.
 _SIDE_EVENT_FLAGS = 0x2 | 0x20000000
 
 

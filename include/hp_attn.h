@@ -246,8 +246,7 @@ hp_status hp_cascade_step(const hp_query *query, const hp_prefix_tree *tree,
  *                waited on by `stream` before the merge.  They only order
  *                two streams of one device, so events created with
  *                hipEventDisableSystemFence as well serve (the kernels' own
- *                device-scope release and acquire carry the data), and spare
- *                each eager step two system-scope cache write-backs; under
+ *                device-scope release and acquire carry the data); under
  *                graph capture the events become graph edges either way;
  *   mode         0: never (exactly hp_cascade_step); 1: when the plan expects
  *                a gain, that is when, with the prefix pass planned for 160 of
