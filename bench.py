@@ -569,8 +569,8 @@ def main():
 
     world = int(os.environ.get("WORLD_SIZE", "1"))
     if args.gpus != 1 or world != 1:
-        print("bench.py measures one GPU only: this build has no multi-GPU path (it would "
-              "shard by KV head with no exchange; see the design notes). Run with --gpus 1.",
+        print("bench.py measures one GPU only: the library has no multi-GPU path (a step "
+              "would shard by KV head with no exchange between GPUs). Run with --gpus 1.",
               file=sys.stderr)
         sys.exit(2)
 
