@@ -501,10 +501,12 @@ class CascadeCall:
     costs one ctypes call (used for timing and graph capture).
 
     overlap: 0 runs the passes one after the other on the caller's stream
-    (hp_cascade_step); 1 (the default) or 2 passes the library a second stream and two
-    events owned by this object (hp_cascade_step_overlap, mode 1: when the plan expects a
-    gain, 2: whenever there is a prefix and a suffix).  ``concurrent`` says whether the
-    passes run side by side.  share_min: which tree nodes the prefix pass batches (see
+    (hp_cascade_step); 1 (the default), 2 or 3 calls hp_cascade_step_overlap in that
+    mode (1: side by side when the plan expects a gain, on a second stream or in one
+    launch; 2: on a second stream whenever there is a prefix and a suffix; 3: in one
+    launch whenever the step qualifies), with a second stream and two events owned by
+    this object when the plan uses them.  ``concurrent`` says whether the passes run
+    side by side, ``one_launch`` whether they share one launch.  share_min: which tree nodes the prefix pass batches (see
     make_tree; 0, the default, is the library's batching policy)."""
 
     def __init__(self, q: torch.Tensor, levels, k_pool=None, v_pool=None, block_table=None,
@@ -531,9 +533,18 @@ class CascadeCall:
         _check(L.hp_cascade_overlap_plan(ctypes.byref(self.query), self._tree_p, self._kv_p,
                                          int(overlap), ctypes.byref(flag)),
                "hp_cascade_overlap_plan")
-        self.concurrent = bool(flag.value)  # suffix pass beside the prefix pass
-        self.side = SideStreams(q.device, int(overlap)) if self.concurrent else None
-        self._ov_p = ctypes.byref(self.side.desc) if self.side is not None else None
+        # the suffix pass beside the prefix pass: on a second stream (1) or in the
+        # prefix pass's launch (2, no stream or event needed)
+        self.concurrent = bool(flag.value)
+        self.one_launch = flag.value == 2
+        self.side = SideStreams(q.device, int(overlap)) if flag.value == 1 else None
+        if self.side is not None:
+            self._ov = self.side.desc
+        elif self.one_launch:
+            self._ov = Overlap(None, None, None, int(overlap))
+        else:
+            self._ov = None
+        self._ov_p = ctypes.byref(self._ov) if self._ov is not None else None
         self._refs = (levels, k_pool, v_pool, block_table, seq_lens)
 
     def __call__(self, stream=None):

@@ -302,6 +302,7 @@ struct CascadePlan {
     LevelPlan levels[HP_MAX_LEVELS];
     bool has_suffix = false;
     bool conc = false;   // suffix pass beside the prefix pass, then one merge
+    bool one_launch = false;  // conc, with both passes in one launch (step_pp_kernel)
     size_t node_off[HP_MAX_NODES];
     size_t suf_off = 0;  // concurrent plan: the suffix pass's (O, LSE) rows
     size_t bytes = 0;
@@ -381,9 +382,44 @@ size_t plan_prefix(const hp_query *q, const hp_prefix_tree *tree, CascadePlan &c
 // mode: 0 the passes one after the other on one stream; 1 side by side when
 // the plan expects a gain; 2 side by side whenever there is a prefix and a
 // suffix.
+// Both passes in one launch (step_pp_kernel) for a plan whose prefix is laid
+// out for kConcCUs: one prefix launch of the ping-pong kernel, no private
+// nodes, G in {1, 2, 4}, 16-bit, d = 128, K/V of both passes within the
+// last-level cache (the kernel's loads are plain), and every suffix wave's
+// units and blocks within its LDS tables (kFatMaxRows, kFatMaxSteps).
+int one_launch_suffix_wgs(const CascadePlan &cp) {
+    int wg = 0;
+    const LevelPlan &lp = cp.levels[0];
+    for (int i = 0; i < lp.count; ++i) wg += lp.nodes[i].wgs;
+    return kCUs - wg;
+}
+
+bool one_launch_ok(const hp_query *q, const hp_paged_kv *kv, const CascadePlan &cp) {
+    if (!kv || cp.nseg > 0 || cp.num_levels != 1 || q->B <= 0) return false;
+    const int G = q->Hq / q->Hkv;
+    const LevelPlan &lp = cp.levels[0];
+    if (lp.count < 1 || lp.count > kMaxLaunchNodes || !step_supported(q->dtype, q->d, G, lp.nw))
+        return false;
+    if (kv->max_blocks < 1 || kv->num_blocks < 1) return false;
+    if ((int64_t)q->B * q->Hq >= (int64_t(1) << 24)) return false;
+    const hp_prefix_tree view = cp.view();
+    int64_t kv_bytes = 0;
+    for (int i = 0; i < lp.count; ++i) {
+        const hp_prefix_node &n = view.nodes[lp.first + i];
+        if ((int64_t)kTileKeys * n.stride_tok + q->d > (int64_t)INT32_MAX) return false;
+        kv_bytes += (int64_t)n.len * q->Hkv * q->d * esize(q->dtype) * 2;
+    }
+    if (kv_bytes >= kLlcBytes) return false;
+    if (suffix_args(*q, kv, RowDest{}).stream_kv) return false;
+    const int swgs = one_launch_suffix_wgs(cp);
+    if (swgs < 32) return false;
+    const int64_t per_wave = cdiv((int64_t)q->B * q->Hkv, (int64_t)swgs * 8);
+    return per_wave * G <= kFatMaxRows && per_wave * kv->max_blocks <= kFatMaxSteps - 4;
+}
+
 hp_status plan_cascade(const hp_query *q, const hp_prefix_tree *tree, const hp_paged_kv *kv,
                        int mode, CascadePlan &cp, bool batch_all = false) {
-    if (mode < 0 || mode > 2) return HP_ERR_INVALID_ARG;
+    if (mode < 0 || mode > 3) return HP_ERR_INVALID_ARG;
     hp_status st = check_query(q);
     if (st != HP_OK) return st;
     int total = 0;
@@ -434,9 +470,17 @@ hp_status plan_cascade(const hp_query *q, const hp_prefix_tree *tree, const hp_p
         for (int l = 0; l < alt.num_levels && pays; ++l)
             for (int i = 0; i < alt.levels[l].count; ++i)
                 pays = pays && alt.levels[l].nodes[i].tiles_per_split >= kConcMinTiles;
-        if (mode == 2 || pays) {
+        // Both passes in one launch (no second stream): in mode 1 for MHA steps
+        // whose suffix is too small for the second stream's fork and join to pay
+        // (with several query heads per KV head a suffix wave's unit is too much
+        // work for one wave, and the serial plan is faster).
+        const bool one = one_launch_ok(q, kv, alt) &&
+                         (mode == 3 || (mode == 1 && !pays && q->Hq == q->Hkv &&
+                                        (int64_t)q->B * q->Hkv < kConcMinUnits));
+        if (mode == 2 || (mode == 1 && pays) || one) {
             cp = alt;
             cp.conc = true;
+            cp.one_launch = one;
             cp.suf_off = pbytes;
             cp.bytes = pbytes + round_up((size_t)q->B * q->Hq * q->d * sizeof(float), kWsAlign) +
                        round_up((size_t)q->B * q->Hq * sizeof(float), kWsAlign);
@@ -636,7 +680,7 @@ hp_status hp_cascade_overlap_plan(const hp_query *q, const hp_prefix_tree *tree,
         CascadePlan cp;
         hp_status st = plan_cascade(q, tree, kv, mode, cp);
         if (st != HP_OK) return st;
-        *overlapped = cp.conc ? 1 : 0;
+        *overlapped = cp.one_launch ? 2 : cp.conc ? 1 : 0;
         return HP_OK;
     });
 }
@@ -661,6 +705,71 @@ hp_status record(void *const *events, int i, hipStream_t s) {
 
 hp_status run_prefix_levels(const hp_query *q, const CascadePlan &cp, char *base, MergeArgs &m,
                             hipStream_t s);
+
+// Both passes in one launch on s (step_pp_kernel: the prefix workgroups of
+// the plan's single prefix launch, then one suffix workgroup per compute
+// unit they leave free), then one merge of every prefix partial with the
+// suffix rows on s.
+hp_status cascade_one_launch(const hp_query *q, const hp_paged_kv *kv, const CascadePlan &cp,
+                             float *o, float *lse, char *base, hipStream_t s,
+                             void *const *events) {
+    float *so = (float *)(base + cp.suf_off);
+    float *sl = (float *)((char *)so +
+                          round_up((size_t)q->B * q->Hq * q->d * sizeof(float), kWsAlign));
+    const hp_prefix_tree view = cp.view();
+    const LevelPlan &lp = cp.levels[0];
+    MergeArgs m;
+    std::memset(&m, 0, sizeof m);
+    PrefixArgs a = base_prefix_args(*q);
+    int wg = 0;
+    for (int i = 0; i < lp.count; ++i) {
+        const NodePlan &np = lp.nodes[i];
+        const hp_prefix_node &nd = view.nodes[lp.first + i];
+        float *wo = (float *)(base + cp.node_off[lp.first + i]);
+        float *wl = (float *)((char *)wo +
+                              round_up((size_t)np.nsplit * np.rows * q->d * 4, kWsAlign));
+        a.nodes[a.num_nodes++] =
+            node_arg(nd, np, wg, RowDest{wo, wl, np.rows * q->d, np.rows, nd.seq_begin});
+        m.src[m.nsrc++] = MergeSrc{wo, wl, np.rows * q->d, np.rows, np.nsplit, 0,
+                                   nd.seq_begin, nd.seq_end};
+        wg += np.wgs;
+    }
+    a.stream_kv = 0;  // one_launch_ok: the launch's K/V are within the last-level cache
+    const SuffixArgs sa = suffix_args(*q, kv, RowDest{so, sl, 0, 0, 0});
+    FatSuffixArgs f;
+    std::memset(&f, 0, sizeof f);
+    f.q = q->q;
+    f.k_pool = kv->k_pool;
+    f.v_pool = kv->v_pool;
+    f.table = kv->block_table;
+    f.lens = kv->seq_lens;
+    f.o = so;
+    f.lse = sl;
+    f.B = q->B;
+    f.Hq = q->Hq;
+    f.Hkv = q->Hkv;
+    f.max_blocks = kv->max_blocks;
+    f.num_blocks = kv->num_blocks;
+    f.kv_hnd = sa.kv_hnd;
+    f.scale_log2 = sa.scale_log2;
+    f.prefix_wgs = wg;
+    hp_status st = record(events, 0, s);
+    if (st != HP_OK) return st;
+    if ((st = record(events, 4, s)) != HP_OK) return st;
+    hipError_t e = launch_step(a, wg, f, one_launch_suffix_wgs(cp), q->dtype, q->d,
+                               q->Hq / q->Hkv, s);
+    if (e != hipSuccess) return fail_hip(e);
+    if ((st = record(events, 1, s)) != HP_OK) return st;
+    if ((st = record(events, 2, s)) != HP_OK) return st;
+    m.src[m.nsrc++] = MergeSrc{so, sl, 0, 0, 1, 0, 0, q->B};
+    m.Hq = q->Hq;
+    m.row_b0 = 0;
+    m.row_b1 = q->B;
+    m.o = o;
+    m.lse = lse;
+    if ((e = launch_merge(m, q->d, s)) != hipSuccess) return fail_hip(e);
+    return record(events, 3, s);
+}
 
 // Suffix pass beside the prefix pass: fork the caller's side stream from s,
 // prefix launches on s, the suffix pass (its own (O, LSE) rows, no merge) on
@@ -733,7 +842,7 @@ hp_status cascade_impl(const hp_query *q, const hp_prefix_tree *tree, const hp_p
     if (st != HP_OK) return st;
     st = check_out(o, lse);
     if (st != HP_OK) return st;
-    if (cp.conc) {
+    if (cp.conc && !cp.one_launch) {
         if (!ov->side_stream || !ov->fork_event || !ov->join_event) return HP_ERR_NULL;
         if (ov->side_stream == stream) return HP_ERR_INVALID_ARG;
     }
@@ -741,6 +850,7 @@ hp_status cascade_impl(const hp_query *q, const hp_prefix_tree *tree, const hp_p
     if (cp.bytes > 0 && (!ws || ws_bytes < cp.bytes || !aligned16(ws))) return HP_ERR_WORKSPACE;
     hipStream_t s = (hipStream_t)stream;
     char *base = (char *)ws;
+    if (cp.one_launch) return cascade_one_launch(q, kv, cp, o, lse, base, s, events);
     if (cp.conc) return cascade_concurrent(q, tree, kv, cp, o, lse, base, s, *ov, events);
     if ((st = record(events, 0, s)) != HP_OK) return st;
 

@@ -9,6 +9,7 @@
 #include <cstdint>
 
 #include "common.hpp"
+#include "fat_suffix.hpp"
 #include "hp_attn.h"
 
 namespace hp {
@@ -23,6 +24,9 @@ hipError_t launch_merge(const MergeArgs &a, int d, hipStream_t s);
 hipError_t launch_token_suffix(const SuffixArgs &a, int dtype, int d, int G, int nws,
                                hipStream_t s);
 hipError_t launch_stream_select(const StreamSelectArgs &a, hipStream_t s);
+bool step_supported(int dtype, int d, int G, int nw);
+hipError_t launch_step(const PrefixArgs &a, int prefix_wgs, const FatSuffixArgs &f,
+                       int suffix_wgs, int dtype, int d, int G, hipStream_t s);
 hipError_t launch_read_probe(const void *buf, int64_t bytes, uint32_t *sink, int wgs,
                              hipStream_t s);
 hipError_t launch_kv_append(const void *k_new, const void *v_new, const int32_t *rows, int32_t n,

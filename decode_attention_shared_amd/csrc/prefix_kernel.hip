@@ -25,6 +25,7 @@
 // folding log2(e) into the scale; P is rounded to the input type for the
 // second product, as the matrix cores require.
 #include "common.hpp"
+#include "fat_suffix.hpp"
 
 namespace hp {
 
@@ -588,10 +589,12 @@ __global__ __launch_bounds__(64 * NW) void tree_mfma16_kernel(PrefixArgs args) {
 // matrix core and the vector ALUs of a SIMD can work at the same time.
 // ---------------------------------------------------------------------------
 
-template <bool kBf16, int D, bool kNT, class Tiles>
+// The LDS ring is the body's own static array, or (kExtLds) the one a
+// kernel that also runs other work passes in (ext_lds, kStages x 2 tiles).
+template <bool kBf16, int D, bool kNT, class Tiles, bool kExtLds = false>
 __device__ __forceinline__ void pp_body(const PrefixArgs &args, const WgTask &task,
                                         const PrefixNodeArg &nd, const Tiles &src, int tb,
-                                        int te) {
+                                        int te, uint16_t *ext_lds = nullptr) {
     constexpr int NW = 8;
     constexpr int kDSteps = D / 16;
     constexpr int kDBlocks = D / 32;
@@ -604,7 +607,10 @@ __device__ __forceinline__ void pp_body(const PrefixArgs &args, const WgTask &ta
     // tile u-2, whose stage it takes: four stages, two tiles in flight.
     constexpr int kStages = 4;
     constexpr int kTileElems = kTile * D;
-    __shared__ __attribute__((aligned(1024))) uint16_t lds[kStages][2][kTileElems];
+    using Ring = uint16_t[kStages][2][kTileElems];
+    __shared__ __attribute__((aligned(1024)))
+    uint16_t own_lds[kExtLds ? 1 : kStages][2][kExtLds ? 1 : kTileElems];
+    Ring &lds = *reinterpret_cast<Ring *>(kExtLds ? ext_lds : &own_lds[0][0][0]);
 
     const int G = args.G;
     const int M = (nd.seq_end - nd.seq_begin) * G;
@@ -1092,6 +1098,63 @@ hipError_t launch_tree_prefix(const PrefixArgs &a, int dtype, int d, int nw, int
     case 4: return launch_tree_nw<4>(a, dtype, d, wgs, s);
     default: return launch_tree_nw<8>(a, dtype, d, wgs, s);
     }
+}
+
+// Both passes of a cascade step in one launch: workgroups [0, prefix_wgs)
+// are the ping-pong prefix pass (as prefix_mfma16_pp_kernel), the rest run
+// the suffix pass, each of their 8 waves its own list of (sequence, KV head)
+// units.  No workgroup waits for another, so the two passes share the chip
+// without a second stream; the merge follows on the same stream.  For steps
+// whose K/V stay within the last-level cache (plain loads in both passes).
+template <bool kBf16, int G>
+__global__ __launch_bounds__(512) void step_pp_kernel(PrefixArgs args, FatSuffixArgs fa) {
+    constexpr int D = 128;
+    // the prefix pass's ring; a suffix workgroup stages its rows there
+    __shared__ __attribute__((aligned(1024))) uint16_t lds[4 * 2 * kTile * D];
+    static_assert(sizeof(lds) >= 8 * kFatStageBytes, "suffix staging");
+    if ((int)blockIdx.x >= fa.prefix_wgs) {
+        const int S = ((int)gridDim.x - fa.prefix_wgs) * 8;
+        const int wave = (int)threadIdx.x / kWave;
+        const int sw = ((int)blockIdx.x - fa.prefix_wgs) * 8 + wave;
+        fat_suffix_wave<kBf16, D, G, false>(fa, sw, S, (char *)lds + wave * kFatStageBytes);
+        return;
+    }
+    const WgTask task = decode_wg(args);
+    if (!task.valid) return;
+    const PrefixNodeArg &nd = args.nodes[task.node];
+    const int ntiles = (nd.len + kTile - 1) / kTile;
+    const int tb = task.split * nd.tiles_per_split;
+    const int te = min(tb + nd.tiles_per_split, ntiles);
+    pp_body<kBf16, D, false, ContigTiles, true>(args, task, nd, ContigTiles{nd.len}, tb, te, lds);
+}
+
+template <bool kBf16>
+static hipError_t launch_step_dt(const PrefixArgs &a, const FatSuffixArgs &f, int G, dim3 grid,
+                                 hipStream_t s) {
+    switch (G) {
+    case 1: step_pp_kernel<kBf16, 1><<<grid, 512, 0, s>>>(a, f); break;
+    case 2: step_pp_kernel<kBf16, 2><<<grid, 512, 0, s>>>(a, f); break;
+    default: step_pp_kernel<kBf16, 4><<<grid, 512, 0, s>>>(a, f); break;
+    }
+    return hipGetLastError();
+}
+
+bool step_supported(int dtype, int d, int G, int nw) {
+    return kPingPongEnabled && nw == 8 && d == 128 && (G == 1 || G == 2 || G == 4) &&
+           (dtype == HP_F16 || dtype == HP_BF16);
+}
+
+hipError_t launch_step(const PrefixArgs &a, int prefix_wgs, const FatSuffixArgs &f,
+                       int suffix_wgs, int dtype, int d, int G, hipStream_t s) {
+    bool fits32 = true;
+    for (int i = 0; i < a.num_nodes; ++i)
+        fits32 = fits32 && (int64_t)kTile * a.nodes[i].stride_tok + d <= (int64_t)INT32_MAX;
+    if (!step_supported(dtype, d, G, 8) || !fits32 || a.stream_kv || prefix_wgs < 0 ||
+        suffix_wgs < 1 || f.prefix_wgs != prefix_wgs)
+        return hipErrorInvalidValue;
+    const dim3 grid((unsigned)(prefix_wgs + suffix_wgs));
+    return dtype == HP_BF16 ? launch_step_dt<true>(a, f, G, grid, s)
+                            : launch_step_dt<false>(a, f, G, grid, s);
 }
 
 }  // namespace hp

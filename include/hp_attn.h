@@ -252,15 +252,28 @@ hp_status hp_cascade_step(const hp_query *query, const hp_prefix_tree *tree,
  *                a gain, that is when, with the prefix pass planned for 160 of
  *                the 256 compute units, every prefix split still covers at
  *                least 4 tiles of 64 keys and the suffix has at least 2048
- *                (sequence, KV head) units; 2: whenever the step has both a
- *                prefix and a suffix.
+ *                (sequence, KV head) units (second stream), or, for a step
+ *                with one query head per KV head that qualifies for one
+ *                launch (below) and has fewer units, in one launch; 2: on the
+ *                second stream whenever the step has both a prefix and a
+ *                suffix; 3: in one launch whenever the step qualifies, else
+ *                as mode 0.
+ * One launch: the prefix pass's workgroups and suffix workgroups of the same
+ * shape (one per compute unit the prefix plan leaves free) share a kernel,
+ * so no second stream or event is used (side_stream and the events may then
+ * be NULL), then one merge on `stream`.  A step qualifies when its batched
+ * nodes form one prefix launch of the 256-row kernel (at least 129 stacked
+ * query rows per KV head), the dtype is 16-bit, d = 128, Hq/Hkv is 1, 2 or 4,
+ * no node is read privately, the K/V of both passes stay under 256 MiB, and
+ * each suffix wave's share fits its tables (at most 31 query rows and 500
+ * blocks).
  * Everything enqueued on `stream` before the call is ordered before both
  * passes and everything after it after the merge, eagerly and under graph
  * capture alike (the events become the graph's fork and join).  Calls that
  * share the same events or side stream must not run concurrently from
- * several host threads.  HP_ERR_NULL when the plan runs side by side and a
- * handle is NULL; HP_ERR_INVALID_ARG for side_stream == stream or another
- * mode.
+ * several host threads.  HP_ERR_NULL when the plan uses the second stream
+ * and a handle is NULL; HP_ERR_INVALID_ARG for side_stream == stream (the
+ * second stream used) or another mode.
  */
 typedef struct hp_overlap {
     void *side_stream;
@@ -275,8 +288,8 @@ hp_status hp_cascade_step_overlap(const hp_query *query, const hp_prefix_tree *t
 
 /*
  * *overlapped = 1 when hp_cascade_step_overlap with these arguments and this
- * mode would run the passes side by side, else 0.  Validates the arguments
- * like hp_cascade_workspace_size.
+ * mode would run the passes side by side on the second stream, 2 when in one
+ * launch, else 0.  Validates the arguments like hp_cascade_workspace_size.
  */
 hp_status hp_cascade_overlap_plan(const hp_query *query, const hp_prefix_tree *tree,
                                   const hp_paged_kv *kv, int32_t mode, int32_t *overlapped);

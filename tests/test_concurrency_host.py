@@ -60,7 +60,9 @@ def _plan(L, args, mode=1):
     ((256, 40, 40, 128, 512, 8), 0),      # 2 tiles per split
     ((64, 32, 8, 128, 4096, 16), 0),      # GQA, 512 suffix units
     ((128, 32, 8, 128, 16384, 8), 0),     # GQA, 1024 suffix units
-    ((256, 5, 5, 128, 16384, 8), 0),      # one 8-way head share: 1280 units
+    ((256, 5, 5, 128, 16384, 8), 2),      # one 8-way head share, 1280 units: one launch
+    ((160, 8, 8, 128, 900, 9), 2),        # a small MHA step: one launch
+    ((160, 8, 8, 64, 900, 9), 0),         # the same at d = 64: serial
     ((256, 32, 8, 128, 4096, 8), 1),      # GQA, 2048 suffix units
     ((16, 8, 8, 64, 16384, 4), 0),        # too few suffix units
 ])
@@ -107,10 +109,26 @@ def test_modes_and_workspace(L):
     assert _plan(L, _args(B, Hq, Hkv, d, 300, 4), mode=2) == (0, 0)
 
 
+def test_one_launch_mode(L):
+    """Mode 3 puts both passes in one launch whenever the step qualifies (one prefix
+    launch of the 256-row kernel, 16-bit, d = 128, G in {1, 2, 4}, K/V within the
+    last-level cache, no private nodes), else it runs them one after the other."""
+    assert _plan(L, _args(64, 32, 8, 128, 4096, 16), mode=3)[0] == 2    # GQA, 4 per KV head
+    assert _plan(L, _args(96, 16, 8, 128, 700, 13), mode=3)[0] == 2     # GQA, 2 per KV head
+    assert _plan(L, _args(160, 8, 8, 128, 900, 9), mode=3)[0] == 2      # MHA
+    assert _plan(L, _args(256, 40, 40, 128, 16384, 8), mode=3)[0] == 0  # K/V beyond 256 MiB
+    assert _plan(L, _args(160, 8, 8, 64, 900, 9), mode=3)[0] == 0       # d = 64
+    assert _plan(L, _args(64, 64, 8, 128, 4096, 16), mode=3)[0] == 0    # 8 per KV head
+    assert _plan(L, _args(64, 32, 8, 128, 4096, 16, suffix=False), mode=3)[0] == 0
+    # the one-launch plan lays out the same workspace as the side-by-side one
+    assert _plan(L, _args(160, 8, 8, 128, 900, 9), mode=3)[1] == \
+        _plan(L, _args(160, 8, 8, 128, 900, 9), mode=2)[1]
+
+
 def test_mode_validation(L):
     query, tree, kv, _ = _args(4, 2, 2, 64, 100, 2)
     flag = ctypes.c_int32(0)
-    for bad in (3, -1):
+    for bad in (4, -1):
         assert L.hp_cascade_overlap_plan(ctypes.byref(query), ctypes.byref(tree),
                                          ctypes.byref(kv), bad, ctypes.byref(flag)) == 2
     assert L.hp_cascade_overlap_plan(ctypes.byref(query), ctypes.byref(tree), ctypes.byref(kv),
