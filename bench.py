@@ -45,7 +45,7 @@ MFMA_F16_PEAK_TFLOPS = 2500.0   # dense fp16/bf16 matrix peak
 MFMA_F32_PEAK_TFLOPS = 157.3
 METRIC = "decode attention steps/s + effective HBM GB/s (% roofline) at B=256, 16K prefix"
 KERNEL_SOURCES = ["prefix_kernel.hip", "suffix_kernel.hip", "merge_kernel.hip", "api.cpp", "host.hpp",
-                  "common.hpp"]
+                  "common.hpp", "fat_suffix.hpp"]
 
 
 class HipEvents:
