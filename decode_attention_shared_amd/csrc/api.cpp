@@ -413,9 +413,15 @@ bool one_launch_ok(const hp_query *q, const hp_paged_kv *kv, const CascadePlan &
     if (suffix_args(*q, kv, RowDest{}).stream_kv) return false;
     const int swgs = one_launch_suffix_wgs(cp);
     if (swgs < 32) return false;
-    const int64_t per_wave = cdiv((int64_t)q->B * q->Hkv, (int64_t)swgs * 8);
-    return per_wave * G <= kFatMaxRows && per_wave * kv->max_blocks <= kFatMaxSteps - 4;
+    const int64_t nsp = cdiv(kv->max_blocks, kFatSplitBlocks);
+    if ((int64_t)q->B * q->Hq * nsp >= (int64_t(1) << 24)) return false;
+    const int64_t per_wave = cdiv((int64_t)q->B * q->Hkv * nsp, (int64_t)swgs * 8);
+    return per_wave * G <= kFatMaxRows && per_wave * kFatSplitBlocks <= kFatMaxSteps - 4;
 }
+
+// The one-launch plan's suffix items per (sequence, KV head): each covers
+// kFatSplitBlocks blocks and has its own slot of (O, LSE) rows.
+int64_t one_launch_splits(const hp_paged_kv *kv) { return cdiv(kv->max_blocks, kFatSplitBlocks); }
 
 hp_status plan_cascade(const hp_query *q, const hp_prefix_tree *tree, const hp_paged_kv *kv,
                        int mode, CascadePlan &cp, bool batch_all = false) {
@@ -478,27 +484,32 @@ hp_status plan_cascade(const hp_query *q, const hp_prefix_tree *tree, const hp_p
                          (mode == 3 || (mode == 1 && !pays && q->Hq == q->Hkv &&
                                         (int64_t)q->B * q->Hkv < kConcMinUnits));
         if (mode == 2 || (mode == 1 && pays) || one) {
+            // the suffix rows: one slot (second stream) or one per item split
+            const size_t nsp = one ? (size_t)one_launch_splits(kv) : 1;
             cp = alt;
             cp.conc = true;
             cp.one_launch = one;
             cp.suf_off = pbytes;
-            cp.bytes = pbytes + round_up((size_t)q->B * q->Hq * q->d * sizeof(float), kWsAlign) +
-                       round_up((size_t)q->B * q->Hq * sizeof(float), kWsAlign);
+            cp.bytes = pbytes +
+                       round_up(nsp * q->B * q->Hq * q->d * sizeof(float), kWsAlign) +
+                       round_up(nsp * q->B * q->Hq * sizeof(float), kWsAlign);
         }
     }
     return HP_OK;
 }
 
-// Workspace that serves every mode: the larger of the serial plan and the
-// always-side-by-side plan.
+// Workspace that serves every mode: the largest of the serial plan, the
+// always-side-by-side plan and the one-launch plan.
 hp_status cascade_ws_bytes(const hp_query *q, const hp_prefix_tree *tree, const hp_paged_kv *kv,
                            size_t *bytes) {
-    CascadePlan serial, conc;
+    CascadePlan serial, conc, one;
     hp_status st = plan_cascade(q, tree, kv, 0, serial);
     if (st != HP_OK) return st;
     st = plan_cascade(q, tree, kv, 2, conc);
     if (st != HP_OK) return st;
-    *bytes = std::max(serial.bytes, conc.bytes);
+    st = plan_cascade(q, tree, kv, 3, one);
+    if (st != HP_OK) return st;
+    *bytes = std::max({serial.bytes, conc.bytes, one.bytes});
     return HP_OK;
 }
 
@@ -713,9 +724,10 @@ hp_status run_prefix_levels(const hp_query *q, const CascadePlan &cp, char *base
 hp_status cascade_one_launch(const hp_query *q, const hp_paged_kv *kv, const CascadePlan &cp,
                              float *o, float *lse, char *base, hipStream_t s,
                              void *const *events) {
+    const int64_t nsp = one_launch_splits(kv);
     float *so = (float *)(base + cp.suf_off);
-    float *sl = (float *)((char *)so +
-                          round_up((size_t)q->B * q->Hq * q->d * sizeof(float), kWsAlign));
+    float *sl = (float *)((char *)so + round_up((size_t)nsp * q->B * q->Hq * q->d * sizeof(float),
+                                                kWsAlign));
     const hp_prefix_tree view = cp.view();
     const LevelPlan &lp = cp.levels[0];
     MergeArgs m;
@@ -753,6 +765,7 @@ hp_status cascade_one_launch(const hp_query *q, const hp_paged_kv *kv, const Cas
     f.kv_hnd = sa.kv_hnd;
     f.scale_log2 = sa.scale_log2;
     f.prefix_wgs = wg;
+    f.nsplit = (int32_t)nsp;
     hp_status st = record(events, 0, s);
     if (st != HP_OK) return st;
     if ((st = record(events, 4, s)) != HP_OK) return st;
@@ -761,7 +774,12 @@ hp_status cascade_one_launch(const hp_query *q, const hp_paged_kv *kv, const Cas
     if (e != hipSuccess) return fail_hip(e);
     if ((st = record(events, 1, s)) != HP_OK) return st;
     if ((st = record(events, 2, s)) != HP_OK) return st;
-    m.src[m.nsrc++] = MergeSrc{so, sl, 0, 0, 1, 0, 0, q->B};
+    // the items' rows: only the splits that hold blocks of the sequence are read,
+    // and a length out of range makes the row NaN
+    const int64_t bhq = (int64_t)q->B * q->Hq;
+    m.src[m.nsrc++] = MergeSrc{so, sl, bhq * q->d, bhq, (int32_t)nsp, kFatSplitBlocks, 0, q->B};
+    m.lens = kv->seq_lens;
+    m.max_len = kv->max_blocks * kBlock;
     m.Hq = q->Hq;
     m.row_b0 = 0;
     m.row_b1 = q->B;

@@ -9,16 +9,20 @@
 //
 // A workgroup of the prefix pass's shape is the only one on its compute
 // unit, so its 8 waves must keep that unit's loads in flight on their own.
-// Every wave walks a fixed list of (sequence, KV head) units as one stream of
-// steps, one 16-token block per step (an empty unit takes one step with no
-// keys): before the first step the wave gathers its units' lengths and block
-// ids into a table of steps in LDS, then keeps the loads of the next kRing - 1
-// steps in flight while it computes the current one.  Every step issues the
+// The work is split into items: block range s of (sequence, KV head) unit u
+// (blocks [s * split_blocks, (s + 1) * split_blocks) of the sequence), each
+// with its own (O, LSE) rows in split slot s, which the merge combines like
+// any other partial (items past a sequence's blocks hold nothing and are
+// neither computed nor read).  Every wave walks a fixed list of items as one
+// stream of steps, one 16-token block per step: before the first step the
+// wave gathers its items' lengths and block ids into a table of steps in
+// LDS, then keeps the loads of the next kRing - 1 steps in flight while it
+// computes the current one.  Every step issues the
 // same loads (a step without a block loads one that exists and masks it) and
 // no vector-memory store sits in the loop (finished rows wait in LDS and are
 // written after it), so the compiler's waits for the ring are exact counts
 // rather than full drains.  Each token group of lanes keeps its own running
-// max; the groups are combined once per unit.
+// max; the groups are combined once per item.
 //
 // 16-bit K/V, d = 128: a token's d values are spread over 16 lanes of 16-byte
 // slices, one load instruction covers 4 tokens, and partial dot products are
@@ -29,14 +33,16 @@
 
 namespace hp {
 
-// Steps (16-token blocks, or one per empty unit) one suffix wave may take:
-// the wave's table of them lives in LDS beside the prefix pass's ring.
+// Steps (16-token blocks) one suffix wave may take: the wave's table of them
+// lives in LDS beside the prefix pass's ring.
 constexpr int kFatMaxSteps = 504;
-// Rows (units x G) of one suffix wave, whose finished (O, LSE) wait in the
+// Rows (items x G) of one suffix wave, whose finished (O, LSE) wait in the
 // wave's kFatStageBytes share of the prefix pass's LDS ring until the wave
 // writes them all out at its end.
 constexpr int kFatMaxRows = 31;
 constexpr int kFatStageBytes = 16384;
+// Blocks of one item (64 keys): a long suffix is spread over several waves.
+constexpr int kFatSplitBlocks = 4;
 
 struct FatSuffixArgs {
     const void *q;          // [B][Hq][d]
@@ -44,13 +50,14 @@ struct FatSuffixArgs {
     const void *v_pool;
     const int32_t *table;   // [B][max_blocks]
     const int32_t *lens;    // [B]
-    float *o;               // [B][Hq][d] the suffix rows, normalised
-    float *lse;             // [B][Hq] natural-log LSE (-inf: no keys)
+    float *o;               // [nsplit][B][Hq][d] the items' rows, normalised
+    float *lse;             // [nsplit][B][Hq] natural-log LSE
     int32_t B, Hq, Hkv;
     int32_t max_blocks, num_blocks;
     int32_t kv_hnd;
     float scale_log2;
     int32_t prefix_wgs;     // workgroups of the launch before the suffix ones
+    int32_t nsplit;         // items per unit: ceil(max_blocks / kFatSplitBlocks)
 };
 
 namespace fs {
@@ -111,10 +118,11 @@ __device__ __forceinline__ int lane_read(int v, int i) { return __builtin_amdgcn
 
 }  // namespace fs
 
-// Wave `sw` of `S` suffix waves: units sw, sw + S, ... of the B * Hkv
-// (sequence, KV head) units, each with the G query heads of its KV head.
-// The host keeps a wave's units within kFatMaxRows / G and their blocks
-// within kFatMaxSteps; `stage` is the wave's kFatStageBytes of LDS.
+// Wave `sw` of `S` suffix waves: items sw, sw + S, ... of the B * Hkv * nsplit
+// items (item i: unit i / nsplit, split i % nsplit), each with the G query
+// heads of its KV head.  The host keeps a wave's items within kFatMaxRows / G
+// and their blocks within kFatMaxSteps; `stage` is the wave's kFatStageBytes
+// of LDS.
 template <bool kBf16, int D, int G, bool kNT>
 __device__ __forceinline__ void fat_suffix_wave(const FatSuffixArgs &a, int sw, int S,
                                                 char *stage) {
@@ -124,7 +132,7 @@ __device__ __forceinline__ void fat_suffix_wave(const FatSuffixArgs &a, int sw, 
     constexpr int kTpp = kWave / kLpt;  // tokens per load (4)
     constexpr int kPasses = kBlock / kTpp;
     constexpr int kRing = G >= 4 ? 3 : 4;  // steps whose registers the ring holds
-    constexpr int kMaxUnits = kFatMaxRows / G;
+    constexpr int kMaxItems = kFatMaxRows / G;
     static_assert(kFatMaxSteps % 12 == 0, "table a multiple of every ring depth");
     static_assert(kFatMaxRows * (D + 2) * 4 <= kFatStageBytes, "staging");
     float *st_o = (float *)stage;                   // [kFatMaxRows][D]
@@ -134,35 +142,41 @@ __device__ __forceinline__ void fat_suffix_wave(const FatSuffixArgs &a, int sw, 
     const int lane = threadIdx.x % kWave;
     const int tg = lane / kLpt;
     const int d0 = (lane % kLpt) * kEpl;
-    const int units = a.B * a.Hkv;
-    if (sw >= units) return;
+    const int items = a.B * a.Hkv * a.nsplit;
+    if (sw >= items) return;
     // (the clamp only keeps a violated host bound inside the staging area)
-    const int K = min((units - sw + S - 1) / S, kMaxUnits);
+    const int K = min((items - sw + S - 1) / S, kMaxItems);
 
-    // Unit k of this wave in lane k: sequence, head, length, blocks, steps.
+    // Item k of this wave in lane k: sequence, head, split, length, its blocks
+    // [j0, j1).  A sequence whose length is out of range gets no item: the
+    // merge, which checks the same length, makes its rows NaN.
     const bool has = lane < K;
-    const int u = has ? sw + lane * S : sw;
+    const int it = has ? sw + lane * S : sw;
+    const int u = it / a.nsplit, sp = it % a.nsplit;
     const int ub = u / a.Hkv, ug = u % a.Hkv;
     const int len = a.lens[ub];
-    const bool ubad = has && (len < 0 || len > a.max_blocks * kBlock);
-    const int nblk = (has && !ubad) ? (len + kBlock - 1) / kBlock : 0;
-    int incl = has ? max(nblk, 1) : 0;
+    const bool ubad = len < 0 || len > a.max_blocks * kBlock;
+    const int nblk = ubad ? 0 : (len + kBlock - 1) / kBlock;
+    const int j0 = sp * kFatSplitBlocks;
+    const int nit = has ? max(min(nblk - j0, kFatSplitBlocks), 0) : 0;  // steps
+    int incl = nit;
 #pragma unroll
     for (int off = 1; off < kWave; off <<= 1) {
         const int t = __shfl_up(incl, off, kWave);
         incl += lane >= off ? t : 0;
     }
-    const int excl = incl - (has ? max(nblk, 1) : 0);
+    const int excl = incl - nit;
     const int T = fs::lane_read(incl, kWave - 1);
+    if (T == 0) return;  // no item of this wave holds a key
     const int Tpad = min((T + kRing - 1) / kRing * kRing, kFatMaxSteps);
 
     // The wave's table of steps in LDS, one 8-byte entry per step:
     //   x: the block to load (0 when the step has none: a block that exists)
-    //   y: the unit's first output row b * Hq + g * G (bits 0-23), valid keys
-    //      (bits 24-28), first step of its unit (bit 29), unit bad (bit 30),
-    //      last step of its unit (bit 31)
-    // Steps past the last unit (up to a multiple of kRing) repeat its row with
-    // no keys, which leaves its values as they are.
+    //   y: the item's first output row split * B * Hq + b * Hq + g * G (bits
+    //      0-23), valid keys (bits 24-28), first step of its item (bit 29), a
+    //      block id out of range (bit 30), last step of its item (bit 31)
+    // Steps past the last item (up to a multiple of kRing) repeat a row with
+    // no keys and no flags, which changes nothing.
     __shared__ uint2 steps[8][kFatMaxSteps];
     uint2 *tab = steps[threadIdx.x / kWave];
 #pragma unroll 1
@@ -174,20 +188,21 @@ __device__ __forceinline__ void fat_suffix_wave(const FatSuffixArgs &a, int sw, 
         const bool pad = k >= K;
         const int kc = pad ? K - 1 : k;
         const int ex = __shfl(excl, kc, kWave);
-        const int nb = __shfl(nblk, kc, kWave);
+        const int n = __shfl(nit, kc, kWave);
         const int ln = __shfl(len, kc, kWave);
         const int bb = __shfl(ub, kc, kWave);
         const int gg = __shfl(ug, kc, kWave);
-        const bool bd = __shfl(ubad ? 1 : 0, kc, kWave) != 0;
-        const int j = s - ex;
-        const bool real = !pad && j < nb;
-        const int bid = a.table[(int64_t)bb * a.max_blocks + (real ? j : 0)];
+        const int spl = __shfl(sp, kc, kWave);
+        const int i = s - ex;  // step within the item
+        const bool real = !pad && i < n;
+        const int j = spl * kFatSplitBlocks + (real ? i : 0);  // block of the sequence
+        const int bid = a.table[(int64_t)bb * a.max_blocks + min(j, a.max_blocks - 1)];
         const bool id_ok = bid >= 0 && bid < a.num_blocks;
         const int valid = real && id_ok ? min(kBlock, ln - j * kBlock) : 0;
-        const bool bad = bd || (real && !id_ok);
-        const uint32_t y = (uint32_t)(bb * a.Hq + gg * G) | ((uint32_t)valid << 24) |
-                           ((!pad && j == 0) ? (1u << 29) : 0u) | (bad ? (1u << 30) : 0u) |
-                           ((!pad && j == max(nb, 1) - 1) ? (1u << 31) : 0u);
+        const bool bad = real && !id_ok;
+        const uint32_t y = (uint32_t)((spl * a.B + bb) * a.Hq + gg * G) |
+                           ((uint32_t)valid << 24) | ((real && i == 0) ? (1u << 29) : 0u) |
+                           (bad ? (1u << 30) : 0u) | ((real && i == n - 1) ? (1u << 31) : 0u);
         if (s < Tpad) tab[s] = uint2{(uint32_t)(real && id_ok ? bid : 0), y};
     }
 
@@ -212,7 +227,7 @@ __device__ __forceinline__ void fat_suffix_wave(const FatSuffixArgs &a, int sw, 
         const uint32_t id = __builtin_amdgcn_readfirstlane(e.x);
         const uint32_t y = __builtin_amdgcn_readfirstlane(e.y);
         r_y[r] = y;
-        const int row = (int)(y & 0xffffffu);
+        const int row = (int)(y & 0xffffffu) % (a.B * a.Hq);  // the query row
         const int g = (row % a.Hq) / G;
         const int64_t base = (int64_t)id * blk_bytes + g * head_mul + d0 * 2;
 #pragma unroll
@@ -235,11 +250,11 @@ __device__ __forceinline__ void fat_suffix_wave(const FatSuffixArgs &a, int sw, 
         for (int e = 0; e < kEpl; ++e) acc[j][e] = 0.f;
     }
     bool sbad = false;
-    int ku = -1;  // the unit of the step being computed (this wave's count)
+    int ku = -1;  // the item of the step being computed (this wave's count)
 
-    // One block of slot r into the running state of its unit; at the unit's
+    // One block of slot r into the running state of its item; at the item's
     // last step the token groups are combined (weights 2^(m_group - M)) and
-    // the unit's G rows go to their staging slots.
+    // the item's G rows go to their staging slots.
     auto compute = [&](int r) {
         const uint32_t y = r_y[r];
         const int valid = (int)((y >> 24) & 31u);
@@ -345,7 +360,7 @@ __device__ __forceinline__ void fat_suffix_wave(const FatSuffixArgs &a, int sw, 
     }
 
     // The finished rows, two per pass (32 lanes x 4 floats each).
-    const int rows = K * G;
+    const int rows = (ku + 1) * G;
 #pragma unroll 1
     for (int k0 = 0; k0 < rows; k0 += 2) {
         const int k = k0 + lane / 32;

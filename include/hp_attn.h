@@ -266,7 +266,7 @@ hp_status hp_cascade_step(const hp_query *query, const hp_prefix_tree *tree,
  * query rows per KV head), the dtype is 16-bit, d = 128, Hq/Hkv is 1, 2 or 4,
  * no node is read privately, the K/V of both passes stay under 256 MiB, and
  * each suffix wave's share fits its tables (at most 31 query rows and 500
- * blocks).
+ * blocks; the suffix work goes to the waves in items of 4 blocks).
  * Everything enqueued on `stream` before the call is ordered before both
  * passes and everything after it after the merge, eagerly and under graph
  * capture alike (the events become the graph's fork and join).  Calls that
