@@ -471,7 +471,7 @@ hp_status plan_cascade(const hp_query *q, const hp_prefix_tree *tree, const hp_p
     // merge combines them with the prefix partials.
     if (cp.has_suffix && cp.total_nodes > 0 && q->B > 0 && mode != 0) {
         CascadePlan alt = cp;
-        const size_t pbytes = plan_prefix(q, tree ? &bt : nullptr, alt, kConcCUs);
+        size_t pbytes = plan_prefix(q, tree ? &bt : nullptr, alt, kConcCUs);
         bool pays = (int64_t)q->B * q->Hkv >= kConcMinUnits;
         for (int l = 0; l < alt.num_levels && pays; ++l)
             for (int i = 0; i < alt.levels[l].count; ++i)
@@ -480,9 +480,19 @@ hp_status plan_cascade(const hp_query *q, const hp_prefix_tree *tree, const hp_p
         // whose suffix is too small for the second stream's fork and join to pay
         // (with several query heads per KV head a suffix wave's unit is too much
         // work for one wave, and the serial plan is faster).
-        const bool one = one_launch_ok(q, kv, alt) &&
-                         (mode == 3 || (mode == 1 && !pays && q->Hq == q->Hkv &&
-                                        (int64_t)q->B * q->Hkv < kConcMinUnits));
+        const bool want_one = mode == 3 || (mode == 1 && !pays && q->Hq == q->Hkv &&
+                                            (int64_t)q->B * q->Hkv < kConcMinUnits);
+        CascadePlan one_plan = cp;
+        size_t one_pbytes = 0;
+        bool one = false;
+        if (want_one) {
+            one_pbytes = plan_prefix(q, tree ? &bt : nullptr, one_plan, kOneLaunchCUs);
+            one = one_launch_ok(q, kv, one_plan);
+        }
+        if (one) {
+            alt = one_plan;
+            pbytes = one_pbytes;
+        }
         if (mode == 2 || (mode == 1 && pays) || one) {
             // the suffix rows: one slot (second stream) or one per item split
             const size_t nsp = one ? (size_t)one_launch_splits(kv) : 1;

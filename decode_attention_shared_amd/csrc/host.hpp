@@ -110,6 +110,10 @@ void plan_splits(const SplitItem *items, int count, int Hkv, int d, int nw, int6
 // units gains 5 %; with 512 (Llama-3-8B shape) or 1 280 units (one 8-way head
 // share of the 16K MHA shape) the side-by-side step loses 13-16 %.
 constexpr int kConcCUs = 160;
+// Both passes in one launch: the prefix plan's compute units (the rest host
+// one suffix workgroup each).  Measured on the one-GPU head share of the 16K
+// MHA shape: 160 units 52.5 us per step, 192 or 208 units 56.8.
+constexpr int kOneLaunchCUs = 160;
 constexpr int kConcMinTiles = 4;
 constexpr int64_t kConcMinUnits = 2048;
 
