@@ -154,3 +154,58 @@ def test_auto_policy_takes_one_launch_for_small_steps():
     lens = torch.full((256,), 100, dtype=torch.int32, device=DEV)
     call = hp.CascadeCall(q, [[(kv, kv, 0, 256)]], pool, pool, table, lens, 0.088, overlap=1)
     assert call.concurrent and not call.one_launch, big.name
+
+
+NEG = -16384.0  # exact in bf16 and fp16; scale * NEG underflows exp to exactly 0
+
+
+@pytest.mark.parametrize("shape", [(160, 8, 8, "f16"), (64, 16, 4, "bf16")],
+                         ids=["G1", "G4"])
+def test_one_launch_needles_every_position(shape):
+    """Every logical suffix position found exactly by the one-launch suffix waves (their
+    step tables walk the block table in items of 4 blocks): one needle key per (sequence,
+    KV head) scores 0 and every other key, prefix included, scores far below, so the
+    output is the needle's value row exactly and the LSE exactly 0."""
+    B, Hq, Hkv, dt = shape
+    cfg = workloads.custom(f"needle_one_{Hq // Hkv}", B=B, Hq=Hq, Hkv=Hkv, d=128, dtype=dt,
+                           levels=(((600, 0, B),),), suffix_lo=1, suffix_hi=70)
+    step = workloads.generate(cfg, seed=21)
+    ds = dev_step(step)
+    ds["q"].zero_()
+    ds["q"][:, :, 0] = 1.0
+    pk = ds["k_pool"]
+    for lvl in ds["levels"]:
+        for (k, v, _, _) in lvl:
+            k[:, :, 0] = NEG
+    lens = step.seq_lens.tolist()
+    tbl = step.block_table
+    valid = torch.zeros(pk.shape[:3], dtype=torch.bool)
+    for b in range(B):
+        for t in range(lens[b]):
+            valid[int(tbl[b, t // 16]), t % 16, :] = True
+    pk[..., 0][valid.to(DEV)] = NEG
+    call = _call(ds, step.scale)
+    assert call.one_launch
+    suf_v = step.suf_v.float()
+    offs = step.suf_offsets.tolist()
+    G = Hq // Hkv
+    for r in range(max(lens)):
+        blks, slots, heads, want_rows = [], [], [], []
+        for b in range(B):
+            for g in range(Hkv):
+                t = (r + 3 * g) % lens[b]
+                blks.append(int(tbl[b, t // 16]))
+                slots.append(t % 16)
+                heads.append(g)
+                want_rows.append(suf_v[offs[b] + t, g])
+        idx = (torch.tensor(blks, device=DEV), torch.tensor(slots, device=DEV),
+               torch.tensor(heads, device=DEV))
+        pk[idx + (0,)] = 0.0
+        out, lse = call()
+        got = out.cpu()
+        want = torch.stack(want_rows).view(B, Hkv, 1, 128).expand(B, Hkv, G, 128).reshape(
+            B, Hq, 128)
+        assert torch.equal(got, want), f"needle run {r}: wrong key picked"
+        assert torch.all(lse.cpu() == 0.0), f"needle run {r}: LSE must be exactly 0"
+        pk[idx + (0,)] = NEG
+    say(f"  one-launch suffix needles (G = {G}): {max(lens)} runs")
