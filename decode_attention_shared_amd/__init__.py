@@ -47,6 +47,7 @@ STATUS = {0: "HP_OK", 1: "HP_ERR_NULL", 2: "HP_ERR_INVALID_ARG", 3: "HP_ERR_UNSU
 EXPORTS = ["hp_prefix_attn_workspace_size", "hp_prefix_attn", "hp_suffix_decode_workspace_size",
            "hp_suffix_decode", "hp_lse_merge", "hp_cascade_workspace_size", "hp_cascade_step",
            "hp_cascade_step_timed", "hp_stream_decode_workspace_size", "hp_stream_decode",
+           "hp_stream_decode_overlap", "hp_stream_overlap_plan",
            "hp_tree_plan_build", "hp_share_decision", "hp_tree_step", "hp_kv_append",
            "hp_pakv_create", "hp_pakv_destroy", "hp_pakv_insert", "hp_pakv_append",
            "hp_pakv_remove", "hp_pakv_context", "hp_pakv_seq_rows", "hp_pakv_get_stats",
@@ -207,6 +208,15 @@ def lib():
             L.hp_stream_decode.argtypes = [ctypes.POINTER(Query), ctypes.POINTER(PrefixTree),
                                            ctypes.POINTER(StreamRows), p, p, p,
                                            ctypes.c_size_t, p]
+            L.hp_stream_decode_overlap.restype = st
+            L.hp_stream_decode_overlap.argtypes = [ctypes.POINTER(Query),
+                                                   ctypes.POINTER(PrefixTree),
+                                                   ctypes.POINTER(StreamRows), p, p, p,
+                                                   ctypes.c_size_t, p, ctypes.POINTER(Overlap)]
+            L.hp_stream_overlap_plan.restype = st
+            L.hp_stream_overlap_plan.argtypes = [ctypes.POINTER(Query), ctypes.POINTER(PrefixTree),
+                                                 ctypes.POINTER(StreamRows), i32,
+                                                 ctypes.POINTER(ctypes.c_int32)]
             L.hp_tree_plan_build.restype = st
             L.hp_tree_plan_build.argtypes = [ctypes.POINTER(Query), p, i32, i32, i64, p,
                                              ctypes.c_size_t, ctypes.POINTER(TreePlan)]
@@ -662,12 +672,18 @@ def make_stream_rows(k_pool: torch.Tensor, v_pool: torch.Tensor, row_slots: torc
 class StreamCall:
     """A prepared hp_stream_decode: every stream query attends its document (the
     prefix tree ``doc_levels``, as in CascadeCall) and the positions of its
-    request's KV row whose stream id is -1 or its own."""
+    request's KV row whose stream id is -1 or its own.
+
+    overlap: 0 runs the passes one after the other on the caller's stream
+    (hp_stream_decode); 1 (the default) or 2 calls hp_stream_decode_overlap in that
+    mode, with a second stream and fork/join events owned by this object when the plan
+    uses them.  ``concurrent`` says whether the stream pass runs beside the document's
+    prefix pass."""
 
     def __init__(self, q: torch.Tensor, doc_levels, k_pool: torch.Tensor, v_pool: torch.Tensor,
                  row_slots: torch.Tensor, slot_sid: torch.Tensor, row_len: torch.Tensor,
                  q_req: torch.Tensor, q_sid: torch.Tensor, scale: Optional[float] = None,
-                 out=None, lse=None):
+                 out=None, lse=None, overlap: int = 1):
         L = lib()
         self._L = L
         if q_req.shape != (q.shape[0],):
@@ -684,9 +700,23 @@ class StreamCall:
         self.workspace_bytes = nbytes.value
         self.ws = _workspace(nbytes.value, q.device)
         self._refs = (q, doc_levels, k_pool, v_pool, row_slots, slot_sid, row_len, q_req, q_sid)
+        flag = ctypes.c_int32(0)
+        _check(L.hp_stream_overlap_plan(ctypes.byref(self.query), self._tree_p,
+                                        ctypes.byref(self.rows), int(overlap),
+                                        ctypes.byref(flag)), "hp_stream_overlap_plan")
+        self.concurrent = bool(flag.value)
+        self.side = SideStreams(q.device, int(overlap)) if self.concurrent else None
+        self._ov_p = ctypes.byref(self.side.desc) if self.side is not None else None
 
     def __call__(self, stream=None):
         _record(stream, (self.ws, self.out, self.lse))
+        if self._ov_p is not None:
+            _check(self._L.hp_stream_decode_overlap(ctypes.byref(self.query), self._tree_p,
+                                                    ctypes.byref(self.rows), self.out.data_ptr(),
+                                                    _ptr(self.lse), _ptr(self.ws),
+                                                    self.workspace_bytes, _stream(stream),
+                                                    self._ov_p), "hp_stream_decode_overlap")
+            return self.out, self.lse
         _check(self._L.hp_stream_decode(ctypes.byref(self.query), self._tree_p,
                                         ctypes.byref(self.rows), self.out.data_ptr(),
                                         _ptr(self.lse), _ptr(self.ws), self.workspace_bytes,
@@ -695,10 +725,11 @@ class StreamCall:
 
 
 def stream_decode(q: torch.Tensor, doc_levels, k_pool, v_pool, row_slots, slot_sid, row_len,
-                  q_req, q_sid, scale: Optional[float] = None, out=None, lse=None, stream=None):
+                  q_req, q_sid, scale: Optional[float] = None, out=None, lse=None, stream=None,
+                  overlap: int = 1):
     with _on(stream, q.device):
         return StreamCall(q, doc_levels, k_pool, v_pool, row_slots, slot_sid, row_len, q_req,
-                          q_sid, scale, out, lse)(stream)
+                          q_sid, scale, out, lse, overlap)(stream)
 
 
 def _descs_array(descs) -> Tuple[ctypes.Array, int]:

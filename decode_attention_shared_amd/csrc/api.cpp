@@ -934,17 +934,131 @@ hp_status check_stream_rows(const hp_query *q, const hp_stream_rows *r) {
 // per-query visible-row counts and tables.
 struct StreamPlan {
     CascadePlan cp;
+    bool conc = false;      // the stream pass beside the document's prefix pass
+    size_t suf_off = 0;     // conc: the stream pass's own (O, LSE) rows
     size_t len_off = 0, table_off = 0, bytes = 0;
 };
 
+// mode as hp_overlap.mode 0-2: the stream selection and the stream pass run
+// on the second stream beside the prefix pass (planned for kConcCUs) by the
+// same rule as the cascade step's.
 hp_status plan_stream(const hp_query *q, const hp_prefix_tree *doc, const hp_stream_rows *r,
-                      StreamPlan &sp) {
+                      StreamPlan &sp, int mode = 0) {
+    if (mode < 0 || mode > 2) return HP_ERR_INVALID_ARG;
     hp_status st = plan_cascade(q, doc, nullptr, 0, sp.cp, /*batch_all=*/true);
     if (st != HP_OK) return st;
     if ((st = check_stream_rows(q, r)) != HP_OK) return st;
+    if (mode != 0 && sp.cp.total_nodes > 0 && q->B > 0) {
+        CascadePlan alt = sp.cp;
+        const hp_prefix_tree bt = alt.view();
+        const size_t pbytes = plan_prefix(q, &bt, alt, kConcCUs);
+        bool pays = (int64_t)q->B * q->Hkv >= kConcMinUnits;
+        for (int l = 0; l < alt.num_levels && pays; ++l)
+            for (int i = 0; i < alt.levels[l].count; ++i)
+                pays = pays && alt.levels[l].nodes[i].tiles_per_split >= kConcMinTiles;
+        if (mode == 2 || pays) {
+            sp.cp = alt;
+            sp.conc = true;
+            sp.suf_off = pbytes;
+            sp.cp.bytes = pbytes + round_up((size_t)q->B * q->Hq * q->d * sizeof(float), kWsAlign) +
+                          round_up((size_t)q->B * q->Hq * sizeof(float), kWsAlign);
+        }
+    }
     sp.len_off = round_up(sp.cp.bytes, kWsAlign);
     sp.table_off = sp.len_off + round_up((size_t)q->B * 4, kWsAlign);
     sp.bytes = sp.table_off + round_up((size_t)q->B * (size_t)r->row_cap * 4, kWsAlign);
+    return HP_OK;
+}
+
+// One stream-decode step (hp_stream_decode, or _overlap with ov).
+hp_status stream_impl(const hp_query *q, const hp_prefix_tree *doc, const hp_stream_rows *rows,
+                      float *o, float *lse, void *ws, size_t ws_bytes, void *stream,
+                      const hp_overlap *ov) {
+    StreamPlan sp;
+    hp_status st = plan_stream(q, doc, rows, sp, ov ? ov->mode : 0);
+    if (st != HP_OK) return st;
+    if ((st = check_out(o, lse)) != HP_OK) return st;
+    if (sp.conc) {
+        if (!ov->side_stream || !ov->fork_event || !ov->join_event) return HP_ERR_NULL;
+        if (ov->side_stream == stream) return HP_ERR_INVALID_ARG;
+    }
+    if (q->B == 0) return HP_OK;
+    if (!ws || ws_bytes < sp.bytes || !aligned16(ws)) return HP_ERR_WORKSPACE;
+    hipStream_t s = (hipStream_t)stream;
+    char *base = (char *)ws;
+    int32_t *tok_len = (int32_t *)(base + sp.len_off);
+    int32_t *tok_table = (int32_t *)(base + sp.table_off);
+    hipError_t e;
+    // side by side: the selection and the stream pass wait for everything
+    // before the call on `stream`, and run on the second stream
+    const hipStream_t ss = sp.conc ? (hipStream_t)ov->side_stream : s;
+    if (sp.conc) {
+        if ((e = hipEventRecord((hipEvent_t)ov->fork_event, s)) != hipSuccess) return fail_hip(e);
+        if ((e = hipStreamWaitEvent(ss, (hipEvent_t)ov->fork_event, 0)) != hipSuccess)
+            return fail_hip(e);
+    }
+
+    MergeArgs m;
+    std::memset(&m, 0, sizeof m);
+    if ((st = run_prefix_levels(q, sp.cp, base, m, s)) != HP_OK) return st;
+
+    StreamSelectArgs sel;
+    std::memset(&sel, 0, sizeof sel);
+    sel.row_slots = rows->row_slots;
+    sel.slot_sid = rows->slot_sid;
+    sel.row_len = rows->row_len;
+    sel.q_req = rows->q_req;
+    sel.q_sid = rows->q_sid;
+    sel.B = q->B;
+    sel.R = rows->num_requests;
+    sel.row_cap = rows->row_cap;
+    sel.tok_table = tok_table;
+    sel.tok_len = tok_len;
+    if ((e = launch_stream_select(sel, ss)) != hipSuccess) return fail_hip(e);
+
+    float *so = (float *)(base + sp.suf_off);
+    float *sl = (float *)((char *)so +
+                          round_up((size_t)q->B * q->Hq * q->d * sizeof(float), kWsAlign));
+    SuffixArgs a;
+    std::memset(&a, 0, sizeof a);
+    a.q = q->q;
+    a.k_pool = rows->k_pool;
+    a.v_pool = rows->v_pool;
+    a.table = tok_table;
+    a.lens = tok_len;
+    a.B = q->B;
+    a.Hq = q->Hq;
+    a.Hkv = q->Hkv;
+    a.max_blocks = rows->row_cap;  // capacity of each query's table
+    a.has_suffix = 1;
+    a.scale_log2 = (float)((double)q->scale * 1.4426950408889634);
+    a.dest = sp.conc ? RowDest{so, sl, 0, 0, 0} : RowDest{o, lse, 0, 0, 0};
+    a.pool_rows = rows->pool_rows;
+    // K/V footprint: the pool rows, or what the token tables can reach if less.
+    const int64_t kv_rows = std::min<int64_t>(rows->pool_rows, (int64_t)q->B * rows->row_cap);
+    a.stream_kv = kv_rows * q->Hkv * q->d * esize(q->dtype) * 2 >= kLlcBytes ? 1 : 0;
+    if (!sp.conc) {  // the document partials merged in the stream pass's epilogue
+        a.nsrc = m.nsrc;
+        for (int i = 0; i < m.nsrc; ++i) a.src[i] = m.src[i];
+        a.stage_floats = stage_floats(m.src, m.nsrc, q->Hq / q->Hkv, q->d);
+    }
+    const int blocks = (int)cdiv(rows->row_cap, HP_BLOCK_SIZE);
+    const int nws = blocks <= 2 ? 1 : blocks <= 16 ? 2 : 4;
+    if ((e = launch_token_suffix(a, q->dtype, q->d, q->Hq / q->Hkv, nws, ss)) != hipSuccess)
+        return fail_hip(e);
+    if (!sp.conc) return HP_OK;
+
+    // join, then one merge of the document partials with the stream rows
+    if ((e = hipEventRecord((hipEvent_t)ov->join_event, ss)) != hipSuccess) return fail_hip(e);
+    if ((e = hipStreamWaitEvent(s, (hipEvent_t)ov->join_event, 0)) != hipSuccess)
+        return fail_hip(e);
+    m.src[m.nsrc++] = MergeSrc{so, sl, 0, 0, 1, 0, 0, q->B};
+    m.Hq = q->Hq;
+    m.row_b0 = 0;
+    m.row_b1 = q->B;
+    m.o = o;
+    m.lse = lse;
+    if ((e = launch_merge(m, q->d, s)) != hipSuccess) return fail_hip(e);
     return HP_OK;
 }
 
@@ -978,10 +1092,23 @@ hp_status hp_stream_decode_workspace_size(const hp_query *q, const hp_prefix_tre
                                           const hp_stream_rows *rows, size_t *bytes) {
     return hp::guarded([&]() -> hp_status {
         if (!bytes) return HP_ERR_NULL;
-        StreamPlan sp;
-        hp_status st = plan_stream(q, doc, rows, sp);
+        StreamPlan serial, conc;  // one size for every mode
+        hp_status st = plan_stream(q, doc, rows, serial, 0);
         if (st != HP_OK) return st;
-        *bytes = sp.bytes;
+        if ((st = plan_stream(q, doc, rows, conc, 2)) != HP_OK) return st;
+        *bytes = std::max(serial.bytes, conc.bytes);
+        return HP_OK;
+    });
+}
+
+hp_status hp_stream_overlap_plan(const hp_query *q, const hp_prefix_tree *doc,
+                                 const hp_stream_rows *rows, int32_t mode, int32_t *overlapped) {
+    return hp::guarded([&]() -> hp_status {
+        if (!overlapped) return HP_ERR_NULL;
+        StreamPlan sp;
+        hp_status st = plan_stream(q, doc, rows, sp, mode);
+        if (st != HP_OK) return st;
+        *overlapped = sp.conc ? 1 : 0;
         return HP_OK;
     });
 }
@@ -990,61 +1117,16 @@ hp_status hp_stream_decode(const hp_query *q, const hp_prefix_tree *doc,
                            const hp_stream_rows *rows, float *o, float *lse, void *ws,
                            size_t ws_bytes, void *stream) {
     return hp::guarded([&]() -> hp_status {
-        StreamPlan sp;
-        hp_status st = plan_stream(q, doc, rows, sp);
-        if (st != HP_OK) return st;
-        if ((st = check_out(o, lse)) != HP_OK) return st;
-        if (q->B == 0) return HP_OK;
-        if (!ws || ws_bytes < sp.bytes || !aligned16(ws)) return HP_ERR_WORKSPACE;
-        hipStream_t s = (hipStream_t)stream;
-        char *base = (char *)ws;
-        int32_t *tok_len = (int32_t *)(base + sp.len_off);
-        int32_t *tok_table = (int32_t *)(base + sp.table_off);
+        return stream_impl(q, doc, rows, o, lse, ws, ws_bytes, stream, nullptr);
+    });
+}
 
-        MergeArgs m;
-        std::memset(&m, 0, sizeof m);
-        if ((st = run_prefix_levels(q, sp.cp, base, m, s)) != HP_OK) return st;
-
-        StreamSelectArgs sel;
-        std::memset(&sel, 0, sizeof sel);
-        sel.row_slots = rows->row_slots;
-        sel.slot_sid = rows->slot_sid;
-        sel.row_len = rows->row_len;
-        sel.q_req = rows->q_req;
-        sel.q_sid = rows->q_sid;
-        sel.B = q->B;
-        sel.R = rows->num_requests;
-        sel.row_cap = rows->row_cap;
-        sel.tok_table = tok_table;
-        sel.tok_len = tok_len;
-        hipError_t e = launch_stream_select(sel, s);
-        if (e != hipSuccess) return fail_hip(e);
-
-        SuffixArgs a;
-        std::memset(&a, 0, sizeof a);
-        a.q = q->q;
-        a.k_pool = rows->k_pool;
-        a.v_pool = rows->v_pool;
-        a.table = tok_table;
-        a.lens = tok_len;
-        a.B = q->B;
-        a.Hq = q->Hq;
-        a.Hkv = q->Hkv;
-        a.max_blocks = rows->row_cap;  // capacity of each query's table
-        a.has_suffix = 1;
-        a.scale_log2 = (float)((double)q->scale * 1.4426950408889634);
-        a.dest = RowDest{o, lse, 0, 0, 0};
-        a.pool_rows = rows->pool_rows;
-        // K/V footprint: the pool rows, or what the token tables can reach if less.
-        const int64_t kv_rows = std::min<int64_t>(rows->pool_rows, (int64_t)q->B * rows->row_cap);
-        a.stream_kv = kv_rows * q->Hkv * q->d * esize(q->dtype) * 2 >= kLlcBytes ? 1 : 0;
-        a.nsrc = m.nsrc;
-        for (int i = 0; i < m.nsrc; ++i) a.src[i] = m.src[i];
-        a.stage_floats = stage_floats(m.src, m.nsrc, q->Hq / q->Hkv, q->d);
-        const int blocks = (int)cdiv(rows->row_cap, HP_BLOCK_SIZE);
-        const int nws = blocks <= 2 ? 1 : blocks <= 16 ? 2 : 4;
-        e = launch_token_suffix(a, q->dtype, q->d, q->Hq / q->Hkv, nws, s);
-        return e == hipSuccess ? HP_OK : fail_hip(e);
+hp_status hp_stream_decode_overlap(const hp_query *q, const hp_prefix_tree *doc,
+                                   const hp_stream_rows *rows, float *o, float *lse, void *ws,
+                                   size_t ws_bytes, void *stream, const hp_overlap *overlap) {
+    return hp::guarded([&]() -> hp_status {
+        if (!overlap) return HP_ERR_NULL;
+        return stream_impl(q, doc, rows, o, lse, ws, ws_bytes, stream, overlap);
     });
 }
 

@@ -388,6 +388,30 @@ hp_status hp_stream_decode(const hp_query *query, const hp_prefix_tree *doc,
                            const hp_stream_rows *rows, float *o, float *lse, void *workspace,
                            size_t workspace_bytes, void *stream);
 
+/*
+ * hp_stream_decode with the stream selection and the stream pass on a second
+ * stream beside the document's prefix pass, as hp_cascade_step_overlap does
+ * for the suffix pass: the stream pass then writes its own (O, LSE) rows to
+ * the workspace and one merge on `stream` combines them with the document
+ * partials.  overlap->mode: 0 serial (hp_stream_decode); 1 side by side by
+ * the cascade step's rule (the prefix pass planned for 160 compute units,
+ * every prefix split at least 4 tiles of 64 keys, at least 2048 (query, KV
+ * head) units), else serial; 2 side by side whenever the document has a node.  One launch (mode 3) is
+ * not offered here.  Ordering, event and stream rules, and errors as for
+ * hp_cascade_step_overlap (HP_ERR_INVALID_ARG for mode 3).  The workspace
+ * size from hp_stream_decode_workspace_size serves every mode.
+ */
+hp_status hp_stream_decode_overlap(const hp_query *query, const hp_prefix_tree *doc,
+                                   const hp_stream_rows *rows, float *o, float *lse,
+                                   void *workspace, size_t workspace_bytes, void *stream,
+                                   const hp_overlap *overlap);
+
+/* *overlapped = 1 when hp_stream_decode_overlap with these arguments and this
+ * mode would run the stream pass on the second stream, else 0.  Validates the
+ * arguments like hp_stream_decode_workspace_size. */
+hp_status hp_stream_overlap_plan(const hp_query *query, const hp_prefix_tree *doc,
+                                 const hp_stream_rows *rows, int32_t mode, int32_t *overlapped);
+
 /* ------------------------------------------------------------------------
  * Chunked prefix tree: device-resident (C, i, j) plans
  * ------------------------------------------------------------------------

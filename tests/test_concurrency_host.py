@@ -157,3 +157,51 @@ def test_timed_event_count_validation(L):
         assert L.hp_cascade_step_timed(ctypes.byref(query), ctypes.byref(tree), ctypes.byref(kv),
                                        FAKE, FAKE, None, 0, None, None, ctypes.addressof(ev),
                                        n) == 2
+
+
+def _stream_args(B, Hq, Hkv, d, P, R=4, cap=512):
+    query, tree, _, keep = _args(B, Hq, Hkv, d, P, 1, suffix=False)
+    rows = hp.StreamRows(FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, R, cap, R * cap)
+    return query, tree, rows, keep
+
+
+def _stream_plan(L, args, mode):
+    query, tree, rows, _ = args
+    flag = ctypes.c_int32(-1)
+    tp = ctypes.byref(tree) if tree is not None else None
+    st = L.hp_stream_overlap_plan(ctypes.byref(query), tp, ctypes.byref(rows), mode,
+                                  ctypes.byref(flag))
+    return st, flag.value
+
+
+@pytest.mark.parametrize("shape,want", [
+    ((256, 32, 8, 128, 16384), 1),   # 2048 (query, KV head) units, 64 tiles per split
+    ((256, 32, 8, 128, 512), 0),     # 2 tiles per split
+    ((128, 32, 8, 128, 16384), 0),   # 1024 units
+])
+def test_stream_decode_policy(L, shape, want):
+    args = _stream_args(*shape)
+    assert _stream_plan(L, args, 1) == (0, want)
+    assert _stream_plan(L, args, 0) == (0, 0)
+    assert _stream_plan(L, args, 2) == (0, 1)
+
+
+def test_stream_decode_modes_validated(L):
+    query, tree, rows, _ = args = _stream_args(8, 4, 2, 64, 300)
+    for bad in (3, 4, -1):
+        assert _stream_plan(L, args, bad)[0] == 2
+    # no document: nothing to put beside the stream pass
+    assert L.hp_stream_overlap_plan(ctypes.byref(query), None, ctypes.byref(rows), 2,
+                                    ctypes.byref(ctypes.c_int32())) == 0
+    nb = ctypes.c_size_t(0)
+    assert L.hp_stream_decode_workspace_size(ctypes.byref(query), ctypes.byref(tree),
+                                             ctypes.byref(rows), ctypes.byref(nb)) == 0
+    step = L.hp_stream_decode_overlap
+    a = (ctypes.byref(query), ctypes.byref(tree), ctypes.byref(rows), FAKE, FAKE, FAKE, 1 << 30)
+    S, E1, E2 = 0x1000, 0x2000, 0x3000  # never dereferenced: validation fails first
+    assert step(*a, None, None) == 1
+    assert step(*a, None, ctypes.byref(hp.Overlap(None, E1, E2, 2))) == 1
+    assert step(*a, None, ctypes.byref(hp.Overlap(S, None, E2, 2))) == 1
+    assert step(*a, None, ctypes.byref(hp.Overlap(S, E1, None, 2))) == 1
+    assert step(*a, S, ctypes.byref(hp.Overlap(S, E1, E2, 2))) == 2
+    assert step(*a, None, ctypes.byref(hp.Overlap(S, E1, E2, 3))) == 2

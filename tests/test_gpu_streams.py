@@ -36,10 +36,15 @@ def dev(step):
                 q_req=step.q_req.to(DEV), q_sid=step.q_sid.to(DEV))
 
 
-def call_of(ds, scale, levels=None):
+def call_of(ds, scale, levels=None, overlap=1):
     return hp.StreamCall(ds["q"], ds["levels"] if levels is None else levels, ds["k_pool"],
                          ds["v_pool"], ds["row_slots"], ds["slot_sid"], ds["row_len"],
-                         ds["q_req"], ds["q_sid"], scale)
+                         ds["q_req"], ds["q_sid"], scale, overlap=overlap)
+
+
+# 0: the serial step (document partials merged in the stream pass's epilogue); 2: the
+# stream pass on a second stream beside the document's prefix pass, then one merge
+MODES = [0, 2]
 
 
 CASES = [
@@ -55,14 +60,17 @@ CASES = [
 
 @pytest.mark.parametrize("case", CASES, ids=lambda c: c[0])
 @pytest.mark.parametrize("seed", [0, 1])
-def test_stream_decode_reduced(case, seed):
+@pytest.mark.parametrize("mode", MODES)
+def test_stream_decode_reduced(case, seed, mode):
     name, dtype, d, B, Hq, Hkv, levels, lo, hi, P, ans, shared = case
-    say(f"streams {name} seed {seed}")
+    say(f"streams {name} seed {seed} mode {mode}")
     cfg = workloads.custom(name, B=B, Hq=Hq, Hkv=Hkv, d=d, dtype=dtype, levels=levels,
                            suffix_lo=lo, suffix_hi=hi)
     step = workloads.stream_step(cfg, P=P, seed=seed, answer_len=ans, shared_len=shared)
     ds = dev(step)
-    out, lse = call_of(ds, step.scale)()
+    call = call_of(ds, step.scale, overlap=mode)
+    assert call.concurrent == (mode == 2)
+    out, lse = call()
     torch.cuda.synchronize()
     ref_o, ref_l = oracle.stream_attention(step)
     compare(out, lse, ref_o, ref_l, dtype, name)
@@ -74,7 +82,9 @@ def test_stream_decode_without_document_and_empty_streams():
     step = workloads.stream_step(cfg, P=5, seed=3, answer_len=0, shared_len=0)
     step.levels = []                       # no document: only the row tokens
     ds = dev(step)
-    out, lse = call_of(ds, step.scale, levels=[])()
+    call = call_of(ds, step.scale, levels=[], overlap=2)
+    assert not call.concurrent  # no document: nothing runs beside the stream pass
+    out, lse = call()
     torch.cuda.synchronize()
     ref_o, ref_l = oracle.stream_attention(step)
     compare(out, lse, ref_o, ref_l, "bf16", "no document")
@@ -83,7 +93,8 @@ def test_stream_decode_without_document_and_empty_streams():
         assert torch.all(out[b] == 0) and torch.all(lse[b] == -float("inf"))
 
 
-def test_stream_decode_bad_metadata_gives_nan_rows_only():
+@pytest.mark.parametrize("mode", MODES)
+def test_stream_decode_bad_metadata_gives_nan_rows_only(mode):
     cfg = workloads.custom("bad", B=16, Hq=8, Hkv=2, d=128, dtype="f16",
                            levels=(((100, 0, 16),),), suffix_lo=2, suffix_hi=30)
     step = workloads.stream_step(cfg, P=4, seed=4, answer_len=2)
@@ -95,7 +106,7 @@ def test_stream_decode_bad_metadata_gives_nan_rows_only():
     vis = oracle.visible_positions(step.row_sid[r0, :int(step.row_len[r0])].tolist(),
                                    int(step.q_sid[5]))
     ds["row_slots"][r0, int(vis[-1])] = step.k_pool.shape[0]   # a visible slot past the pool
-    out, lse = call_of(ds, step.scale)()
+    out, lse = call_of(ds, step.scale, overlap=mode)()
     torch.cuda.synchronize()
     bad = [1, 2, 5, 12, 13, 14, 15]
     assert torch.isnan(out[bad]).all() and torch.isnan(lse[bad]).all()
@@ -163,12 +174,16 @@ def test_stream_needles_every_visible_position():
     say(f"  stream needles: {runs} runs cover every visible position of every stream")
 
 
-def test_stream_decode_deterministic_and_graph_replay():
+@pytest.mark.parametrize("mode", MODES)
+def test_stream_decode_deterministic_and_graph_replay(mode):
+    """Eager calls agree bit for bit; every replay of a captured step equals them, with
+    eager work (a fill) between replays."""
     cfg = workloads.custom("graph", B=16, Hq=8, Hkv=8, d=128, dtype="bf16",
                            levels=(((500, 0, 16),),), suffix_lo=8, suffix_hi=100)
     step = workloads.stream_step(cfg, P=8, seed=6, answer_len=4)
     ds = dev(step)
-    call = call_of(ds, step.scale)
+    call = call_of(ds, step.scale, overlap=mode)
+    assert call.concurrent == (mode == 2)
     o1, l1 = [t.clone() for t in call()]
     torch.cuda.synchronize()
     s = torch.cuda.Stream()
@@ -181,19 +196,26 @@ def test_stream_decode_deterministic_and_graph_replay():
         g.capture_end()
     for _ in range(3):
         call.out.fill_(5.0)
+        call.lse.fill_(5.0)
         torch.cuda.synchronize()
         g.replay()
         torch.cuda.synchronize()
         assert torch.equal(call.out, o1) and torch.equal(call.lse, l1)
+    ref_o, ref_l = oracle.stream_attention(step)
+    compare(call.out, call.lse, ref_o, ref_l, "bf16", f"graph replay, mode {mode}")
 
 
-def test_stream_decode_full_size_sampled():
+@pytest.mark.parametrize("mode", [0, 1])
+def test_stream_decode_full_size_sampled(mode):
+    """The full-size step in both of the plans the default policy can pick."""
     cfg = workloads.docqa_streams(32)
-    say(f"full {cfg.name}: generating")
+    say(f"full {cfg.name} mode {mode}: generating")
     step = workloads.stream_step(cfg, P=32, seed=0)
     ds = dev(step)
     say(f"full {cfg.name}: running")
-    out, lse = call_of(ds, step.scale)()
+    call = call_of(ds, step.scale, overlap=mode)
+    say(f"  side by side: {call.concurrent}")
+    out, lse = call()
     torch.cuda.synchronize()
     rows = sample_rows(cfg.B, cfg.Hq, 48)
     ref_o, ref_l = oracle.stream_attention(step, rows=rows)
