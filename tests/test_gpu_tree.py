@@ -12,7 +12,7 @@ import torch
 import decode_attention_shared_amd as hp
 import oracle
 import workloads
-from gpu_util import DEV, compare, sample_rows, say
+from gpu_util import DEV, compare, say
 
 pytestmark = pytest.mark.gpu
 
@@ -74,9 +74,11 @@ def test_tree_long_segment_splits():
     say("tree long segment")
     o, l, plan = _run_tree(step, 2)
     assert plan.num_segs == 1 and plan.num_pieces == 313
-    rows = sample_rows(step.B, step.Hq, 48, seed=3)
-    ro, rl = oracle.tree_attention(step, rows=rows)
-    compare(o, l, ro, rl, "bf16", "tree long segment", rows=rows)
+    per = 64  # sequences per oracle pass (each pass gathers their keys from the pool)
+    for b0 in range(0, step.B, per):
+        rows = np.arange(b0 * step.Hq, min(step.B, b0 + per) * step.Hq)
+        ro, rl = oracle.tree_attention(step, rows=rows)
+        compare(o, l, ro, rl, "bf16", f"tree long segment, sequences {b0}..", rows=rows)
 
 
 def test_tree_without_lengths_reads_every_row():
@@ -120,14 +122,19 @@ def test_tree_empty_batch_rows():
 
 # ------------------------------------------------------------- headline shape
 
-def test_tree_codellama13b_16k_sampled():
-    """The 16K-prefix CodeLlama-13B step as 256 root chunks + private suffix chunks."""
+def test_tree_codellama13b_16k_every_row():
+    """The 16K-prefix CodeLlama-13B step as 256 root chunks + private suffix chunks: every
+    row against the oracle, 16 sequences per oracle pass (each pass gathers its
+    sequences' keys from the pool)."""
     step = workloads.chunked_config(workloads.codellama13b_mha(16384), seed=0)
     say("tree codellama13b 16K")
     o, l, plan = _run_tree(step, 2)
-    rows = sample_rows(step.B, step.Hq, 24, seed=0)
-    ro, rl = oracle.tree_attention(step, rows=rows)
-    compare(o, l, ro, rl, "f16", "tree codellama13b 16K", rows=rows)
+    per = 16
+    for b0 in range(0, step.B, per):
+        rows = np.arange(b0 * step.Hq, min(step.B, b0 + per) * step.Hq)
+        ro, rl = oracle.tree_attention(step, rows=rows)
+        compare(o, l, ro, rl, "f16", f"tree codellama13b 16K, sequences {b0}..", rows=rows)
+    say(f"  tree 16K: all {step.B * step.Hq} rows checked")
 
 
 # ------------------------------------------------------------------ append
