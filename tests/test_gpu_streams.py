@@ -225,3 +225,61 @@ def test_stream_decode_full_size_every_row():
     for mode, (out, lse) in outs.items():
         compare(out, lse, ref_o, ref_l, cfg.dtype, f"{cfg.name} mode {mode} (all rows)")
         assert torch.isfinite(out).all() and torch.isfinite(lse).all()
+
+
+def _small_stream_step(seed):
+    cfg = workloads.custom("side", B=24, Hq=8, Hkv=4, d=128, dtype="bf16",
+                           levels=(((700, 0, 24),),), suffix_lo=8, suffix_hi=120)
+    return cfg, workloads.stream_step(cfg, P=6, seed=seed, answer_len=3)
+
+
+def test_stream_side_by_side_orders_with_caller_stream():
+    """Side by side: a change of q enqueued on the caller's stream right before the step
+    is seen by both passes, and a copy enqueued right after it sees the merged result."""
+    cfg, step = _small_stream_step(31)
+    ds = dev(step)
+    call = call_of(ds, step.scale, overlap=2)
+    assert call.concurrent
+    s = torch.cuda.Stream()
+    q0 = step.q.clone()
+    with torch.cuda.stream(s):
+        for rep in range(3):
+            q_rep = (q0.float() * (1.0 + 0.5 * rep)).to(q0.dtype)
+            ds["q"].copy_(q_rep.to(DEV), non_blocking=True)
+            call(stream=s)
+            got_o, got_l = call.out.clone(), call.lse.clone()  # ordered after the merge on s
+            call.out.fill_(5.0)                                 # and before the next step
+            s.synchronize()
+            step.q = q_rep
+            ref_o, ref_l = oracle.stream_attention(step)
+            compare(got_o, got_l, ref_o, ref_l, "bf16", f"stream ordered step {rep}")
+    step.q = q0
+
+
+def test_stream_side_by_side_first_call_captured():
+    """The very first call of a side-by-side stream step may be the one captured into a
+    graph: every replay equals a separate eager step on the same inputs."""
+    cfg, step = _small_stream_step(33)
+    ds = dev(step)
+    ref_call = call_of(ds, step.scale, overlap=2)
+    eager_o, eager_l = [t.clone() for t in ref_call()]
+    torch.cuda.synchronize()
+    call = call_of(ds, step.scale, overlap=2)
+    assert call.concurrent
+    s = torch.cuda.Stream()
+    with torch.cuda.stream(s):
+        g = torch.cuda.CUDAGraph()
+        g.capture_begin()
+        call(stream=s)
+        g.capture_end()
+    for rep in range(4):
+        call.out.fill_(3.0)
+        call.lse.fill_(3.0)
+        torch.cuda.synchronize()
+        g.replay()
+        torch.cuda.synchronize()
+        assert torch.equal(call.out, eager_o) and torch.equal(call.lse, eager_l), f"replay {rep}"
+        ref_call()  # eager work between replays
+        torch.cuda.synchronize()
+    ref_o, ref_l = oracle.stream_attention(step)
+    compare(call.out, call.lse, ref_o, ref_l, "bf16", "stream first call captured")
