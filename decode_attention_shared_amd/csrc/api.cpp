@@ -423,6 +423,16 @@ bool one_launch_ok(const hp_query *q, const hp_paged_kv *kv, const CascadePlan &
 // kFatSplitBlocks blocks and has its own slot of (O, LSE) rows.
 int64_t one_launch_splits(const hp_paged_kv *kv) { return cdiv(kv->max_blocks, kFatSplitBlocks); }
 
+// The prefix pass's compute units beside the suffix pass: kConcCUs, or
+// kConcCUsHeavy when the suffix pass's K/V bound (suffix_kv bytes) is at least
+// kConcHeavyRatio times the batched nodes' K/V.
+int conc_prefix_cus(const hp_query *q, const CascadePlan &cp, int64_t suffix_kv) {
+    int64_t prefix_kv = 0;
+    for (int i = 0; i < cp.total_nodes; ++i)
+        prefix_kv += (int64_t)cp.batched[i].len * q->Hkv * q->d * esize(q->dtype) * 2;
+    return suffix_kv >= kConcHeavyRatio * prefix_kv ? kConcCUsHeavy : kConcCUs;
+}
+
 hp_status plan_cascade(const hp_query *q, const hp_prefix_tree *tree, const hp_paged_kv *kv,
                        int mode, CascadePlan &cp, bool batch_all = false) {
     if (mode < 0 || mode > 3) return HP_ERR_INVALID_ARG;
@@ -492,6 +502,14 @@ hp_status plan_cascade(const hp_query *q, const hp_prefix_tree *tree, const hp_p
         if (one) {
             alt = one_plan;
             pbytes = one_pbytes;
+        } else {
+            const int64_t suffix_kv =
+                (int64_t)q->B * kv->max_blocks * kBlock * q->Hkv * q->d * esize(q->dtype) * 2;
+            const int cus = conc_prefix_cus(q, cp, suffix_kv);
+            if (cus != kConcCUs) {  // the gain test above stays the one at kConcCUs
+                alt = cp;
+                pbytes = plan_prefix(q, tree ? &bt : nullptr, alt, cus);
+            }
         }
         if (mode == 2 || (mode == 1 && pays) || one) {
             // the suffix rows: one slot (second stream) or one per item split
@@ -951,11 +969,18 @@ hp_status plan_stream(const hp_query *q, const hp_prefix_tree *doc, const hp_str
     if (mode != 0 && sp.cp.total_nodes > 0 && q->B > 0) {
         CascadePlan alt = sp.cp;
         const hp_prefix_tree bt = alt.view();
-        const size_t pbytes = plan_prefix(q, &bt, alt, kConcCUs);
+        size_t pbytes = plan_prefix(q, &bt, alt, kConcCUs);
         bool pays = (int64_t)q->B * q->Hkv >= kConcMinUnits;
         for (int l = 0; l < alt.num_levels && pays; ++l)
             for (int i = 0; i < alt.levels[l].count; ++i)
                 pays = pays && alt.levels[l].nodes[i].tiles_per_split >= kConcMinTiles;
+        const int64_t stream_kv =
+            (int64_t)q->B * r->row_cap * q->Hkv * q->d * esize(q->dtype) * 2;
+        const int cus = conc_prefix_cus(q, sp.cp, stream_kv);
+        if (cus != kConcCUs) {  // the gain test above stays the one at kConcCUs
+            alt = sp.cp;
+            pbytes = plan_prefix(q, &bt, alt, cus);
+        }
         if (mode == 2 || pays) {
             sp.cp = alt;
             sp.conc = true;

@@ -114,6 +114,11 @@ constexpr int kConcCUs = 160;
 // one suffix workgroup each).  Measured on the one-GPU head share of the 16K
 // MHA shape: 160 units 52.5 us per step, 192 or 208 units 56.8.
 constexpr int kOneLaunchCUs = 160;
+// Suffix-heavy steps (a bound on the suffix pass's K/V bytes, B * max_blocks
+// blocks, at least kConcHeavyRatio times the batched prefix's K/V bytes) plan
+// the prefix for kConcCUsHeavy units instead, leaving more to the suffix pass.
+constexpr int kConcCUsHeavy = 96;
+constexpr int64_t kConcHeavyRatio = 6;
 constexpr int kConcMinTiles = 4;
 constexpr int64_t kConcMinUnits = 2048;
 
