@@ -267,6 +267,9 @@ hp_status hp_cascade_step(const hp_query *query, const hp_prefix_tree *tree,
  * no node is read privately, the K/V of both passes stay under 256 MiB, and
  * each suffix wave's share fits its tables (at most 31 query rows and 500
  * blocks; the suffix work goes to the waves in items of 4 blocks).
+ * Side by side, the prefix pass is planned for 160 compute units, or for 96
+ * when B * max_blocks suffix blocks hold at least 6 times the K/V bytes of
+ * the batched nodes (the test of mode 1 is made on the 160-unit plan).
  * Everything enqueued on `stream` before the call is ordered before both
  * passes and everything after it after the merge, eagerly and under graph
  * capture alike (the events become the graph's fork and join).  Calls that
@@ -396,7 +399,9 @@ hp_status hp_stream_decode(const hp_query *query, const hp_prefix_tree *doc,
  * partials.  overlap->mode: 0 serial (hp_stream_decode); 1 side by side by
  * the cascade step's rule (the prefix pass planned for 160 compute units,
  * every prefix split at least 4 tiles of 64 keys, at least 2048 (query, KV
- * head) units), else serial; 2 side by side whenever the document has a node.  One launch (mode 3) is
+ * head) units), else serial; 2 side by side whenever the document has a node.
+ * The prefix pass then runs on 96 compute units when B * row_cap row
+ * positions hold at least 6 times the document's K/V bytes, else on 160.  One launch (mode 3) is
  * not offered here.  Ordering, event and stream rules, and errors as for
  * hp_cascade_step_overlap (HP_ERR_INVALID_ARG for mode 3).  The workspace
  * size from hp_stream_decode_workspace_size serves every mode.
