@@ -269,7 +269,12 @@ hp_status hp_cascade_step(const hp_query *query, const hp_prefix_tree *tree,
  * blocks; the suffix work goes to the waves in items of 4 blocks).
  * Side by side, the prefix pass is planned for 160 compute units, or for 96
  * when B * max_blocks suffix blocks hold at least 6 times the K/V bytes of
- * the batched nodes (the test of mode 1 is made on the 160-unit plan).
+ * the batched nodes (the test of mode 1 is made on the 160-unit plan).  The
+ * host cannot read the lengths, so max_blocks stands for the suffix size: a
+ * table cut to the batch's longest suffix (as the workloads here use) keeps
+ * the estimate within about twice the mean; a table far wider than any
+ * suffix can make a prefix-bound step take the 96-unit plan, which is slower
+ * for it (an 8K-token prefix over 256 MHA sequences: 170 against 123 us).
  * Everything enqueued on `stream` before the call is ordered before both
  * passes and everything after it after the merge, eagerly and under graph
  * capture alike (the events become the graph's fork and join).  Calls that
